@@ -1,0 +1,287 @@
+"""ctypes binding of libcsa2.so: the same entry points as include/csa2.h, taking torch
+tensors.  Argument marshalling only: tensors become device pointers, the current torch
+stream becomes the HIP stream, outputs and workspaces are allocated with torch (device
+memory plumbing).  Every step of the path runs in the library's HIP kernels; when the
+library is missing this module raises instead of computing anything itself.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcsa2.so")
+
+CSA2_OK, CSA2_E_ARG, CSA2_E_UNSUPPORTED, CSA2_E_WORKSPACE, CSA2_E_LAUNCH = 0, 1, 2, 3, 4
+F32, BF16, MXFP4, MXFP8_E4M3 = 0, 1, 2, 3
+OP_TOPK, OP_TOPK_HIER, OP_ATTN = 1, 2, 3
+
+# Every symbol include/csa2.h declares.
+EXPORTS = ["csa2_index_score", "csa2_topk", "csa2_topk_hier", "csa2_sparse_swa_attn", "csa2_replay_tail_layout",
+           "csa2_workspace_size", "csa2_last_error", "csa2_version", "csa2_quant_mx"]
+
+
+class Csa2Error(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("csa2 error %d: %s" % (code, msg))
+        self.code = code
+
+
+class _Rows(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int32), ("req_of_row", ctypes.c_void_p), ("pos_of_row", ctypes.c_void_p),
+                ("win_lo", ctypes.c_void_p)]
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("nreq", ctypes.c_int32), ("ratio_m", ctypes.c_int32), ("n_entries", ctypes.c_void_p),
+                ("row_start", ctypes.c_void_p)]
+
+
+class _IndexKeys(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int), ("dim", ctypes.c_int32), ("data", ctypes.c_void_p),
+                ("scale", ctypes.c_void_p)]
+
+
+class _Pool(ctypes.Structure):
+    _fields_ = [("block", ctypes.c_int32), ("max_blocks", ctypes.c_int32), ("blocks", ctypes.c_void_p),
+                ("nblocks", ctypes.c_void_p), ("row_map", ctypes.c_void_p)]
+
+
+class _Swa(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int), ("data", ctypes.c_void_p), ("scale", ctypes.c_void_p),
+                ("row_start", ctypes.c_void_p), ("pos_start", ctypes.c_void_p), ("window", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libcsa2.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libcsa2.so is not built (%s); run __graft_entry__.build() or "
+                               "python -m compressed_sparse_attention_fp4_amd.build_lib" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        L.csa2_last_error.restype = ctypes.c_char_p
+        L.csa2_workspace_size.restype = ctypes.c_size_t
+        L.csa2_workspace_size.argtypes = [ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                          ctypes.c_int32]
+        _lib = L
+    return _lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    assert t.is_contiguous(), "tensors passed to libcsa2 must be contiguous"
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        if not torch.cuda.is_available():
+            return None
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(rc: int):
+    if rc != CSA2_OK:
+        raise Csa2Error(rc, lib().csa2_last_error().decode())
+
+
+# ------------------------------------------------------------------ descriptors
+@dataclass
+class Rows:
+    req_of_row: torch.Tensor           # int32 [n]
+    pos_of_row: torch.Tensor           # int32 [n]
+    win_lo: Optional[torch.Tensor] = None
+
+    def c(self):
+        return _Rows(self.req_of_row.numel(), _ptr(self.req_of_row), _ptr(self.pos_of_row), _ptr(self.win_lo))
+
+    @property
+    def n(self):
+        return self.req_of_row.numel()
+
+
+@dataclass
+class Cache:
+    ratio_m: int
+    n_entries: torch.Tensor            # int32 [nreq]
+    row_start: torch.Tensor            # int64 [nreq]
+
+    def c(self):
+        return _Cache(self.n_entries.numel(), self.ratio_m, _ptr(self.n_entries), _ptr(self.row_start))
+
+
+@dataclass
+class IndexKeys:
+    data: torch.Tensor                 # uint8 [rows, dim/2] (MXFP4) or float32 [rows, dim]
+    scale: Optional[torch.Tensor]      # uint8 [rows, dim/32] or None
+    dim: int
+
+    def c(self):
+        dt = MXFP4 if self.scale is not None else F32
+        return _IndexKeys(dt, self.dim, _ptr(self.data), _ptr(self.scale))
+
+
+@dataclass
+class Pool:
+    blocks: torch.Tensor               # int32 [prows, max_blocks]
+    nblocks: torch.Tensor              # int32 [prows]
+    block: int = 8
+    row_map: Optional[torch.Tensor] = None
+
+    @property
+    def max_blocks(self):
+        return self.blocks.shape[1]
+
+    def c(self):
+        return _Pool(self.block, self.max_blocks, _ptr(self.blocks), _ptr(self.nblocks), _ptr(self.row_map))
+
+
+@dataclass
+class Window:
+    data: torch.Tensor                 # [rows, dim]: uint8 codes (MXFP8), bfloat16 or float32
+    scale: Optional[torch.Tensor]      # uint8 [rows, dim/32] for MXFP8
+    row_start: torch.Tensor            # int64 [nreq]
+    pos_start: torch.Tensor            # int32 [nreq]
+    window: int = 128
+
+    @property
+    def dtype(self):
+        if self.scale is not None:
+            return MXFP8_E4M3
+        return BF16 if self.data.dtype == torch.bfloat16 else F32
+
+    def c(self):
+        return _Swa(self.dtype, _ptr(self.data), _ptr(self.scale), _ptr(self.row_start), _ptr(self.pos_start),
+                    self.window)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError("unsupported tensor dtype %s" % t.dtype)
+
+
+# ---------------------------------------------------------------- entry points
+def index_score(rows: Rows, cache: Cache, q_idx: torch.Tensor, w: torch.Tensor, keys: IndexKeys,
+                pool: Optional[Pool] = None, score_stride: Optional[int] = None, scores: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    """csa2_index_score.  q_idx [n, heads, dim]; w [n, heads] or [heads] (shared)."""
+    n, heads = q_idx.shape[0], q_idx.shape[1]
+    if scores is None:
+        if score_stride is None:
+            raise ValueError("score_stride or scores is required")
+        scores = torch.empty((n, score_stride), dtype=torch.float32, device=q_idx.device)
+    w_stride = 0 if w.dim() == 1 else w.stride(0)
+    rc = lib().csa2_index_score(ctypes.byref(rows.c()), ctypes.byref(cache.c()), _ptr(q_idx),
+                                ctypes.c_int(_dtype_code(q_idx)), ctypes.c_int32(heads), _ptr(w),
+                                ctypes.c_int64(w_stride), ctypes.byref(keys.c()),
+                                ctypes.byref(pool.c()) if pool is not None else None, _ptr(scores),
+                                ctypes.c_int64(scores.stride(0)), _stream(stream))
+    _check(rc)
+    return scores
+
+
+def workspace_size(op: int, n: int, cols: int, k: int, max_blocks: int = 0) -> int:
+    return int(lib().csa2_workspace_size(op, n, cols, k, max_blocks))
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=device)
+
+
+def topk(rows: Rows, cache: Cache, scores: torch.Tensor, k: int, pool: Optional[Pool] = None,
+         out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """csa2_topk: int32 [n, k] ascending positions, -1 padded."""
+    n = rows.n
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.int32, device=scores.device)
+    cols = pool.block * pool.max_blocks if pool is not None else scores.stride(0)
+    if workspace is None:
+        workspace = _workspace(workspace_size(OP_TOPK, n, cols, k), scores.device)
+    rc = lib().csa2_topk(ctypes.byref(rows.c()), ctypes.byref(cache.c()), _ptr(scores),
+                         ctypes.c_int64(scores.stride(0)), ctypes.byref(pool.c()) if pool is not None else None,
+                         ctypes.c_int32(k), _ptr(out), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+                         _stream(stream))
+    _check(rc)
+    return out
+
+
+def topk_hier(rows: Rows, cache: Cache, scores: torch.Tensor, k: int, block: int = 8, max_blocks: int = 2048,
+              workspace: Optional[torch.Tensor] = None, stream=None):
+    """csa2_topk_hier: (flat top-k [n, k], pool blocks [n, max_blocks], pool nblocks [n])."""
+    n = rows.n
+    dev = scores.device
+    idx = torch.empty((n, k), dtype=torch.int32, device=dev)
+    blocks = torch.empty((n, max_blocks), dtype=torch.int32, device=dev)
+    nblocks = torch.empty((n,), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = _workspace(workspace_size(OP_TOPK_HIER, n, scores.stride(0), k, max_blocks), dev)
+    rc = lib().csa2_topk_hier(ctypes.byref(rows.c()), ctypes.byref(cache.c()), _ptr(scores),
+                              ctypes.c_int64(scores.stride(0)), ctypes.c_int32(k), ctypes.c_int32(block),
+                              ctypes.c_int32(max_blocks), _ptr(idx), _ptr(blocks), _ptr(nblocks), _ptr(workspace),
+                              ctypes.c_size_t(workspace.numel()), _stream(stream))
+    _check(rc)
+    return idx, blocks, nblocks
+
+
+def sparse_swa_attn(rows: Rows, cache: Cache, q: torch.Tensor, kv: torch.Tensor, sel_idx: Optional[torch.Tensor],
+                    window: Window, sm_scale: float, sel_row_map: Optional[torch.Tensor] = None,
+                    sink: Optional[torch.Tensor] = None, want_lse: bool = False, out: Optional[torch.Tensor] = None,
+                    stream=None):
+    """csa2_sparse_swa_attn: out [n, heads, dim] (q's dtype), and lse [n, heads] if asked."""
+    n, heads, dim = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    lse = torch.empty((n, heads), dtype=torch.float32, device=q.device) if want_lse else None
+    k = 0 if sel_idx is None else sel_idx.shape[1]
+    sel_stride = 0 if sel_idx is None else sel_idx.stride(0)
+    rc = lib().csa2_sparse_swa_attn(ctypes.byref(rows.c()), ctypes.byref(cache.c()), _ptr(q),
+                                    ctypes.c_int(_dtype_code(q)), ctypes.c_int32(heads), ctypes.c_int32(dim), _ptr(kv),
+                                    ctypes.c_int(_dtype_code(kv)), _ptr(sel_idx), ctypes.c_int32(k),
+                                    ctypes.c_int64(sel_stride), _ptr(sel_row_map), ctypes.byref(window.c()),
+                                    ctypes.c_float(sm_scale), _ptr(sink), _ptr(out), ctypes.c_int(_dtype_code(out)),
+                                    _ptr(lse), None, ctypes.c_size_t(0), _stream(stream))
+    _check(rc)
+    return (out, lse) if want_lse else out
+
+
+def replay_tail_layout(ext_len: torch.Tensor, seq_len: torch.Tensor, budget: int = 128, stream=None) -> dict:
+    """csa2_replay_tail_layout; returns device tensors sized for budget * nreq rows."""
+    nreq = ext_len.numel()
+    dev = ext_len.device
+    cap = budget * nreq
+    t = dict(tail_len=torch.empty(nreq, dtype=torch.int32, device=dev),
+             tail_row_start=torch.empty(nreq + 1, dtype=torch.int32, device=dev))
+    for name in ("src_row", "abs_pos", "win_lo", "req_of_row"):
+        t[name] = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    rc = lib().csa2_replay_tail_layout(ctypes.c_int32(nreq), _ptr(ext_len), _ptr(seq_len), ctypes.c_int32(budget),
+                                       _ptr(t["tail_len"]), _ptr(t["tail_row_start"]), _ptr(t["src_row"]),
+                                       _ptr(t["abs_pos"]), _ptr(t["win_lo"]), _ptr(t["req_of_row"]),
+                                       ctypes.c_int32(cap), _stream(stream))
+    _check(rc)
+    return t
+
+
+def quant_mx(fmt: int, x: torch.Tensor, stream=None):
+    """csa2_quant_mx over the last axis of x (multiple of 32): (codes uint8, scales uint8)."""
+    assert x.shape[-1] % 32 == 0
+    d = x.shape[-1]
+    nblocks = x.numel() // 32
+    codes = torch.empty(x.shape[:-1] + ((d // 2) if fmt == MXFP4 else d,), dtype=torch.uint8, device=x.device)
+    scales = torch.empty(x.shape[:-1] + (d // 32,), dtype=torch.uint8, device=x.device)
+    rc = lib().csa2_quant_mx(ctypes.c_int(fmt), _ptr(x), ctypes.c_int(_dtype_code(x)), ctypes.c_int64(nblocks),
+                             _ptr(codes), _ptr(scales), _stream(stream))
+    _check(rc)
+    return codes, scales

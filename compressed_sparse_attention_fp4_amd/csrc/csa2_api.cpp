@@ -1,0 +1,296 @@
+// C ABI of the CSA2 hot path: argument validation, workspace sizing and dispatch to
+// the gfx950 kernels.  Every check on scalar or host-visible arguments happens before
+// any HIP call, so argument errors are reported identically with or without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/csa2.h"
+#include "csa2_launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok()
+{
+    g_err.clear();
+    return CSA2_OK;
+}
+
+int launch_result(hipError_t e, const char* what)
+{
+    if (e != hipSuccess) return fail(CSA2_E_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+// The kernels use gfx950 instructions (scaled FP4 MFMA, lane swaps): refuse others.
+int check_device()
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(CSA2_E_LAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
+    static std::mutex mu;
+    static int known[64] = {0};  // 0 unknown, 1 gfx950, 2 other
+    if (dev < 0 || dev >= 64) return fail(CSA2_E_UNSUPPORTED, "device index %d out of range", dev);
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        if (known[dev] == 0) {
+            hipDeviceProp_t prop;
+            e = hipGetDeviceProperties(&prop, dev);
+            if (e != hipSuccess) return fail(CSA2_E_LAUNCH, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+            known[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        }
+        if (known[dev] != 1) return fail(CSA2_E_UNSUPPORTED, "device %d is not gfx950", dev);
+    }
+    return CSA2_OK;
+}
+
+int check_rows(const csa2_rows* rows)
+{
+    if (!rows) return fail(CSA2_E_ARG, "rows is NULL");
+    if (rows->n < 0) return fail(CSA2_E_ARG, "rows->n = %d < 0", rows->n);
+    if (rows->n > 0 && (!rows->req_of_row || !rows->pos_of_row))
+        return fail(CSA2_E_ARG, "rows->req_of_row / pos_of_row is NULL");
+    return CSA2_OK;
+}
+
+int check_cache(const csa2_cache* cache)
+{
+    if (!cache) return fail(CSA2_E_ARG, "cache is NULL");
+    if (cache->nreq < 1) return fail(CSA2_E_ARG, "cache->nreq = %d < 1", cache->nreq);
+    if (cache->ratio_m != 1 && cache->ratio_m != 2)
+        return fail(CSA2_E_UNSUPPORTED, "cache->ratio_m = %d (1 or 2)", cache->ratio_m);
+    if (!cache->n_entries || !cache->row_start) return fail(CSA2_E_ARG, "cache->n_entries / row_start is NULL");
+    return CSA2_OK;
+}
+
+int check_pool(const csa2_pool* pool, int64_t score_stride)
+{
+    if (!pool) return CSA2_OK;
+    if (!pool->blocks || !pool->nblocks) return fail(CSA2_E_ARG, "pool->blocks / nblocks is NULL");
+    if (pool->block < 1 || pool->block > 64) return fail(CSA2_E_ARG, "pool->block = %d (1..64)", pool->block);
+    if (pool->max_blocks < 1 || pool->max_blocks > 65536)
+        return fail(CSA2_E_ARG, "pool->max_blocks = %d (1..65536)", pool->max_blocks);
+    if ((int64_t)pool->block * pool->max_blocks > score_stride)
+        return fail(CSA2_E_ARG, "pool columns %lld exceed score_stride %lld",
+                    (long long)pool->block * pool->max_blocks, (long long)score_stride);
+    return CSA2_OK;
+}
+
+csa2::RowsArg rows_arg(const csa2_rows* r) { return csa2::RowsArg{r->n, r->req_of_row, r->pos_of_row, r->win_lo}; }
+csa2::CacheArg cache_arg(const csa2_cache* c) { return csa2::CacheArg{c->ratio_m, c->n_entries, c->row_start}; }
+csa2::PoolArg pool_arg(const csa2_pool* p)
+{
+    if (!p) return csa2::PoolArg{nullptr, nullptr, nullptr, 0, 0};
+    return csa2::PoolArg{p->blocks, p->nblocks, p->row_map, p->block, p->max_blocks};
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* csa2_last_error(void) { return g_err.c_str(); }
+
+int csa2_version(void) { return CSA2_VERSION; }
+
+size_t csa2_workspace_size(int op, int32_t n, int64_t cols, int32_t k, int32_t max_blocks)
+{
+    if (n <= 0 || cols <= 0) return 0;
+    switch (op) {
+        case CSA2_OP_TOPK:
+            return csa2::topk_workspace(n, cols, k);
+        case CSA2_OP_TOPK_HIER:
+            return csa2::topk_hier_workspace(n, cols, k, 8, max_blocks > 0 ? max_blocks : 1);
+        case CSA2_OP_ATTN:
+            return 0;
+        default:
+            return 0;
+    }
+}
+
+int csa2_index_score(const csa2_rows* rows, const csa2_cache* cache, const void* q_idx, csa2_dtype q_dtype,
+                     int32_t heads, const float* w, int64_t w_row_stride, const csa2_index_keys* keys,
+                     const csa2_pool* pool, float* scores, int64_t score_stride, void* stream)
+{
+    int rc;
+    if ((rc = check_rows(rows)) || (rc = check_cache(cache))) return rc;
+    if (!keys) return fail(CSA2_E_ARG, "keys is NULL");
+    if (!q_idx || !w || !scores || !keys->data) return fail(CSA2_E_ARG, "q_idx / w / scores / keys->data is NULL");
+    if (score_stride < 1) return fail(CSA2_E_ARG, "score_stride = %lld < 1", (long long)score_stride);
+    if (w_row_stride < 0) return fail(CSA2_E_ARG, "w_row_stride < 0");
+    if ((rc = check_pool(pool, score_stride))) return rc;
+    if (keys->dtype == CSA2_MXFP4) {
+        if (q_dtype != CSA2_BF16) return fail(CSA2_E_UNSUPPORTED, "MXFP4 keys need a BF16 index q");
+        if (keys->dim != 128) return fail(CSA2_E_UNSUPPORTED, "MXFP4 keys: dim %d (128 supported)", keys->dim);
+        if (!keys->scale) return fail(CSA2_E_ARG, "MXFP4 keys without a scale plane");
+        if (heads < 16 || heads > 128 || heads % 16)
+            return fail(CSA2_E_UNSUPPORTED, "MXFP4 scoring: heads %d (multiple of 16, at most 128)", heads);
+        if (w_row_stride != 0 && w_row_stride < heads) return fail(CSA2_E_ARG, "w_row_stride < heads");
+    } else if (keys->dtype == CSA2_F32) {
+        if (q_dtype != CSA2_F32) return fail(CSA2_E_UNSUPPORTED, "F32 keys need an F32 index q");
+        if (keys->dim < 1 || keys->dim > 1024) return fail(CSA2_E_UNSUPPORTED, "F32 keys: dim %d", keys->dim);
+        if (heads < 4 || heads > 128 || heads % 4)
+            return fail(CSA2_E_UNSUPPORTED, "F32 scoring: heads %d (multiple of 4, at most 128)", heads);
+        if (w_row_stride != 0 && w_row_stride < heads) return fail(CSA2_E_ARG, "w_row_stride < heads");
+    } else {
+        return fail(CSA2_E_UNSUPPORTED, "index key dtype %d", (int)keys->dtype);
+    }
+    if (rows->n == 0) return ok();
+    if ((rc = check_device())) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (keys->dtype == CSA2_MXFP4)
+        return launch_result(csa2::launch_index_score_mxfp4(rows_arg(rows), cache_arg(cache),
+                                                            static_cast<const uint16_t*>(q_idx), heads, w,
+                                                            w_row_stride, static_cast<const uint8_t*>(keys->data),
+                                                            keys->scale, pool_arg(pool), scores, score_stride, s),
+                             "csa2_index_score");
+    return launch_result(csa2::launch_index_score_f32(rows_arg(rows), cache_arg(cache), static_cast<const float*>(q_idx),
+                                                      heads, keys->dim, w, w_row_stride,
+                                                      static_cast<const float*>(keys->data), pool_arg(pool), scores,
+                                                      score_stride, s),
+                         "csa2_index_score");
+}
+
+int csa2_topk(const csa2_rows* rows, const csa2_cache* cache, const float* scores, int64_t score_stride,
+              const csa2_pool* pool, int32_t k, int32_t* out_idx, void* workspace, size_t workspace_bytes,
+              void* stream)
+{
+    int rc;
+    if ((rc = check_rows(rows)) || (rc = check_cache(cache))) return rc;
+    if (!scores || !out_idx) return fail(CSA2_E_ARG, "scores / out_idx is NULL");
+    if (k < 1 || k > 2048) return fail(CSA2_E_ARG, "k = %d (1..2048)", k);
+    if (score_stride < 1) return fail(CSA2_E_ARG, "score_stride = %lld < 1", (long long)score_stride);
+    if ((rc = check_pool(pool, score_stride))) return rc;
+    const int64_t cols = pool ? (int64_t)pool->block * pool->max_blocks : score_stride;
+    const size_t need = csa2::topk_workspace(rows->n, cols, k);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(CSA2_E_WORKSPACE, "csa2_topk needs %zu workspace bytes, got %zu", need, workspace_bytes);
+    if (rows->n == 0) return ok();
+    if ((rc = check_device())) return rc;
+    csa2::SelSource src{scores, score_stride, rows_arg(rows), cache_arg(cache), pool_arg(pool)};
+    return launch_result(csa2::launch_topk(src, k, out_idx, workspace, workspace_bytes, static_cast<hipStream_t>(stream)),
+                         "csa2_topk");
+}
+
+int csa2_topk_hier(const csa2_rows* rows, const csa2_cache* cache, const float* scores, int64_t score_stride,
+                   int32_t k, int32_t block, int32_t max_blocks, int32_t* out_idx, int32_t* out_pool_blocks,
+                   int32_t* out_pool_nblocks, void* workspace, size_t workspace_bytes, void* stream)
+{
+    int rc;
+    if ((rc = check_rows(rows)) || (rc = check_cache(cache))) return rc;
+    if (!scores || !out_idx || !out_pool_blocks || !out_pool_nblocks)
+        return fail(CSA2_E_ARG, "scores / out_idx / out_pool_blocks / out_pool_nblocks is NULL");
+    if (k < 1 || k > 2048) return fail(CSA2_E_ARG, "k = %d (1..2048)", k);
+    if (block != 8) return fail(CSA2_E_UNSUPPORTED, "block = %d (8 supported)", block);
+    if (max_blocks < 1 || max_blocks > 4096) return fail(CSA2_E_ARG, "max_blocks = %d (1..4096)", max_blocks);
+    if (score_stride < 1) return fail(CSA2_E_ARG, "score_stride = %lld < 1", (long long)score_stride);
+    const size_t need = csa2::topk_hier_workspace(rows->n, score_stride, k, block, max_blocks);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(CSA2_E_WORKSPACE, "csa2_topk_hier needs %zu workspace bytes, got %zu", need, workspace_bytes);
+    if (rows->n == 0) return ok();
+    if ((rc = check_device())) return rc;
+    csa2::SelSource src{scores, score_stride, rows_arg(rows), cache_arg(cache), pool_arg(nullptr)};
+    return launch_result(csa2::launch_topk_hier(src, k, block, max_blocks, out_idx, out_pool_blocks, out_pool_nblocks,
+                                                workspace, workspace_bytes, static_cast<hipStream_t>(stream)),
+                         "csa2_topk_hier");
+}
+
+int csa2_sparse_swa_attn(const csa2_rows* rows, const csa2_cache* cache, const void* q, csa2_dtype q_dtype,
+                         int32_t heads, int32_t dim, const void* kv, csa2_dtype kv_dtype, const int32_t* sel_idx,
+                         int32_t k, int64_t sel_stride, const int32_t* sel_row_map, const csa2_swa* swa,
+                         float sm_scale, const float* sink, void* out, csa2_dtype out_dtype, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream)
+{
+    (void)workspace;
+    (void)workspace_bytes;
+    int rc;
+    if ((rc = check_rows(rows)) || (rc = check_cache(cache))) return rc;
+    if (!q || !kv || !out || !swa) return fail(CSA2_E_ARG, "q / kv / out / swa is NULL");
+    if (k < 0 || k > 2048) return fail(CSA2_E_ARG, "k = %d (0..2048)", k);
+    if (k > 0 && !sel_idx) return fail(CSA2_E_ARG, "sel_idx is NULL with k = %d", k);
+    if (k > sel_stride) return fail(CSA2_E_ARG, "k = %d exceeds sel_stride %lld", k, (long long)sel_stride);
+    if (!swa->data || !swa->row_start || !swa->pos_start) return fail(CSA2_E_ARG, "swa data / row_start / pos_start is NULL");
+    if (swa->window < 1 || swa->window > 4096) return fail(CSA2_E_ARG, "swa->window = %d (1..4096)", swa->window);
+    if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return fail(CSA2_E_ARG, "sm_scale must be positive and finite");
+    if (heads < 1 || dim < 1) return fail(CSA2_E_ARG, "heads / dim < 1");
+    const bool f32 = q_dtype == CSA2_F32 && kv_dtype == CSA2_F32 && swa->dtype == CSA2_F32 && out_dtype == CSA2_F32;
+    const bool bf = q_dtype == CSA2_BF16 && kv_dtype == CSA2_BF16 &&
+                    (swa->dtype == CSA2_MXFP8_E4M3 || swa->dtype == CSA2_BF16) && out_dtype == CSA2_BF16;
+    if (f32) {
+        if (dim > 256) return fail(CSA2_E_UNSUPPORTED, "F32 attention: dim %d > 256", dim);
+        if (heads > 1024) return fail(CSA2_E_UNSUPPORTED, "F32 attention: heads %d > 1024", heads);
+    } else if (bf) {
+        if (dim != 512) return fail(CSA2_E_UNSUPPORTED, "BF16 attention: dim %d (512 supported)", dim);
+        if (heads % 16 || heads > 1024) return fail(CSA2_E_UNSUPPORTED, "BF16 attention: heads %d (multiple of 16)", heads);
+        if (swa->dtype == CSA2_MXFP8_E4M3 && !swa->scale) return fail(CSA2_E_ARG, "MXFP8 window without scales");
+    } else {
+        return fail(CSA2_E_UNSUPPORTED, "attention dtypes (q %d, kv %d, window %d, out %d)", (int)q_dtype,
+                    (int)kv_dtype, (int)swa->dtype, (int)out_dtype);
+    }
+    if (rows->n == 0) return ok();
+    if ((rc = check_device())) return rc;
+    csa2::SwaArg sa{(int)swa->dtype, swa->data, swa->scale, swa->row_start, swa->pos_start, swa->window};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (f32)
+        return launch_result(csa2::launch_attn_f32(rows_arg(rows), cache_arg(cache), static_cast<const float*>(q), heads,
+                                                   dim, static_cast<const float*>(kv), sel_idx, k, sel_stride,
+                                                   sel_row_map, sa, sm_scale, sink, static_cast<float*>(out), lse, s),
+                             "csa2_sparse_swa_attn");
+    return launch_result(csa2::launch_attn_bf16(rows_arg(rows), cache_arg(cache), static_cast<const uint16_t*>(q), heads,
+                                                static_cast<const uint16_t*>(kv), sel_idx, k, sel_stride, sel_row_map,
+                                                sa, sm_scale, sink, static_cast<uint16_t*>(out), lse, s),
+                         "csa2_sparse_swa_attn");
+}
+
+int csa2_replay_tail_layout(int32_t nreq, const int32_t* ext_len, const int32_t* seq_len, int32_t budget,
+                            int32_t* tail_len, int32_t* tail_row_start, int32_t* src_row, int32_t* abs_pos,
+                            int32_t* win_lo, int32_t* req_of_row, int32_t capacity, void* stream)
+{
+    if (nreq < 0) return fail(CSA2_E_ARG, "nreq = %d < 0", nreq);
+    if (budget < 1) return fail(CSA2_E_ARG, "budget = %d < 1", budget);
+    if (!tail_row_start) return fail(CSA2_E_ARG, "tail_row_start is NULL");
+    if (nreq > 0 && (!ext_len || !seq_len || !tail_len || !src_row || !abs_pos || !win_lo || !req_of_row))
+        return fail(CSA2_E_ARG, "a tail-layout array is NULL");
+    if ((int64_t)capacity < (int64_t)budget * nreq)
+        return fail(CSA2_E_ARG, "capacity %d < budget %d x nreq %d", capacity, budget, nreq);
+    if ((int64_t)budget * nreq > 0x7FFFFFFF) return fail(CSA2_E_ARG, "budget x nreq overflows int32");
+    int rc;
+    if ((rc = check_device())) return rc;
+    return launch_result(csa2::launch_replay_tail_layout(nreq, ext_len, seq_len, budget, tail_len, tail_row_start,
+                                                         src_row, abs_pos, win_lo, req_of_row,
+                                                         static_cast<hipStream_t>(stream)),
+                         "csa2_replay_tail_layout");
+}
+
+int csa2_quant_mx(csa2_dtype fmt, const void* x, csa2_dtype x_dtype, int64_t nblocks, uint8_t* codes,
+                  uint8_t* scales, void* stream)
+{
+    if (fmt != CSA2_MXFP4 && fmt != CSA2_MXFP8_E4M3) return fail(CSA2_E_UNSUPPORTED, "fmt %d", (int)fmt);
+    if (x_dtype != CSA2_F32 && x_dtype != CSA2_BF16) return fail(CSA2_E_UNSUPPORTED, "x_dtype %d", (int)x_dtype);
+    if (nblocks < 0) return fail(CSA2_E_ARG, "nblocks < 0");
+    if (nblocks > 0 && (!x || !codes || !scales)) return fail(CSA2_E_ARG, "x / codes / scales is NULL");
+    if (nblocks == 0) return ok();
+    int rc;
+    if ((rc = check_device())) return rc;
+    return launch_result(csa2::launch_quant_mx(fmt == CSA2_MXFP4, x_dtype == CSA2_BF16, x, nblocks, codes, scales,
+                                               static_cast<hipStream_t>(stream)),
+                         "csa2_quant_mx");
+}
+
+}  // extern "C"

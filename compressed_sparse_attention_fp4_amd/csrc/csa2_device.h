@@ -1,0 +1,131 @@
+// Device helpers shared by the CSA2 kernels (gfx950 only).
+//
+// Formats are the OCP Microscaling (MX) v1.0 ones the pages name ("DeepSeek V4.1
+// Flash modeling", section "Mixed precision": index Q/K in MXFP4 with 32-element
+// groups, window KV in FP8).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// Entries of a request visible to the query at position p ("DeepSeek V4.1 Flash
+// modeling", section "CSA2": non-overlapping groups of m tokens, complete groups only;
+// entry j covers tokens [j*m, j*m+m-1] and is visible iff j*m+m-1 <= p).
+__device__ __forceinline__ int64_t reach(int p, int m, int n_entries)
+{
+    int64_t r = ((int64_t)p + 1) / m;
+    return r < n_entries ? r : (int64_t)n_entries;
+}
+
+// floor(log2(a)) of a finite a > 0, subnormals included.
+__device__ __forceinline__ int floor_log2(float a)
+{
+    uint32_t u = __float_as_uint(a);
+    int e = (int)((u >> 23) & 0xFF);
+    if (e == 0) return (31 - __clz(u & 0x7FFFFF)) - 149;
+    return e - 127;
+}
+
+// Shared MX exponent of a block with max magnitude amax: floor(log2 amax) - emax,
+// clamped to the E8M0 range; an all-zero block gets -127.
+__device__ __forceinline__ int mx_shared_exp(float amax, int emax)
+{
+    if (amax == 0.0f) return -127;
+    int e = floor_log2(amax) - emax;
+    return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// E2M1 magnitude code of y >= 0, rounded to nearest with ties to the even code and
+// saturated at 6: the grid is {0, .5, 1, 1.5, 2, 3, 4, 6}; the decision points are
+// the midpoints, and at a midpoint the even code wins.
+__device__ __forceinline__ uint32_t e2m1_code(float y)
+{
+    uint32_t c = 0;
+    c = (y > 0.25f) ? 1u : c;
+    c = (y >= 0.75f) ? 2u : c;
+    c = (y > 1.25f) ? 3u : c;
+    c = (y >= 1.75f) ? 4u : c;
+    c = (y > 2.5f) ? 5u : c;
+    c = (y >= 3.5f) ? 6u : c;
+    c = (y > 5.0f) ? 7u : c;
+    return c;
+}
+
+// E4M3 ("fn") magnitude code of 0 <= y, rounded to nearest even, saturated at 448.
+// Below 2^-6 the grid step is 2^-9 (subnormals; code = y / 2^-9 also lands on the
+// first normal code 8); above, the code is the biased exponent and 3 mantissa bits
+// of y rounded at 2^(E-3), a carry into the exponent field being the next binade.
+__device__ __forceinline__ uint32_t e4m3_code(float y)
+{
+    y = fminf(y, 448.0f);
+    if (y < 0.015625f) return (uint32_t)__builtin_rintf(y * 512.0f);
+    int E = floor_log2(y);
+    float mant = __builtin_ldexpf(y, -E) - 1.0f;          // [0, 1), exact
+    uint32_t m = (uint32_t)__builtin_rintf(mant * 8.0f);  // 0..8
+    return ((uint32_t)(E + 7) << 3) + m;
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Quantize one 32-element block to MXFP4: 16 packed bytes (element 2i in the low
+// nibble) returned as 4 dwords, and the E8M0 byte.  The sign bit follows x.
+__device__ __forceinline__ void quant_block_e2m1(const float* x, uint32_t out[4], uint32_t* scale_byte)
+{
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; i++) amax = fmaxf(amax, fabsf(x[i]));
+    int e = mx_shared_exp(amax, 2);
+    *scale_byte = (uint32_t)(e + 127);
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            float v = x[w * 8 + j];
+            uint32_t c = e2m1_code(__builtin_ldexpf(fabsf(v), -e));
+            c |= (__float_as_uint(v) >> 28) & 8u;
+            word |= c << (4 * j);
+        }
+        out[w] = word;
+    }
+}
+
+// Quantize one 32-element block to MXFP8 E4M3: 32 code bytes as 8 dwords, E8M0 byte.
+__device__ __forceinline__ void quant_block_e4m3(const float* x, uint32_t out[8], uint32_t* scale_byte)
+{
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; i++) amax = fmaxf(amax, fabsf(x[i]));
+    int e = mx_shared_exp(amax, 8);
+    *scale_byte = (uint32_t)(e + 127);
+#pragma unroll
+    for (int w = 0; w < 8; w++) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            float v = x[w * 4 + j];
+            uint32_t c = e4m3_code(__builtin_ldexpf(fabsf(v), -e));
+            c |= (__float_as_uint(v) >> 24) & 0x80u;
+            word |= c << (8 * j);
+        }
+        out[w] = word;
+    }
+}
+
+// Monotone map of a non-NaN float to uint32 (larger float -> larger key, -0 == +0).
+// Every non-NaN value maps above 0, so 0 marks "no candidate".
+__device__ __forceinline__ uint32_t order_key(float s)
+{
+    uint32_t u = __float_as_uint(s);
+    if (u == 0x80000000u) u = 0;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace csa2

@@ -1,0 +1,83 @@
+// Internal launchers of the CSA2 kernels (host side).  The C ABI in csa2_api.cpp
+// validates arguments and calls these; each returns the launch's hipError_t.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+// Row / cache / pool descriptors flattened for kernel arguments.
+struct RowsArg {
+    int n;
+    const int32_t* req;
+    const int32_t* pos;
+    const int32_t* win_lo;  // may be null
+};
+
+struct CacheArg {
+    int ratio_m;
+    const int32_t* n_entries;
+    const int64_t* row_start;
+};
+
+struct PoolArg {
+    const int32_t* blocks;   // null: full range
+    const int32_t* nblocks;
+    const int32_t* row_map;  // may be null
+    int block;
+    int max_blocks;
+};
+
+hipError_t launch_replay_tail_layout(int nreq, const int32_t* ext_len, const int32_t* seq_len, int budget,
+                                     int32_t* tail_len, int32_t* tail_row_start, int32_t* src_row,
+                                     int32_t* abs_pos, int32_t* win_lo, int32_t* req_of_row, hipStream_t stream);
+
+hipError_t launch_quant_mx(bool fp4, bool bf16_in, const void* x, int64_t nblocks, uint8_t* codes,
+                           uint8_t* scales, hipStream_t stream);
+
+// Index scores.  MXFP4 path: q bf16 [n][heads][128]; F32 path: q, keys fp32.
+hipError_t launch_index_score_mxfp4(const RowsArg& rows, const CacheArg& cache, const uint16_t* q, int heads,
+                                    const float* w, int64_t w_stride, const uint8_t* kdata, const uint8_t* kscale,
+                                    const PoolArg& pool, float* scores, int64_t stride, hipStream_t stream);
+hipError_t launch_index_score_f32(const RowsArg& rows, const CacheArg& cache, const float* q, int heads, int dim,
+                                  const float* w, int64_t w_stride, const float* keys, const PoolArg& pool,
+                                  float* scores, int64_t stride, hipStream_t stream);
+
+// Selection.  Source of the candidate rows of a top-k.
+struct SelSource {
+    const float* scores;
+    int64_t stride;
+    RowsArg rows;
+    CacheArg cache;
+    PoolArg pool;  // pool.blocks non-null: candidates are the row's pool columns
+};
+
+size_t topk_workspace(int n, int64_t stride, int k);
+hipError_t launch_topk(const SelSource& src, int k, int32_t* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+size_t topk_hier_workspace(int n, int64_t stride, int k, int block, int max_blocks);
+hipError_t launch_topk_hier(const SelSource& src, int k, int block, int max_blocks, int32_t* out_idx,
+                            int32_t* out_blocks, int32_t* out_nblocks, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+// Attention.
+struct SwaArg {
+    int dtype;  // 0 f32, 1 bf16, 3 mxfp8
+    const void* data;
+    const uint8_t* scale;
+    const int64_t* row_start;
+    const int32_t* pos_start;
+    int window;
+};
+
+hipError_t launch_attn_f32(const RowsArg& rows, const CacheArg& cache, const float* q, int heads, int dim,
+                           const float* kv, const int32_t* sel, int k, int64_t sel_stride, const int32_t* sel_row_map,
+                           const SwaArg& swa, float sm_scale, const float* sink, float* out, float* lse,
+                           hipStream_t stream);
+hipError_t launch_attn_bf16(const RowsArg& rows, const CacheArg& cache, const uint16_t* q, int heads,
+                            const uint16_t* kv, const int32_t* sel, int k, int64_t sel_stride,
+                            const int32_t* sel_row_map, const SwaArg& swa, float sm_scale, const float* sink,
+                            uint16_t* out, float* lse, hipStream_t stream);
+
+}  // namespace csa2

@@ -1,0 +1,250 @@
+// Index scoring: s_j = sum_h w_h * ReLU(q_h . k_j) over every reachable compressed
+// position of a query row, or over the row's candidate pool.
+//
+// Pages: "SGLang and Miles Day-0 support for DeepSeek-V4.1", section 5 (the indexer
+// scores the FP4 cache directly; MQA form: one key per position shared by all index
+// heads, heads replicated); "DeepSeek V4.1 Flash modeling", sections "Mixed precision"
+// (index Q/K are MXFP4 with 32-element groups) and "Hierarchical Sparse Indexer"
+// (Reindex layers rescore only the candidate pool).
+//
+// Head order.  The head sum is taken in fp32 in one fixed order: 4 contiguous head
+// groups, P_g = fma(w_h, max(d_h, 0), P_g) over the group's heads in ascending order
+// from +0, s = (P_0 + P_1) + (P_2 + P_3).  In the MFMA kernel the A-operand rows are
+// permuted so that the 16x16 output tile of a lane group holds consecutive heads of
+// one group: A row m of head tile t is head (H/4)*(m/4) + 4t + m%4, and the output
+// rows 4g..4g+3 that lane group g holds are therefore heads (H/4)*g + 4t + 0..3.  Each
+// lane runs its group's fma chain in registers; two lane swaps finish the sum.
+#include "csa2_device.h"
+#include "csa2_launch.h"
+
+#pragma clang fp contract(off)
+
+namespace csa2 {
+
+__device__ __forceinline__ int64_t row_columns(const RowsArg& rows, const CacheArg& cache, const PoolArg& pool,
+                                               int row, int64_t stride, int64_t* R_out, int* prow_out)
+{
+    const int r = rows.req[row];
+    const int64_t R = reach(rows.pos[row], cache.ratio_m, cache.n_entries[r]);
+    int64_t ncol = R;
+    int prow = row;
+    if (pool.blocks) {
+        prow = pool.row_map ? pool.row_map[row] : row;
+        ncol = R > 0 ? (int64_t)pool.nblocks[prow] * pool.block : 0;
+    }
+    *R_out = R;
+    *prow_out = prow;
+    return ncol < stride ? ncol : stride;
+}
+
+__device__ __forceinline__ int64_t column_position(const PoolArg& pool, int prow, int64_t c)
+{
+    if (!pool.blocks) return c;
+    const int64_t i = c / pool.block;
+    return (int64_t)pool.blocks[(int64_t)prow * pool.max_blocks + i] * pool.block + (c - i * pool.block);
+}
+
+// ----------------------------------------------------------------------------- fp32
+// One thread per (row, column): the dot product is an fma chain over the dimension in
+// ascending order from +0, then the canonical head reduction.
+__global__ __launch_bounds__(256) void k_score_f32(RowsArg rows, CacheArg cache, const float* __restrict__ q,
+                                                   int H, int D, const float* __restrict__ w, int64_t w_stride,
+                                                   const float* __restrict__ keys, PoolArg pool,
+                                                   float* __restrict__ scores, int64_t stride, int nchunks)
+{
+    const int row = blockIdx.x / nchunks;
+    int64_t R;
+    int prow;
+    const int64_t ncol = row_columns(rows, cache, pool, row, stride, &R, &prow);
+    const int64_t c = (int64_t)(blockIdx.x % nchunks) * blockDim.x + threadIdx.x;
+    if (c >= ncol) return;
+    const int64_t j = column_position(pool, prow, c);
+    float* dst = scores + (int64_t)row * stride + c;
+    if (j >= R) {
+        *dst = -INFINITY;
+        return;
+    }
+    const float* kr = keys + (cache.row_start[rows.req[row]] + j) * D;
+    const float* wr = w + (int64_t)row * w_stride;
+    const int G = H / 4;
+    float P[4];
+    for (int g = 0; g < 4; g++) {
+        float acc = 0.0f;
+        for (int h = g * G; h < (g + 1) * G; h++) {
+            const float* qr = q + ((int64_t)row * H + h) * D;
+            float d = 0.0f;
+            for (int i = 0; i < D; i++) d = __builtin_fmaf(qr[i], kr[i], d);
+            acc = __builtin_fmaf(wr[h], fmaxf(d, 0.0f), acc);
+        }
+        P[g] = acc;
+    }
+    *dst = (P[0] + P[1]) + (P[2] + P[3]);
+}
+
+// ---------------------------------------------------------------------------- MXFP4
+// Workgroup = 4 waves on one query row and a chunk of columns.  The row's bf16 index q
+// is quantized once per workgroup into LDS (one 32-element block per lane, which is
+// exactly the lane's slice of the MFMA A operand).  Each wave then takes 64 columns
+// at a time: 4 key tiles of 16 positions, each scored against NHT head tiles with
+// v_mfma_scale_f32_16x16x128_f8f6f4 (E2M1 x E2M1, E8M0 block scales): key tile lane
+// (g, c) loads position c's 16-byte code block g (one 32-element block) and its scale.
+template <int NHT>
+__global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cache, const uint16_t* __restrict__ q,
+                                                     const float* __restrict__ w, int64_t w_stride,
+                                                     const uint8_t* __restrict__ kdata,
+                                                     const uint8_t* __restrict__ kscale, PoolArg pool,
+                                                     float* __restrict__ scores, int64_t stride, int chunk,
+                                                     int nchunks)
+{
+    constexpr int H = NHT * 16;
+    constexpr int G = H / 4;
+    __shared__ uint4 s_qa[NHT][64];
+    __shared__ uint32_t s_qs[NHT][64];
+
+    const int row = blockIdx.x / nchunks;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    int64_t R;
+    int prow;
+    const int64_t ncol = row_columns(rows, cache, pool, row, stride, &R, &prow);
+    const int64_t c_begin = (int64_t)(blockIdx.x % nchunks) * chunk;
+    if (c_begin >= ncol) return;
+    const int64_t c_end = (c_begin + chunk < ncol) ? c_begin + chunk : ncol;
+    const int64_t krow0 = cache.row_start[rows.req[row]];
+
+    // quantize the row's index q into A operands
+    for (int idx = threadIdx.x; idx < NHT * 64; idx += 256) {
+        const int t = idx >> 6, l = idx & 63;
+        const int m = l & 15, kb = l >> 4;
+        const int head = G * (m >> 2) + 4 * t + (m & 3);
+        const uint4* src = reinterpret_cast<const uint4*>(q + ((int64_t)row * H + head) * 128 + kb * 32);
+        float v[32];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const uint4 u = src[i];
+            const uint32_t ws[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++) {
+                v[i * 8 + 2 * jj] = __uint_as_float(ws[jj] << 16);
+                v[i * 8 + 2 * jj + 1] = __uint_as_float(ws[jj] & 0xFFFF0000u);
+            }
+        }
+        uint32_t o[4], sb;
+        quant_block_e2m1(v, o, &sb);
+        s_qa[t][l] = make_uint4(o[0], o[1], o[2], o[3]);
+        s_qs[t][l] = sb;
+    }
+    __syncthreads();
+
+    i32x8 a[NHT];
+    int sa[NHT];
+#pragma unroll
+    for (int t = 0; t < NHT; t++) {
+        const uint4 u = s_qa[t][lane];
+        a[t] = i32x8{(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
+        sa[t] = (int)s_qs[t][lane];
+    }
+    const int g = lane >> 4;
+    float wr[NHT * 4];
+    {
+        const float* wrow = w + (int64_t)row * w_stride + G * g;
+#pragma unroll
+        for (int t = 0; t < NHT; t++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) wr[4 * t + i] = wrow[4 * t + i];
+    }
+
+    for (int64_t c0 = c_begin + 64 * wave; c0 < c_end; c0 += 256) {
+        float P[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const int64_t c = c0 + 16 * u + (lane & 15);
+            int64_t j = 0;
+            if (c < c_end) {
+                j = column_position(pool, prow, c);
+                if (j >= R) j = 0;
+            }
+            const int64_t krow = krow0 + j;
+            const uint4 kd = *reinterpret_cast<const uint4*>(kdata + krow * 64 + 16 * g);
+            const int sbk = (int)kscale[krow * 4 + g];
+            const i32x8 b = i32x8{(int)kd.x, (int)kd.y, (int)kd.z, (int)kd.w, 0, 0, 0, 0};
+            float pp = 0.0f;
+#pragma unroll
+            for (int t = 0; t < NHT; t++) {
+                const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+                const f32x4 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[t], b, zero, 4, 4, 0, sa[t], 0,
+                                                                                 sbk);
+#pragma unroll
+                for (int i = 0; i < 4; i++) pp = __builtin_fmaf(wr[4 * t + i], fmaxf(d[i], 0.0f), pp);
+            }
+            P[u] = pp;
+        }
+        // Lane group g holds P_g for tiles 0..3.  Pair groups (0,1) and (2,3) per tile,
+        // then (01, 23): lane (g, c) ends with the score of tile g, position c.
+        auto s01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(P[0]), __float_as_uint(P[1]), false, false);
+        auto s23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(P[2]), __float_as_uint(P[3]), false, false);
+        const float h01 = __uint_as_float(s01[0]) + __uint_as_float(s01[1]);
+        const float h23 = __uint_as_float(s23[0]) + __uint_as_float(s23[1]);
+        auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(h01), __float_as_uint(h23), false, false);
+        float score = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+
+        const int64_t c = c0 + lane;
+        if (c < c_end) {
+            if (pool.blocks && column_position(pool, prow, c) >= R) score = -INFINITY;
+            scores[(int64_t)row * stride + c] = score;
+        }
+    }
+}
+
+static int pick_chunk(int n, int64_t cols)
+{
+    // at least ~2048 workgroups when the rows are few; 256..4096 columns per workgroup
+    int64_t chunk = 4096;
+    while (chunk > 256 && (int64_t)n * ((cols + chunk - 1) / chunk) < 2048) chunk >>= 1;
+    return (int)chunk;
+}
+
+hipError_t launch_index_score_mxfp4(const RowsArg& rows, const CacheArg& cache, const uint16_t* q, int heads,
+                                    const float* w, int64_t w_stride, const uint8_t* kdata, const uint8_t* kscale,
+                                    const PoolArg& pool, float* scores, int64_t stride, hipStream_t stream)
+{
+    if (rows.n == 0) return hipSuccess;
+    const int64_t cols = pool.blocks ? (int64_t)pool.block * pool.max_blocks : stride;
+    const int chunk = pick_chunk(rows.n, cols);
+    const int nchunks = (int)((cols + chunk - 1) / chunk);
+    dim3 grid((unsigned)((int64_t)nchunks * rows.n));
+    switch (heads / 16) {
+#define CSA2_SCORE_CASE(T)                                                                                      \
+    case T:                                                                                                     \
+        hipLaunchKernelGGL((k_score_mxfp4<T>), grid, dim3(256), 0, stream, rows, cache, q, w, w_stride, kdata, \
+                           kscale, pool, scores, stride, chunk, nchunks);                                               \
+        break;
+        CSA2_SCORE_CASE(1)
+        CSA2_SCORE_CASE(2)
+        CSA2_SCORE_CASE(3)
+        CSA2_SCORE_CASE(4)
+        CSA2_SCORE_CASE(5)
+        CSA2_SCORE_CASE(6)
+        CSA2_SCORE_CASE(7)
+        CSA2_SCORE_CASE(8)
+#undef CSA2_SCORE_CASE
+        default:
+            return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_index_score_f32(const RowsArg& rows, const CacheArg& cache, const float* q, int heads, int dim,
+                                  const float* w, int64_t w_stride, const float* keys, const PoolArg& pool,
+                                  float* scores, int64_t stride, hipStream_t stream)
+{
+    if (rows.n == 0) return hipSuccess;
+    const int64_t cols = pool.blocks ? (int64_t)pool.block * pool.max_blocks : stride;
+    const int nchunks = (int)((cols + 255) / 256);
+    dim3 grid((unsigned)((int64_t)nchunks * rows.n));
+    hipLaunchKernelGGL(k_score_f32, grid, dim3(256), 0, stream, rows, cache, q, heads, dim, w, w_stride, keys, pool,
+                       scores, stride, nchunks);
+    return hipGetLastError();
+}
+
+}  // namespace csa2

@@ -1,0 +1,170 @@
+// Decoder bounded-replay tail layout and the MX quantization kernel.
+#include "csa2_device.h"
+#include "csa2_launch.h"
+
+namespace csa2 {
+
+// Per-request tail layout ("SGLang: how DeepSeek V4.1 Flash late layers only process
+// tail tokens", sections 2.1-2.3 and the rule block after the window table): T =
+// min(budget, E); rows [S-T, S) keep their absolute positions; window lower bound S-T;
+// tail row u maps to row ext_start + E - T + u of the original extend.
+//
+// One workgroup of 256 threads walks the requests in chunks of 256: a block scan gives
+// each request's first tail row and first extend row, then the chunk's rows are written
+// by all threads, each finding its request by binary search in the chunk's prefix.
+__global__ __launch_bounds__(256) void k_replay_tail_layout(int nreq, const int32_t* __restrict__ ext_len,
+                                                            const int32_t* __restrict__ seq_len, int budget,
+                                                            int32_t* __restrict__ tail_len,
+                                                            int32_t* __restrict__ tail_row_start,
+                                                            int32_t* __restrict__ src_row,
+                                                            int32_t* __restrict__ abs_pos,
+                                                            int32_t* __restrict__ win_lo,
+                                                            int32_t* __restrict__ req_of_row)
+{
+    __shared__ int s_tstart[257];  // exclusive prefix of T within the chunk (+ total)
+    __shared__ int s_estart[256];  // exclusive prefix of E within the chunk
+    __shared__ int s_T[256], s_S[256], s_E[256];
+    __shared__ int s_scan[256];
+    const int tid = threadIdx.x;
+    int carry_t = 0, carry_e = 0;
+
+    for (int base = 0; base < nreq; base += 256) {
+        const int r = base + tid;
+        int E = 0, S = 0, T = 0;
+        if (r < nreq) {
+            E = ext_len[r];
+            S = seq_len[r];
+            T = E < budget ? E : budget;
+            if (T < 0) T = 0;
+        }
+        // inclusive scan of T (Hillis-Steele), then of E
+        s_scan[tid] = T;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {
+            int v = tid >= off ? s_scan[tid - off] : 0;
+            __syncthreads();
+            s_scan[tid] += v;
+            __syncthreads();
+        }
+        const int incl_t = s_scan[tid];
+        const int chunk_t = s_scan[255];
+        __syncthreads();
+        s_scan[tid] = E;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {
+            int v = tid >= off ? s_scan[tid - off] : 0;
+            __syncthreads();
+            s_scan[tid] += v;
+            __syncthreads();
+        }
+        const int incl_e = s_scan[tid];
+        const int chunk_e = s_scan[255];
+
+        s_tstart[tid] = incl_t - T;
+        s_estart[tid] = incl_e - E;
+        s_T[tid] = T;
+        s_S[tid] = S;
+        s_E[tid] = E;
+        if (tid == 0) s_tstart[256] = chunk_t;
+        if (r < nreq) {
+            tail_len[r] = T;
+            tail_row_start[r] = carry_t + incl_t - T;
+        }
+        __syncthreads();
+
+        for (int i = tid; i < chunk_t; i += 256) {
+            // largest request slot q with s_tstart[q] <= i (slots with T = 0 are skipped
+            // because the next slot shares their start)
+            int lo = 0, hi = 255;
+            while (lo < hi) {
+                int mid = (lo + hi + 1) >> 1;
+                if (s_tstart[mid] <= i) lo = mid; else hi = mid - 1;
+            }
+            const int q = lo;
+            const int u = i - s_tstart[q];
+            const int Tq = s_T[q], Sq = s_S[q];
+            const int row = carry_t + i;
+            src_row[row] = carry_e + s_estart[q] + s_E[q] - Tq + u;
+            abs_pos[row] = Sq - Tq + u;
+            win_lo[row] = Sq - Tq;
+            req_of_row[row] = base + q;
+        }
+        carry_t += chunk_t;
+        carry_e += chunk_e;
+        __syncthreads();
+    }
+    if (tid == 0) tail_row_start[nreq] = carry_t;
+}
+
+// MX quantization, one thread per 32-element block.
+template <bool kBf16In, bool kFp4>
+__global__ __launch_bounds__(256) void k_quant_mx(const void* __restrict__ x, int64_t nblocks,
+                                                  uint8_t* __restrict__ codes, uint8_t* __restrict__ scales)
+{
+    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= nblocks) return;
+    float v[32];
+    if (kBf16In) {
+        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + b * 32);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            uint4 w = p[i];
+            uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                v[i * 8 + 2 * j] = __uint_as_float(ws[j] << 16);
+                v[i * 8 + 2 * j + 1] = __uint_as_float(ws[j] & 0xFFFF0000u);
+            }
+        }
+    } else {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + b * 32);
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            float4 w = p[i];
+            v[4 * i] = w.x;
+            v[4 * i + 1] = w.y;
+            v[4 * i + 2] = w.z;
+            v[4 * i + 3] = w.w;
+        }
+    }
+    uint32_t sb;
+    if (kFp4) {
+        uint32_t o[4];
+        quant_block_e2m1(v, o, &sb);
+        reinterpret_cast<uint4*>(codes)[b] = make_uint4(o[0], o[1], o[2], o[3]);
+    } else {
+        uint32_t o[8];
+        quant_block_e4m3(v, o, &sb);
+        uint4* dst = reinterpret_cast<uint4*>(codes) + 2 * b;
+        dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+        dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+    scales[b] = (uint8_t)sb;
+}
+
+hipError_t launch_replay_tail_layout(int nreq, const int32_t* ext_len, const int32_t* seq_len, int budget,
+                                     int32_t* tail_len, int32_t* tail_row_start, int32_t* src_row,
+                                     int32_t* abs_pos, int32_t* win_lo, int32_t* req_of_row, hipStream_t stream)
+{
+    hipLaunchKernelGGL(k_replay_tail_layout, dim3(1), dim3(256), 0, stream, nreq, ext_len, seq_len, budget,
+                       tail_len, tail_row_start, src_row, abs_pos, win_lo, req_of_row);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_mx(bool fp4, bool bf16_in, const void* x, int64_t nblocks, uint8_t* codes,
+                           uint8_t* scales, hipStream_t stream)
+{
+    if (nblocks == 0) return hipSuccess;
+    dim3 grid((unsigned)((nblocks + 255) / 256));
+    if (fp4 && bf16_in)
+        hipLaunchKernelGGL((k_quant_mx<true, true>), grid, dim3(256), 0, stream, x, nblocks, codes, scales);
+    else if (fp4)
+        hipLaunchKernelGGL((k_quant_mx<false, true>), grid, dim3(256), 0, stream, x, nblocks, codes, scales);
+    else if (bf16_in)
+        hipLaunchKernelGGL((k_quant_mx<true, false>), grid, dim3(256), 0, stream, x, nblocks, codes, scales);
+    else
+        hipLaunchKernelGGL((k_quant_mx<false, false>), grid, dim3(256), 0, stream, x, nblocks, codes, scales);
+    return hipGetLastError();
+}
+
+}  // namespace csa2

@@ -1,0 +1,247 @@
+/*
+ * csa2.h -- C ABI of the CSA2 compressed-sparse-attention hot path on MI355X (gfx950).
+ *
+ * The path (one layer of DeepSeek V4.1 Flash's "Compressed Sparse Attention 2"):
+ *   1. csa2_index_score      MQA-style index scores over FP4 (MXFP4) index keys
+ *   2. csa2_topk             top-k per query (flat, or restricted to a candidate pool)
+ *   3. csa2_topk_hier        flat top-k plus the hierarchical candidate pool
+ *   4. csa2_sparse_swa_attn  attention over the selected compressed entries and the
+ *                            query's own sliding window, one joint softmax
+ *   5. csa2_replay_tail_layout  per-request tail rows of the decoder bounded replay
+ *
+ * Pages (cited by title and section):
+ *   [MOD]  "DeepSeek V4.1 Flash modeling" (pages.haorui.li): sections "CSA2",
+ *          "Hierarchical Sparse Indexer", "Decoder Bounded Replay", "Mixed precision".
+ *   [TAIL] "SGLang: how DeepSeek V4.1 Flash late layers only process tail tokens"
+ *          (lab.ttaoai.cn): sections 2.1, 2.2, 2.3, 2.6, 3.1.
+ *   [DAY0] "SGLang and Miles Day-0 support for DeepSeek-V4.1" (theainews.cc summary of
+ *          the LMSYS post): sections 1, 2, 4.2, 5.
+ *
+ * Conventions shared by every call:
+ *   - Every array argument is a DEVICE pointer owned by the caller.  The library never
+ *     allocates, frees or retains memory; scratch space comes in through `workspace`
+ *     (size from csa2_workspace_size).  Structs are passed by host pointer and read
+ *     during the call only.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call validates its
+ *     scalar arguments on the host, enqueues kernels on `stream` and returns without
+ *     synchronizing.  Inputs must stay valid until the stream reaches the work.
+ *   - Return value: CSA2_OK, or an error code; nothing is enqueued when the error is
+ *     detected before launch (every CSA2_E_ARG / CSA2_E_UNSUPPORTED / CSA2_E_WORKSPACE).
+ *     csa2_last_error() gives a message for the calling thread.
+ *   - Device-array contents (positions, lengths, indices) are preconditions stated per
+ *     call; they are not checked.
+ *   - Results are deterministic: the same inputs give bitwise-identical outputs, and a
+ *     row's outputs do not depend on the other rows of the batch.
+ *   - Calls are reentrant; the library keeps no state between calls.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA2_VERSION 1
+
+enum {
+    CSA2_OK = 0,
+    CSA2_E_ARG = 1,         /* null pointer, count/stride/size out of range */
+    CSA2_E_UNSUPPORTED = 2, /* dtype / dim / head-count combination, or device is not gfx950 */
+    CSA2_E_WORKSPACE = 3,   /* workspace missing or smaller than csa2_workspace_size */
+    CSA2_E_LAUNCH = 4       /* a HIP launch or runtime call failed */
+};
+
+typedef enum csa2_dtype {
+    CSA2_F32 = 0,        /* IEEE binary32 */
+    CSA2_BF16 = 1,       /* bfloat16 */
+    CSA2_MXFP4 = 2,      /* OCP MX: E2M1 codes, two per byte (element 2i in the low nibble),
+                            one E8M0 scale byte per 32 elements in a separate plane */
+    CSA2_MXFP8_E4M3 = 3  /* OCP MX: E4M3 ("fn") codes, one per byte, one E8M0 scale per 32 */
+} csa2_dtype;
+
+/* Query rows of one call.  Row q belongs to request req_of_row[q] and sits at
+ * absolute token position pos_of_row[q] (0-based; the original position is kept
+ * for replayed tail rows, [TAIL] section 2.2).  win_lo[q] is the lowest absolute
+ * position the row's sliding window may read (the replay lower bound of [TAIL]
+ * section 2.3); NULL means 0. */
+typedef struct csa2_rows {
+    int32_t n;
+    const int32_t* req_of_row; /* [n] */
+    const int32_t* pos_of_row; /* [n] */
+    const int32_t* win_lo;     /* [n] or NULL */
+} csa2_rows;
+
+/* Geometry of a KV owner's compressed cache ([MOD] "CSA2": non-overlapping groups of
+ * ratio_m tokens; only complete groups are entries).  Entry j of request r covers
+ * tokens [j*m, j*m+m-1] and is visible to the query at position p iff j*m+m-1 <= p,
+ * so R(q) = min(floor((p+1)/m), n_entries[r]) entries are reachable.  Entry j of
+ * request r lives in row row_start[r] + j of every per-entry buffer of the owner
+ * (index keys and main KV share the row numbering). */
+typedef struct csa2_cache {
+    int32_t nreq;
+    int32_t ratio_m;          /* 1 or 2 */
+    const int32_t* n_entries; /* [nreq] complete entries C_r */
+    const int64_t* row_start; /* [nreq] */
+} csa2_cache;
+
+/* Index keys of the owner ([MOD] "Mixed precision": MXFP4 with 32-element groups, 68 B
+ * per 128-d entry = 64 B codes + 4 B scales, stored as two planes). */
+typedef struct csa2_index_keys {
+    csa2_dtype dtype;     /* CSA2_MXFP4 (dim 128) or CSA2_F32 (dim 16..256, multiple of 4) */
+    int32_t dim;
+    const void* data;     /* MXFP4: uint8[rows][dim/2]; F32: float[rows][dim] */
+    const uint8_t* scale; /* MXFP4: uint8[rows][dim/32] E8M0; F32: NULL */
+} csa2_index_keys;
+
+/* Candidate pool of the hierarchical indexer ([MOD] "Hierarchical Sparse Indexer";
+ * [DAY0] section 2): per pool row, nblocks[r] ascending block ids in blocks[r][0..);
+ * block b holds positions [b*block, b*block+block).  A query row q uses pool row
+ * row_map[q] (NULL = q). */
+typedef struct csa2_pool {
+    int32_t block;          /* positions per block, 8 on the pages (1..64) */
+    int32_t max_blocks;     /* row stride of `blocks`, 2048 on the pages */
+    const int32_t* blocks;  /* [pool_rows][max_blocks] */
+    const int32_t* nblocks; /* [pool_rows], each <= max_blocks */
+    const int32_t* row_map; /* [n] or NULL */
+} csa2_pool;
+
+/* Sliding-window KV of one layer ([DAY0] section 1: every layer keeps its own FP8
+ * window of the last 128 positions; [MOD] "Mixed precision").  Position t of request
+ * r is row row_start[r] + (t - pos_start[r]); the buffer must hold every position
+ * the windows read: [max(win_lo, p - window + 1, pos_start[r]), p]. */
+typedef struct csa2_swa {
+    csa2_dtype dtype;         /* CSA2_MXFP8_E4M3, CSA2_BF16 or CSA2_F32 */
+    const void* data;         /* [rows][dim] */
+    const uint8_t* scale;     /* MXFP8: uint8[rows][dim/32] E8M0; otherwise NULL */
+    const int64_t* row_start; /* [nreq] */
+    const int32_t* pos_start; /* [nreq] */
+    int32_t window;           /* W (128 on the pages): the window of p is [p-W+1, p] */
+} csa2_swa;
+
+/* ---------------------------------------------------------------------------------
+ * csa2_index_score -- indexer scores over every reachable compressed position, or over
+ * a candidate pool.
+ *
+ * Defines ([DAY0] section 5: the indexer scores the FP4 cache directly, heads
+ * replicated; the formula is the problem statement's MQA form):
+ *     s_j = sum_h w_h * ReLU(q_h . k_j)
+ * With MXFP4 keys the BF16 index q is first quantized to MXFP4 (32-element blocks,
+ * OCP MX rule; [MOD] "Mixed precision": index Q/K are MXFP4), so every q_h . k_j is an
+ * exact product sum; the head sum is taken in fp32 in a fixed order: 4 contiguous
+ * head groups, P_g = fma(w_h, max(d_h,0), P_g) over the group in ascending h from +0,
+ * s = (P_0 + P_1) + (P_2 + P_3).
+ *
+ * q_idx   [n][heads][keys->dim]: BF16 for MXFP4 keys, F32 for F32 keys (q_dtype says which).
+ * heads   MXFP4: a multiple of 16, at most 128; F32: a multiple of 4, at most 128.
+ * w       float [n][heads] with row stride w_row_stride (0: one row shared by all).
+ * pool    NULL: column j of row q is compressed position j, written for j < min(R(q),
+ *         score_stride).  Non-NULL: column c is position blocks[c/block]*block + c%block
+ *         of the row's pool, written for c < block*nblocks, -inf where the position is
+ *         not reachable; requires block*max_blocks <= score_stride.
+ * scores  float [n][score_stride]; columns beyond those listed are not written.
+ * Errors: E_ARG (null pointers, n < 0, bad strides), E_UNSUPPORTED (dtype/dim/heads).
+ * ------------------------------------------------------------------------------- */
+int csa2_index_score(const csa2_rows* rows, const csa2_cache* cache, const void* q_idx, csa2_dtype q_dtype,
+                     int32_t heads, const float* w, int64_t w_row_stride, const csa2_index_keys* keys,
+                     const csa2_pool* pool, float* scores, int64_t score_stride, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * csa2_topk -- the k best candidates of every row ([MOD] "Hierarchical Sparse Indexer":
+ * top-512 per query; [DAY0] section 1: at most 512 positions).
+ *
+ * Candidates: positions j < min(R(q), score_stride) (pool == NULL), or the reachable
+ * positions of the row's pool (pool != NULL, columns as in csa2_index_score).
+ * Order: larger score first (-0 equals +0), then lower position; the first k are kept.
+ * Scores must not be NaN.  out_idx [n][k]: the kept absolute compressed positions in
+ * ascending order, then -1 padding (fewer than k candidates keeps them all).
+ * k: 1..2048.  workspace: csa2_workspace_size(CSA2_OP_TOPK, ...).
+ * ------------------------------------------------------------------------------- */
+int csa2_topk(const csa2_rows* rows, const csa2_cache* cache, const float* scores, int64_t score_stride,
+              const csa2_pool* pool, int32_t k, int32_t* out_idx, void* workspace, size_t workspace_bytes,
+              void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * csa2_topk_hier -- the source pass of the hierarchical indexer ([MOD] "Hierarchical
+ * Sparse Indexer"; [DAY0] section 2, "two-level selection"): the flat top-k over all
+ * reachable positions (as csa2_topk without a pool) AND the candidate pool: blocks
+ * [b*block, b*block+block) are scored by the maximum over their reachable members;
+ * when ceil(R/block) <= max_blocks every block is kept, otherwise the block holding
+ * the newest reachable position plus the max_blocks-1 best other blocks by (block
+ * score desc, block id asc).  out_pool_blocks [n][max_blocks] ascending ids, -1 padded;
+ * out_pool_nblocks [n].  block 1..64, max_blocks 1..4096, k 1..2048.
+ * ------------------------------------------------------------------------------- */
+int csa2_topk_hier(const csa2_rows* rows, const csa2_cache* cache, const float* scores, int64_t score_stride,
+                   int32_t k, int32_t block, int32_t max_blocks, int32_t* out_idx, int32_t* out_pool_blocks,
+                   int32_t* out_pool_nblocks, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * csa2_sparse_swa_attn -- each query row attends, per head, to its selected compressed
+ * entries together with its own sliding window, in one softmax ([DAY0] section 1;
+ * [MOD] "CSA2": Full, Reindex and Reuse layers all keep their own attention; Reuse
+ * passes the latest top-k of its KV group as sel_idx).
+ *
+ * Keys = values: the main entry is one shared 512-d latent ([MOD] "Mixed precision").
+ * For row q at position p of request r, head h:
+ *   set  = { kv[row_start[r] + j] : j = sel_idx[s][i] >= 0 }   (s = sel_row_map ? sel_row_map[q] : q)
+ *        U { window row of t : max(win_lo[q], p - W + 1, pos_start[r]) <= t <= p }
+ *   out  = sum_x softmax_x(sm_scale * q_h . x) * x; the optional sink adds exp(sink_h - max)
+ *          to the denominator only; lse = max + log(denominator) (natural log).
+ * Selected indices must be < R(q) (or -1); k = 0 gives window-only attention.
+ *
+ * q [n][heads][dim] and out [n][heads][dim]; lse float [n][heads] or NULL.
+ * Supported: (q, kv, window, out) = (F32, F32, F32, F32) with dim <= 256 and any heads;
+ *            (BF16, BF16, MXFP8_E4M3 or BF16, BF16) with dim = 512 and heads % 16 == 0.
+ * sel_idx [*][sel_stride] int32, k <= sel_stride, k 0..2048.
+ * ------------------------------------------------------------------------------- */
+int csa2_sparse_swa_attn(const csa2_rows* rows, const csa2_cache* cache, const void* q, csa2_dtype q_dtype,
+                         int32_t heads, int32_t dim, const void* kv, csa2_dtype kv_dtype, const int32_t* sel_idx,
+                         int32_t k, int64_t sel_stride, const int32_t* sel_row_map, const csa2_swa* swa,
+                         float sm_scale, const float* sink, void* out, csa2_dtype out_dtype, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * csa2_replay_tail_layout -- per-request tail rows of the decoder bounded replay
+ * ([TAIL] sections 2.1-2.3 and the rule block after the window table; [DAY0] 4.2).
+ * For request r with extend length E = ext_len[r] and total length S = seq_len[r]:
+ *   T = min(budget, E); the late layers process absolute positions [S - T, S);
+ *   the window lower bound of those rows is S - T (also for E < budget, [TAIL] 2.6);
+ *   tail row u of r is row ext_start(r) + E - T + u of the original extend, where
+ *   ext_start(r) = sum of ext_len over the requests before r.
+ * Outputs: tail_len [nreq]; tail_row_start [nreq+1] (exclusive prefix sum of tail_len);
+ * per tail row (at most capacity): src_row, abs_pos, win_lo, req_of_row.
+ * Precondition 0 <= E <= S.  capacity >= budget*nreq (host-checked), budget >= 1.
+ * ------------------------------------------------------------------------------- */
+int csa2_replay_tail_layout(int32_t nreq, const int32_t* ext_len, const int32_t* seq_len, int32_t budget,
+                            int32_t* tail_len, int32_t* tail_row_start, int32_t* src_row, int32_t* abs_pos,
+                            int32_t* win_lo, int32_t* req_of_row, int32_t capacity, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Helpers.
+ * ------------------------------------------------------------------------------- */
+enum { CSA2_OP_TOPK = 1, CSA2_OP_TOPK_HIER = 2, CSA2_OP_ATTN = 3 };
+
+/* Workspace bytes for an op: n rows, `cols` = score_stride (TOPK / TOPK_HIER) or
+ * the number of selected entries k (ATTN), k, max_blocks (TOPK_HIER). */
+size_t csa2_workspace_size(int op, int32_t n, int64_t cols, int32_t k, int32_t max_blocks);
+
+/* Message of the calling thread's last error ("" after success). */
+const char* csa2_last_error(void);
+
+int csa2_version(void);
+
+/* OCP MX quantization of nblocks 32-element blocks of x (F32 or BF16, contiguous) into
+ * codes (MXFP4: 16 B per block, MXFP8_E4M3: 32 B per block) and one E8M0 scale byte
+ * per block: shared exponent floor(log2(max|x|)) - emax (emax 2 for E2M1, 8 for E4M3;
+ * -127 for an all-zero block), elements rounded to nearest even and saturated, the
+ * sign bit copied from x.  This is the same quantizer csa2_index_score applies to the
+ * BF16 index q; it also prepares index keys and window KV.  Inputs must be finite. */
+int csa2_quant_mx(csa2_dtype fmt, const void* x, csa2_dtype x_dtype, int64_t nblocks, uint8_t* codes,
+                  uint8_t* scales, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA2_H */

@@ -1,0 +1,59 @@
+"""Helpers shared by the GPU parity tests (not a test module).
+
+Inputs come from the seeded generator; each side prepares its own copy: the HIP side
+quantizes on the device with csa2_quant_mx, the oracle on the host with its own
+quantizer, and the tests check that both produce the same bytes before comparing
+anything downstream.
+"""
+import sys
+
+import numpy as np
+import torch
+
+from compressed_sparse_attention_fp4_amd import binding as B
+
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def i32(x):
+    return torch.as_tensor(np.asarray(x), dtype=torch.int32)
+
+
+def i64(x):
+    return torch.as_tensor(np.asarray(x), dtype=torch.int64)
+
+
+def dev_rows(rows):
+    return B.Rows(i32(rows["req_of_row"]).to(DEV), i32(rows["pos_of_row"]).to(DEV),
+                  None if rows.get("win_lo") is None else i32(rows["win_lo"]).to(DEV))
+
+
+def dev_cache(cache):
+    return B.Cache(cache["ratio_m"], i32(cache["n_entries"]).to(DEV), i64(cache["row_start"]).to(DEV))
+
+
+def np_rows(rows):
+    return {k: (None if v is None else np.asarray(v)) for k, v in rows.items()}
+
+
+def quant_both(orc, fmt_hip, fmt_orc, x_f32: torch.Tensor):
+    """Quantize x (float32, host) on both sides; assert identical bytes; return both."""
+    codes_d, scales_d = B.quant_mx(fmt_hip, x_f32.to(DEV))
+    codes_o, scales_o = orc.mx_quant(fmt_orc, x_f32.numpy())
+    cd, sd = codes_d.cpu().numpy(), scales_d.cpu().numpy()
+    assert np.array_equal(sd, scales_o), "scale bytes differ"
+    assert np.array_equal(cd, codes_o), "code bytes differ"
+    return (codes_d, scales_d), (codes_o, scales_o)
+
+
+def allclose_report(got, ref, atol, rtol):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    err = np.abs(got - ref)
+    bad = err > atol + rtol * np.abs(ref)
+    return int(bad.sum()), float(err.max(initial=0.0)), float((err / (np.abs(ref) + 1e-30)).max(initial=0.0))

@@ -1,0 +1,148 @@
+"""Host-side checks of the C ABI (no GPU): libcsa2.so loads, exports every symbol that
+include/csa2.h declares, and rejects invalid arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from compressed_sparse_attention_fp4_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa2.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="libcsa2.so not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(csa2_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared() == sorted(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = B.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    assert L.csa2_version() == 1
+
+
+def _rows(n=4):
+    return B._Rows(n, ctypes.c_void_p(16), ctypes.c_void_p(32), None)
+
+
+def _cache(nreq=1, m=2):
+    return B._Cache(nreq, m, ctypes.c_void_p(64), ctypes.c_void_p(128))
+
+
+def _err():
+    return B.lib().csa2_last_error().decode()
+
+
+P = ctypes.c_void_p(4096)  # a non-null pointer that is never dereferenced on these paths
+
+
+def test_index_score_arg_errors():
+    L = B.lib()
+    keys = B._IndexKeys(B.MXFP4, 128, P, P)
+    args = lambda **kw: dict(dict(rows=ctypes.byref(_rows()), cache=ctypes.byref(_cache()), q=P, qdt=B.BF16, heads=64,
+                                  w=P, ws=64, keys=ctypes.byref(keys), pool=None, scores=P, stride=512), **kw)
+
+    def call(a):
+        return L.csa2_index_score(a["rows"], a["cache"], a["q"], a["qdt"], a["heads"], a["w"], ctypes.c_int64(a["ws"]),
+                                  a["keys"], a["pool"], a["scores"], ctypes.c_int64(a["stride"]), None)
+
+    assert call(args(rows=None)) == B.CSA2_E_ARG
+    assert call(args(q=None)) == B.CSA2_E_ARG
+    assert call(args(stride=0)) == B.CSA2_E_ARG
+    assert call(args(heads=8)) == B.CSA2_E_UNSUPPORTED and "heads" in _err()
+    assert call(args(qdt=B.F32)) == B.CSA2_E_UNSUPPORTED
+    assert call(args(cache=ctypes.byref(_cache(m=3)))) == B.CSA2_E_UNSUPPORTED
+    bad_dim = B._IndexKeys(B.MXFP4, 64, P, P)
+    assert call(args(keys=ctypes.byref(bad_dim))) == B.CSA2_E_UNSUPPORTED
+    no_scale = B._IndexKeys(B.MXFP4, 128, P, None)
+    assert call(args(keys=ctypes.byref(no_scale))) == B.CSA2_E_ARG
+    pool = B._Pool(8, 2048, P, P, None)
+    assert call(args(pool=ctypes.byref(pool), stride=1000)) == B.CSA2_E_ARG and "score_stride" in _err()
+    f32 = B._IndexKeys(B.F32, 64, P, None)
+    assert call(args(keys=ctypes.byref(f32), qdt=B.F32, heads=6)) == B.CSA2_E_UNSUPPORTED
+    # zero rows: valid and a no-op
+    zero = B._Rows(0, None, None, None)
+    assert call(args(rows=ctypes.byref(zero))) == B.CSA2_OK
+
+
+def test_topk_arg_errors():
+    L = B.lib()
+
+    def call(k=512, stride=8192, ws=None, nbytes=0, rows=None, pool=None):
+        return L.csa2_topk(ctypes.byref(rows or _rows()), ctypes.byref(_cache()), P, ctypes.c_int64(stride), pool,
+                           ctypes.c_int32(k), P, ws, ctypes.c_size_t(nbytes), None)
+
+    assert call(k=0) == B.CSA2_E_ARG
+    assert call(k=2049) == B.CSA2_E_ARG
+    # a 65536-column row needs merge workspace
+    need = B.workspace_size(B.OP_TOPK, 4, 65536, 512)
+    assert need > 0
+    assert call(stride=65536) == B.CSA2_E_WORKSPACE
+    assert call(stride=65536, ws=P, nbytes=need - 1) == B.CSA2_E_WORKSPACE
+    assert B.workspace_size(B.OP_TOPK, 4, 8192, 512) == 0
+
+
+def test_topk_hier_arg_errors():
+    L = B.lib()
+
+    def call(k=512, block=8, maxb=2048):
+        return L.csa2_topk_hier(ctypes.byref(_rows()), ctypes.byref(_cache()), P, ctypes.c_int64(1024),
+                                ctypes.c_int32(k), ctypes.c_int32(block), ctypes.c_int32(maxb), P, P, P, None,
+                                ctypes.c_size_t(0), None)
+
+    assert call(block=16) == B.CSA2_E_UNSUPPORTED
+    assert call(maxb=0) == B.CSA2_E_ARG
+    assert call(k=0) == B.CSA2_E_ARG
+
+
+def test_attn_arg_errors():
+    L = B.lib()
+    swa = B._Swa(B.MXFP8_E4M3, P, P, P, P, 128)
+
+    def call(qdt=B.BF16, kvdt=B.BF16, odt=B.BF16, heads=64, dim=512, k=512, stride=512, sel=P, w=None, scale=0.04):
+        s = w or swa
+        return L.csa2_sparse_swa_attn(ctypes.byref(_rows()), ctypes.byref(_cache()), P, qdt, ctypes.c_int32(heads),
+                                      ctypes.c_int32(dim), P, kvdt, sel, ctypes.c_int32(k), ctypes.c_int64(stride), None,
+                                      ctypes.byref(s), ctypes.c_float(scale), None, P, odt, None, None,
+                                      ctypes.c_size_t(0), None)
+
+    assert call(dim=256) == B.CSA2_E_UNSUPPORTED
+    assert call(heads=40) == B.CSA2_E_UNSUPPORTED
+    assert call(kvdt=B.F32) == B.CSA2_E_UNSUPPORTED
+    assert call(k=600) == B.CSA2_E_ARG            # k > sel_stride
+    assert call(sel=None) == B.CSA2_E_ARG         # k > 0 without indices
+    assert call(k=4096, stride=4096) == B.CSA2_E_ARG
+    assert call(scale=0.0) == B.CSA2_E_ARG
+    noscale = B._Swa(B.MXFP8_E4M3, P, None, P, P, 128)
+    assert call(w=noscale) == B.CSA2_E_ARG
+    f32win = B._Swa(B.F32, P, None, P, P, 128)
+    assert call(qdt=B.F32, kvdt=B.F32, odt=B.F32, dim=300, w=f32win) == B.CSA2_E_UNSUPPORTED
+
+
+def test_tail_layout_arg_errors():
+    L = B.lib()
+
+    def call(nreq=8, budget=128, cap=1024):
+        return L.csa2_replay_tail_layout(ctypes.c_int32(nreq), P, P, ctypes.c_int32(budget), P, P, P, P, P, P,
+                                         ctypes.c_int32(cap), None)
+
+    assert call(cap=1023) == B.CSA2_E_ARG and "capacity" in _err()
+    assert call(budget=0) == B.CSA2_E_ARG
+    assert call(nreq=-1) == B.CSA2_E_ARG
+
+
+def test_quant_arg_errors():
+    L = B.lib()
+    assert L.csa2_quant_mx(B.BF16, P, B.F32, ctypes.c_int64(4), P, P, None) == B.CSA2_E_UNSUPPORTED
+    assert L.csa2_quant_mx(B.MXFP4, P, B.MXFP4, ctypes.c_int64(4), P, P, None) == B.CSA2_E_UNSUPPORTED
+    assert L.csa2_quant_mx(B.MXFP4, None, B.F32, ctypes.c_int64(4), P, P, None) == B.CSA2_E_ARG
+    assert L.csa2_quant_mx(B.MXFP4, None, B.F32, ctypes.c_int64(0), None, None, None) == B.CSA2_OK

@@ -1,0 +1,409 @@
+"""GPU parity of every entry point against the oracle, on seeded inputs sized so that the
+oracle finishes in seconds while the kernels still cross several tiles and a ragged
+tail.  Index sets and scores must match bit for bit; attention outputs within
+|g - r| <= atol + rtol |r| (bf16: 2e-2 + 1e-2 |r|, plus a per-row relative L2 error
+<= 1e-2; fp32: 1e-4 + 1e-4 |r|)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from compressed_sparse_attention_fp4_amd import binding as B
+from compressed_sparse_attention_fp4_amd import synth
+
+from gpu_util import DEV, allclose_report, dev_cache, dev_rows, i32, i64, quant_both, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+
+
+# ------------------------------------------------------------------ quantizer
+def test_quant_mx_all_bf16_patterns(orc):
+    say("case: quant_mx over every bf16 bit pattern (finite), MXFP4 and MXFP8")
+    bits = torch.arange(65536, dtype=torch.int32).to(torch.int16)
+    vals = bits.view(torch.bfloat16).float()
+    vals = vals[torch.isfinite(vals)]
+    vals = vals[: (vals.numel() // 32) * 32]
+    # shuffle so blocks mix magnitudes (several shared exponents per pattern)
+    g = torch.Generator().manual_seed(0)
+    for rep in range(3):
+        x = vals[torch.randperm(vals.numel(), generator=g)].reshape(-1, 32).contiguous()
+        quant_both(orc, B.MXFP4, orc.E2M1, x)
+        quant_both(orc, B.MXFP8_E4M3, orc.E4M3, x)
+    # also from bf16 input directly
+    x = vals[torch.randperm(vals.numel(), generator=g)].reshape(-1, 32).contiguous()
+    cd, sd = B.quant_mx(B.MXFP4, x.to(torch.bfloat16).to(DEV))
+    co, so = orc.mx_quant(orc.E2M1, x.numpy())
+    assert np.array_equal(cd.cpu().numpy(), co) and np.array_equal(sd.cpu().numpy(), so)
+
+
+def test_quant_mx_ties_and_ranges(orc):
+    say("case: quant_mx ties, saturation, zero blocks, tiny and huge magnitudes")
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((4096, 32)).astype(np.float32)
+    x *= (2.0 ** rng.integers(-120, 120, size=(4096, 1))).astype(np.float32)
+    x[0] = 0.0
+    x[1, :8] = [6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    x[2, :4] = [448.0, 460.0, 470.0, 511.0]
+    x[3] = -0.0
+    quant_both(orc, B.MXFP4, orc.E2M1, torch.from_numpy(x))
+    quant_both(orc, B.MXFP8_E4M3, orc.E4M3, torch.from_numpy(x))
+
+
+# ---------------------------------------------------------------- tail layout
+def test_replay_tail_layout(orc):
+    say("case: replay tail layout, page examples and a random batch")
+    cases = [([8192], [8192]), ([64], [8256]), ([8192] * 4, [8192, 16384, 24576, 32768]),
+             (synth.C2_EXTENDS, [8192] * 8), ([0, 1, 127, 128, 129, 5, 0], [10, 50, 127, 1000, 129, 5, 7])]
+    rng = np.random.default_rng(4)
+    e = rng.integers(0, 400, size=700)
+    cases.append((e.tolist(), (e + rng.integers(0, 1000, size=700)).tolist()))
+    for ext, seq in cases:
+        t = B.replay_tail_layout(i32(ext).to(DEV), i32(seq).to(DEV), 128)
+        o = orc.replay_tail_layout(ext, seq, 128)
+        tot = int(o["tail_row_start"][-1])
+        assert t["tail_len"].cpu().numpy().tolist() == o["tail_len"].tolist()
+        assert t["tail_row_start"].cpu().numpy().tolist() == o["tail_row_start"].tolist()
+        for name in ("src_row", "abs_pos", "win_lo", "req_of_row"):
+            assert np.array_equal(t[name][:tot].cpu().numpy(), o[name]), name
+
+
+# --------------------------------------------------------------------- scores
+def _score_case(seed, S, m, H, D, nrows_per_req, fp4=True):
+    rng = np.random.default_rng(seed)
+    geom = synth.Geometry(list(S), m)
+    req, pos = [], []
+    for r, s in enumerate(S):
+        special = [0, 1, 2, m * 16 - 1, m * 16, s - 1, s - 2, min(s - 1, 8191), min(s - 1, 8192)]
+        pick = set(p for p in special if 0 <= p < s) | set(rng.choice(s, size=nrows_per_req, replace=False).tolist())
+        for p in sorted(pick):
+            req.append(r)
+            pos.append(p)
+    rows = dict(req_of_row=np.array(req), pos_of_row=np.array(pos))
+    cache = dict(ratio_m=m, n_entries=np.array(geom.n_entries), row_start=np.array(geom.row_start))
+    keys = synth.normal((geom.total_entries, D), seed, "index_keys")
+    n = len(req)
+    if fp4:
+        q = synth.normal_bf16((n, H, D), seed, "index_q")
+    else:
+        q = synth.normal((n, H, D), seed, "index_q")
+    w = synth.uniform((n, H), seed, "index_w")
+    return rows, cache, keys, q, w
+
+
+@pytest.mark.parametrize("H", [64, 32, 16])
+def test_index_score_mxfp4_full_range(orc, H):
+    say("case: index_score MXFP4 full range, heads=%d" % H)
+    rows, cache, keys, q, w = _score_case(10 + H, (3000, 1234, 77), 2, H, 128, 12)
+    stride = 1536
+    (kd, ksd), (ko, kso) = quant_both(orc, B.MXFP4, orc.E2M1, keys)
+    s_d = B.index_score(dev_rows(rows), dev_cache(cache), q.to(DEV), w.to(DEV), B.IndexKeys(kd, ksd, 128),
+                        score_stride=stride)
+    s_o, bad = orc.index_score(rows, cache, q.float().numpy(), w.numpy(), ko, key_scales=kso, heads=H, dim=128,
+                               score_stride=stride)
+    assert bad == 0
+    got = s_d.cpu().numpy()
+    for i in range(len(rows["req_of_row"])):
+        r, p = rows["req_of_row"][i], rows["pos_of_row"][i]
+        R = min((p + 1) // 2, cache["n_entries"][r])
+        if not np.array_equal(got[i, :R], s_o[i, :R]):
+            bad_cols = np.nonzero(got[i, :R] != s_o[i, :R])[0]
+            raise AssertionError("row %d (p=%d R=%d): %d columns differ, first %s: gpu %r oracle %r" % (
+                i, p, R, len(bad_cols), bad_cols[:8], got[i, bad_cols[:4]], s_o[i, bad_cols[:4]]))
+
+
+def test_index_score_mxfp4_pool(orc):
+    say("case: index_score MXFP4 over a candidate pool (ragged newest block, row map)")
+    rows, cache, keys, q, w = _score_case(21, (4000, 999), 1, 64, 128, 10)
+    rng = np.random.default_rng(22)
+    n = len(rows["req_of_row"])
+    B_, NB = 8, 64
+    blocks = np.full((n, NB), -1, np.int32)
+    nblocks = np.zeros(n, np.int32)
+    for i in range(n):
+        r, p = rows["req_of_row"][i], rows["pos_of_row"][i]
+        R = min(p + 1, cache["n_entries"][r])
+        nb = (R + B_ - 1) // B_
+        others = rng.choice(max(nb - 1, 1), size=min(NB - 1, max(nb - 1, 0)), replace=False) if nb > 1 else []
+        pick = sorted(set(np.asarray(others).tolist()) | {nb - 1}) if nb > 0 else []
+        blocks[i, :len(pick)] = pick
+        nblocks[i] = len(pick)
+    # the row map sends every row to its own pool row in reverse storage order
+    perm = np.arange(n)[::-1].copy()
+    pool_blocks = np.empty_like(blocks)
+    pool_n = np.empty_like(nblocks)
+    pool_blocks[perm] = blocks
+    pool_n[perm] = nblocks
+    pool_o = dict(blocks=pool_blocks, nblocks=pool_n, block=B_, max_blocks=NB, row_map=perm)
+    pool_d = B.Pool(i32(pool_blocks).to(DEV), i32(pool_n).to(DEV), B_, i32(perm).to(DEV))
+    stride = NB * B_
+    (kd, ksd), (ko, kso) = quant_both(orc, B.MXFP4, orc.E2M1, keys)
+    s_d = B.index_score(dev_rows(rows), dev_cache(cache), q.to(DEV), w.to(DEV), B.IndexKeys(kd, ksd, 128),
+                        pool=pool_d, score_stride=stride)
+    s_o, bad = orc.index_score(rows, cache, q.float().numpy(), w.numpy(), ko, key_scales=kso, heads=64, dim=128,
+                               score_stride=stride, pool=pool_o)
+    assert bad == 0
+    got = s_d.cpu().numpy()
+    for i in range(n):
+        ncol = nblocks[i] * B_
+        assert np.array_equal(got[i, :ncol], s_o[i, :ncol]), i
+
+
+def test_index_score_f32_c0(orc):
+    say("case: index_score fp32 (C0 shapes)")
+    cfg = synth.config(0)
+    rows_t = synth.prefill_rows(cfg.geom)
+    rows = {k: v.numpy() for k, v in rows_t.items()}
+    g = cfg.geom
+    cache = dict(ratio_m=g.ratio_m, n_entries=np.array(g.n_entries), row_start=np.array(g.row_start))
+    n = len(rows["req_of_row"])
+    keys = synth.normal((g.total_entries, cfg.index_dim), 0, "index_keys")
+    q = synth.normal((n, cfg.index_heads, cfg.index_dim), 0, "index_q")
+    w = synth.uniform((n, cfg.index_heads), 0, "index_w")
+    stride = 512
+    s_d = B.index_score(dev_rows(rows), dev_cache(cache), q.to(DEV), w.to(DEV), B.IndexKeys(keys.to(DEV), None, 64),
+                        score_stride=stride)
+    s_o, _ = orc.index_score(rows, cache, q.numpy(), w.numpy(), keys.numpy(), heads=8, dim=64, score_stride=stride)
+    got = s_d.cpu().numpy()
+    for i in range(n):
+        R = min((rows["pos_of_row"][i] + 1) // 2, 512)
+        assert np.array_equal(got[i, :R], s_o[i, :R]), i
+
+
+# ---------------------------------------------------------------------- top-k
+def _topk_inputs(seed, R_list, stride, ties=None):
+    rng = np.random.default_rng(seed)
+    n = len(R_list)
+    rows = dict(req_of_row=np.arange(n), pos_of_row=np.array([max(R - 1, 0) for R in R_list]))
+    cache = dict(ratio_m=1, n_entries=np.array(R_list), row_start=np.zeros(n, np.int64))
+    scores = np.full((n, stride), np.nan, np.float32)
+    for i, R in enumerate(R_list):
+        v = (rng.standard_normal(R) * 30 + 150).astype(np.float32)
+        if ties is not None:
+            v = np.floor(v / ties).astype(np.float32) * ties
+        scores[i, :R] = v
+    return rows, cache, scores
+
+
+@pytest.mark.parametrize("ties", [None, 4.0, 1000.0])
+@pytest.mark.parametrize("k", [64, 512, 2048])
+def test_topk_flat(orc, k, ties):
+    say("case: topk flat k=%d ties=%s" % (k, ties))
+    R_list = [0, 1, 511, 512, 513, 2047, 2048, 2049, 5000, 8191, 8192, 8193, 16385, 40000]
+    stride = 40960
+    rows, cache, scores = _topk_inputs(100 + k, R_list, stride, ties)
+    got = B.topk(dev_rows(rows), dev_cache(cache), torch.from_numpy(scores).to(DEV), k).cpu().numpy()
+    ref = orc.topk(rows, cache, scores, k)
+    for i in range(len(R_list)):
+        assert np.array_equal(got[i], ref[i]), (i, R_list[i])
+
+
+def test_topk_pool(orc):
+    say("case: topk over a pool")
+    rng = np.random.default_rng(7)
+    R_list = [100, 8000, 20000, 65536]
+    B_, NB = 8, 2048
+    rows = dict(req_of_row=np.arange(4), pos_of_row=np.array([R - 1 for R in R_list]))
+    cache = dict(ratio_m=1, n_entries=np.array(R_list), row_start=np.zeros(4, np.int64))
+    blocks = np.full((4, NB), -1, np.int32)
+    nb_ = np.zeros(4, np.int32)
+    for i, R in enumerate(R_list):
+        nb = (R + B_ - 1) // B_
+        if nb <= NB:
+            pick = list(range(nb))
+        else:
+            pick = sorted(set(rng.choice(nb - 1, NB - 1, replace=False).tolist()) | {nb - 1})
+        blocks[i, :len(pick)] = pick
+        nb_[i] = len(pick)
+    scores = np.full((4, NB * B_), np.nan, np.float32)
+    for i, R in enumerate(R_list):
+        for c in range(nb_[i] * B_):
+            j = blocks[i, c // B_] * B_ + c % B_
+            scores[i, c] = -np.inf if j >= R else np.float32(rng.standard_normal() * 20 + 100)
+    pool_o = dict(blocks=blocks, nblocks=nb_, block=B_, max_blocks=NB)
+    pool_d = B.Pool(i32(blocks).to(DEV), i32(nb_).to(DEV), B_)
+    got = B.topk(dev_rows(rows), dev_cache(cache), torch.from_numpy(scores).to(DEV), 512, pool=pool_d).cpu().numpy()
+    ref = orc.topk(rows, cache, scores, 512, pool=pool_o)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("ties", [None, 2.0])
+def test_topk_hier(orc, ties):
+    say("case: topk_hier ties=%s" % ties)
+    R_list = [1, 9, 100, 16383, 16384, 16385, 16392, 16393, 30000, 65536]
+    stride = 65536
+    rows, cache, scores = _topk_inputs(55, R_list, stride, ties)
+    idx, blocks, nblocks = B.topk_hier(dev_rows(rows), dev_cache(cache), torch.from_numpy(scores).to(DEV), 512, 8, 2048)
+    ri, rb, rn = orc.topk_hier(rows, cache, scores, 512, 8, 2048)
+    assert np.array_equal(nblocks.cpu().numpy(), rn)
+    assert np.array_equal(blocks.cpu().numpy(), rb)
+    assert np.array_equal(idx.cpu().numpy(), ri)
+
+
+# ------------------------------------------------------------------ attention
+def test_attn_f32_c0(orc):
+    say("case: sparse+window attention fp32 (C0), k=64 and k=512 (dense equivalence)")
+    cfg = synth.config(0)
+    g = cfg.geom
+    rows_t = synth.prefill_rows(g)
+    rows = {k: v.numpy() for k, v in rows_t.items()}
+    n = len(rows["req_of_row"])
+    cache = dict(ratio_m=2, n_entries=np.array(g.n_entries), row_start=np.array(g.row_start))
+    q = synth.normal((n, 8, 64), 0, "q")
+    kv = synth.normal((g.total_entries, 64), 0, "kv")
+    win = synth.window_cache_geometry(g, 128, rows_held=g.seq_len)
+    swa_data = synth.normal((win["rows"], 64), 0, "swa")
+    rng = np.random.default_rng(0)
+    sel = np.full((n, 64), -1, np.int32)
+    for i in range(n):
+        R = min((rows["pos_of_row"][i] + 1) // 2, 512)
+        take = min(R, 64)
+        sel[i, :take] = np.sort(rng.choice(R, size=take, replace=False)) if take else []
+    scale = 1.0 / 8.0
+    wd = B.Window(swa_data.to(DEV), None, win["row_start"].to(DEV), win["pos_start"].to(DEV), 128)
+    wo = dict(data=swa_data.numpy(), dtype=0, scale=None, row_start=win["row_start"].numpy(),
+              pos_start=win["pos_start"].numpy(), window=128)
+    out_d, lse_d = B.sparse_swa_attn(dev_rows(rows), dev_cache(cache), q.to(DEV), kv.to(DEV), i32(sel).to(DEV), wd,
+                                     scale, want_lse=True)
+    out_o, lse_o = orc.sparse_swa_attn(rows, cache, q.numpy(), 0, kv.numpy(), 0, sel, wo, heads=8, dim=64,
+                                       sm_scale=scale)
+    nb, emax, _ = allclose_report(out_d.cpu().numpy(), out_o, 1e-4, 1e-4)
+    assert nb == 0, (nb, emax)
+    assert allclose_report(lse_d.cpu().numpy(), lse_o, 1e-4, 1e-4)[0] == 0
+    # k = 512 >= R: equal to dense brute force over every reachable entry
+    sel_all = np.full((n, 512), -1, np.int32)
+    for i in range(n):
+        R = min((rows["pos_of_row"][i] + 1) // 2, 512)
+        sel_all[i, :R] = np.arange(R)
+    out_d2 = B.sparse_swa_attn(dev_rows(rows), dev_cache(cache), q.to(DEV), kv.to(DEV), i32(sel_all).to(DEV), wd, scale)
+    dense, _ = orc.sparse_swa_attn(rows, cache, q.numpy(), 0, kv.numpy(), 0, None, wo, heads=8, dim=64, sm_scale=scale,
+                                   dense=True)
+    nb, emax, _ = allclose_report(out_d2.cpu().numpy(), dense, 1e-4, 1e-4)
+    assert nb == 0, (nb, emax)
+
+
+def _attn_bf16_case(seed, S, m, H, k, nrows_per_req, win_lo_tail=False, swa_fp8=True):
+    rng = np.random.default_rng(seed)
+    geom = synth.Geometry(list(S), m)
+    req, pos = [], []
+    for r, s in enumerate(S):
+        special = [0, 1, 126, 127, 128, 129, s - 1]
+        pick = set(p for p in special if 0 <= p < s) | set(rng.choice(s, size=nrows_per_req, replace=False).tolist())
+        for p in sorted(pick):
+            req.append(r)
+            pos.append(p)
+    n = len(req)
+    rows = dict(req_of_row=np.array(req), pos_of_row=np.array(pos))
+    if win_lo_tail:
+        rows["win_lo"] = np.array([max(0, p - int(rng.integers(0, 130))) for p in pos])
+    cache = dict(ratio_m=m, n_entries=np.array(geom.n_entries), row_start=np.array(geom.row_start))
+    D = 512
+    q = synth.normal_bf16((n, H, D), seed, "q")
+    kv = synth.normal_bf16((geom.total_entries, D), seed, "kv")
+    win = synth.window_cache_geometry(geom, 128, rows_held=geom.seq_len)
+    swa_raw = synth.normal((win["rows"], D), seed, "swa")
+    sel = np.full((n, k), -1, np.int32)
+    for i in range(n):
+        R = min((pos[i] + 1) // m, geom.n_entries[req[i]])
+        take = min(R, k)
+        if take:
+            chosen = rng.choice(R, size=take, replace=False)
+            slots = rng.choice(k, size=take, replace=False)   # -1 holes anywhere
+            sel[i, np.sort(slots)] = np.sort(chosen)
+    return rows, cache, q, kv, win, swa_raw, sel
+
+
+def _run_attn_bf16(orc, rows, cache, q, kv, win, swa_raw, sel, H, sm_scale, swa_fp8=True, sel_row_map=None):
+    n = len(rows["req_of_row"])
+    if swa_fp8:
+        (cd, sd), (co, so) = quant_both(orc, B.MXFP8_E4M3, orc.E4M3, swa_raw)
+        wd = B.Window(cd, sd, win["row_start"].to(DEV), win["pos_start"].to(DEV), 128)
+        wo = dict(data=co, dtype=3, scale=so, row_start=win["row_start"].numpy(), pos_start=win["pos_start"].numpy(),
+                  window=128)
+    else:
+        sb = swa_raw.to(torch.bfloat16)
+        wd = B.Window(sb.to(DEV), None, win["row_start"].to(DEV), win["pos_start"].to(DEV), 128)
+        wo = dict(data=sb.view(torch.int16).numpy().view(np.uint16), dtype=1, scale=None,
+                  row_start=win["row_start"].numpy(), pos_start=win["pos_start"].numpy(), window=128)
+    out_d, lse_d = B.sparse_swa_attn(dev_rows(rows), dev_cache(cache), q.to(DEV), kv.to(DEV), i32(sel).to(DEV), wd,
+                                     sm_scale, sel_row_map=None if sel_row_map is None else i32(sel_row_map).to(DEV),
+                                     want_lse=True)
+    qb = q.view(torch.int16).numpy().view(np.uint16)
+    kvb = kv.view(torch.int16).numpy().view(np.uint16)
+    out_o, lse_o = orc.sparse_swa_attn(rows, cache, qb, 1, kvb, 1, sel, wo, heads=H, dim=512, sm_scale=sm_scale,
+                                       sel_row_map=sel_row_map)
+    return out_d.float().cpu().numpy(), lse_d.cpu().numpy(), out_o, lse_o
+
+
+def _check_bf16_attn(got, ref, lse_g, lse_r):
+    nb, emax, _ = allclose_report(got, ref, 2e-2, 1e-2)
+    assert nb == 0, ("elements out of tolerance", nb, emax)
+    n, H, D = ref.shape
+    rel = np.linalg.norm((got - ref).reshape(n * H, D), axis=1) / (np.linalg.norm(ref.reshape(n * H, D), axis=1) + 1e-30)
+    assert rel.max() <= 1e-2, ("row relative L2", rel.max())
+    nb, emax, _ = allclose_report(lse_g, lse_r, 1e-3, 1e-3)
+    assert nb == 0, ("lse", nb, emax)
+
+
+@pytest.mark.parametrize("H,k,swa_fp8,tail", [(64, 512, True, False), (16, 64, True, True), (32, 512, False, False),
+                                              (64, 0, True, False), (16, 2048, True, False)])
+def test_attn_bf16(orc, H, k, swa_fp8, tail):
+    say("case: sparse+window attention bf16 H=%d k=%d fp8=%s tail=%s" % (H, k, swa_fp8, tail))
+    rows, cache, q, kv, win, swa_raw, sel = _attn_bf16_case(30 + H + k, (2600, 700), 2 if k != 2048 else 1, H, k, 6,
+                                                            win_lo_tail=tail)
+    got, lse_g, ref, lse_r = _run_attn_bf16(orc, rows, cache, q, kv, win, swa_raw, sel, H, 1 / math.sqrt(512),
+                                            swa_fp8=swa_fp8)
+    _check_bf16_attn(got, ref, lse_g, lse_r)
+
+
+def test_attn_bf16_dense_equivalence(orc):
+    say("case: bf16 attention with every reachable entry selected equals dense brute force")
+    rows, cache, q, kv, win, swa_raw, _ = _attn_bf16_case(77, (900,), 2, 16, 512, 8)
+    n = len(rows["req_of_row"])
+    sel = np.full((n, 512), -1, np.int32)
+    for i in range(n):
+        R = min((rows["pos_of_row"][i] + 1) // 2, 450)
+        sel[i, :R] = np.arange(R)
+    got, lse_g, _, _ = _run_attn_bf16(orc, rows, cache, q, kv, win, swa_raw, sel, 16, 1 / math.sqrt(512))
+    (cd, sd), (co, so) = quant_both(orc, B.MXFP8_E4M3, orc.E4M3, swa_raw)
+    wo = dict(data=co, dtype=3, scale=so, row_start=win["row_start"].numpy(), pos_start=win["pos_start"].numpy(),
+              window=128)
+    dense, lse_dense = orc.sparse_swa_attn(rows, cache, q.view(torch.int16).numpy().view(np.uint16), 1,
+                                           kv.view(torch.int16).numpy().view(np.uint16), 1, None, wo, heads=16, dim=512,
+                                           sm_scale=1 / math.sqrt(512), dense=True)
+    _check_bf16_attn(got, dense, lse_g, lse_dense)
+
+
+def test_attn_bf16_reuse_row_map(orc):
+    say("case: Reuse layer reads another layer's index rows through sel_row_map")
+    rows, cache, q, kv, win, swa_raw, sel = _attn_bf16_case(88, (1500,), 2, 16, 512, 10)
+    n = len(rows["req_of_row"])
+    rng = np.random.default_rng(1)
+    # producer rows live in a larger table; each consumer row maps to its producer row
+    table = np.full((3 * n, 512), -1, np.int32)
+    row_map = rng.permutation(3 * n)[:n].astype(np.int32)
+    table[row_map] = sel
+    got, lse_g, ref, lse_r = _run_attn_bf16(orc, rows, cache, q, kv, win, swa_raw, table, 16, 0.05,
+                                            sel_row_map=row_map)
+    _check_bf16_attn(got, ref, lse_g, lse_r)
+    got2, _, _, _ = _run_attn_bf16(orc, rows, cache, q, kv, win, swa_raw, sel, 16, 0.05)
+    assert np.array_equal(got, got2)  # same indices through the map: bitwise identical
+
+
+def test_determinism_and_batch_invariance(orc):
+    say("case: run twice bitwise equal; a row alone equals the row inside a batch")
+    rows, cache, q, kv, win, swa_raw, sel = _attn_bf16_case(99, (1200, 800), 2, 32, 512, 6)
+    a, _, _, _ = _run_attn_bf16(orc, rows, cache, q, kv, win, swa_raw, sel, 32, 0.04)
+    b, _, _, _ = _run_attn_bf16(orc, rows, cache, q, kv, win, swa_raw, sel, 32, 0.04)
+    assert np.array_equal(a, b)
+    i = 3
+    rows1 = {k: v[i:i + 1] for k, v in rows.items()}
+    c, _, _, _ = _run_attn_bf16(orc, rows1, cache, q[i:i + 1].contiguous(), kv, win, swa_raw, sel[i:i + 1], 32, 0.04)
+    assert np.array_equal(a[i:i + 1], c)
