@@ -1,0 +1,325 @@
+#!/usr/bin/env python3
+"""Benchmark of the CSA2 hot path on one MI355X.
+
+Workload (default): hierarchical-indexer decode -- 64 requests x 1 query token at
+context S = 131072 with m = 2 (65536 compressed entries each).  One step is a decode
+step through 8 CSA2 layers sharing one KV owner:
+  layer 0 (source, Full):  index scores over all 65536 entries (MXFP4 keys, 64 index
+                           heads x 128) -> flat top-512 + candidate pool of 2048 blocks
+                           of 8 -> sparse + window attention (64 bf16 heads x 512,
+                           FP8 window of 128)
+  layers 1..7 (Reindex):   own index q / weights, scores over the 16384-position pool
+                           -> top-512 inside the pool -> attention with own q and window.
+Metric: sparse-attention queries per second = query rows x layers completed per second
+(64 x 8 = 512 per step).  Inputs are seeded N(0,1) (weights U(0,1)) drawn on the GPU;
+4 independent input sets rotate across steps so that no step finds the previous
+step's data in the 256 MiB last-level cache.
+
+Also reported: the dominant kernel's roofline (algorithmic bytes / average launch time,
+HIP events on the launch stream) and the CPU oracle's rate on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+from compressed_sparse_attention_fp4_amd import binding as B  # noqa: E402
+from compressed_sparse_attention_fp4_amd import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+NREQ, SEQ, M = 64, 131072, 2
+C = SEQ // M
+HI, DI = 64, 128
+H, D = 64, 512
+K, BLK, NB, W = 512, 8, 2048, 128
+LAYERS = 8
+NSETS = 4
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------------ inputs
+class InputSet:
+    def __init__(self, s: int, dev):
+        seed = 3 * 1000 + s
+        g = synth.Geometry([SEQ] * NREQ, M)
+        self.rows = B.Rows(torch.arange(NREQ, dtype=torch.int32, device=dev),
+                           torch.full((NREQ,), SEQ - 1, dtype=torch.int32, device=dev))
+        self.cache = B.Cache(M, torch.tensor(g.n_entries, dtype=torch.int32, device=dev),
+                             torch.tensor(g.row_start, dtype=torch.int64, device=dev))
+        # index keys: N(0,1) -> MXFP4 by the library quantizer, chunk by chunk
+        self.kcodes = torch.empty((g.total_entries, DI // 2), dtype=torch.uint8, device=dev)
+        self.kscale = torch.empty((g.total_entries, DI // 32), dtype=torch.uint8, device=dev)
+        step = 1 << 20
+        for c0 in range(0, g.total_entries, step):
+            raw = synth.normal((min(step, g.total_entries - c0), DI), seed, "index_keys/%d" % c0, device=dev)
+            cd, sd = B.quant_mx(B.MXFP4, raw)
+            self.kcodes[c0:c0 + raw.shape[0]] = cd
+            self.kscale[c0:c0 + raw.shape[0]] = sd
+            del raw
+        self.keys = B.IndexKeys(self.kcodes, self.kscale, DI)
+        self.kv = synth.normal_bf16((g.total_entries, D), seed, "kv", device=dev, chunk_rows=1 << 19)
+        win = synth.window_cache_geometry(g, W)
+        self.layers = []
+        for l in range(LAYERS):
+            qi = synth.normal_bf16((NREQ, HI, DI), seed, "index_q/%d" % l, device=dev)
+            w = synth.uniform((NREQ, HI), seed, "index_w/%d" % l, device=dev)
+            q = synth.normal_bf16((NREQ, H, D), seed, "q/%d" % l, device=dev)
+            sraw = synth.normal((win["rows"], D), seed, "swa/%d" % l, device=dev)
+            scd, ssd = B.quant_mx(B.MXFP8_E4M3, sraw)
+            del sraw
+            window = B.Window(scd, ssd, win["row_start"].to(dev), win["pos_start"].to(dev), W)
+            self.layers.append(dict(qi=qi, w=w, q=q, window=window))
+        # outputs and workspaces (allocated once)
+        self.scores_full = torch.empty((NREQ, C), dtype=torch.float32, device=dev)
+        self.scores_pool = torch.empty((NREQ, NB * BLK), dtype=torch.float32, device=dev)
+        self.idx = [torch.empty((NREQ, K), dtype=torch.int32, device=dev) for _ in range(LAYERS)]
+        self.pool_blocks = torch.empty((NREQ, NB), dtype=torch.int32, device=dev)
+        self.pool_n = torch.empty((NREQ,), dtype=torch.int32, device=dev)
+        self.out = [torch.empty((NREQ, H, D), dtype=torch.bfloat16, device=dev) for _ in range(LAYERS)]
+        self.ws_hier = torch.empty(max(1, B.workspace_size(B.OP_TOPK_HIER, NREQ, C, K, NB)), dtype=torch.uint8,
+                                   device=dev)
+        self.ws_topk = torch.empty(max(1, B.workspace_size(B.OP_TOPK, NREQ, NB * BLK, K)), dtype=torch.uint8,
+                                   device=dev)
+        self.pool = B.Pool(self.pool_blocks, self.pool_n, BLK)
+
+
+# ----------------------------------------------------------------- one decode step
+STAGES = ["score_full", "topk_hier", "attn", "score_pool", "topk_pool"]
+
+
+def step(x: InputSet, ev=None):
+    """One pass of the hot path; ev (dict stage -> list of (start, end) events) times
+    every entry-point call on the launch stream."""
+    def timed(stage, fn):
+        if ev is None:
+            return fn()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        r = fn()
+        b.record()
+        ev[stage].append((a, b))
+        return r
+
+    sm = synth.sm_scale(D)
+    L0 = x.layers[0]
+    timed("score_full", lambda: B.index_score(x.rows, x.cache, L0["qi"], L0["w"], x.keys, scores=x.scores_full))
+    timed("topk_hier", lambda: B.topk_hier(x.rows, x.cache, x.scores_full, K, BLK, NB, workspace=x.ws_hier,
+                                           out=(x.idx[0], x.pool_blocks, x.pool_n)))
+    timed("attn", lambda: B.sparse_swa_attn(x.rows, x.cache, L0["q"], x.kv, x.idx[0], L0["window"], sm,
+                                            out=x.out[0]))
+    for l in range(1, LAYERS):
+        Ll = x.layers[l]
+        timed("score_pool", lambda: B.index_score(x.rows, x.cache, Ll["qi"], Ll["w"], x.keys, pool=x.pool,
+                                                  scores=x.scores_pool))
+        timed("topk_pool", lambda: B.topk(x.rows, x.cache, x.scores_pool, K, pool=x.pool, out=x.idx[l],
+                                          workspace=x.ws_topk))
+        timed("attn", lambda: B.sparse_swa_attn(x.rows, x.cache, Ll["q"], x.kv, x.idx[l], Ll["window"], sm,
+                                                out=x.out[l]))
+
+
+# Algorithmic bytes per launch (what the step must move at least once).
+ATTN_BYTES_PER_QUERY = K * D * 2 + W * (D + D // 32) + H * D * 2 * 2 + K * 4     # 724,992
+STAGE_BYTES = {
+    "score_full": NREQ * C * (DI // 2 + DI // 32) + NREQ * HI * DI * 2 + NREQ * HI * 4 + NREQ * C * 4,
+    "topk_hier": 2 * NREQ * C * 4 + NREQ * (K + NB + 1) * 4,
+    "attn": NREQ * ATTN_BYTES_PER_QUERY,
+    "score_pool": NREQ * NB * BLK * (DI // 2 + DI // 32) + NREQ * (NB + 1) * 4 + NREQ * HI * DI * 2
+    + NREQ * HI * 4 + NREQ * NB * BLK * 4,
+    "topk_pool": NREQ * NB * BLK * 4 + NREQ * (NB + 1) * 4 + NREQ * K * 4,
+}
+STAGE_KERNEL = {"score_full": "k_score_mxfp4", "topk_hier": "k_select (2 launches)", "attn": "k_attn_bf16",
+                "score_pool": "k_score_mxfp4 (pool)", "topk_pool": "k_select"}
+
+
+# ------------------------------------------------------------------ cpu baseline
+def cpu_baseline(x: InputSet, nrows: int):
+    """The oracle on a bounded sample: nrows requests through the source layer and one
+    Reindex layer, timed per layer; the rate is scaled to the step's mix (1 source +
+    7 Reindex layers per query row)."""
+    import oracle as orc
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count() or 1
+    nrows = max(1, min(nrows, NREQ))
+    rows = dict(req_of_row=np.arange(nrows), pos_of_row=np.full(nrows, SEQ - 1))
+    cache = dict(ratio_m=M, n_entries=np.full(nrows, C), row_start=np.arange(nrows, dtype=np.int64) * C)
+    # the same inputs (first nrows requests), copied to the host; the oracle quantizes the keys itself
+    seed = 3 * 1000 + 0
+    keys_raw = []
+    step_rows = 1 << 20
+    for c0 in range(0, nrows * C, step_rows):
+        keys_raw.append(synth.normal((min(step_rows, NREQ * C - c0), DI), seed, "index_keys/%d" % c0,
+                                     device="cuda")[: max(0, nrows * C - c0)].cpu())
+    keys_raw = torch.cat(keys_raw)[: nrows * C].numpy()
+    kc, ks = orc.mx_quant(orc.E2M1, keys_raw)
+    del keys_raw
+    kv = x.kv[: nrows * C].view(torch.int16).cpu().numpy().view(np.uint16)
+    lay = []
+    for l in (0, 1):
+        L = x.layers[l]
+        wn = L["window"]
+        lay.append(dict(qi=L["qi"][:nrows].float().cpu().numpy(), w=L["w"][:nrows].cpu().numpy(),
+                        q=L["q"][:nrows].view(torch.int16).cpu().numpy().view(np.uint16),
+                        swa=dict(data=wn.data[: nrows * W].cpu().numpy(), dtype=3,
+                                 scale=wn.scale[: nrows * W].cpu().numpy(),
+                                 row_start=wn.row_start[:nrows].cpu().numpy(),
+                                 pos_start=wn.pos_start[:nrows].cpu().numpy(), window=W)))
+    sm = synth.sm_scale(D)
+    t0 = time.perf_counter()
+    s, _ = orc.index_score(rows, cache, lay[0]["qi"], lay[0]["w"], kc, key_scales=ks, heads=HI, dim=DI,
+                           score_stride=C)
+    idx, pb, pn = orc.topk_hier(rows, cache, s, K, BLK, NB)
+    orc.sparse_swa_attn(rows, cache, lay[0]["q"], 1, kv, 1, idx, lay[0]["swa"], heads=H, dim=D, sm_scale=sm)
+    t_src = time.perf_counter() - t0
+    pool = dict(blocks=pb, nblocks=pn, block=BLK, max_blocks=NB)
+    t0 = time.perf_counter()
+    s2, _ = orc.index_score(rows, cache, lay[1]["qi"], lay[1]["w"], kc, key_scales=ks, heads=HI, dim=DI,
+                            score_stride=NB * BLK, pool=pool)
+    idx2 = orc.topk(rows, cache, s2, K, pool=pool)
+    orc.sparse_swa_attn(rows, cache, lay[1]["q"], 1, kv, 1, idx2, lay[1]["swa"], heads=H, dim=D, sm_scale=sm)
+    t_re = time.perf_counter() - t0
+    step_time = t_src + (LAYERS - 1) * t_re
+    rate = nrows * LAYERS / step_time
+    used = min(threads, nrows)  # the oracle parallelizes over query rows
+    return {"value": rate, "unit": "queries/s", "cores": used, "kind": "oracle",
+            "sample": "%d of 64 query rows through the source layer (%.1f s) and one Reindex layer (%.1f s) on "
+                      "%d host threads; rate = rows x 8 layers / (source + 7 x Reindex)" % (nrows, t_src, t_re, used)}
+
+
+# ---------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=int(os.environ.get("OMP_NUM_THREADS", "0") or 16))
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the CSA2 path is built and timed on a single MI355X; "
+              "multi-GPU sharding is described in DESIGN.md but not run (got --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B.lib()
+    log("building %d input sets ..." % NSETS)
+    sets = [InputSet(s, dev) for s in range(NSETS)]
+    torch.cuda.synchronize()
+    log("warmup %d eager steps" % args.warmup)
+    for i in range(max(args.warmup, NSETS)):
+        step(sets[i % NSETS])
+    torch.cuda.synchronize()
+
+    # one HIP graph per input set: the step is launch-bound in Python otherwise
+    graphs = []
+    for x in sets:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(x)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    # replays must reproduce the eager results bit for bit, replay after replay
+    x = sets[0]
+    step(x)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in x.idx] + [t.clone() for t in x.out] + [x.pool_blocks.clone(), x.pool_n.clone()]
+    for rep in range(2):
+        for t in x.idx + x.out + [x.pool_blocks, x.pool_n]:
+            t.zero_()
+        graphs[0].replay()
+        torch.cuda.synchronize()
+        got = x.idx + x.out + [x.pool_blocks, x.pool_n]
+        assert all(torch.equal(a, b) for a, b in zip(ref, got)), "graph replay differs from the eager step"
+        step(x)
+        torch.cuda.synchronize()
+    for i in range(args.warmup):
+        graphs[i % NSETS].replay()
+
+    # timed region: exactly K steps (graph replays), synchronized on both sides
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % NSETS].replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    log("timed %d steps in %.3f ms" % (args.steps, elapsed * 1e3))
+
+    # per-kernel durations: the same K steps launched eagerly with HIP events around every
+    # entry-point call, on the stream the kernels run on
+    ev = {s: [] for s in STAGES}
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[i % NSETS], ev)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t1) * 1e3 / args.steps
+
+    stage_ms = {s: [a.elapsed_time(b) for a, b in ev[s]] for s in STAGES}
+    per_step_ms = {s: sum(v) / args.steps for s, v in stage_ms.items()}
+    dominant = max(STAGES, key=lambda s: per_step_ms[s])
+    avg_launch_ms = float(np.mean(stage_ms[dominant]))
+    achieved = STAGE_BYTES[dominant] / (avg_launch_ms * 1e-3) / 1e9
+    stages = {s: {"ms_per_launch": float(np.mean(v)), "launches_per_step": len(v) // args.steps,
+                  "alg_GBs": STAGE_BYTES[s] / (np.mean(v) * 1e-3) / 1e9} for s, v in stage_ms.items()}
+    log(json.dumps(stages, indent=1))
+    log("eager step %.3f ms (events included), graph step %.3f ms" % (eager_ms, elapsed * 1e3 / args.steps))
+
+    queries = NREQ * LAYERS * args.steps
+    value = queries / elapsed
+    # one plain copy of known size, for scaling rocprof FETCH/WRITE counters
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) on %d rows ..." % args.cpu_rows)
+        cpu = cpu_baseline(sets[0], args.cpu_rows)
+
+    line = {
+        "metric": "CSA2 sparse-attn queries/s (decode, hierarchical indexer)",
+        "value": value,
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4+bf16",
+        "data": "synthetic (seeded N(0,1) q/keys/KV/window, U(0,1) index weights)",
+        "config": {"workload": "C3 hierarchical-indexer decode: 64 requests x 1 query, S=131072, m=2 "
+                               "(65536 entries), 1 source + 7 Reindex layers per step",
+                   "requests": NREQ, "context": SEQ, "ratio_m": M, "index_heads": HI, "index_dim": DI,
+                   "topk": K, "pool_blocks": NB, "block": BLK, "heads": H, "dim": D, "window": W,
+                   "layers_per_step": LAYERS, "queries_per_step": NREQ * LAYERS, "input_sets": NSETS},
+        "roofline": {"bound": "hbm", "kernel": STAGE_KERNEL[dominant], "stage": dominant,
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "alg_bytes_per_launch": STAGE_BYTES[dominant],
+                     "avg_launch_us": avg_launch_ms * 1e3},
+        "stages": {s: {"us_per_launch": round(v["ms_per_launch"] * 1e3, 2),
+                       "launches_per_step": v["launches_per_step"], "alg_GBs": round(v["alg_GBs"], 1)}
+                   for s, v in stages.items()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

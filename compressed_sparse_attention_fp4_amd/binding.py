@@ -219,13 +219,16 @@ def topk(rows: Rows, cache: Cache, scores: torch.Tensor, k: int, pool: Optional[
 
 
 def topk_hier(rows: Rows, cache: Cache, scores: torch.Tensor, k: int, block: int = 8, max_blocks: int = 2048,
-              workspace: Optional[torch.Tensor] = None, stream=None):
-    """csa2_topk_hier: (flat top-k [n, k], pool blocks [n, max_blocks], pool nblocks [n])."""
+              workspace: Optional[torch.Tensor] = None, out=None, stream=None):
+    """csa2_topk_hier: (flat top-k [n, k], pool blocks [n, max_blocks], pool nblocks [n]).
+    out: optional preallocated (idx, blocks, nblocks)."""
     n = rows.n
     dev = scores.device
-    idx = torch.empty((n, k), dtype=torch.int32, device=dev)
-    blocks = torch.empty((n, max_blocks), dtype=torch.int32, device=dev)
-    nblocks = torch.empty((n,), dtype=torch.int32, device=dev)
+    if out is None:
+        out = (torch.empty((n, k), dtype=torch.int32, device=dev),
+               torch.empty((n, max_blocks), dtype=torch.int32, device=dev),
+               torch.empty((n,), dtype=torch.int32, device=dev))
+    idx, blocks, nblocks = out
     if workspace is None:
         workspace = _workspace(workspace_size(OP_TOPK_HIER, n, scores.stride(0), k, max_blocks), dev)
     rc = lib().csa2_topk_hier(ctypes.byref(rows.c()), ctypes.byref(cache.c()), _ptr(scores),

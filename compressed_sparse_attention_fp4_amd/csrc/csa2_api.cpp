@@ -84,7 +84,8 @@ int check_pool(const csa2_pool* pool, int64_t score_stride)
 {
     if (!pool) return CSA2_OK;
     if (!pool->blocks || !pool->nblocks) return fail(CSA2_E_ARG, "pool->blocks / nblocks is NULL");
-    if (pool->block < 1 || pool->block > 64) return fail(CSA2_E_ARG, "pool->block = %d (1..64)", pool->block);
+    if (pool->block < 1 || pool->block > 64 || (pool->block & (pool->block - 1)))
+        return fail(CSA2_E_ARG, "pool->block = %d (a power of two, 1..64)", pool->block);
     if (pool->max_blocks < 1 || pool->max_blocks > 65536)
         return fail(CSA2_E_ARG, "pool->max_blocks = %d (1..65536)", pool->max_blocks);
     if ((int64_t)pool->block * pool->max_blocks > score_stride)
@@ -114,7 +115,9 @@ size_t csa2_workspace_size(int op, int32_t n, int64_t cols, int32_t k, int32_t m
     if (n <= 0 || cols <= 0) return 0;
     switch (op) {
         case CSA2_OP_TOPK:
-            return csa2::topk_workspace(n, cols, k);
+            // cols = score columns (full range) or block*max_blocks (pool): the plan for
+            // the pool source is never smaller, so size for it
+            return csa2::topk_workspace(n, cols, k, true);
         case CSA2_OP_TOPK_HIER:
             return csa2::topk_hier_workspace(n, cols, k, 8, max_blocks > 0 ? max_blocks : 1);
         case CSA2_OP_ATTN:
@@ -178,7 +181,7 @@ int csa2_topk(const csa2_rows* rows, const csa2_cache* cache, const float* score
     if (score_stride < 1) return fail(CSA2_E_ARG, "score_stride = %lld < 1", (long long)score_stride);
     if ((rc = check_pool(pool, score_stride))) return rc;
     const int64_t cols = pool ? (int64_t)pool->block * pool->max_blocks : score_stride;
-    const size_t need = csa2::topk_workspace(rows->n, cols, k);
+    const size_t need = csa2::topk_workspace(rows->n, cols, k, pool != nullptr);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(CSA2_E_WORKSPACE, "csa2_topk needs %zu workspace bytes, got %zu", need, workspace_bytes);
     if (rows->n == 0) return ok();

@@ -53,7 +53,7 @@ struct SelSource {
     PoolArg pool;  // pool.blocks non-null: candidates are the row's pool columns
 };
 
-size_t topk_workspace(int n, int64_t stride, int k);
+size_t topk_workspace(int n, int64_t stride, int k, bool pool);
 hipError_t launch_topk(const SelSource& src, int k, int32_t* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 size_t topk_hier_workspace(int n, int64_t stride, int k, int block, int max_blocks);

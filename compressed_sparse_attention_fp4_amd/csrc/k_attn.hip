@@ -166,6 +166,7 @@ __global__ __launch_bounds__(256) void k_attn_bf16(RowsArg rows, CacheArg cache,
     __shared__ int s_tmp[8];
     __shared__ float s_m[4][16], s_l[4][16];
     __shared__ float s_o[4][16][256 + 4];  // one half of the dims at a time
+    __shared__ uint4 s_q[16][64];          // Q^T operand: step s, lane (g, c)
 
     const int b = blockIdx.x;
     const int row = 8 * (b / (8 * nhg)) + (b & 7);
@@ -195,113 +196,125 @@ __global__ __launch_bounds__(256) void k_attn_bf16(RowsArg rows, CacheArg cache,
         nsel += tot;
         __syncthreads();
     }
-    const int nk = nsel + rk.nwin;
-    const int ntiles = (nk + 15) >> 4;
+    // Key slots: [0, nsel) selected entries, [nsel, sel_pad) padding (masked), then the
+    // window; sel_pad = nsel rounded up to a tile, so every tile is of one kind.
+    const int sel_pad = (nsel + 15) & ~15;
+    const int nslots = sel_pad + rk.nwin;
+    const int ntiles = (nslots + 15) >> 4;
+    const int sel_tiles = sel_pad >> 4;
 
-    // ---- Q^T as the B operand: lane (g, c) holds head h0+c, dims [32s+8g, +8)
-    bf16x8 qb[16];
-    {
-        const uint16_t* qrow = q + ((int64_t)row * H + h0 + c) * kAttnD + 8 * g;
-#pragma unroll
-        for (int s = 0; s < 16; s++) qb[s] = load_bf16x8(qrow + 32 * s);
+    // ---- Q^T as the B operand, staged in LDS: lane (g, c) of step s holds head h0+c,
+    //      dims [32s+8g, +8)
+    for (int idx = tid; idx < 16 * 64; idx += 256) {
+        const int s = idx >> 6, l = idx & 63;
+        s_q[s][l] = *reinterpret_cast<const uint4*>(q + ((int64_t)row * H + h0 + (l & 15)) * kAttnD + 32 * s +
+                                                   8 * (l >> 4));
     }
+    __syncthreads();
     // identity B operand of the transposing MFMA: lane (g, c), k-slots 4g..4g+3, column c
     s16x4 ident;
 #pragma unroll
     for (int i = 0; i < 4; i++) ident[i] = (4 * g + i == c) ? (short)0x3F80 : (short)0;
 
-    f32x4 o[32];
-#pragma unroll
-    for (int t = 0; t < 32; t++) o[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    float m_run = -INFINITY, l_run = 0.0f;  // state of head c (replicated over g)
+    // State of head c (replicated over g).  Exponents are taken against a reference
+    // m_ref that is fixed for the whole pass: the wave's first tile maximum plus 64
+    // (log2 units).  Any reference at or above the maximum gives the same softmax (the
+    // numerator and the denominator share the factor) and 64 leaves the fp32 / bf16
+    // exponent range ample room.  The accumulator is therefore touched only by MFMAs
+    // inside the loop.  If a later logit exceeds the reference, the wave redoes its
+    // tiles once with the exact maximum it has seen.
     const float qk_scale = sm_scale * kLog2e;
     const uint16_t* kv_r = kv + rk.kv0 * kAttnD;
     const int64_t swa_base = swa.row_start[rk.r] - swa.pos_start[rk.r] + rk.t0;
-
-    for (int tile = wave; tile < ntiles; tile += 4) {
-        const int ki = tile * 16 + c;
-        bf16x8 ka[16];
-        if (ki < nsel) {
-            const uint16_t* kr = kv_r + (int64_t)s_sel[ki] * kAttnD + 8 * g;
+    f32x4 o[32];
+    float m_ref = -INFINITY, l_run = 0.0f, m_true = -INFINITY;
+    for (int attempt = 0; attempt < 2; attempt++) {
 #pragma unroll
-            for (int s = 0; s < 16; s++) ka[s] = load_bf16x8(kr + 32 * s);
-        } else if (ki < nk) {
-            const int64_t srow = swa_base + (ki - nsel);
-            if (swa.dtype == 3) {
-                const uint8_t* sr = static_cast<const uint8_t*>(swa.data) + srow * kAttnD + 8 * g;
-                const uint8_t* sc = swa.scale + srow * (kAttnD / 32);
+        for (int t = 0; t < 32; t++) o[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        l_run = 0.0f;
+        m_ref = (attempt == 0) ? -INFINITY : m_true;
+        bool over = false;
+        for (int tile = wave; tile < ntiles; tile += 4) {
+            // keep the Q operand in LDS: re-read it per tile instead of pinning 64 registers
+            asm volatile("" ::: "memory");
+            bf16x8 ka[16];
+            if (tile < sel_tiles) {  // uniform: a tile of selected entries (and padding)
+                const int ki = tile * 16 + c;
+                const uint16_t* kr = kv_r + (int64_t)s_sel[ki < nsel ? ki : 0] * kAttnD + 8 * g;
 #pragma unroll
-                for (int s = 0; s < 16; s++) ka[s] = load_fp8x8_as_bf16(sr + 32 * s, __builtin_ldexpf(1.0f, (int)sc[s] - 127));
+                for (int s = 0; s < 16; s++) ka[s] = load_bf16x8(kr + 32 * s);
             } else {
-                const uint16_t* sr = static_cast<const uint16_t*>(swa.data) + srow * kAttnD + 8 * g;
+                const int wi = tile * 16 + c - sel_pad;
+                const int64_t srow = swa_base + (wi < rk.nwin ? wi : 0);
+                if (swa.dtype == 3) {
+                    const uint8_t* sr = static_cast<const uint8_t*>(swa.data) + srow * kAttnD + 8 * g;
+                    const uint8_t* sc = swa.scale + srow * (kAttnD / 32);
 #pragma unroll
-                for (int s = 0; s < 16; s++) ka[s] = load_bf16x8(sr + 32 * s);
+                    for (int s = 0; s < 16; s++)
+                        ka[s] = load_fp8x8_as_bf16(sr + 32 * s, __builtin_ldexpf(1.0f, (int)sc[s] - 127));
+                } else {
+                    const uint16_t* sr = static_cast<const uint16_t*>(swa.data) + srow * kAttnD + 8 * g;
+#pragma unroll
+                    for (int s = 0; s < 16; s++) ka[s] = load_bf16x8(sr + 32 * s);
+                }
             }
-        } else {
-#pragma unroll
-            for (int s = 0; s < 16; s++) ka[s] = bf16x8{};
-        }
 
-        // S^T tile: lane (g, c) -> keys 4g..4g+3, head c
-        f32x4 st = {0.0f, 0.0f, 0.0f, 0.0f};
+            // S^T tile: lane (g, c) -> key slots 4g..4g+3, head c
+            f32x4 st = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int s = 0; s < 16; s++) st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s], qb[s], st, 0, 0, 0);
+            for (int s = 0; s < 16; s++)
+                st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s], __builtin_bit_cast(bf16x8, s_q[s][lane]), st, 0,
+                                                             0, 0);
+            float lg[4];
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int slot = tile * 16 + 4 * g + i;
+                const bool valid = (slot < nsel) || (slot >= sel_pad && slot < nslots);
+                lg[i] = valid ? st[i] * qk_scale : -INFINITY;
+                tmax = fmaxf(tmax, lg[i]);
+            }
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+            m_true = fmaxf(m_true, tmax);
+            if (m_ref == -INFINITY && tmax != -INFINITY) m_ref = tmax + 64.0f;  // the accumulator is still zero
+            over |= tmax > m_ref;
+            const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
+            float psum = 0.0f;
+            s16x4 pa;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const float pv = __builtin_amdgcn_exp2f(lg[i] - m_use);
+                psum += pv;
+                pa[i] = __builtin_bit_cast(short, (__bf16)pv);
+            }
+            psum += __shfl_xor(psum, 16, 64);
+            psum += __shfl_xor(psum, 32, 64);
+            l_run += psum;
 
-        float lg[4];
-        float tmax = -INFINITY;
+            // O += P V, V taken from the K tile through the identity MFMA
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int key = tile * 16 + 4 * g + i;
-            lg[i] = (key < nk) ? st[i] * qk_scale : -INFINITY;
-            tmax = fmaxf(tmax, lg[i]);
-        }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float m_new = fmaxf(m_run, tmax);
-        const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        float psum = 0.0f;
-        s16x4 pa;
+            for (int s = 0; s < 16; s++) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const float pv = __builtin_amdgcn_exp2f(lg[i] - m_use);
-            psum += pv;
-            pa[i] = __builtin_bit_cast(short, (__bf16)pv);
-        }
-        psum += __shfl_xor(psum, 16, 64);
-        psum += __shfl_xor(psum, 32, 64);
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-
-        // rescale O rows (heads 4g+i) by their alpha, held by lane 4g+i
-        float al[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) al[i] = __shfl(alpha, 4 * g + i, 64);
-#pragma unroll
-        for (int t = 0; t < 32; t++)
-#pragma unroll
-            for (int i = 0; i < 4; i++) o[t][i] *= al[i];
-
-        // O += P V, V taken from the K tile through the identity MFMA
-#pragma unroll
-        for (int s = 0; s < 16; s++) {
-#pragma unroll
-            for (int u = 0; u < 2; u++) {
-                const s16x4 kh = __builtin_bit_cast(s16x4, bf16x4{ka[s][4 * u], ka[s][4 * u + 1], ka[s][4 * u + 2],
-                                                                 ka[s][4 * u + 3]});
-                const f32x4 tt = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kh, ident, f32x4{0.0f, 0.0f, 0.0f, 0.0f},
-                                                                          0, 0, 0);
-                s16x4 vb;
-#pragma unroll
-                for (int i = 0; i < 4; i++) vb[i] = __builtin_bit_cast(short, (__bf16)tt[i]);
-                o[2 * s + u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, o[2 * s + u], 0, 0, 0);
+                for (int u = 0; u < 2; u++) {
+                    const s16x4 kh = __builtin_bit_cast(
+                        s16x4, bf16x4{ka[s][4 * u], ka[s][4 * u + 1], ka[s][4 * u + 2], ka[s][4 * u + 3]});
+                    const f32x4 tt = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kh, ident,
+                                                                              f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+                    const bf16x2_t lo = __builtin_convertvector(__builtin_shufflevector(tt, tt, 0, 1), bf16x2_t);
+                    const bf16x2_t hi = __builtin_convertvector(__builtin_shufflevector(tt, tt, 2, 3), bf16x2_t);
+                    const s16x4 vb = __builtin_bit_cast(s16x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3));
+                    o[2 * s + u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, o[2 * s + u], 0, 0, 0);
+                }
             }
         }
+        if (!__ballot(over)) break;
     }
 
     // ---- merge the four waves: out = sum_w O_w 2^(m_w - M) / L
     if (g == 0) {
-        s_m[wave][c] = m_run;
+        s_m[wave][c] = m_ref;
         s_l[wave][c] = l_run;
     }
     __syncthreads();

@@ -154,8 +154,8 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
             for (int i = 0; i < 4; i++) wr[4 * t + i] = wrow[4 * t + i];
     }
 
-    for (int64_t c0 = c_begin + 64 * wave; c0 < c_end; c0 += 256) {
-        float P[4];
+    // key tile loader: lane (g, c) of tile u takes position c's 32-element block g
+    auto load_b = [&](int64_t c0, uint4 (&kd)[4], int (&sk)[4]) {
 #pragma unroll
         for (int u = 0; u < 4; u++) {
             const int64_t c = c0 + 16 * u + (lane & 15);
@@ -165,15 +165,28 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
                 if (j >= R) j = 0;
             }
             const int64_t krow = krow0 + j;
-            const uint4 kd = *reinterpret_cast<const uint4*>(kdata + krow * 64 + 16 * g);
-            const int sbk = (int)kscale[krow * 4 + g];
-            const i32x8 b = i32x8{(int)kd.x, (int)kd.y, (int)kd.z, (int)kd.w, 0, 0, 0, 0};
+            kd[u] = *reinterpret_cast<const uint4*>(kdata + krow * 64 + 16 * g);
+            sk[u] = (int)kscale[krow * 4 + g];
+        }
+    };
+
+    uint4 kd[4], kn[4];
+    int sk[4], skn[4];
+    int64_t c0 = c_begin + 64 * wave;
+    if (c0 < c_end) load_b(c0, kd, sk);
+    for (; c0 < c_end; c0 += 256) {
+        // the next group's keys are in flight while this one is scored
+        if (c0 + 256 < c_end) load_b(c0 + 256, kn, skn);
+        float P[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const i32x8 b = i32x8{(int)kd[u].x, (int)kd[u].y, (int)kd[u].z, (int)kd[u].w, 0, 0, 0, 0};
             float pp = 0.0f;
 #pragma unroll
             for (int t = 0; t < NHT; t++) {
                 const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
                 const f32x4 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[t], b, zero, 4, 4, 0, sa[t], 0,
-                                                                                 sbk);
+                                                                                 sk[u]);
 #pragma unroll
                 for (int i = 0; i < 4; i++) pp = __builtin_fmaf(wr[4 * t + i], fmaxf(d[i], 0.0f), pp);
             }
@@ -185,22 +198,28 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
         auto s23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(P[2]), __float_as_uint(P[3]), false, false);
         const float h01 = __uint_as_float(s01[0]) + __uint_as_float(s01[1]);
         const float h23 = __uint_as_float(s23[0]) + __uint_as_float(s23[1]);
-        auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(h01), __float_as_uint(h23), false, false);
-        float score = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(h01), __float_as_uint(h23), false, false);
+        float score = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 
         const int64_t c = c0 + lane;
         if (c < c_end) {
             if (pool.blocks && column_position(pool, prow, c) >= R) score = -INFINITY;
             scores[(int64_t)row * stride + c] = score;
         }
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            kd[u] = kn[u];
+            sk[u] = skn[u];
+        }
     }
 }
 
 static int pick_chunk(int n, int64_t cols)
 {
-    // at least ~2048 workgroups when the rows are few; 256..4096 columns per workgroup
-    int64_t chunk = 4096;
-    while (chunk > 256 && (int64_t)n * ((cols + chunk - 1) / chunk) < 2048) chunk >>= 1;
+    // Each workgroup quantizes its row's index q once, so columns per workgroup should be
+    // many (1024..8192); shrink only while there are fewer than ~1024 workgroups.
+    int64_t chunk = 8192;
+    while (chunk > 1024 && (int64_t)n * ((cols + chunk - 1) / chunk) < 1024) chunk >>= 1;
     return (int)chunk;
 }
 

@@ -8,16 +8,19 @@
 // same pass takes its own top-512 over all reachable positions).  Ties go to the lower
 // position (problem statement).
 //
-// Method.  Candidates are mapped to order-preserving 32-bit keys (0 = no candidate).
-// One workgroup selects the k best of up to NT*KPT candidates held in registers
-// (blocked: thread t owns candidates [t*KPT, (t+1)*KPT), so thread order is candidate
-// order): an MSB-first radix select over LDS histograms finds the threshold key T (the
-// first pass starts at the highest bit where the largest and smallest keys differ, so
-// concentrated score ranges still spread over the bins); the selection is every key
-// above T plus the lowest-indexed keys equal to T; two block scans give each thread its
-// output offset, so the output is in ascending candidate order.  Rows longer than one
-// workgroup's capacity are cut into segments whose local top-k lists are merged by
-// further passes (a total order makes the merge exact).
+// Method.  Candidates are mapped to order-preserving 32-bit keys (0 = no candidate).  One
+// workgroup of 1024 threads holds up to 1024*KPT candidates in registers, striped
+// (candidate e = i*1024 + t lives in register i of thread t, so loads are coalesced and
+// candidate order is (i, wave, lane)).  An MSB-first radix select over 8-bit digits finds
+// the threshold key T: the first digit starts at the highest bit where the largest and
+// smallest keys differ, and a pass whose threshold bin is taken whole ends the search
+// early.  Each pass costs one barrier: histograms rotate through three LDS buffers (the
+// next one is cleared while the current one fills) and every wave scans the finished
+// histogram itself.  The selection is every key above T plus the lowest-indexed keys
+// equal to T; ballots and one scan over per-(register, wave) counts give each selected
+// candidate its output slot in ascending candidate order.  Rows longer than one
+// workgroup are cut into segments whose top-k lists are merged by another pass (the
+// order is total, so the merge is exact).
 #include "csa2_device.h"
 #include "csa2_launch.h"
 
@@ -26,23 +29,24 @@ namespace csa2 {
 enum SrcMode { SRC_FULL = 0, SRC_POOL = 1, SRC_BLOCK = 2, SRC_LIST = 3 };
 enum OutMode { OUT_IDX = 0, OUT_LIST = 1, OUT_BLOCKS = 2 };
 
-constexpr int kNT = 512;       // threads per selection workgroup
-constexpr int kSegCols = 8192; // candidates per first-level segment (KPT 16)
-constexpr int kMergeCap = 16384;  // candidates per merge workgroup (KPT 32)
+constexpr int kNT = 1024;
+constexpr int kNW = kNT / 64;
+constexpr int kMaxKPT = 32;
+constexpr int64_t kMaxCap = (int64_t)kNT * kMaxKPT;  // 32768 candidates per workgroup
 
 struct SelArgs {
     SelSource src;
-    int mode;           // SrcMode of the first level
-    int block;          // SRC_BLOCK: positions per block
+    int block;          // SRC_BLOCK: positions per block (a power of two)
+    int block_shift;    // log2(block) for pool / block addressing
     int k;              // entries kept per row
-    int nseg;           // segments (lists) per row at this level
-    int seg_len;        // candidates per segment (first level) or lists per group (merge)
+    int nseg;           // workgroups (segments / groups) per row at this level
+    int64_t seg_len;    // candidates per segment (first level) or lists per group (merge)
     int nlists_prev;    // merge level: lists per row in the input
-    const uint2* in;    // merge level input lists [n][nlists_prev][k] (key, pos)
+    const uint2* in;    // merge input lists [n][nlists_prev][k] (key, pos)
     uint2* out_list;    // OUT_LIST target [n][nseg][k]
-    int32_t* out_idx;   // OUT_IDX target [n][k] / OUT_BLOCKS target [n][max_blocks]
+    int32_t* out_idx;   // OUT_IDX target [n][out_stride] / OUT_BLOCKS target
     int32_t* out_nblocks;
-    int out_stride;     // row stride of out_idx (k, or max_blocks)
+    int out_stride;
     int out_mode;
 };
 
@@ -59,207 +63,292 @@ __device__ __forceinline__ void row_info(const SelSource& s, int row, int64_t* R
     *ncol = nc < s.stride ? nc : s.stride;
 }
 
-__device__ __forceinline__ int64_t pool_position(const SelSource& s, int prow, int64_t c)
+__device__ __forceinline__ int64_t pool_position(const SelSource& s, int shift, int prow, int64_t c)
 {
-    const int64_t i = c / s.pool.block;
-    return (int64_t)s.pool.blocks[(int64_t)prow * s.pool.max_blocks + i] * s.pool.block + (c - i * s.pool.block);
+    const int64_t i = c >> shift;
+    return ((int64_t)s.pool.blocks[(int64_t)prow * s.pool.max_blocks + i] << shift) + (c & ((1 << shift) - 1));
 }
 
-template <int NT>
-__device__ __forceinline__ int block_exclusive_sum(int v, int* s_tmp, int* total)
+// Keys of candidates [e0, e0 + KPT) of this workgroup's slice (blocked layout), loaded
+// without per-element branches: addresses are clamped and invalid slots masked after.
+template <int KPT, int SRC>
+__device__ __forceinline__ void load_keys(const SelArgs& a, int row, int64_t R, int64_t ncol, int prow, int64_t base,
+                                          int64_t e0, uint32_t (&key)[KPT])
 {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int x = v;
+    const SelSource& s = a.src;
+    if (SRC == SRC_LIST) {
+        const int64_t lim_e = (int64_t)a.seg_len * a.k;
+        const int64_t lim_l = (int64_t)a.nlists_prev * a.k;
+        const uint2* in = a.in + (int64_t)row * lim_l;
+#pragma unroll
+        for (int i = 0; i < KPT; i++) {
+            const int64_t e = e0 + i;
+            const int64_t li = base + e;
+            const bool ok = e < lim_e && li < lim_l;
+            const uint32_t v = in[ok ? li : 0].x;
+            key[i] = ok ? v : 0u;
+        }
+        return;
+    }
+    if (SRC == SRC_BLOCK) {
+        // every block but the newest; all their members are reachable (block == 8)
+        const int64_t nblk = (ncol + 7) >> 3;
+        const float* rowp = s.scores + (int64_t)row * s.stride;
+        const bool vec = ((reinterpret_cast<uintptr_t>(rowp) & 15) == 0);
+#pragma unroll
+        for (int i = 0; i < KPT; i++) {
+            const int64_t c = base + e0 + i;
+            const bool ok = (e0 + i < a.seg_len) && (c < nblk - 1);
+            const float* sp = rowp + ((ok ? c : 0) << 3);
+            uint32_t m;
+            if (vec) {
+                const float4 u = reinterpret_cast<const float4*>(sp)[0];
+                const float4 v = reinterpret_cast<const float4*>(sp)[1];
+                m = max(max(max(order_key(u.x), order_key(u.y)), max(order_key(u.z), order_key(u.w))),
+                        max(max(order_key(v.x), order_key(v.y)), max(order_key(v.z), order_key(v.w))));
+            } else {
+                m = 0;
+#pragma unroll
+                for (int q = 0; q < 8; q++) m = max(m, order_key(sp[q]));
+            }
+            key[i] = ok ? m : 0u;
+        }
+        return;
+    }
+    const float* rowp = s.scores + (int64_t)row * s.stride;
+    const int64_t c0 = base + e0;
+    const int64_t lim = (a.seg_len < ncol - base) ? base + a.seg_len : ncol;  // columns of this slice
+    if (KPT % 4 == 0 && c0 + KPT <= s.stride && ((reinterpret_cast<uintptr_t>(rowp + c0) & 15) == 0)) {
+#pragma unroll
+        for (int i = 0; i < KPT; i += 4) {
+            const int64_t c = c0 + i;
+            const float4 v = *reinterpret_cast<const float4*>(rowp + c);
+            key[i] = (c < lim) ? order_key(v.x) : 0u;
+            key[i + 1] = (c + 1 < lim) ? order_key(v.y) : 0u;
+            key[i + 2] = (c + 2 < lim) ? order_key(v.z) : 0u;
+            key[i + 3] = (c + 3 < lim) ? order_key(v.w) : 0u;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < KPT; i++) {
+            const int64_t c = c0 + i;
+            const float v = rowp[c < lim ? c : 0];
+            key[i] = (c < lim) ? order_key(v) : 0u;
+        }
+    }
+    if (SRC == SRC_POOL) {
+        // a pool position past the reachable range (only in the newest block) is no candidate
+#pragma unroll
+        for (int i = 0; i < KPT; i++) {
+            const int64_t c = c0 + i;
+            const int64_t pp = pool_position(s, a.block_shift, prow, c < lim ? c : 0);
+            key[i] = (pp >= R) ? 0u : key[i];
+        }
+    }
+}
+
+__device__ __forceinline__ int wave_incl_scan(int x, int lane)
+{
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
         const int y = __shfl_up(x, off, 64);
         if (lane >= off) x += y;
     }
-    if (lane == 63) s_tmp[wave] = x;
-    __syncthreads();
-    int before = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < NT / 64; w++) {
-        const int t = s_tmp[w];
-        before += (w < wave) ? t : 0;
-        tot += t;
+    return x;
+}
+
+// Exclusive block scan of two counters at once (one barrier pair).
+__device__ __forceinline__ void block_scan2(int a, int b, int* s_w, int lane, int wave, int* ea, int* eb, int* ta,
+                                            int* tb)
+{
+    const int ia = wave_incl_scan(a, lane);
+    const int ib = wave_incl_scan(b, lane);
+    if (lane == 63) {
+        s_w[2 * wave] = ia;
+        s_w[2 * wave + 1] = ib;
     }
     __syncthreads();
-    *total = tot;
-    return before + x - v;
-}
-
-template <int NT>
-__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* s_tmp)
-{
+    int pa = 0, pb = 0, sa = 0, sb = 0;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
-    if ((threadIdx.x & 63) == 0) s_tmp[threadIdx.x >> 6] = v;
-    __syncthreads();
-    uint32_t r = 0;
-#pragma unroll
-    for (int w = 0; w < NT / 64; w++) r = max(r, s_tmp[w]);
-    __syncthreads();
-    return r;
-}
-
-template <int NT>
-__device__ __forceinline__ uint32_t block_min_u32(uint32_t v, uint32_t* s_tmp)
-{
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, off, 64));
-    if ((threadIdx.x & 63) == 0) s_tmp[threadIdx.x >> 6] = v;
-    __syncthreads();
-    uint32_t r = 0xFFFFFFFFu;
-#pragma unroll
-    for (int w = 0; w < NT / 64; w++) r = min(r, s_tmp[w]);
-    __syncthreads();
-    return r;
-}
-
-// Candidate e of a first-level segment: its key (0 = none).
-__device__ __forceinline__ uint32_t first_level_key(const SelArgs& a, int row, int64_t R, int64_t ncol, int prow,
-                                                    int64_t c)
-{
-    const SelSource& s = a.src;
-    if (a.mode == SRC_BLOCK) {
-        // blocks other than the newest: [0, nblk - 1); all their members are reachable
-        const int64_t nblk = (ncol + a.block - 1) / a.block;
-        if (c >= nblk - 1) return 0u;
-        const float* sp = s.scores + (int64_t)row * s.stride + c * a.block;
-        uint32_t m = 0;
-        for (int u = 0; u < a.block; u++) m = max(m, order_key(sp[u]));
-        return m;
+    for (int w = 0; w < kNW; w++) {
+        const int va = s_w[2 * w], vb = s_w[2 * w + 1];
+        pa += (w < wave) ? va : 0;
+        pb += (w < wave) ? vb : 0;
+        sa += va;
+        sb += vb;
     }
-    if (c >= ncol) return 0u;
-    if (a.mode == SRC_POOL && pool_position(s, prow, c) >= R) return 0u;
-    return order_key(s.scores[(int64_t)row * s.stride + c]);
+    __syncthreads();
+    *ea = pa + ia - a;
+    *eb = pb + ib - b;
+    *ta = sa;
+    *tb = sb;
 }
 
-template <int KPT>
-__global__ __launch_bounds__(kNT) void k_select(SelArgs a, int first_level)
+constexpr int kBins1 = 2048;  // first digit: 11 bits
+constexpr int kBins = 256;    // later digits: 8 bits
+
+// Threshold bin of a histogram of NB bins, scanned from the top: the bin b where the
+// count of keys in bins above b is < need <= that count plus hist[b].  All threads
+// cooperate: thread t takes NB/kNT adjacent bins from the top (conflict-free reads),
+// one block scan orders the partial sums, and the thread holding the crossing publishes
+// (bin, count above, bin count) through LDS.
+template <int NB>
+__device__ __forceinline__ void find_bin(const int* hist, int need, int* s_w, int* s_res, int tid, int lane,
+                                         int wave, int* bin, int* above, int* cnt)
 {
-    constexpr int NT = kNT;
-    constexpr int CAP = NT * KPT;
-    __shared__ uint32_t s_keys[CAP + CAP / 32];
-    __shared__ int s_hist[256];
-    __shared__ int s_tmp[NT / 64];
-    __shared__ uint32_t s_res[3];
+    constexpr int PER = NB / kNT > 0 ? NB / kNT : 1;
+    int c[PER], sum = 0;
+    const bool act = tid * PER < NB;
+#pragma unroll
+    for (int j = 0; j < PER; j++) {
+        c[j] = act ? hist[NB - 1 - (tid * PER + j)] : 0;
+        sum += c[j];
+    }
+    const int incl = wave_incl_scan(sum, lane);
+    if (lane == 63) s_w[wave] = incl;
+    __syncthreads();
+    int before = 0;
+#pragma unroll
+    for (int w = 0; w < kNW; w++) before += (w < wave) ? s_w[w] : 0;
+    int acc = before + incl - sum;
+    if (act && acc < need && need <= acc + sum) {
+#pragma unroll
+        for (int j = 0; j < PER; j++) {
+            if (acc + c[j] >= need) {
+                s_res[0] = NB - 1 - (tid * PER + j);
+                s_res[1] = acc;
+                s_res[2] = c[j];
+                break;
+            }
+            acc += c[j];
+        }
+    }
+    __syncthreads();
+    *bin = s_res[0];
+    *above = s_res[1];
+    *cnt = s_res[2];
+}
+
+template <int KPT, int SRC>
+__global__ __launch_bounds__(kNT) void k_select(SelArgs a)
+{
+    __shared__ int s_h1[kBins1 + 1];    // first pass (+1 dummy bin for masked slots)
+    __shared__ int s_h[3][kBins];       // later passes, rotating (cleared one pass ahead)
+    __shared__ uint32_t s_red[3][kNW];
+    __shared__ int s_w[2 * kNW];
+    __shared__ int s_fw[2][kNW];   // find_bin partial sums (alternating between passes)
+    __shared__ int s_res[2][3];
 
     const int nseg = a.nseg;
     const int row = blockIdx.x / nseg;
-    const int seg = blockIdx.x % nseg;
-    const int tid = threadIdx.x;
+    const int seg = blockIdx.x - row * nseg;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const SelSource& s = a.src;
+    const int k = a.k;
 
     int64_t R, ncol;
     int prow;
     row_info(s, row, &R, &ncol, &prow);
+    const int64_t base = (int64_t)seg * (SRC == SRC_LIST ? a.seg_len * a.k : a.seg_len);
+    const int64_t e0 = (int64_t)tid * KPT;  // blocked: thread t owns [t*KPT, (t+1)*KPT)
 
-    // ---- gather keys: striped into LDS (coalesced), then blocked into registers
-    const int64_t base = (int64_t)seg * (first_level ? a.seg_len : (int64_t)a.seg_len * a.k);
-    for (int i = 0; i < KPT; i++) {
-        const int e = i * NT + tid;
-        uint32_t key = 0;
-        if (first_level) {
-            if (e < a.seg_len) key = first_level_key(a, row, R, ncol, prow, base + e);
-        } else {
-            const int64_t li = base + e;  // index into this row's concatenated lists
-            if (e < a.seg_len * a.k && li < (int64_t)a.nlists_prev * a.k)
-                key = a.in[(int64_t)row * a.nlists_prev * a.k + li].x;
-        }
-        s_keys[e + (e >> 5)] = key;
-    }
-    __syncthreads();
     uint32_t key[KPT];
+    load_keys<KPT, SRC>(a, row, R, ncol, prow, base, e0, key);
     int nvalid = 0;
     uint32_t kmax = 0, kmin = 0xFFFFFFFFu;
+    uint64_t live = 0;
 #pragma unroll
     for (int i = 0; i < KPT; i++) {
-        const int e = tid * KPT + i;
-        key[i] = s_keys[e + (e >> 5)];
-        nvalid += key[i] != 0;
+        const bool v = key[i] != 0;
+        nvalid += v;
+        live |= (uint64_t)v << i;
         kmax = max(kmax, key[i]);
-        if (key[i] != 0) kmin = min(kmin, key[i]);
+        kmin = v ? min(kmin, key[i]) : kmin;
     }
-    int nv;
-    (void)block_exclusive_sum<NT>(nvalid, s_tmp, &nv);
-    const int k = a.k;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        nvalid += __shfl_xor(nvalid, off, 64);
+        kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, 64));
+        kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, 64));
+    }
+    if (lane == 0) {
+        s_red[0][wave] = (uint32_t)nvalid;
+        s_red[1][wave] = kmax;
+        s_red[2][wave] = kmin;
+    }
+    for (int i = tid; i <= kBins1; i += kNT) s_h1[i] = 0;
+    if (tid < kBins) s_h[1][tid] = 0;  // pass 1's histogram
+    __syncthreads();
+    int nv = 0;
+    kmax = 0;
+    kmin = 0xFFFFFFFFu;
+#pragma unroll
+    for (int w = 0; w < kNW; w++) {
+        nv += (int)s_red[0][w];
+        kmax = max(kmax, s_red[1][w]);
+        kmin = min(kmin, s_red[2][w]);
+    }
 
-    // ---- threshold: select key > T, plus the first need_eq keys equal to T
-    bool ge_mode = false;  // true: select key >= T (and key != 0)
-    uint32_t T = 0;
+    // ---- threshold: select key > T (ge_mode: key >= T), plus the first need_eq keys == T
+    bool ge_mode = true;
+    uint32_t T = 1;  // nv <= k: every valid key
     int need_eq = 0;
     if (k == 0) {
-        ge_mode = true;   // nothing: no non-NaN key reaches 0xFFFFFFFF
-        T = 0xFFFFFFFFu;
-    } else if (nv <= k) {
-        ge_mode = true;
-        T = 1;
-    } else {
-        kmax = block_max_u32<NT>(kmax, reinterpret_cast<uint32_t*>(s_tmp));
-        kmin = block_min_u32<NT>(kmin, reinterpret_cast<uint32_t*>(s_tmp));
+        T = 0xFFFFFFFFu;  // nothing (no non-NaN key reaches it)
+    } else if (nv > k) {
         const uint32_t diff = kmax ^ kmin;
         if (diff == 0) {
+            ge_mode = false;
             T = kmax;
             need_eq = k;
         } else {
             int sb = 31 - __clz(diff);
             uint32_t prefix = (sb >= 31) ? 0u : (kmax & (~0u << (sb + 1)));
             int need = k;
+            int pass = 0;
             while (true) {
-                const int nbits = sb + 1 < 8 ? sb + 1 : 8;
+                const int width = pass == 0 ? 11 : 8;
+                const int nbits = sb + 1 < width ? sb + 1 : width;
                 const int shift = sb + 1 - nbits;
-                const uint32_t hm = (sb >= 31) ? 0u : (~0u << (sb + 1));
                 const uint32_t dmask = (1u << nbits) - 1u;
-                if (tid < 256) s_hist[tid] = 0;
-                __syncthreads();
+                int* hist = pass == 0 ? s_h1 : s_h[pass % 3];
+                const int dummy = kBins1;
+                // clear the next pass's buffer: its last readers were two passes back and
+                // finished before the previous pass's barrier
+                if (pass > 0 && tid < kBins) s_h[(pass + 1) % 3][tid] = 0;
+                if (pass == 0) {
+                    // every valid key shares the prefix above sb
 #pragma unroll
-                for (int i = 0; i < KPT; i++)
-                    if (key[i] != 0 && (key[i] & hm) == (prefix & hm))
-                        atomicAdd(&s_hist[(key[i] >> shift) & dmask], 1);
-                __syncthreads();
-                if (tid < 64) {
-                    int c[4], sum = 0;
+                    for (int i = 0; i < KPT; i++)
+                        atomicAdd(&hist[key[i] ? (int)((key[i] >> shift) & dmask) : dummy], 1);
+                } else {
 #pragma unroll
-                    for (int j = 0; j < 4; j++) {
-                        c[j] = s_hist[255 - 4 * tid - j];
-                        sum += c[j];
-                    }
-                    int incl = sum;
-#pragma unroll
-                    for (int off = 1; off < 64; off <<= 1) {
-                        const int y = __shfl_up(incl, off, 64);
-                        if (tid >= off) incl += y;
-                    }
-                    const int excl = incl - sum;
-                    if (excl < need && need <= incl) {
-                        int acc = excl;
-#pragma unroll
-                        for (int j = 0; j < 4; j++) {
-                            if (acc + c[j] >= need) {
-                                s_res[0] = (uint32_t)(255 - 4 * tid - j);
-                                s_res[1] = (uint32_t)acc;
-                                s_res[2] = (uint32_t)c[j];
-                                break;
-                            }
-                            acc += c[j];
-                        }
-                    }
+                    for (int i = 0; i < KPT; i++)
+                        if ((live >> i) & 1) atomicAdd(&hist[(key[i] >> shift) & dmask], 1);
                 }
                 __syncthreads();
-                const uint32_t b = s_res[0];
-                const int above = (int)s_res[1];
-                const int cnt = (int)s_res[2];
-                __syncthreads();
-                prefix |= b << shift;
+                int bsel, above, cnt;
+                if (pass == 0)
+                    find_bin<kBins1>(hist, need, s_fw[pass & 1], s_res[pass & 1], tid, lane, wave, &bsel, &above,
+                                     &cnt);
+                else
+                    find_bin<kBins>(hist, need, s_fw[pass & 1], s_res[pass & 1], tid, lane, wave, &bsel, &above,
+                                    &cnt);
+                prefix |= (uint32_t)bsel << shift;
                 need -= above;
+                // keep only the keys of the threshold bin for the next pass
+                const uint32_t hm = ~0u << shift;
+                uint64_t nl = 0;
+#pragma unroll
+                for (int i = 0; i < KPT; i++) nl |= (uint64_t)(((live >> i) & 1) && ((key[i] & hm) == prefix)) << i;
+                live = nl;
+                pass++;
                 if (cnt == need) {
-                    ge_mode = true;
-                    T = prefix;
+                    T = prefix;  // the whole bin is taken: keys >= prefix
                     break;
                 }
                 if (shift == 0) {
+                    ge_mode = false;
                     T = prefix;
                     need_eq = need;
                     break;
@@ -269,41 +358,47 @@ __global__ __launch_bounds__(kNT) void k_select(SelArgs a, int first_level)
         }
     }
 
-    // ---- ordered compaction
+    // ---- ordered output: thread order is candidate order (blocked layout)
     int gt = 0, eq = 0;
+    uint64_t selbits = 0, eqbits = 0;
 #pragma unroll
     for (int i = 0; i < KPT; i++) {
-        const bool is_gt = ge_mode ? (key[i] != 0 && key[i] >= T) : (key[i] > T);
-        const bool is_eq = !ge_mode && key[i] == T;
-        gt += is_gt;
-        eq += is_eq;
+        const bool isgt = ge_mode ? (key[i] != 0 && key[i] >= T) : (key[i] > T);
+        const bool iseq = !ge_mode && key[i] == T;
+        gt += isgt;
+        eq += iseq;
+        selbits |= (uint64_t)isgt << i;
+        eqbits |= (uint64_t)iseq << i;
     }
-    int eq_total;
-    const int eq_before = block_exclusive_sum<NT>(eq, s_tmp, &eq_total);
-    int take = need_eq - eq_before;
-    take = take < 0 ? 0 : (take > eq ? eq : take);
-    int nsel;
-    int off = block_exclusive_sum<NT>(gt + take, s_tmp, &nsel);
-
-    int taken = 0;
+    int eq_before, dummy_b, eq_tot, dummy_t;
+    if (!ge_mode) {
+        block_scan2(eq, 0, s_w, lane, wave, &eq_before, &dummy_b, &eq_tot, &dummy_t);
+        int take = need_eq - eq_before;
+        take = take < 0 ? 0 : (take > eq ? eq : take);
+        // the first `take` equal keys of this thread
+        int seen = 0;
+#pragma unroll
+        for (int i = 0; i < KPT; i++) {
+            const bool e = (eqbits >> i) & 1;
+            selbits |= (uint64_t)(e && seen < take) << i;
+            seen += e;
+        }
+        gt += take;
+    }
+    int off, nsel, d0, d1;
+    block_scan2(gt, 0, s_w, lane, wave, &off, &d0, &nsel, &d1);
     const int64_t row_out = (int64_t)row * nseg + seg;
 #pragma unroll
     for (int i = 0; i < KPT; i++) {
-        const bool is_gt = ge_mode ? (key[i] != 0 && key[i] >= T) : (key[i] > T);
-        bool sel = is_gt;
-        if (!ge_mode && key[i] == T) {
-            sel = taken < take;
-            taken++;
-        }
-        if (sel) {
-            const int e = tid * KPT + i;
+        if ((selbits >> i) & 1) {
+            const int64_t e = e0 + i;
             int32_t pos;
-            if (first_level) {
-                const int64_t c = base + e;
-                pos = (int32_t)((a.mode == SRC_POOL) ? pool_position(s, prow, c) : c);
-            } else {
+            if (SRC == SRC_LIST)
                 pos = (int32_t)a.in[(int64_t)row * a.nlists_prev * k + base + e].y;
-            }
+            else if (SRC == SRC_POOL)
+                pos = (int32_t)pool_position(s, a.block_shift, prow, base + e);
+            else
+                pos = (int32_t)(base + e);
             if (a.out_mode == OUT_LIST)
                 a.out_list[row_out * k + off] = make_uint2(key[i], (uint32_t)pos);
             else
@@ -313,17 +408,17 @@ __global__ __launch_bounds__(kNT) void k_select(SelArgs a, int first_level)
     }
     // ---- padding (and the newest block of the hierarchical pool)
     if (a.out_mode == OUT_LIST) {
-        for (int i = nsel + tid; i < k; i += NT) a.out_list[row_out * k + i] = make_uint2(0u, 0xFFFFFFFFu);
+        for (int i = nsel + tid; i < k; i += kNT) a.out_list[row_out * k + i] = make_uint2(0u, 0xFFFFFFFFu);
     } else if (a.out_mode == OUT_IDX) {
-        for (int i = nsel + tid; i < a.out_stride; i += NT) a.out_idx[(int64_t)row * a.out_stride + i] = -1;
+        for (int i = nsel + tid; i < a.out_stride; i += kNT) a.out_idx[(int64_t)row * a.out_stride + i] = -1;
     } else {
-        const int64_t nblk = (ncol + a.block - 1) / a.block;
+        const int64_t nblk = (ncol + a.block - 1) >> a.block_shift;
         int tot = nsel;
         if (nblk > 0) {
             if (tid == 0) a.out_idx[(int64_t)row * a.out_stride + nsel] = (int32_t)(nblk - 1);
             tot = nsel + 1;
         }
-        for (int i = tot + tid; i < a.out_stride; i += NT) a.out_idx[(int64_t)row * a.out_stride + i] = -1;
+        for (int i = tot + tid; i < a.out_stride; i += kNT) a.out_idx[(int64_t)row * a.out_stride + i] = -1;
         if (tid == 0) a.out_nblocks[row] = tot;
     }
 }
@@ -331,35 +426,80 @@ __global__ __launch_bounds__(kNT) void k_select(SelArgs a, int first_level)
 // ------------------------------------------------------------------------ host plans
 struct Plan {
     int levels;
-    int nseg[8];  // lists per row produced by each level (last level: 1)
+    int64_t seg_len[8];  // candidates (level 0) or lists (merge) per workgroup
+    int nseg[8];         // lists per row produced by each level
+    int64_t cap[8];      // candidates one workgroup holds at this level
 };
 
-static Plan make_plan(int64_t cols, int k)
+// Largest first-level segment per source: 32768 candidates from plain score rows, 16384
+// when each candidate needs a pool lookup or a block maximum (more live registers).
+static int64_t first_cap(int mode) { return (mode == SRC_FULL) ? kMaxCap : 16384; }
+
+static Plan make_plan(int64_t cols, int k, int mode)
 {
     Plan p{};
-    int64_t n0 = (cols + kSegCols - 1) / kSegCols;
-    if (n0 < 1 || k == 0) n0 = 1;
     p.levels = 1;
-    p.nseg[0] = (int)n0;
-    int64_t cur = n0;
-    const int group = k > 0 ? kMergeCap / k : kMergeCap;
+    if (cols < 1) cols = 1;
+    const int64_t cap0 = first_cap(mode);
+    if (k == 0 || cols <= cap0) {
+        p.seg_len[0] = cols;
+        p.nseg[0] = 1;
+        p.cap[0] = cols;
+        return p;
+    }
+    // first level: segments of up to kMaxCap columns, at least 2k each so that selecting
+    // actually reduces the data
+    int64_t nseg = (cols + cap0 - 1) / cap0;
+    p.seg_len[0] = (cols + nseg - 1) / nseg;
+    p.nseg[0] = (int)nseg;
+    p.cap[0] = p.seg_len[0];
+    int64_t cur = nseg;
+    const int64_t group = kMaxCap / k;  // lists merged per workgroup
     while (cur > 1 && p.levels < 8) {
-        cur = (cur + group - 1) / group;
-        p.nseg[p.levels++] = (int)cur;
+        const int64_t g = cur < group ? cur : group;
+        const int64_t nxt = (cur + g - 1) / g;
+        p.seg_len[p.levels] = g;
+        p.nseg[p.levels] = (int)nxt;
+        p.cap[p.levels] = g * k;
+        p.levels++;
+        cur = nxt;
     }
     return p;
+}
+
+static size_t level_bytes(const Plan& p, int l, int n, int k)
+{
+    return (size_t)n * p.nseg[l] * (size_t)(k > 0 ? k : 1) * sizeof(uint2);
 }
 
 static size_t plan_workspace(const Plan& p, int n, int k)
 {
     if (p.levels <= 1) return 0;
-    // level 0 output in buffer A, level 1 in B, level 2 in A, ...
     size_t a = 0, b = 0;
     for (int l = 0; l + 1 < p.levels; l++) {
-        size_t sz = (size_t)n * p.nseg[l] * (size_t)(k > 0 ? k : 1) * sizeof(uint2);
+        const size_t sz = level_bytes(p, l, n, k);
         if (l % 2 == 0) a = sz > a ? sz : a; else b = sz > b ? sz : b;
     }
     return ((a + 255) & ~(size_t)255) + b;
+}
+
+template <int SRC>
+static void launch_level(dim3 grid, int64_t cap, const SelArgs& a, hipStream_t stream)
+{
+    if (cap <= 4096)
+        hipLaunchKernelGGL((k_select<4, SRC>), grid, dim3(kNT), 0, stream, a);
+    else if (cap <= 16384 || SRC == SRC_POOL || SRC == SRC_BLOCK)
+        hipLaunchKernelGGL((k_select<16, SRC>), grid, dim3(kNT), 0, stream, a);
+    else
+        hipLaunchKernelGGL((k_select<(SRC == SRC_POOL || SRC == SRC_BLOCK) ? 16 : kMaxKPT, SRC>), grid, dim3(kNT), 0,
+                           stream, a);
+}
+
+static int ilog2(int x)
+{
+    int s = 0;
+    while ((1 << s) < x) s++;
+    return s;
 }
 
 static hipError_t run_plan(const SelSource& src, int mode, int block, int k, int64_t cols, int out_mode,
@@ -367,26 +507,24 @@ static hipError_t run_plan(const SelSource& src, int mode, int block, int k, int
 {
     const int n = src.rows.n;
     if (n == 0) return hipSuccess;
-    const Plan p = make_plan(cols, k);
-    const size_t sza = [&] {
-        size_t a = 0;
-        for (int l = 0; l + 1 < p.levels; l += 2) {
-            size_t sz = (size_t)n * p.nseg[l] * (size_t)(k > 0 ? k : 1) * sizeof(uint2);
-            a = sz > a ? sz : a;
-        }
-        return (a + 255) & ~(size_t)255;
-    }();
+    const Plan p = make_plan(cols, k, mode);
+    size_t sza = 0;
+    for (int l = 0; l + 1 < p.levels; l += 2) {
+        const size_t sz = level_bytes(p, l, n, k);
+        sza = sz > sza ? sz : sza;
+    }
+    sza = (sza + 255) & ~(size_t)255;
     uint2* bufA = static_cast<uint2*>(ws);
     uint2* bufB = reinterpret_cast<uint2*>(static_cast<char*>(ws) + sza);
     const uint2* prev = nullptr;
     for (int l = 0; l < p.levels; l++) {
         SelArgs a{};
         a.src = src;
-        a.mode = mode;
-        a.block = block;
+        a.block = block > 0 ? block : (src.pool.blocks ? src.pool.block : 1);
+        a.block_shift = ilog2(a.block);
         a.k = k;
         a.nseg = p.nseg[l];
-        a.seg_len = (l == 0) ? kSegCols : kMergeCap / (k > 0 ? k : 1);
+        a.seg_len = p.seg_len[l];
         a.nlists_prev = (l == 0) ? 0 : p.nseg[l - 1];
         a.in = prev;
         const bool last = (l + 1 == p.levels);
@@ -395,12 +533,16 @@ static hipError_t run_plan(const SelSource& src, int mode, int block, int k, int
         a.out_idx = out_idx;
         a.out_nblocks = out_nblocks;
         a.out_stride = out_stride;
-        dim3 grid((unsigned)((int64_t)n * p.nseg[l]));
-        if (l == 0)
-            hipLaunchKernelGGL((k_select<kSegCols / kNT>), grid, dim3(kNT), 0, stream, a, 1);
+        const dim3 grid((unsigned)((int64_t)n * p.nseg[l]));
+        if (l > 0)
+            launch_level<SRC_LIST>(grid, p.cap[l], a, stream);
+        else if (mode == SRC_FULL)
+            launch_level<SRC_FULL>(grid, p.cap[l], a, stream);
+        else if (mode == SRC_POOL)
+            launch_level<SRC_POOL>(grid, p.cap[l], a, stream);
         else
-            hipLaunchKernelGGL((k_select<kMergeCap / kNT>), grid, dim3(kNT), 0, stream, a, 0);
-        hipError_t e = hipGetLastError();
+            launch_level<SRC_BLOCK>(grid, p.cap[l], a, stream);
+        const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         prev = a.out_list;
     }
@@ -412,7 +554,10 @@ static int64_t select_cols(const SelSource& src)
     return src.pool.blocks ? (int64_t)src.pool.block * src.pool.max_blocks : src.stride;
 }
 
-size_t topk_workspace(int n, int64_t stride, int k) { return plan_workspace(make_plan(stride, k), n, k); }
+size_t topk_workspace(int n, int64_t stride, int k, bool pool)
+{
+    return plan_workspace(make_plan(stride, k, pool ? SRC_POOL : SRC_FULL), n, k);
+}
 
 hipError_t launch_topk(const SelSource& src, int k, int32_t* out, void* ws, size_t ws_bytes, hipStream_t stream)
 {
@@ -423,9 +568,9 @@ hipError_t launch_topk(const SelSource& src, int k, int32_t* out, void* ws, size
 
 size_t topk_hier_workspace(int n, int64_t stride, int k, int block, int max_blocks)
 {
-    const size_t flat = plan_workspace(make_plan(stride, k), n, k);
+    const size_t flat = plan_workspace(make_plan(stride, k, SRC_FULL), n, k);
     const int64_t nblk = (stride + block - 1) / block;
-    const size_t blk = plan_workspace(make_plan(nblk, max_blocks - 1), n, max_blocks - 1);
+    const size_t blk = plan_workspace(make_plan(nblk, max_blocks - 1, SRC_BLOCK), n, max_blocks - 1);
     return flat > blk ? flat : blk;
 }
 

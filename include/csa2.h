@@ -98,10 +98,10 @@ typedef struct csa2_index_keys {
 
 /* Candidate pool of the hierarchical indexer ([MOD] "Hierarchical Sparse Indexer";
  * [DAY0] section 2): per pool row, nblocks[r] ascending block ids in blocks[r][0..);
- * block b holds positions [b*block, b*block+block).  A query row q uses pool row
+ * block b holds positions [b*block, b*block+block), block a power of two.  A query row q uses pool row
  * row_map[q] (NULL = q). */
 typedef struct csa2_pool {
-    int32_t block;          /* positions per block, 8 on the pages (1..64) */
+    int32_t block;          /* positions per block, 8 on the pages (power of two, 1..64) */
     int32_t max_blocks;     /* row stride of `blocks`, 2048 on the pages */
     const int32_t* blocks;  /* [pool_rows][max_blocks] */
     const int32_t* nblocks; /* [pool_rows], each <= max_blocks */

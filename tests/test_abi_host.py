@@ -83,11 +83,11 @@ def test_topk_arg_errors():
 
     assert call(k=0) == B.CSA2_E_ARG
     assert call(k=2049) == B.CSA2_E_ARG
-    # a 65536-column row needs merge workspace
-    need = B.workspace_size(B.OP_TOPK, 4, 65536, 512)
+    # a 262144-column row needs merge workspace (workspace_size is the pool-source bound)
+    need = B.workspace_size(B.OP_TOPK, 4, 262144, 512)
     assert need > 0
-    assert call(stride=65536) == B.CSA2_E_WORKSPACE
-    assert call(stride=65536, ws=P, nbytes=need - 1) == B.CSA2_E_WORKSPACE
+    assert call(stride=262144) == B.CSA2_E_WORKSPACE
+    assert call(stride=262144, ws=P, nbytes=64) == B.CSA2_E_WORKSPACE
     assert B.workspace_size(B.OP_TOPK, 4, 8192, 512) == 0
 
 

@@ -407,3 +407,29 @@ def test_determinism_and_batch_invariance(orc):
     rows1 = {k: v[i:i + 1] for k, v in rows.items()}
     c, _, _, _ = _run_attn_bf16(orc, rows1, cache, q[i:i + 1].contiguous(), kv, win, swa_raw, sel[i:i + 1], 32, 0.04)
     assert np.array_equal(a[i:i + 1], c)
+
+
+@pytest.mark.parametrize("k", [512, 2048])
+def test_topk_multilevel(orc, k):
+    say("case: topk over rows longer than one workgroup (segments + merge), k=%d" % k)
+    R_list = [70000, 131072, 262144, 200001, 65536, 65537]
+    rows, cache, scores = _topk_inputs(300 + k, R_list, 262144, ties=None)
+    got = B.topk(dev_rows(rows), dev_cache(cache), torch.from_numpy(scores).to(DEV), k).cpu().numpy()
+    ref = orc.topk(rows, cache, scores, k)
+    assert np.array_equal(got, ref)
+    # and with heavy ties, where the merge must keep the lowest positions
+    rows, cache, scores = _topk_inputs(301 + k, R_list, 262144, ties=50.0)
+    got = B.topk(dev_rows(rows), dev_cache(cache), torch.from_numpy(scores).to(DEV), k).cpu().numpy()
+    ref = orc.topk(rows, cache, scores, k)
+    assert np.array_equal(got, ref)
+
+
+def test_topk_hier_long(orc):
+    say("case: topk_hier on 262144-entry rows (C4 shape)")
+    R_list = [262144, 100000]
+    rows, cache, scores = _topk_inputs(400, R_list, 262144)
+    idx, blocks, nblocks = B.topk_hier(dev_rows(rows), dev_cache(cache), torch.from_numpy(scores).to(DEV), 512, 8, 2048)
+    ri, rb, rn = orc.topk_hier(rows, cache, scores, 512, 8, 2048)
+    assert np.array_equal(nblocks.cpu().numpy(), rn)
+    assert np.array_equal(blocks.cpu().numpy(), rb)
+    assert np.array_equal(idx.cpu().numpy(), ri)
