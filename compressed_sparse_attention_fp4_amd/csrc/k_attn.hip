@@ -112,25 +112,68 @@ __global__ __launch_bounds__(256) void k_attn_f32(RowsArg rows, CacheArg cache, 
 }
 
 // ----------------------------------------------------------------------------- bf16
-// MQA with one shared 512-d latent (key = value) on bf16 MFMA.
+// MQA with one shared 512-d latent (key = value) on bf16 MFMA, for dim 512.
 //
 // Workgroup = 4 waves on one query row and 16 heads (h0 .. h0+15).  The row's key list
-// (selected entries with -1 removed, then window positions) is cut into tiles of 16 keys;
-// wave w takes tiles w, w+4, ... and keeps its own online-softmax state and output.
-//   * K tile = A operand of S^T = K Q^T (v_mfma_f32_16x16x32_bf16, 16 steps over 512
-//     dims): lane (g, c) holds key c, dims [32s+8g, 32s+8g+8).  Window rows in FP8 are
-//     dequantized to bf16 on load (exact: E4M3 times a power of two).
+// (selected entries with -1 removed and padded to a multiple of 16, then the window
+// positions) is cut into tiles of 16 keys; wave w takes tiles w, w+4, ... with its own
+// online-softmax state and output.  Each wave double-buffers its tiles in LDS: while it
+// computes on one tile, the next one is already on its way (selected rows by direct
+// global-to-LDS copies, one 1 KiB row per instruction; FP8 window rows are dequantized
+// to bf16 through registers: E4M3 times a power of two is exact in bf16).
+//   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16, 16 steps over the 512 dims: A = K rows
+//     from LDS (lane (g, c) holds key c, dims [32s+8g, +8)), B = Q^T in registers.
 //   * S^T output: lane (g, c) holds keys 4g..4g+3 of head c, which is the A operand of
 //     P V with v_mfma_f32_16x16x16_bf16 (keys are the contraction index).
-//   * V = K transposed: v_mfma_f32_16x16x16_bf16 of a 16-key x 16-dim K slice with the
-//     identity gives, in lane (g, c), keys 4g..4g+3 of one dim: the B operand of P V.
-//     Output tile 2s+u column c is dim 32s + 8(c/4) + 4u + c%4.
-//   * Output O: 32 tiles of 16 heads x 16 dims; lane (g, c) holds heads 4g..4g+3.
+//   * The V operand (lane (g, c): keys 4g..4g+3 of dim c) comes straight from the row-
+//     major tile with the LDS transpose read ds_read_b64_tr_b16: within a 16-lane group,
+//     element j of lane i comes from the 8-byte chunk that lane 4j + i/4 addresses, so
+//     lane (g, 4j+q) points at V[4g+j][16t+4q].
+//   * Output O: 32 tiles of 16 heads x 16 dims (lane (g, c): heads 4g..4g+3, dim 16t+c).
 // The four waves' partial results are merged in fixed order through LDS.
 // Blocks are mapped so that the head groups of one row share an XCD (and its L2): block
 // b serves row 8*(b / (8*NHG)) + b%8 and head group (b/8) % NHG.
 constexpr int kAttnD = 512;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kRowBytes = kAttnD * 2 + 32;           // LDS row pitch of a tile (32 B pad)
+constexpr int kTileBytes = 16 * kRowBytes;            // one tile of 16 keys
+constexpr int kWaveBytes = 2 * kTileBytes;            // double buffer per wave
+constexpr int kMergeBytes = 4 * 16 * (256 + 4) * 4;   // merge scratch (aliases the tiles)
+static_assert(kMergeBytes <= 4 * kWaveBytes, "merge scratch must fit in the tile buffers");
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p)
+{
+    return (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p);
+}
+
+// Copy one 1 KiB row from global memory into LDS at byte address `lds` (wave-uniform):
+// lane l moves bytes [16 l, 16 l + 16).  The copy is asynchronous; it is complete once
+// the wave's vector-memory counter has dropped past it (s_waitcnt vmcnt).  Issued as
+// inline assembly so the compiler does not add a wait for it before unrelated LDS reads.
+__device__ __forceinline__ void dma_row(const void* gptr, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gptr)
+                 : "memory", "m0");
+}
+
+// Reductions over the four 16-lane rows (lanes c, c+16, c+32, c+48).
+__device__ __forceinline__ float max_over_g(float x)
+{
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float sum_over_g(float x)
+{
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p)
 {
@@ -138,9 +181,8 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p)
     return __builtin_bit_cast(bf16x8, u);
 }
 
-__device__ __forceinline__ bf16x8 load_fp8x8_as_bf16(const uint8_t* p, float scale)
+__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 u, float scale)
 {
-    const uint2 u = *reinterpret_cast<const uint2*>(p);
     bf16x8 r;
 #define CSA2_CVT(word, b, idx) r[idx] = (__bf16)(__builtin_amdgcn_cvt_f32_fp8((int)(word), b) * scale)
     CSA2_CVT(u.x, 0, 0);
@@ -152,7 +194,7 @@ __device__ __forceinline__ bf16x8 load_fp8x8_as_bf16(const uint8_t* p, float sca
     CSA2_CVT(u.y, 2, 6);
     CSA2_CVT(u.y, 3, 7);
 #undef CSA2_CVT
-    return r;
+    return __builtin_bit_cast(uint4, r);
 }
 
 __global__ __launch_bounds__(256) void k_attn_bf16(RowsArg rows, CacheArg cache, const uint16_t* __restrict__ q,
@@ -162,11 +204,10 @@ __global__ __launch_bounds__(256) void k_attn_bf16(RowsArg rows, CacheArg cache,
                                                    float sm_scale, const float* __restrict__ sink,
                                                    uint16_t* __restrict__ out, float* __restrict__ lse)
 {
-    __shared__ int32_t s_sel[2048];
+    __shared__ __attribute__((aligned(16))) char s_tiles[4 * kWaveBytes];
+    __shared__ __attribute__((aligned(16))) int32_t s_sel[2048];
     __shared__ int s_tmp[8];
     __shared__ float s_m[4][16], s_l[4][16];
-    __shared__ float s_o[4][16][256 + 4];  // one half of the dims at a time
-    __shared__ uint4 s_q[16][64];          // Q^T operand: step s, lane (g, c)
 
     const int b = blockIdx.x;
     const int row = 8 * (b / (8 * nhg)) + (b & 7);
@@ -199,22 +240,68 @@ __global__ __launch_bounds__(256) void k_attn_bf16(RowsArg rows, CacheArg cache,
     // Key slots: [0, nsel) selected entries, [nsel, sel_pad) padding (masked), then the
     // window; sel_pad = nsel rounded up to a tile, so every tile is of one kind.
     const int sel_pad = (nsel + 15) & ~15;
+    if (tid < sel_pad - nsel) s_sel[nsel + tid] = s_sel[0];  // padding slots point at a real entry
+    __syncthreads();
     const int nslots = sel_pad + rk.nwin;
     const int ntiles = (nslots + 15) >> 4;
     const int sel_tiles = sel_pad >> 4;
 
-    // ---- Q^T as the B operand, staged in LDS: lane (g, c) of step s holds head h0+c,
-    //      dims [32s+8g, +8)
-    for (int idx = tid; idx < 16 * 64; idx += 256) {
-        const int s = idx >> 6, l = idx & 63;
-        s_q[s][l] = *reinterpret_cast<const uint4*>(q + ((int64_t)row * H + h0 + (l & 15)) * kAttnD + 32 * s +
-                                                   8 * (l >> 4));
-    }
-    __syncthreads();
-    // identity B operand of the transposing MFMA: lane (g, c), k-slots 4g..4g+3, column c
-    s16x4 ident;
+    // ---- Q^T as the B operand: lane (g, c) holds head h0+c, dims [32s+8g, +8)
+    bf16x8 qb[16];
+    {
+        const uint16_t* qrow = q + ((int64_t)row * H + h0 + c) * kAttnD + 8 * g;
 #pragma unroll
-    for (int i = 0; i < 4; i++) ident[i] = (4 * g + i == c) ? (short)0x3F80 : (short)0;
+        for (int s = 0; s < 16; s++) qb[s] = load_bf16x8(qrow + 32 * s);
+        // Make the compiler wait for these loads here, not inside the tile loop where a
+        // wait would also hold back the next tile's copies.
+#pragma unroll
+        for (int s = 0; s < 16; s++) asm volatile("" : "+v"(qb[s]));
+    }
+
+    const uint16_t* kv_r = kv + rk.kv0 * kAttnD;
+    const int64_t swa_base = swa.row_start[rk.r] - swa.pos_start[rk.r] + rk.t0;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    char* my_tiles = s_tiles + wave_u * kWaveBytes;
+    const uint32_t my_tiles_lds = lds_addr(my_tiles);
+    // a tile that arrives by direct copies (selected rows, or a bf16 window)
+    const int dma_tiles = (swa.dtype == 3) ? sel_tiles : ntiles;
+
+    // Start the copy of tile `tile` into buffer `buf`.  Rows that arrive by direct copy
+    // are only issued here; FP8 window rows are loaded, dequantized and stored to LDS.
+    auto fetch = [&](int tile, int buf) {
+        const uint32_t dst = my_tiles_lds + buf * kTileBytes;
+        if (tile < sel_tiles) {
+            int4 jv[4];
+#pragma unroll
+            for (int u = 0; u < 4; u++) jv[u] = reinterpret_cast<const int4*>(s_sel + tile * 16)[u];
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int32_t j = jv[r >> 2][r & 3];
+                dma_row(kv_r + (int64_t)j * kAttnD + 8 * lane, dst + r * kRowBytes);
+            }
+        } else if (swa.dtype != 3) {
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                int wi = tile * 16 + r - sel_pad;
+                wi = wi < rk.nwin ? wi : rk.nwin - 1;
+                dma_row(static_cast<const uint16_t*>(swa.data) + (swa_base + wi) * kAttnD + 8 * lane,
+                        dst + r * kRowBytes);
+            }
+        } else {
+            int wi = tile * 16 + c - sel_pad;
+            wi = wi < rk.nwin ? wi : rk.nwin - 1;
+            const int64_t srow = swa_base + wi;
+            const uint8_t* sr = static_cast<const uint8_t*>(swa.data) + srow * kAttnD + 8 * g;
+            const uint8_t* sc = swa.scale + srow * (kAttnD / 32);
+            char* dp = my_tiles + buf * kTileBytes + c * kRowBytes + 16 * g;
+            uint2 raw[16];
+#pragma unroll
+            for (int s = 0; s < 16; s++) raw[s] = *reinterpret_cast<const uint2*>(sr + 32 * s);
+#pragma unroll
+            for (int s = 0; s < 16; s++)
+                *reinterpret_cast<uint4*>(dp + 64 * s) = fp8x8_to_bf16x8(raw[s], __builtin_ldexpf(1.0f, (int)sc[s] - 127));
+        }
+    };
 
     // State of head c (replicated over g).  Exponents are taken against a reference
     // m_ref that is fixed for the whole pass: the wave's first tile maximum plus 64
@@ -224,8 +311,8 @@ __global__ __launch_bounds__(256) void k_attn_bf16(RowsArg rows, CacheArg cache,
     // inside the loop.  If a later logit exceeds the reference, the wave redoes its
     // tiles once with the exact maximum it has seen.
     const float qk_scale = sm_scale * kLog2e;
-    const uint16_t* kv_r = kv + rk.kv0 * kAttnD;
-    const int64_t swa_base = swa.row_start[rk.r] - swa.pos_start[rk.r] + rk.t0;
+    const int k_off = c * kRowBytes + 16 * g;                            // K operand, step s at +64 s
+    const int v_off = (4 * g + (c >> 2)) * kRowBytes + (c & 3) * 8;     // V operand, dim tile t at +32 t
     f32x4 o[32];
     float m_ref = -INFINITY, l_run = 0.0f, m_true = -INFINITY;
     for (int attempt = 0; attempt < 2; attempt++) {
@@ -234,37 +321,38 @@ __global__ __launch_bounds__(256) void k_attn_bf16(RowsArg rows, CacheArg cache,
         l_run = 0.0f;
         m_ref = (attempt == 0) ? -INFINITY : m_true;
         bool over = false;
-        for (int tile = wave; tile < ntiles; tile += 4) {
-            // keep the Q operand in LDS: re-read it per tile instead of pinning 64 registers
-            asm volatile("" ::: "memory");
-            bf16x8 ka[16];
-            if (tile < sel_tiles) {  // uniform: a tile of selected entries (and padding)
-                const int ki = tile * 16 + c;
-                const uint16_t* kr = kv_r + (int64_t)s_sel[ki < nsel ? ki : 0] * kAttnD + 8 * g;
-#pragma unroll
-                for (int s = 0; s < 16; s++) ka[s] = load_bf16x8(kr + 32 * s);
-            } else {
-                const int wi = tile * 16 + c - sel_pad;
-                const int64_t srow = swa_base + (wi < rk.nwin ? wi : 0);
-                if (swa.dtype == 3) {
-                    const uint8_t* sr = static_cast<const uint8_t*>(swa.data) + srow * kAttnD + 8 * g;
-                    const uint8_t* sc = swa.scale + srow * (kAttnD / 32);
-#pragma unroll
-                    for (int s = 0; s < 16; s++)
-                        ka[s] = load_fp8x8_as_bf16(sr + 32 * s, __builtin_ldexpf(1.0f, (int)sc[s] - 127));
-                } else {
-                    const uint16_t* sr = static_cast<const uint16_t*>(swa.data) + srow * kAttnD + 8 * g;
-#pragma unroll
-                    for (int s = 0; s < 16; s++) ka[s] = load_bf16x8(sr + 32 * s);
-                }
-            }
+        int buf = 0;
+        if (wave_u < ntiles) fetch(wave_u, 0);
+        for (int tile = wave_u; tile < ntiles; tile += 4, buf ^= 1) {
+            const bool more = tile + 4 < ntiles;
+            if (more) fetch(tile + 4, buf ^ 1);
+            // Wait for this tile's copies, issued one iteration ago.  When the next
+            // tile's 16 copies were just issued they may stay in flight.
+            if (more && tile + 4 < dma_tiles)
+                asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            const char* tb = my_tiles + buf * kTileBytes;
 
-            // S^T tile: lane (g, c) -> key slots 4g..4g+3, head c
-            f32x4 st = {0.0f, 0.0f, 0.0f, 0.0f};
+            // S^T tile: lane (g, c) -> key slots 4g..4g+3, head c.  All operand reads are
+            // issued before the first product so their latencies overlap.
+            bf16x8 ka[16];
 #pragma unroll
             for (int s = 0; s < 16; s++)
-                st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s], __builtin_bit_cast(bf16x8, s_q[s][lane]), st, 0,
-                                                             0, 0);
+                ka[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(tb + k_off + 64 * s));
+            __builtin_amdgcn_sched_barrier(0);
+            f32x4 st = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < 16; s++) st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s], qb[s], st, 0, 0, 0);
+            // V operand, read transposed from the row-major tile (in flight during the
+            // softmax arithmetic below)
+            s16x4 vb[32];
+#pragma unroll
+            for (int t = 0; t < 32; t++)
+                vb[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4*)(tb + v_off + 32 * t));
+            __builtin_amdgcn_sched_barrier(0);
+
             float lg[4];
             float tmax = -INFINITY;
 #pragma unroll
@@ -274,8 +362,7 @@ __global__ __launch_bounds__(256) void k_attn_bf16(RowsArg rows, CacheArg cache,
                 lg[i] = valid ? st[i] * qk_scale : -INFINITY;
                 tmax = fmaxf(tmax, lg[i]);
             }
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+            tmax = max_over_g(tmax);
             m_true = fmaxf(m_true, tmax);
             if (m_ref == -INFINITY && tmax != -INFINITY) m_ref = tmax + 64.0f;  // the accumulator is still zero
             over |= tmax > m_ref;
@@ -288,31 +375,19 @@ __global__ __launch_bounds__(256) void k_attn_bf16(RowsArg rows, CacheArg cache,
                 psum += pv;
                 pa[i] = __builtin_bit_cast(short, (__bf16)pv);
             }
-            psum += __shfl_xor(psum, 16, 64);
-            psum += __shfl_xor(psum, 32, 64);
-            l_run += psum;
+            l_run += sum_over_g(psum);
+            __builtin_amdgcn_sched_barrier(0);
 
-            // O += P V, V taken from the K tile through the identity MFMA
+            // O += P V
 #pragma unroll
-            for (int s = 0; s < 16; s++) {
-#pragma unroll
-                for (int u = 0; u < 2; u++) {
-                    const s16x4 kh = __builtin_bit_cast(
-                        s16x4, bf16x4{ka[s][4 * u], ka[s][4 * u + 1], ka[s][4 * u + 2], ka[s][4 * u + 3]});
-                    const f32x4 tt = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kh, ident,
-                                                                              f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-                    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-                    const bf16x2_t lo = __builtin_convertvector(__builtin_shufflevector(tt, tt, 0, 1), bf16x2_t);
-                    const bf16x2_t hi = __builtin_convertvector(__builtin_shufflevector(tt, tt, 2, 3), bf16x2_t);
-                    const s16x4 vb = __builtin_bit_cast(s16x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3));
-                    o[2 * s + u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, o[2 * s + u], 0, 0, 0);
-                }
-            }
+            for (int t = 0; t < 32; t++) o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb[t], o[t], 0, 0, 0);
         }
         if (!__ballot(over)) break;
     }
+    __syncthreads();  // every wave is done with its tiles: the merge reuses them
 
     // ---- merge the four waves: out = sum_w O_w 2^(m_w - M) / L
+    float(*s_o)[16][256 + 4] = reinterpret_cast<float(*)[16][256 + 4]>(s_tiles);
     if (g == 0) {
         s_m[wave][c] = m_ref;
         s_l[wave][c] = l_run;
@@ -337,8 +412,7 @@ __global__ __launch_bounds__(256) void k_attn_bf16(RowsArg rows, CacheArg cache,
 #pragma unroll
         for (int tt = 0; tt < 16; tt++) {
             const int t = 16 * half + tt;
-            const int s = t >> 1, u = t & 1;
-            const int d = 32 * s + 8 * (c >> 2) + 4 * u + (c & 3) - 256 * half;
+            const int d = 16 * tt + c;
 #pragma unroll
             for (int i = 0; i < 4; i++) s_o[wave][4 * g + i][d] = o[t][i] * fac[i];
         }
@@ -351,6 +425,7 @@ __global__ __launch_bounds__(256) void k_attn_bf16(RowsArg rows, CacheArg cache,
         __syncthreads();
     }
 }
+
 
 hipError_t launch_attn_f32(const RowsArg& rows, const CacheArg& cache, const float* q, int heads, int dim,
                            const float* kv, const int32_t* sel, int k, int64_t sel_stride, const int32_t* sel_row_map,
