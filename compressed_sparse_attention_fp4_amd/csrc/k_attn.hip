@@ -114,13 +114,13 @@ __global__ __launch_bounds__(256) void k_attn_f32(RowsArg rows, CacheArg cache, 
 // ----------------------------------------------------------------------------- bf16
 // MQA with one shared 512-d latent (key = value) on bf16 MFMA, for dim 512.
 //
-// Workgroup = 4 waves on one query row and 16 heads (h0 .. h0+15).  The row's key list
-// (selected entries with -1 removed and padded to a multiple of 16, then the window
-// positions) is cut into tiles of 16 keys; wave w takes tiles w, w+4, ... with its own
-// online-softmax state and output.  Each wave double-buffers its tiles in LDS: while it
-// computes on one tile, the next one is already on its way (selected rows by direct
-// global-to-LDS copies, one 1 KiB row per instruction; FP8 window rows are dequantized
-// to bf16 through registers: E4M3 times a power of two is exact in bf16).
+// Workgroup = 4 waves on one query row and 16 heads (h0 .. h0+15).  The row's key slots
+// are the k selected entries (tiles of 16; an entry -1 is masked and a tile with no valid
+// entry is skipped) followed by the window positions.  Wave w takes tiles w, w+4, ...
+// with its own online-softmax state and output, double-buffering them in LDS: while it
+// computes on one tile, the next one is on its way (selected and bf16 window rows by
+// direct global-to-LDS copies, one 1 KiB row per instruction; FP8 window rows are
+// dequantized to bf16 through registers: E4M3 times a power of two is exact in bf16).
 //   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16, 16 steps over the 512 dims: A = K rows
 //     from LDS (lane (g, c) holds key c, dims [32s+8g, +8)), B = Q^T in registers.
 //   * S^T output: lane (g, c) holds keys 4g..4g+3 of head c, which is the A operand of
@@ -135,11 +135,11 @@ __global__ __launch_bounds__(256) void k_attn_f32(RowsArg rows, CacheArg cache, 
 // b serves row 8*(b / (8*NHG)) + b%8 and head group (b/8) % NHG.
 constexpr int kAttnD = 512;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kRowBytes = kAttnD * 2 + 32;           // LDS row pitch of a tile (32 B pad)
+constexpr int kRowBytes = kAttnD * 2 + 48;           // LDS row pitch of a tile (48 B pad)
 constexpr int kTileBytes = 16 * kRowBytes;            // one tile of 16 keys
 constexpr int kWaveBytes = 2 * kTileBytes;            // double buffer per wave
-constexpr int kMergeBytes = 4 * 16 * (256 + 4) * 4;   // merge scratch (aliases the tiles)
-static_assert(kMergeBytes <= 4 * kWaveBytes, "merge scratch must fit in the tile buffers");
+constexpr int kMergeWave = 512 * 64 + 64 * 16;        // one wave's output in the merge: [dim][16 heads] + pad
+constexpr int kLdsBytes = 4 * kMergeWave > 4 * kWaveBytes ? 4 * kMergeWave : 4 * kWaveBytes;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -148,15 +148,26 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p)
     return (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p);
 }
 
-// Copy one 1 KiB row from global memory into LDS at byte address `lds` (wave-uniform):
-// lane l moves bytes [16 l, 16 l + 16).  The copy is asynchronous; it is complete once
-// the wave's vector-memory counter has dropped past it (s_waitcnt vmcnt).  Issued as
-// inline assembly so the compiler does not add a wait for it before unrelated LDS reads.
-__device__ __forceinline__ void dma_row(const void* gptr, uint32_t lds)
+// Tiles are row-major in LDS with a pitch of 1072 B (1024 + 3 x 16): 16-byte chunk q of
+// key r starts at 67 r + q chunks, so the 16 keys of a K-operand read (same chunk) fall
+// on distinct banks, and so do the 4 keys x 4 chunks of a transposed V read.
+//
+// Copy 4 keys into LDS: key q (0..3) goes to byte address m0v + 1072 q (wave-uniform),
+// lane l passing the global address of the key's byte 16 l minus 1072 q (the immediate
+// offset moves both the global and the LDS address).  The copies are asynchronous: 4
+// vector-memory instructions, complete once s_waitcnt vmcnt has dropped past them.
+// Inline assembly, so the compiler adds no wait for them before unrelated LDS reads.
+__device__ __forceinline__ void dma_rows4(uint32_t m0v, const void* a0, const void* a1, const void* a2,
+                                          const void* a3)
 {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gptr)
-                 : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %4\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %0, off\n\t"
+                 "global_load_lds_dwordx4 %1, off offset:1072\n\t"
+                 "global_load_lds_dwordx4 %2, off offset:2144\n\t"
+                 "global_load_lds_dwordx4 %3, off offset:3216"
+                 :: "v"(a0), "v"(a1), "v"(a2), "v"(a3), "s"(m0v) : "memory", "m0");
 }
+static_assert(kRowBytes == 1072, "dma_rows4 encodes the row pitch");
 
 // Reductions over the four 16-lane rows (lanes c, c+16, c+32, c+48).
 __device__ __forceinline__ float max_over_g(float x)
@@ -204,9 +215,9 @@ __global__ __launch_bounds__(256) void k_attn_bf16(RowsArg rows, CacheArg cache,
                                                    float sm_scale, const float* __restrict__ sink,
                                                    uint16_t* __restrict__ out, float* __restrict__ lse)
 {
-    __shared__ __attribute__((aligned(16))) char s_tiles[4 * kWaveBytes];
+    __shared__ __attribute__((aligned(16))) char s_tiles[kLdsBytes];
     __shared__ __attribute__((aligned(16))) int32_t s_sel[2048];
-    __shared__ int s_tmp[8];
+    __shared__ uint32_t s_vmask[128];
     __shared__ float s_m[4][16], s_l[4][16];
 
     const int b = blockIdx.x;
@@ -216,84 +227,94 @@ __global__ __launch_bounds__(256) void k_attn_bf16(RowsArg rows, CacheArg cache,
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, c = lane & 15;
     const int h0 = 16 * hg;
-    const RowKeys rk = row_keys(rows, cache, swa, sel, sel_stride, sel_row_map, row);
 
-    // ---- compact the selected entries (drop -1), keeping their order
-    int nsel = 0;
-    for (int base = 0; base < k; base += 256) {
-        const int i = base + tid;
-        const int32_t j = (i < k) ? rk.sel[i] : -1;
-        const int valid = j >= 0;
-        const unsigned long long bal = __ballot(valid);
-        const int before_in_wave = __popcll(bal & ((1ull << lane) - 1ull));
-        if (lane == 0) s_tmp[wave] = __popcll(bal);
-        __syncthreads();
-        int before = 0, tot = 0;
-        for (int w = 0; w < 4; w++) {
-            before += (w < wave) ? s_tmp[w] : 0;
-            tot += s_tmp[w];
-        }
-        if (valid) s_sel[nsel + before + before_in_wave] = j;
-        nsel += tot;
-        __syncthreads();
-    }
-    // Key slots: [0, nsel) selected entries, [nsel, sel_pad) padding (masked), then the
-    // window; sel_pad = nsel rounded up to a tile, so every tile is of one kind.
-    const int sel_pad = (nsel + 15) & ~15;
-    if (tid < sel_pad - nsel) s_sel[nsel + tid] = s_sel[0];  // padding slots point at a real entry
-    __syncthreads();
-    const int nslots = sel_pad + rk.nwin;
-    const int ntiles = (nslots + 15) >> 4;
-    const int sel_tiles = sel_pad >> 4;
-
-    // ---- Q^T as the B operand: lane (g, c) holds head h0+c, dims [32s+8g, +8)
+    // ---- Q^T as the B operand (lane (g, c): head h0+c, dims [32s+8g, +8)), issued first
     bf16x8 qb[16];
     {
         const uint16_t* qrow = q + ((int64_t)row * H + h0 + c) * kAttnD + 8 * g;
 #pragma unroll
         for (int s = 0; s < 16; s++) qb[s] = load_bf16x8(qrow + 32 * s);
-        // Make the compiler wait for these loads here, not inside the tile loop where a
-        // wait would also hold back the next tile's copies.
-#pragma unroll
-        for (int s = 0; s < 16; s++) asm volatile("" : "+v"(qb[s]));
     }
+    const RowKeys rk = row_keys(rows, cache, swa, sel, sel_stride, sel_row_map, row);
+
+    // ---- selected slots: indices into LDS (-1 replaced by the request's entry 0, which
+    // exists whenever the tile holds a valid entry) and a 16-bit validity mask per tile
+    const int sel_tiles = (k + 15) >> 4;
+    for (int base = 0; base < sel_tiles * 16; base += 256) {
+        const int i = base + tid;
+        const int32_t j = (i < k) ? rk.sel[i] : -1;
+        const unsigned long long bal = __ballot(j >= 0);
+        if (i < sel_tiles * 16) s_sel[i] = j >= 0 ? j : 0;
+        const int t0 = (base + 64 * wave) / 16 + lane;
+        if (lane < 4 && t0 < sel_tiles) s_vmask[t0] = (uint32_t)(bal >> (16 * lane)) & 0xffffu;
+    }
+    __syncthreads();
+    const int ntiles = sel_tiles + ((rk.nwin + 15) >> 4);
+    // Make the compiler wait for the Q loads here, not inside the tile loop where the
+    // wait would also hold back the next tile's copies.
+#pragma unroll
+    for (int s = 0; s < 16; s++) asm volatile("" : "+v"(qb[s]));
 
     const uint16_t* kv_r = kv + rk.kv0 * kAttnD;
     const int64_t swa_base = swa.row_start[rk.r] - swa.pos_start[rk.r] + rk.t0;
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     char* my_tiles = s_tiles + wave_u * kWaveBytes;
     const uint32_t my_tiles_lds = lds_addr(my_tiles);
-    // a tile that arrives by direct copies (selected rows, or a bf16 window)
+    // Per-lane copy sources: byte 16 lane of a key, less q row pitches for key q of a group
+    // of 4 (the copy's immediate offset adds them back).  Window rows are addressed
+    // relative to the window cache (row swa_row0 + wi for window slot wi).
+    const int64_t swa_row0 = swa_base;
+    const uint64_t sel_lane0 = reinterpret_cast<uint64_t>(kv_r) + 16 * lane;
+    const uint64_t win_lane0 = reinterpret_cast<uint64_t>(swa.data) + 16 * lane;
+    uint32_t row_bytes;  // 1024, opaque to the compiler so the address is one v_mad_u64_u32
+    asm("s_mov_b32 %0, 1024" : "=s"(row_bytes));
+    // tiles that arrive by direct copies: selected rows, and a bf16 window
     const int dma_tiles = (swa.dtype == 3) ? sel_tiles : ntiles;
+    // the wave's next tile at or after t that holds a valid slot
+    auto next_tile = [&](int t) {
+        while (t < sel_tiles && s_vmask[t] == 0) t += 4;
+        return __builtin_amdgcn_readfirstlane(t);
+    };
 
     // Start the copy of tile `tile` into buffer `buf`.  Rows that arrive by direct copy
     // are only issued here; FP8 window rows are loaded, dequantized and stored to LDS.
     auto fetch = [&](int tile, int buf) {
         const uint32_t dst = my_tiles_lds + buf * kTileBytes;
-        if (tile < sel_tiles) {
-            int4 jv[4];
+        if (tile < sel_tiles || swa.dtype != 3) {
+            uint32_t jr[16];  // the tile's rows, relative to the base of its source
+            const bool from_sel = tile < sel_tiles;
+            if (from_sel) {
+                int4 jv[4];
 #pragma unroll
-            for (int u = 0; u < 4; u++) jv[u] = reinterpret_cast<const int4*>(s_sel + tile * 16)[u];
+                for (int u = 0; u < 4; u++) jv[u] = reinterpret_cast<const int4*>(s_sel + tile * 16)[u];
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int32_t j = jv[r >> 2][r & 3];
-                dma_row(kv_r + (int64_t)j * kAttnD + 8 * lane, dst + r * kRowBytes);
+                for (int r = 0; r < 16; r++) jr[r] = (uint32_t)jv[r >> 2][r & 3];
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    int wi = (tile - sel_tiles) * 16 + r;
+                    wi = wi < rk.nwin ? wi : rk.nwin - 1;
+                    jr[r] = (uint32_t)(swa_row0 + wi);
+                }
             }
-        } else if (swa.dtype != 3) {
+            const uint64_t l0 = from_sel ? sel_lane0 : win_lane0;
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                int wi = tile * 16 + r - sel_pad;
-                wi = wi < rk.nwin ? wi : rk.nwin - 1;
-                dma_row(static_cast<const uint16_t*>(swa.data) + (swa_base + wi) * kAttnD + 8 * lane,
-                        dst + r * kRowBytes);
+            for (int r4 = 0; r4 < 4; r4++) {
+                // one multiply-add per key: row * 1024 + lane base
+                const uint64_t a0 = (uint64_t)jr[4 * r4] * row_bytes + l0;
+                const uint64_t a1 = (uint64_t)jr[4 * r4 + 1] * row_bytes + (l0 - kRowBytes);
+                const uint64_t a2 = (uint64_t)jr[4 * r4 + 2] * row_bytes + (l0 - 2 * kRowBytes);
+                const uint64_t a3 = (uint64_t)jr[4 * r4 + 3] * row_bytes + (l0 - 3 * kRowBytes);
+                dma_rows4(dst + 4 * kRowBytes * r4, reinterpret_cast<const void*>(a0), reinterpret_cast<const void*>(a1),
+                          reinterpret_cast<const void*>(a2), reinterpret_cast<const void*>(a3));
             }
         } else {
-            int wi = tile * 16 + c - sel_pad;
+            int wi = (tile - sel_tiles) * 16 + c;
             wi = wi < rk.nwin ? wi : rk.nwin - 1;
             const int64_t srow = swa_base + wi;
             const uint8_t* sr = static_cast<const uint8_t*>(swa.data) + srow * kAttnD + 8 * g;
             const uint8_t* sc = swa.scale + srow * (kAttnD / 32);
-            char* dp = my_tiles + buf * kTileBytes + c * kRowBytes + 16 * g;
+            char* dp = my_tiles + buf * kTileBytes + kRowBytes * c + 16 * g;
             uint2 raw[16];
 #pragma unroll
             for (int s = 0; s < 16; s++) raw[s] = *reinterpret_cast<const uint2*>(sr + 32 * s);
@@ -311,8 +332,8 @@ __global__ __launch_bounds__(256) void k_attn_bf16(RowsArg rows, CacheArg cache,
     // inside the loop.  If a later logit exceeds the reference, the wave redoes its
     // tiles once with the exact maximum it has seen.
     const float qk_scale = sm_scale * kLog2e;
-    const int k_off = c * kRowBytes + 16 * g;                            // K operand, step s at +64 s
-    const int v_off = (4 * g + (c >> 2)) * kRowBytes + (c & 3) * 8;     // V operand, dim tile t at +32 t
+    const int k_off = kRowBytes * c + 16 * g;                    // K operand, step s at +64 s
+    const int v_off = kRowBytes * (4 * g + (c >> 2)) + 8 * (c & 3);  // V operand, dim tile t at +32 t
     f32x4 o[32];
     float m_ref = -INFINITY, l_run = 0.0f, m_true = -INFINITY;
     for (int attempt = 0; attempt < 2; attempt++) {
@@ -322,13 +343,15 @@ __global__ __launch_bounds__(256) void k_attn_bf16(RowsArg rows, CacheArg cache,
         m_ref = (attempt == 0) ? -INFINITY : m_true;
         bool over = false;
         int buf = 0;
-        if (wave_u < ntiles) fetch(wave_u, 0);
-        for (int tile = wave_u; tile < ntiles; tile += 4, buf ^= 1) {
-            const bool more = tile + 4 < ntiles;
-            if (more) fetch(tile + 4, buf ^ 1);
+        int tile = next_tile(wave_u);
+        if (tile < ntiles) fetch(tile, 0);
+        for (; tile < ntiles; buf ^= 1) {
+            const int nxt = next_tile(tile + 4);
+            const bool more = nxt < ntiles;
+            if (more) fetch(nxt, buf ^ 1);
             // Wait for this tile's copies, issued one iteration ago.  When the next
             // tile's 16 copies were just issued they may stay in flight.
-            if (more && tile + 4 < dma_tiles)
+            if (more && nxt < dma_tiles)
                 asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
             else
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -353,12 +376,13 @@ __global__ __launch_bounds__(256) void k_attn_bf16(RowsArg rows, CacheArg cache,
                     (__attribute__((address_space(3))) s16x4*)(tb + v_off + 32 * t));
             __builtin_amdgcn_sched_barrier(0);
 
+            const uint32_t vmask = (tile < sel_tiles) ? __builtin_amdgcn_readfirstlane(s_vmask[tile]) : 0u;
             float lg[4];
             float tmax = -INFINITY;
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                const int slot = tile * 16 + 4 * g + i;
-                const bool valid = (slot < nsel) || (slot >= sel_pad && slot < nslots);
+                const bool valid = (tile < sel_tiles) ? ((vmask >> (4 * g + i)) & 1u) != 0
+                                                      : (tile - sel_tiles) * 16 + 4 * g + i < rk.nwin;
                 lg[i] = valid ? st[i] * qk_scale : -INFINITY;
                 tmax = fmaxf(tmax, lg[i]);
             }
@@ -381,18 +405,20 @@ __global__ __launch_bounds__(256) void k_attn_bf16(RowsArg rows, CacheArg cache,
             // O += P V
 #pragma unroll
             for (int t = 0; t < 32; t++) o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb[t], o[t], 0, 0, 0);
+            tile = nxt;
         }
         if (!__ballot(over)) break;
     }
     __syncthreads();  // every wave is done with its tiles: the merge reuses them
 
-    // ---- merge the four waves: out = sum_w O_w 2^(m_w - M) / L
-    float(*s_o)[16][256 + 4] = reinterpret_cast<float(*)[16][256 + 4]>(s_tiles);
+    // ---- merge the four waves: out = sum_w O_w 2^(m_w - M) / L.  Each wave stores its
+    // scaled output as [dim][16 heads] (16 B per lane store; 16 B of padding every 8
+    // dims spreads the reads over the banks), then every thread sums 4 heads x 8 dims.
     if (g == 0) {
         s_m[wave][c] = m_ref;
         s_l[wave][c] = l_run;
     }
-    __syncthreads();
+    __syncthreads();  // also: every wave is done with its tiles, which the merge reuses
     float fac[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -407,22 +433,31 @@ __global__ __launch_bounds__(256) void k_attn_bf16(RowsArg rows, CacheArg cache,
         if (lse && wave == 0 && c == 0)
             lse[(int64_t)row * H + h0 + hh] = (M == -INFINITY) ? -INFINITY : (M + __log2f(L)) * 0.69314718055994531f;
     }
+    auto o_off = [](int w, int d, int quad) { return w * kMergeWave + d * 64 + (d >> 3) * 16 + quad * 16; };
 #pragma unroll
-    for (int half = 0; half < 2; half++) {
+    for (int t = 0; t < 32; t++)
+        *reinterpret_cast<f32x4*>(s_tiles + o_off(wave, 16 * t + c, g)) =
+            f32x4{o[t][0] * fac[0], o[t][1] * fac[1], o[t][2] * fac[2], o[t][3] * fac[3]};
+    __syncthreads();
+    {
+        const int quad = tid & 3, db = tid >> 2;  // heads 4 quad .. +3, dims 8 db .. +7
+        f32x4 acc[8];
 #pragma unroll
-        for (int tt = 0; tt < 16; tt++) {
-            const int t = 16 * half + tt;
-            const int d = 16 * tt + c;
-#pragma unroll
-            for (int i = 0; i < 4; i++) s_o[wave][4 * g + i][d] = o[t][i] * fac[i];
+        for (int e = 0; e < 8; e++) {
+            const int d = 8 * db + e;
+            const f32x4 v0 = *reinterpret_cast<const f32x4*>(s_tiles + o_off(0, d, quad));
+            const f32x4 v1 = *reinterpret_cast<const f32x4*>(s_tiles + o_off(1, d, quad));
+            const f32x4 v2 = *reinterpret_cast<const f32x4*>(s_tiles + o_off(2, d, quad));
+            const f32x4 v3 = *reinterpret_cast<const f32x4*>(s_tiles + o_off(3, d, quad));
+            acc[e] = ((v0 + v1) + v2) + v3;
         }
-        __syncthreads();
-        for (int e = tid; e < 16 * 256; e += 256) {
-            const int hh = e >> 8, d = e & 255;
-            const float v = ((s_o[0][hh][d] + s_o[1][hh][d]) + s_o[2][hh][d]) + s_o[3][hh][d];
-            out[((int64_t)row * H + h0 + hh) * kAttnD + 256 * half + d] = __builtin_bit_cast(uint16_t, (__bf16)v);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            bf16x8 r;
+#pragma unroll
+            for (int e = 0; e < 8; e++) r[e] = (__bf16)acc[e][i];
+            *reinterpret_cast<bf16x8*>(out + ((int64_t)row * H + h0 + 4 * quad + i) * kAttnD + 8 * db) = r;
         }
-        __syncthreads();
     }
 }
 
