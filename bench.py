@@ -21,6 +21,7 @@ HIP events on the launch stream) and the CPU oracle's rate on a bounded sample.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -142,6 +143,27 @@ STAGE_BYTES = {
     + NREQ * HI * 4 + NREQ * NB * BLK * 4,
     "topk_pool": NREQ * NB * BLK * 4 + NREQ * (NB + 1) * 4 + NREQ * K * 4,
 }
+# Kernel (as rocprofv3 names it, with its workgroup count) and source file behind each
+# stage, for the measured HBM traffic recorded under profiles/.
+STAGE_PROFILE = {"attn": ("csa2::k_attn_bf16", 256, "compressed_sparse_attention_fp4_amd/csrc/k_attn.hip")}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "c3_decode_hbm_traffic.txt")
+
+
+def measured_traffic(stage: str):
+    """HBM bytes per launch of the stage's kernel from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when there is none or the
+    kernel's source has changed since the counters were taken."""
+    if stage not in STAGE_PROFILE or not os.path.exists(TRAFFIC_FILE):
+        return None
+    name, wgs, src = STAGE_PROFILE[stage]
+    digest = hashlib.sha1(open(os.path.join(ROOT, src), "rb").read()).hexdigest()[:16]
+    for line in open(TRAFFIC_FILE):
+        f = line.split()
+        if len(f) == 5 and not line.startswith("#") and f[0] == name and int(f[1]) == wgs:
+            return float(f[3]) if f[4] == digest else None
+    return None
+
+
 STAGE_KERNEL = {"score_full": "k_score_mxfp4", "topk_hier": "k_select (2 launches)", "attn": "k_attn_bf16",
                 "score_pool": "k_score_mxfp4 (pool)", "topk_pool": "k_select"}
 
@@ -311,7 +333,7 @@ def main():
                    "layers_per_step": LAYERS, "queries_per_step": NREQ * LAYERS, "input_sets": NSETS},
         "roofline": {"bound": "hbm", "kernel": STAGE_KERNEL[dominant], "stage": dominant,
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "alg_bytes_per_launch": STAGE_BYTES[dominant],
+                     "traffic": measured_traffic(dominant), "alg_bytes_per_launch": STAGE_BYTES[dominant],
                      "avg_launch_us": avg_launch_ms * 1e3},
         "stages": {s: {"us_per_launch": round(v["ms_per_launch"] * 1e3, 2),
                        "launches_per_step": v["launches_per_step"], "alg_GBs": round(v["alg_GBs"], 1)}
