@@ -102,35 +102,54 @@ class InputSet:
 STAGES = ["score_full", "topk_hier", "attn", "score_pool", "topk_pool"]
 
 
-def step(x: InputSet, ev=None):
-    """One pass of the hot path; ev (dict stage -> list of (start, end) events) times
-    every entry-point call on the launch stream."""
-    def timed(stage, fn):
-        if ev is None:
-            return fn()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        r = fn()
-        b.record()
-        ev[stage].append((a, b))
-        return r
+def step(x: InputSet, only: str | None = None):
+    """One pass of the hot path over one input set; with `only`, just that stage's calls
+    (their inputs are the previous full pass's outputs, so a repeat recomputes the same)."""
+    def run(stage, fn):
+        if only is None or only == stage:
+            fn()
 
     sm = synth.sm_scale(D)
     L0 = x.layers[0]
-    timed("score_full", lambda: B.index_score(x.rows, x.cache, L0["qi"], L0["w"], x.keys, scores=x.scores_full))
-    timed("topk_hier", lambda: B.topk_hier(x.rows, x.cache, x.scores_full, K, BLK, NB, workspace=x.ws_hier,
-                                           out=(x.idx[0], x.pool_blocks, x.pool_n)))
-    timed("attn", lambda: B.sparse_swa_attn(x.rows, x.cache, L0["q"], x.kv, x.idx[0], L0["window"], sm,
-                                            out=x.out[0]))
+    run("score_full", lambda: B.index_score(x.rows, x.cache, L0["qi"], L0["w"], x.keys, scores=x.scores_full))
+    run("topk_hier", lambda: B.topk_hier(x.rows, x.cache, x.scores_full, K, BLK, NB, workspace=x.ws_hier,
+                                         out=(x.idx[0], x.pool_blocks, x.pool_n)))
+    run("attn", lambda: B.sparse_swa_attn(x.rows, x.cache, L0["q"], x.kv, x.idx[0], L0["window"], sm,
+                                          out=x.out[0]))
     for l in range(1, LAYERS):
         Ll = x.layers[l]
-        timed("score_pool", lambda: B.index_score(x.rows, x.cache, Ll["qi"], Ll["w"], x.keys, pool=x.pool,
-                                                  scores=x.scores_pool))
-        timed("topk_pool", lambda: B.topk(x.rows, x.cache, x.scores_pool, K, pool=x.pool, out=x.idx[l],
-                                          workspace=x.ws_topk))
-        timed("attn", lambda: B.sparse_swa_attn(x.rows, x.cache, Ll["q"], x.kv, x.idx[l], Ll["window"], sm,
-                                                out=x.out[l]))
+        run("score_pool", lambda: B.index_score(x.rows, x.cache, Ll["qi"], Ll["w"], x.keys, pool=x.pool,
+                                                scores=x.scores_pool))
+        run("topk_pool", lambda: B.topk(x.rows, x.cache, x.scores_pool, K, pool=x.pool, out=x.idx[l],
+                                        workspace=x.ws_topk))
+        run("attn", lambda: B.sparse_swa_attn(x.rows, x.cache, Ll["q"], x.kv, x.idx[l], Ll["window"], sm,
+                                              out=x.out[l]))
+
+
+STAGE_LAUNCHES = {"score_full": 1, "topk_hier": 1, "attn": LAYERS, "score_pool": LAYERS - 1, "topk_pool": LAYERS - 1}
+
+
+def stage_launch_ms(sets, reps: int) -> dict:
+    """Average duration of one launch of each stage: the stage's calls for every input set
+    captured in one HIP graph, replayed back to back between two HIP events on the stream
+    the kernels run on (the GPU never waits for the host inside the timed replays)."""
+    res = {}
+    for s in STAGES:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for x in sets:
+                step(x, only=s)
+        g.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        res[s] = a.elapsed_time(b) / (reps * len(sets) * STAGE_LAUNCHES[s])
+    return res
 
 
 # Algorithmic bytes per launch (what the step must move at least once).
@@ -280,25 +299,16 @@ def main():
     elapsed = time.perf_counter() - t0
     log("timed %d steps in %.3f ms" % (args.steps, elapsed * 1e3))
 
-    # per-kernel durations: the same K steps launched eagerly with HIP events around every
-    # entry-point call, on the stream the kernels run on
-    ev = {s: [] for s in STAGES}
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for i in range(args.steps):
-        step(sets[i % NSETS], ev)
-    torch.cuda.synchronize()
-    eager_ms = (time.perf_counter() - t1) * 1e3 / args.steps
-
-    stage_ms = {s: [a.elapsed_time(b) for a, b in ev[s]] for s in STAGES}
-    per_step_ms = {s: sum(v) / args.steps for s, v in stage_ms.items()}
+    # per-launch durations of each stage (HIP events around back-to-back graph replays)
+    launch_ms = stage_launch_ms(sets, reps=max(3, args.steps // 4))
+    per_step_ms = {s: launch_ms[s] * STAGE_LAUNCHES[s] for s in STAGES}
     dominant = max(STAGES, key=lambda s: per_step_ms[s])
-    avg_launch_ms = float(np.mean(stage_ms[dominant]))
+    avg_launch_ms = launch_ms[dominant]
     achieved = STAGE_BYTES[dominant] / (avg_launch_ms * 1e-3) / 1e9
-    stages = {s: {"ms_per_launch": float(np.mean(v)), "launches_per_step": len(v) // args.steps,
-                  "alg_GBs": STAGE_BYTES[s] / (np.mean(v) * 1e-3) / 1e9} for s, v in stage_ms.items()}
+    stages = {s: {"ms_per_launch": launch_ms[s], "launches_per_step": STAGE_LAUNCHES[s],
+                  "alg_GBs": STAGE_BYTES[s] / (launch_ms[s] * 1e-3) / 1e9} for s in STAGES}
     log(json.dumps(stages, indent=1))
-    log("eager step %.3f ms (events included), graph step %.3f ms" % (eager_ms, elapsed * 1e3 / args.steps))
+    log("graph step %.3f ms; sum of stage launches %.3f ms" % (elapsed * 1e3 / args.steps, sum(per_step_ms.values())))
 
     queries = NREQ * LAYERS * args.steps
     value = queries / elapsed
