@@ -251,7 +251,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the CSA2 path is built and timed on a single MI355X; "
-              "multi-GPU sharding is described in DESIGN.md but not run (got --gpus %d)" % args.gpus, file=sys.stderr)
+              "multi-GPU sharding is designed but not run (got --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")

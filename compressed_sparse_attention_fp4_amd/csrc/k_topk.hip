@@ -6,7 +6,7 @@
 // index layers select inside that pool); "SGLang and Miles Day-0 support for
 // DeepSeek-V4.1", section 2 (the block holding the newest position is always kept; the
 // same pass takes its own top-512 over all reachable positions).  Ties go to the lower
-// position (problem statement).
+// position (the workload definition; the pages are silent).
 //
 // Method.  Candidates are mapped to order-preserving 32-bit keys (0 = no candidate).  One
 // workgroup of 1024 threads holds up to 1024*KPT candidates in registers, striped

@@ -126,7 +126,7 @@ typedef struct csa2_swa {
  * a candidate pool.
  *
  * Defines ([DAY0] section 5: the indexer scores the FP4 cache directly, heads
- * replicated; the formula is the problem statement's MQA form):
+ * replicated; the formula is the workload definition's ReLU-weighted MQA form):
  *     s_j = sum_h w_h * ReLU(q_h . k_j)
  * With MXFP4 keys the BF16 index q is first quantized to MXFP4 (32-element blocks,
  * OCP MX rule; [MOD] "Mixed precision": index Q/K are MXFP4), so every q_h . k_j is an

@@ -14,7 +14,7 @@
  *  [P4] "SGLang and Miles Day-0 support for DeepSeek-V4.1" (theainews.cc summary of the
  *       LMSYS post), sections 1 (architecture), 2 (sharing and retrieval), 5 (kernels).
  *  The indexer score formula sum_h w_h * ReLU(q_h . k) and the lowest-index tie break
- *  are not on the pages; they come from the problem statement of this path.
+ *  are not on the pages; they come from the workload definition that accompanies them.
  *  OCP Microscaling Formats (MX) v1.0 defines E2M1, E4M3, E8M0 and block scaling.
  *
  * Precision: attention is computed in double from dequantized inputs.  The index

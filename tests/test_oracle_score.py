@@ -4,7 +4,7 @@ Pages: "DeepSeek V4.1 Flash modeling" (pages.haorui.li), sections "CSA2" (non-
 overlapping compression, complete groups only) and "Mixed precision" (index Q/K
 MXFP4, 32-element groups); "SGLang and Miles Day-0 support for DeepSeek-V4.1"
 (theainews.cc), section 5 (FP4 index scoring in MQA form).  The score formula
-s_j = sum_h w_h ReLU(q_h . k_j) comes from the problem statement of this path.
+s_j = sum_h w_h ReLU(q_h . k_j) comes from the workload definition (the pages say only "MQA form").
 
 Pins: reachability against its closed form and the C0 count; the MXFP4 score
 against exact rational arithmetic (a dropped term, a wrong sign, a transposed

@@ -5,7 +5,7 @@ blocks of 8 positions scored by their maximum; at most 2,048 blocks, i.e. at mos
 16,384 candidates); "SGLang and Miles Day-0 support for DeepSeek-V4.1", section 2
 (the block holding the newest position is always kept; the pass also takes its own
 top-512 from all reachable positions; nothing is excluded when every reachable
-position fits the 16,384 budget).  Ties go to the lowest index (problem statement).
+position fits the 16,384 budget).  Ties go to the lowest index (the workload definition; the pages are silent).
 
 Pins: brute force with Python's sort on tiny inputs (tie-heavy too), and the
 invariants the pages state.
