@@ -1,0 +1,357 @@
+"""GPU parity at the workloads' full sizes, on sampled rows.
+
+Each test runs the HIP path on a whole workload (the decode step exactly as the
+benchmark launches it for C3; C1 prefill with its full 8192-token requests; the C2
+bounded-replay flow; C4 long-context decode) and recomputes a sample of rows with the
+oracle, row by row: index scores and index sets bit for bit, attention outputs within
+|g - r| <= 2e-2 + 1e-2 |r| and a per-row relative L2 error <= 1e-2.  Sampled rows
+include the boundary positions (0, 126..129, 510..512, S - 1).  Every oracle input is
+regenerated from the seeded generator and quantized by the oracle's own quantizer; its
+bytes are checked against the library's before use."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from compressed_sparse_attention_fp4_amd import binding as B
+from compressed_sparse_attention_fp4_amd import synth
+
+from gpu_util import DEV, allclose_report, dev_cache, dev_rows, i32, i64, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+
+
+def bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def check_scores(got, ref, ncols):
+    for i, n in enumerate(ncols):
+        if not np.array_equal(got[i, :n], ref[i, :n]):
+            bad = np.nonzero(got[i, :n] != ref[i, :n])[0]
+            raise AssertionError("sample row %d: %d of %d score columns differ, first %s" % (i, len(bad), n, bad[:6]))
+
+
+def check_attn(got, ref):
+    nb, emax, _ = allclose_report(got, ref, 2e-2, 1e-2)
+    assert nb == 0, ("attention elements out of tolerance", nb, emax)
+    n, h, d = ref.shape
+    rel = np.linalg.norm((got - ref).reshape(n * h, d), axis=1) / (np.linalg.norm(ref.reshape(n * h, d), axis=1)
+                                                                   + 1e-30)
+    assert rel.max() <= 1e-2, ("row relative L2", rel.max())
+
+
+def oracle_window(orc, raw_rows, nreq_rows, pos_start, window=128):
+    """Window rows (float32 host) -> the oracle's MXFP8 window dict."""
+    codes, scales = orc.mx_quant(orc.E4M3, raw_rows)
+    return codes, scales, dict(data=codes, dtype=3, scale=scales,
+                               row_start=np.arange(nreq_rows, dtype=np.int64) * window,
+                               pos_start=np.asarray(pos_start, dtype=np.int32), window=window)
+
+
+# ------------------------------------------------------------------------- C3
+def test_c3_decode_step_sampled(orc):
+    """The benchmark's decode step (64 requests x 1 query, S=131072, m=2, source layer
+    with hierarchical selection, then 7 Reindex layers), launched exactly as bench.py
+    times it; the source layer and the last Reindex layer checked on sampled rows."""
+    import bench
+    say("case: C3 full decode step (bench input set 0), oracle on sampled rows")
+    x = bench.InputSet(0, DEV)
+    bench.step(x)
+    torch.cuda.synchronize()
+    seed, C, S, W = 3000, bench.C, bench.SEQ, bench.W
+    sample = [0, 45]
+    ns = len(sample)
+    # index keys of the sampled requests, regenerated (1M-row chunks hold 16 requests)
+    raw = []
+    for r in sample:
+        c0 = (r * C) // (1 << 20) * (1 << 20)
+        chunk = synth.normal((min(1 << 20, bench.NREQ * C - c0), bench.DI), seed, "index_keys/%d" % c0, device=DEV)
+        raw.append(chunk[r * C - c0:r * C - c0 + C].cpu())
+        del chunk
+    raw = torch.cat(raw).numpy()
+    ko, kso = orc.mx_quant(orc.E2M1, raw)
+    for s_i, r in enumerate(sample):
+        assert np.array_equal(ko[s_i * C:(s_i + 1) * C], x.kcodes[r * C:(r + 1) * C].cpu().numpy())
+        assert np.array_equal(kso[s_i * C:(s_i + 1) * C], x.kscale[r * C:(r + 1) * C].cpu().numpy())
+    rows_o = dict(req_of_row=np.arange(ns), pos_of_row=np.full(ns, S - 1))
+    cache_o = dict(ratio_m=bench.M, n_entries=np.full(ns, C), row_start=np.arange(ns, dtype=np.int64) * C)
+    kv_o = np.concatenate([bits(x.kv[r * C:(r + 1) * C]) for r in sample])
+    sm = synth.sm_scale(bench.D)
+
+    def window_for(l):
+        full = synth.normal((bench.NREQ * W, bench.D), seed, "swa/%d" % l, device=DEV)
+        rw = torch.cat([full[r * W:(r + 1) * W] for r in sample]).cpu().numpy()
+        codes, scales, wo = oracle_window(orc, rw, ns, [S - W] * ns, W)
+        wd = x.layers[l]["window"]
+        for s_i, r in enumerate(sample):
+            assert np.array_equal(codes[s_i * W:(s_i + 1) * W], wd.data[r * W:(r + 1) * W].cpu().numpy())
+            assert np.array_equal(scales[s_i * W:(s_i + 1) * W], wd.scale[r * W:(r + 1) * W].cpu().numpy())
+        return wo
+
+    # source layer: full-range scores, hierarchical selection, attention
+    L0 = x.layers[0]
+    s_o, bad = orc.index_score(rows_o, cache_o, L0["qi"][sample].float().cpu().numpy(), L0["w"][sample].cpu().numpy(),
+                               ko, key_scales=kso, heads=bench.HI, dim=bench.DI, score_stride=C)
+    assert bad == 0
+    say("  source scores")
+    check_scores(x.scores_full[sample].cpu().numpy(), s_o, [C] * ns)
+    ri, rb, rn = orc.topk_hier(rows_o, cache_o, s_o, bench.K, bench.BLK, bench.NB)
+    say("  hierarchical selection")
+    assert np.array_equal(x.idx[0][sample].cpu().numpy(), ri)
+    assert np.array_equal(x.pool_n[sample].cpu().numpy(), rn)
+    assert np.array_equal(x.pool_blocks[sample].cpu().numpy(), rb)
+    out_o, _ = orc.sparse_swa_attn(rows_o, cache_o, bits(L0["q"][sample]), 1, kv_o, 1, ri, window_for(0),
+                                   heads=bench.H, dim=bench.D, sm_scale=sm)
+    say("  source attention")
+    check_attn(x.out[0][sample].float().cpu().numpy(), out_o)
+
+    # the last Reindex layer: pool scores, pool top-k, attention
+    L7 = x.layers[bench.LAYERS - 1]
+    pool_o = dict(blocks=rb, nblocks=rn, block=bench.BLK, max_blocks=bench.NB)
+    s7, bad = orc.index_score(rows_o, cache_o, L7["qi"][sample].float().cpu().numpy(), L7["w"][sample].cpu().numpy(),
+                              ko, key_scales=kso, heads=bench.HI, dim=bench.DI, score_stride=bench.NB * bench.BLK,
+                              pool=pool_o)
+    assert bad == 0
+    say("  Reindex scores")
+    check_scores(x.scores_pool[sample].cpu().numpy(), s7, (rn * bench.BLK).tolist())
+    i7 = orc.topk(rows_o, cache_o, s7, bench.K, pool=pool_o)
+    say("  Reindex selection")
+    assert np.array_equal(x.idx[bench.LAYERS - 1][sample].cpu().numpy(), i7)
+    out7, _ = orc.sparse_swa_attn(rows_o, cache_o, bits(L7["q"][sample]), 1, kv_o, 1, i7,
+                                  window_for(bench.LAYERS - 1), heads=bench.H, dim=bench.D, sm_scale=sm)
+    say("  Reindex attention")
+    check_attn(x.out[bench.LAYERS - 1][sample].float().cpu().numpy(), out7)
+
+
+# ------------------------------------------------------------------------- C1
+def test_c1_prefill_sampled(orc):
+    """C1 Full-layer prefill (m=1, 8192-token requests, top-512, fp8 window) on its
+    first two requests: scores, flat top-512 and attention for every row on the GPU,
+    sampled rows checked."""
+    cfg = synth.config(1, nreq=2)
+    g = cfg.geom
+    say("case: %s (2 of 8 requests, every row on the GPU)" % cfg.name)
+    rows = synth.prefill_rows(g)
+    n = rows["req_of_row"].numel()
+    cache = dict(ratio_m=1, n_entries=np.array(g.n_entries), row_start=np.array(g.row_start))
+    keys_raw = synth.normal((g.total_entries, cfg.index_dim), cfg.seed, "index_keys", device=DEV)
+    kd, ksd = B.quant_mx(B.MXFP4, keys_raw)
+    qi = synth.normal_bf16((n, cfg.index_heads, cfg.index_dim), cfg.seed, "index_q", device=DEV)
+    w = synth.uniform((n, cfg.index_heads), cfg.seed, "index_w", device=DEV)
+    rd, cd = dev_rows(rows), dev_cache(cache)
+    scores = B.index_score(rd, cd, qi, w, B.IndexKeys(kd, ksd, cfg.index_dim), score_stride=g.n_entries[0])
+    idx = B.topk(rd, cd, scores, cfg.topk, workspace=torch.empty(
+        max(1, B.workspace_size(B.OP_TOPK, n, g.n_entries[0], cfg.topk)), dtype=torch.uint8, device=DEV))
+    q = synth.normal_bf16((n, cfg.heads, cfg.dim), cfg.seed, "q", device=DEV)
+    kv = synth.normal_bf16((g.total_entries, cfg.dim), cfg.seed, "kv", device=DEV)
+    win = synth.window_cache_geometry(g, 128, rows_held=g.seq_len)
+    swa_raw = synth.normal((win["rows"], cfg.dim), cfg.seed, "swa", device=DEV)
+    scd, ssd = B.quant_mx(B.MXFP8_E4M3, swa_raw)
+    wd = B.Window(scd, ssd, win["row_start"].to(DEV), win["pos_start"].to(DEV), 128)
+    out = B.sparse_swa_attn(rd, cd, q, kv, idx, wd, synth.sm_scale(cfg.dim))
+    torch.cuda.synchronize()
+
+    rng = np.random.default_rng(11)
+    S = g.seq_len[0]
+    sample = []
+    for r in range(g.nreq):
+        pos = {0, 1, 126, 127, 128, 129, 510, 511, 512, S - 1} | set(rng.choice(S, size=4, replace=False).tolist())
+        sample += [r * S + p for p in sorted(pos)]
+    req = rows["req_of_row"].numpy()[sample]
+    pos = rows["pos_of_row"].numpy()[sample]
+    rows_o = dict(req_of_row=req, pos_of_row=pos)
+    ko, kso = orc.mx_quant(orc.E2M1, keys_raw.cpu().numpy())
+    assert np.array_equal(ko, kd.cpu().numpy()) and np.array_equal(kso, ksd.cpu().numpy())
+    s_o, bad = orc.index_score(rows_o, cache, qi[sample].float().cpu().numpy(), w[sample].cpu().numpy(), ko,
+                               key_scales=kso, heads=cfg.index_heads, dim=cfg.index_dim, score_stride=S)
+    assert bad == 0
+    say("  scores")
+    check_scores(scores[sample].cpu().numpy(), s_o, (pos + 1).tolist())
+    i_o = orc.topk(rows_o, cache, s_o, cfg.topk)
+    say("  top-512")
+    assert np.array_equal(idx[sample].cpu().numpy(), i_o)
+    codes, scales = orc.mx_quant(orc.E4M3, swa_raw.cpu().numpy())
+    assert np.array_equal(codes, scd.cpu().numpy()) and np.array_equal(scales, ssd.cpu().numpy())
+    wo = dict(data=codes, dtype=3, scale=scales, row_start=win["row_start"].numpy(), pos_start=win["pos_start"].numpy(),
+              window=128)
+    out_o, _ = orc.sparse_swa_attn(rows_o, cache, bits(q[sample]), 1, bits(kv), 1, i_o, wo, heads=cfg.heads,
+                                   dim=cfg.dim, sm_scale=synth.sm_scale(cfg.dim))
+    say("  attention")
+    check_attn(out[sample].float().cpu().numpy(), out_o)
+
+
+# ------------------------------------------------------------------------- C2
+def test_c2_replay_flow_sampled(orc):
+    """C2 bounded replay: a Full layer over the extends of 8 requests (S=8192 each) gives
+    top-512 and pools; the tail layout picks each request's last min(128, E) rows; a
+    Reindex layer rescoring the source pools (through the tail->extend row map) with its
+    own q, then a Reuse layer attending to the source layer's indices through the same
+    map.  Tail layout checked whole, everything else on sampled tail rows."""
+    cfg = synth.config(2)
+    g = cfg.geom
+    E = synth.C2_EXTENDS
+    say("case: %s" % cfg.name)
+    ext_req = np.concatenate([np.full(e, r) for r, e in enumerate(E)]).astype(np.int32)
+    ext_pos = np.concatenate([np.arange(s - e, s) for s, e in zip(g.seq_len, E)]).astype(np.int32)
+    n_ext = len(ext_req)
+    cache = dict(ratio_m=1, n_entries=np.array(g.n_entries), row_start=np.array(g.row_start))
+    cd = dev_cache(cache)
+    keys_raw = synth.normal((g.total_entries, cfg.index_dim), cfg.seed, "index_keys", device=DEV)
+    kd, ksd = B.quant_mx(B.MXFP4, keys_raw)
+    keys = B.IndexKeys(kd, ksd, cfg.index_dim)
+    C = g.n_entries[0]
+    # source (Full) layer over every extend row
+    rows_ext = dict(req_of_row=ext_req, pos_of_row=ext_pos)
+    re_d = dev_rows(rows_ext)
+    qi_s = synth.normal_bf16((n_ext, cfg.index_heads, cfg.index_dim), cfg.seed, "index_q/src", device=DEV)
+    w_s = synth.uniform((n_ext, cfg.index_heads), cfg.seed, "index_w/src", device=DEV)
+    sc_s = B.index_score(re_d, cd, qi_s, w_s, keys, score_stride=C)
+    ws = torch.empty(max(1, B.workspace_size(B.OP_TOPK_HIER, n_ext, C, cfg.topk, cfg.max_blocks)), dtype=torch.uint8,
+                     device=DEV)
+    idx_s, pb, pn = B.topk_hier(re_d, cd, sc_s, cfg.topk, cfg.block, cfg.max_blocks, workspace=ws)
+    # tail rows
+    t = B.replay_tail_layout(i32(E).to(DEV), i32(g.seq_len).to(DEV), 128)
+    t_o = orc.replay_tail_layout(E, g.seq_len, 128)
+    nt = int(t_o["tail_row_start"][-1])
+    assert nt == 960
+    for name in ("src_row", "abs_pos", "win_lo", "req_of_row"):
+        assert np.array_equal(t[name][:nt].cpu().numpy(), t_o[name]), name
+    rows_t = dict(req_of_row=t_o["req_of_row"], pos_of_row=t_o["abs_pos"], win_lo=t_o["win_lo"])
+    rt_d = B.Rows(t["req_of_row"][:nt], t["abs_pos"][:nt], t["win_lo"][:nt])
+    src_map = t["src_row"][:nt].contiguous()
+    pool_d = B.Pool(pb, pn, cfg.block, src_map)
+    qi_t = synth.normal_bf16((nt, cfg.index_heads, cfg.index_dim), cfg.seed, "index_q/reindex", device=DEV)
+    w_t = synth.uniform((nt, cfg.index_heads), cfg.seed, "index_w/reindex", device=DEV)
+    sc_t = B.index_score(rt_d, cd, qi_t, w_t, keys, pool=pool_d, score_stride=cfg.max_blocks * cfg.block)
+    idx_t = B.topk(rt_d, cd, sc_t, cfg.topk, pool=pool_d, workspace=torch.empty(
+        max(1, B.workspace_size(B.OP_TOPK, nt, cfg.max_blocks * cfg.block, cfg.topk)), dtype=torch.uint8,
+        device=DEV))
+    kv = synth.normal_bf16((g.total_entries, cfg.dim), cfg.seed, "kv", device=DEV)
+    win = synth.window_cache_geometry(g, 128)
+    outs = {}
+    windows = {}
+    for layer, sel, smap in (("reindex", idx_t, None), ("reuse", idx_s, src_map)):
+        raw = synth.normal((win["rows"], cfg.dim), cfg.seed, "swa/" + layer, device=DEV)
+        scd, ssd = B.quant_mx(B.MXFP8_E4M3, raw)
+        windows[layer] = (raw.cpu().numpy(), scd.cpu().numpy(), ssd.cpu().numpy())
+        q = synth.normal_bf16((nt, cfg.heads, cfg.dim), cfg.seed, "q/" + layer, device=DEV)
+        wd = B.Window(scd, ssd, win["row_start"].to(DEV), win["pos_start"].to(DEV), 128)
+        outs[layer] = (q, B.sparse_swa_attn(rt_d, cd, q, kv, sel, wd, synth.sm_scale(cfg.dim), sel_row_map=smap))
+    torch.cuda.synchronize()
+
+    # sampled tail rows: first and last of every request's tail plus a few more
+    rng = np.random.default_rng(12)
+    st = t_o["tail_row_start"]
+    sample = sorted(set([int(st[r]) for r in range(len(E))] + [int(st[r + 1]) - 1 for r in range(len(E))]
+                        + rng.choice(nt, size=8, replace=False).tolist()))
+    ns = len(sample)
+    src = t_o["src_row"][sample]
+    ko, kso = orc.mx_quant(orc.E2M1, keys_raw.cpu().numpy())
+    assert np.array_equal(ko, kd.cpu().numpy()) and np.array_equal(kso, ksd.cpu().numpy())
+    # the source layer on the extend rows the sample reads
+    rows_src = dict(req_of_row=ext_req[src], pos_of_row=ext_pos[src])
+    s_src, bad = orc.index_score(rows_src, cache, qi_s[src].float().cpu().numpy(), w_s[src].cpu().numpy(), ko,
+                                 key_scales=kso, heads=cfg.index_heads, dim=cfg.index_dim, score_stride=C)
+    assert bad == 0
+    check_scores(sc_s[src].cpu().numpy(), s_src, (ext_pos[src] + 1).tolist())
+    ri, rb, rn = orc.topk_hier(rows_src, cache, s_src, cfg.topk, cfg.block, cfg.max_blocks)
+    say("  source layer on the sampled tail rows' extend rows")
+    assert np.array_equal(idx_s[src].cpu().numpy(), ri)
+    assert np.array_equal(pn[src].cpu().numpy(), rn)
+    assert np.array_equal(pb[src].cpu().numpy(), rb)
+    # Reindex on the sampled tail rows, pools read through the row map
+    rows_ts = {k: v[sample] for k, v in rows_t.items()}
+    pool_o = dict(blocks=rb, nblocks=rn, block=cfg.block, max_blocks=cfg.max_blocks, row_map=np.arange(ns))
+    s_t, bad = orc.index_score(rows_ts, cache, qi_t[sample].float().cpu().numpy(), w_t[sample].cpu().numpy(), ko,
+                               key_scales=kso, heads=cfg.index_heads, dim=cfg.index_dim,
+                               score_stride=cfg.max_blocks * cfg.block, pool=pool_o)
+    assert bad == 0
+    check_scores(sc_t[sample].cpu().numpy(), s_t, (rn * cfg.block).tolist())
+    i_t = orc.topk(rows_ts, cache, s_t, cfg.topk, pool=pool_o)
+    say("  Reindex scores and selection")
+    assert np.array_equal(idx_t[sample].cpu().numpy(), i_t)
+    kvb = bits(kv)
+    for layer, sel_o in (("reindex", i_t), ("reuse", ri)):
+        raw, scd, ssd = windows[layer]
+        codes, scales = orc.mx_quant(orc.E4M3, raw)
+        assert np.array_equal(codes, scd) and np.array_equal(scales, ssd)
+        wo = dict(data=codes, dtype=3, scale=scales, row_start=win["row_start"].numpy(),
+                  pos_start=win["pos_start"].numpy(), window=128)
+        q, out = outs[layer]
+        out_o, _ = orc.sparse_swa_attn(rows_ts, cache, bits(q[sample]), 1, kvb, 1, sel_o, wo, heads=cfg.heads,
+                                       dim=cfg.dim, sm_scale=synth.sm_scale(cfg.dim))
+        say("  %s attention" % layer)
+        check_attn(out[sample].float().cpu().numpy(), out_o)
+
+
+# ------------------------------------------------------------------------- C4
+@pytest.mark.parametrize("nreq", [1, 32])
+def test_c4_long_decode_sampled(orc, nreq):
+    """C4 long-context decode (S=524288, m=2: 262144 reachable entries per row): full
+    scan, hierarchical selection and attention for every row; one row checked."""
+    cfg = synth.config(4, nreq=nreq)
+    g = cfg.geom
+    say("case: %s" % cfg.name)
+    C = g.n_entries[0]
+    rows = synth.decode_rows(g)
+    cache = dict(ratio_m=2, n_entries=np.array(g.n_entries), row_start=np.array(g.row_start))
+    rd, cd = dev_rows(rows), dev_cache(cache)
+    sample_r = nreq - 1
+    kd = torch.empty((g.total_entries, cfg.index_dim // 2), dtype=torch.uint8, device=DEV)
+    ksd = torch.empty((g.total_entries, cfg.index_dim // 32), dtype=torch.uint8, device=DEV)
+    raw_sample = None
+    for r in range(nreq):
+        raw = synth.normal((C, cfg.index_dim), cfg.seed, "index_keys/%d" % r, device=DEV)
+        kd[r * C:(r + 1) * C], ksd[r * C:(r + 1) * C] = B.quant_mx(B.MXFP4, raw)
+        if r == sample_r:
+            raw_sample = raw.cpu().numpy()
+        del raw
+    qi = synth.normal_bf16((nreq, cfg.index_heads, cfg.index_dim), cfg.seed, "index_q", device=DEV)
+    w = synth.uniform((nreq, cfg.index_heads), cfg.seed, "index_w", device=DEV)
+    scores = B.index_score(rd, cd, qi, w, B.IndexKeys(kd, ksd, cfg.index_dim), score_stride=C)
+    ws = torch.empty(max(1, B.workspace_size(B.OP_TOPK_HIER, nreq, C, cfg.topk, cfg.max_blocks)), dtype=torch.uint8,
+                     device=DEV)
+    idx, pb, pn = B.topk_hier(rd, cd, scores, cfg.topk, cfg.block, cfg.max_blocks, workspace=ws)
+    q = synth.normal_bf16((nreq, cfg.heads, cfg.dim), cfg.seed, "q", device=DEV)
+    kv = synth.normal_bf16((g.total_entries, cfg.dim), cfg.seed, "kv", device=DEV, chunk_rows=1 << 19)
+    win = synth.window_cache_geometry(g, 128)
+    swa_raw = synth.normal((win["rows"], cfg.dim), cfg.seed, "swa", device=DEV)
+    scd, ssd = B.quant_mx(B.MXFP8_E4M3, swa_raw)
+    wd = B.Window(scd, ssd, win["row_start"].to(DEV), win["pos_start"].to(DEV), 128)
+    out = B.sparse_swa_attn(rd, cd, q, kv, idx, wd, synth.sm_scale(cfg.dim))
+    torch.cuda.synchronize()
+
+    i = sample_r
+    ko, kso = orc.mx_quant(orc.E2M1, raw_sample)
+    assert np.array_equal(ko, kd[i * C:(i + 1) * C].cpu().numpy())
+    assert np.array_equal(kso, ksd[i * C:(i + 1) * C].cpu().numpy())
+    S = g.seq_len[0]
+    rows_o = dict(req_of_row=np.zeros(1), pos_of_row=np.full(1, S - 1))
+    cache_o = dict(ratio_m=2, n_entries=np.full(1, C), row_start=np.zeros(1, dtype=np.int64))
+    s_o, bad = orc.index_score(rows_o, cache_o, qi[i:i + 1].float().cpu().numpy(), w[i:i + 1].cpu().numpy(), ko,
+                               key_scales=kso, heads=cfg.index_heads, dim=cfg.index_dim, score_stride=C)
+    assert bad == 0
+    say("  scores")
+    check_scores(scores[i:i + 1].cpu().numpy(), s_o, [C])
+    ri, rb, rn = orc.topk_hier(rows_o, cache_o, s_o, cfg.topk, cfg.block, cfg.max_blocks)
+    say("  hierarchical selection")
+    assert np.array_equal(idx[i:i + 1].cpu().numpy(), ri)
+    assert np.array_equal(pn[i:i + 1].cpu().numpy(), rn)
+    assert np.array_equal(pb[i:i + 1].cpu().numpy(), rb)
+    W = 128
+    rw = swa_raw[i * W:(i + 1) * W].cpu().numpy()
+    codes, scales, wo = oracle_window(orc, rw, 1, [S - W], W)
+    assert np.array_equal(codes, scd[i * W:(i + 1) * W].cpu().numpy())
+    out_o, _ = orc.sparse_swa_attn(rows_o, cache_o, bits(q[i:i + 1]), 1, bits(kv[i * C:(i + 1) * C]), 1, ri, wo,
+                                   heads=cfg.heads, dim=cfg.dim, sm_scale=synth.sm_scale(cfg.dim))
+    say("  attention")
+    check_attn(out[i:i + 1].float().cpu().numpy(), out_o)
