@@ -26,7 +26,11 @@
 
 namespace csa2 {
 
-enum SrcMode { SRC_FULL = 0, SRC_POOL = 1, SRC_BLOCK = 2, SRC_LIST = 3 };
+// Candidate sources: FULL (score row, column = position), POOL (compact pool score row,
+// column c = pool position c), BLOCK (block maxima computed from the score row), LIST (a
+// previous level's (key, position) lists), BMAX (precomputed block-maximum keys), PGATHER
+// (the pool's positions gathered from the full score row).
+enum SrcMode { SRC_FULL = 0, SRC_POOL = 1, SRC_BLOCK = 2, SRC_LIST = 3, SRC_BMAX = 4, SRC_PGATHER = 5 };
 enum OutMode { OUT_IDX = 0, OUT_LIST = 1, OUT_BLOCKS = 2 };
 
 constexpr int kNT = 1024;
@@ -48,6 +52,8 @@ struct SelArgs {
     int32_t* out_nblocks;
     int out_stride;
     int out_mode;
+    const uint32_t* bmax;  // SRC_BMAX: block-maximum keys [n][bstride]
+    int64_t bstride;
 };
 
 __device__ __forceinline__ void row_info(const SelSource& s, int row, int64_t* R, int64_t* ncol, int* prow)
@@ -87,6 +93,48 @@ __device__ __forceinline__ void load_keys(const SelArgs& a, int row, int64_t R, 
             const bool ok = e < lim_e && li < lim_l;
             const uint32_t v = in[ok ? li : 0].x;
             key[i] = ok ? v : 0u;
+        }
+        return;
+    }
+    if (SRC == SRC_BMAX) {
+        // every block but the newest (its key is 0 in the array, and it is past lim)
+        const int64_t lim = ((ncol + 7) >> 3) - 1;
+        const uint32_t* kp = a.bmax + (int64_t)row * a.bstride;
+#pragma unroll
+        for (int i = 0; i < KPT; i++) {
+            const int64_t c = base + e0 + i;
+            const bool ok = (e0 + i < a.seg_len) && (c < lim);
+            const uint32_t v = kp[ok ? c : 0];
+            key[i] = ok ? v : 0u;
+        }
+        return;
+    }
+    if constexpr (SRC == SRC_PGATHER) {
+        // candidate c is pool position blocks[c / 8] * 8 + c % 8 of the full score row;
+        // a thread's KPT candidates are KPT / 8 whole blocks
+        static_assert(KPT % 8 == 0, "whole blocks per thread");
+        const float* rowp = s.scores + (int64_t)row * s.stride;
+        const bool vec = ((reinterpret_cast<uintptr_t>(rowp) & 15) == 0);
+        const int64_t lim = (a.seg_len < ncol - base) ? base + a.seg_len : ncol;
+#pragma unroll
+        for (int b8 = 0; b8 < KPT / 8; b8++) {
+            const int64_t c = base + e0 + 8 * b8;
+            const bool okb = c < lim;
+            const int64_t blk = okb ? s.pool.blocks[(int64_t)prow * s.pool.max_blocks + (c >> 3)] : 0;
+            float f[8];
+            if (vec && blk * 8 + 8 <= s.stride) {
+                const float4 u = reinterpret_cast<const float4*>(rowp + blk * 8)[0];
+                const float4 v = reinterpret_cast<const float4*>(rowp + blk * 8)[1];
+                f[0] = u.x; f[1] = u.y; f[2] = u.z; f[3] = u.w; f[4] = v.x; f[5] = v.y; f[6] = v.z; f[7] = v.w;
+            } else {
+#pragma unroll
+                for (int q = 0; q < 8; q++) f[q] = rowp[blk * 8 + q < s.stride ? blk * 8 + q : 0];
+            }
+#pragma unroll
+            for (int q = 0; q < 8; q++) {
+                const bool ok = okb && (c + q < lim) && (blk * 8 + q < R);
+                key[8 * b8 + q] = ok ? order_key(f[q]) : 0u;
+            }
         }
         return;
     }
@@ -395,7 +443,7 @@ __global__ __launch_bounds__(kNT) void k_select(SelArgs a)
             int32_t pos;
             if (SRC == SRC_LIST)
                 pos = (int32_t)a.in[(int64_t)row * a.nlists_prev * k + base + e].y;
-            else if (SRC == SRC_POOL)
+            else if (SRC == SRC_POOL || SRC == SRC_PGATHER)
                 pos = (int32_t)pool_position(s, a.block_shift, prow, base + e);
             else
                 pos = (int32_t)(base + e);
@@ -486,12 +534,12 @@ static size_t plan_workspace(const Plan& p, int n, int k)
 template <int SRC>
 static void launch_level(dim3 grid, int64_t cap, const SelArgs& a, hipStream_t stream)
 {
-    if (cap <= 4096)
-        hipLaunchKernelGGL((k_select<4, SRC>), grid, dim3(kNT), 0, stream, a);
-    else if (cap <= 16384 || SRC == SRC_POOL || SRC == SRC_BLOCK)
+    if (cap <= 4096)  // (pool gathers take whole blocks: at least 8 per thread)
+        hipLaunchKernelGGL((k_select<SRC == SRC_PGATHER ? 16 : 4, SRC>), grid, dim3(kNT), 0, stream, a);
+    else if (cap <= 16384 || SRC != SRC_FULL)
         hipLaunchKernelGGL((k_select<16, SRC>), grid, dim3(kNT), 0, stream, a);
     else
-        hipLaunchKernelGGL((k_select<(SRC == SRC_POOL || SRC == SRC_BLOCK) ? 16 : kMaxKPT, SRC>), grid, dim3(kNT), 0,
+        hipLaunchKernelGGL((k_select<SRC == SRC_FULL ? kMaxKPT : 16, SRC>), grid, dim3(kNT), 0,
                            stream, a);
 }
 
@@ -503,7 +551,8 @@ static int ilog2(int x)
 }
 
 static hipError_t run_plan(const SelSource& src, int mode, int block, int k, int64_t cols, int out_mode,
-                           int32_t* out_idx, int out_stride, int32_t* out_nblocks, void* ws, hipStream_t stream)
+                           int32_t* out_idx, int out_stride, int32_t* out_nblocks, void* ws, hipStream_t stream,
+                           const uint32_t* bmax = nullptr, int64_t bstride = 0)
 {
     const int n = src.rows.n;
     if (n == 0) return hipSuccess;
@@ -533,6 +582,8 @@ static hipError_t run_plan(const SelSource& src, int mode, int block, int k, int
         a.out_idx = out_idx;
         a.out_nblocks = out_nblocks;
         a.out_stride = out_stride;
+        a.bmax = bmax;
+        a.bstride = bstride;
         const dim3 grid((unsigned)((int64_t)n * p.nseg[l]));
         if (l > 0)
             launch_level<SRC_LIST>(grid, p.cap[l], a, stream);
@@ -540,6 +591,10 @@ static hipError_t run_plan(const SelSource& src, int mode, int block, int k, int
             launch_level<SRC_FULL>(grid, p.cap[l], a, stream);
         else if (mode == SRC_POOL)
             launch_level<SRC_POOL>(grid, p.cap[l], a, stream);
+        else if (mode == SRC_BMAX)
+            launch_level<SRC_BMAX>(grid, p.cap[l], a, stream);
+        else if (mode == SRC_PGATHER)
+            launch_level<SRC_PGATHER>(grid, p.cap[l], a, stream);
         else
             launch_level<SRC_BLOCK>(grid, p.cap[l], a, stream);
         const hipError_t e = hipGetLastError();
@@ -566,8 +621,55 @@ hipError_t launch_topk(const SelSource& src, int k, int32_t* out, void* ws, size
                     ws, stream);
 }
 
+// Block maxima of the full score row as order-preserving keys: key of block b is the
+// maximum over its 8 members for every block but the newest (whose members may be partly
+// unreachable; it is always kept), 0 (no candidate) for the newest block and beyond.
+__global__ __launch_bounds__(256) void k_block_max(SelSource s, uint32_t* __restrict__ bmax, int64_t bstride,
+                                                   int chunks)
+{
+    const int row = blockIdx.x / chunks;
+    const int64_t c = (int64_t)(blockIdx.x - row * chunks) * 256 + threadIdx.x;
+    if (c >= bstride) return;
+    int64_t R, ncol;
+    int prow;
+    row_info(s, row, &R, &ncol, &prow);
+    const int64_t nblk = (ncol + 7) >> 3;
+    uint32_t m = 0;
+    if (c < nblk - 1) {
+        const float* sp = s.scores + (int64_t)row * s.stride + c * 8;
+        if ((reinterpret_cast<uintptr_t>(sp) & 15) == 0) {
+            const float4 u = reinterpret_cast<const float4*>(sp)[0];
+            const float4 v = reinterpret_cast<const float4*>(sp)[1];
+            m = max(max(max(order_key(u.x), order_key(u.y)), max(order_key(u.z), order_key(u.w))),
+                    max(max(order_key(v.x), order_key(v.y)), max(order_key(v.z), order_key(v.w))));
+        } else {
+#pragma unroll
+            for (int q = 0; q < 8; q++) m = max(m, order_key(sp[q]));
+        }
+    }
+    bmax[(int64_t)row * bstride + c] = m;
+}
+
+// The two-stage hierarchy (blocks of 8, k <= max_blocks - 1): block maxima, the pool's
+// blocks selected from them, then the flat top-k taken over the pool's positions only.
+// The last step is exact: an entry outside the pool lies in a non-newest block with at
+// least max_blocks - 1 >= k other blocks ranked above it, and each of their maxima ranks
+// above the entry in (score desc, position asc) order, so the entry is not in the top-k.
+static bool two_stage(int k, int block, int max_blocks) { return block == 8 && k >= 1 && k <= max_blocks - 1; }
+
+static size_t bmax_bytes(int n, int64_t stride)
+{
+    return (((size_t)n * (size_t)((stride + 7) / 8) * sizeof(uint32_t)) + 255) & ~(size_t)255;
+}
+
 size_t topk_hier_workspace(int n, int64_t stride, int k, int block, int max_blocks)
 {
+    if (two_stage(k, block, max_blocks)) {
+        const int64_t bstride = (stride + 7) / 8;
+        const size_t blk = plan_workspace(make_plan(bstride, max_blocks - 1, SRC_BMAX), n, max_blocks - 1);
+        const size_t flat = plan_workspace(make_plan((int64_t)max_blocks * 8, k, SRC_PGATHER), n, k);
+        return bmax_bytes(n, stride) + (blk > flat ? blk : flat);
+    }
     const size_t flat = plan_workspace(make_plan(stride, k, SRC_FULL), n, k);
     const int64_t nblk = (stride + block - 1) / block;
     const size_t blk = plan_workspace(make_plan(nblk, max_blocks - 1, SRC_BLOCK), n, max_blocks - 1);
@@ -578,6 +680,26 @@ hipError_t launch_topk_hier(const SelSource& src, int k, int block, int max_bloc
                             int32_t* out_blocks, int32_t* out_nblocks, void* ws, size_t ws_bytes, hipStream_t stream)
 {
     (void)ws_bytes;
+    const int n = src.rows.n;
+    if (n == 0) return hipSuccess;
+    if (two_stage(k, block, max_blocks)) {
+        const int64_t bstride = (src.stride + 7) / 8;
+        uint32_t* bmax = static_cast<uint32_t*>(ws);
+        void* ws2 = static_cast<char*>(ws) + bmax_bytes(n, src.stride);
+        const int chunks = (int)((bstride + 255) / 256);
+        SelSource sb = src;
+        sb.pool = PoolArg{nullptr, nullptr, nullptr, 8, max_blocks};
+        hipLaunchKernelGGL(k_block_max, dim3((unsigned)((int64_t)n * chunks)), dim3(256), 0, stream, sb, bmax, bstride,
+                           chunks);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        e = run_plan(sb, SRC_BMAX, 8, max_blocks - 1, bstride, OUT_BLOCKS, out_blocks, max_blocks, out_nblocks, ws2,
+                     stream, bmax, bstride);
+        if (e != hipSuccess) return e;
+        SelSource sp = src;
+        sp.pool = PoolArg{out_blocks, out_nblocks, nullptr, 8, max_blocks};
+        return run_plan(sp, SRC_PGATHER, 8, k, (int64_t)max_blocks * 8, OUT_IDX, out_idx, k, nullptr, ws2, stream);
+    }
     hipError_t e = run_plan(src, SRC_FULL, 0, k, src.stride, OUT_IDX, out_idx, k, nullptr, ws, stream);
     if (e != hipSuccess) return e;
     const int64_t nblk = (src.stride + block - 1) / block;
