@@ -75,12 +75,18 @@ __device__ __forceinline__ int64_t pool_position(const SelSource& s, int shift, 
     return ((int64_t)s.pool.blocks[(int64_t)prow * s.pool.max_blocks + i] << shift) + (c & ((1 << shift) - 1));
 }
 
+constexpr int bid_slots(int kpt) { return kpt / 8 > 0 ? kpt / 8 : 1; }
+
 // Keys of candidates [e0, e0 + KPT) of this workgroup's slice (blocked layout), loaded
 // without per-element branches: addresses are clamped and invalid slots masked after.
+// Pool sources with whole blocks per thread (KPT % 8 == 0, slice start % 8 == 0) also
+// return the thread's pool block ids, so the output needs no second lookup.
 template <int KPT, int SRC>
 __device__ __forceinline__ void load_keys(const SelArgs& a, int row, int64_t R, int64_t ncol, int prow, int64_t base,
-                                          int64_t e0, uint32_t (&key)[KPT])
+                                          int64_t e0, uint32_t (&key)[KPT], int32_t (&bid)[bid_slots(KPT)],
+                                          bool& bid_ok)
 {
+    bid_ok = false;
     const SelSource& s = a.src;
     if (SRC == SRC_LIST) {
         const int64_t lim_e = (int64_t)a.seg_len * a.k;
@@ -121,6 +127,7 @@ __device__ __forceinline__ void load_keys(const SelArgs& a, int row, int64_t R, 
             const int64_t c = base + e0 + 8 * b8;
             const bool okb = c < lim;
             const int64_t blk = okb ? s.pool.blocks[(int64_t)prow * s.pool.max_blocks + (c >> 3)] : 0;
+            bid[b8] = (int32_t)blk;
             float f[8];
             if (vec && blk * 8 + 8 <= s.stride) {
                 const float4 u = reinterpret_cast<const float4*>(rowp + blk * 8)[0];
@@ -136,6 +143,7 @@ __device__ __forceinline__ void load_keys(const SelArgs& a, int row, int64_t R, 
                 key[8 * b8 + q] = ok ? order_key(f[q]) : 0u;
             }
         }
+        bid_ok = ((base + e0) & 7) == 0;
         return;
     }
     if (SRC == SRC_BLOCK) {
@@ -186,11 +194,25 @@ __device__ __forceinline__ void load_keys(const SelArgs& a, int row, int64_t R, 
     }
     if (SRC == SRC_POOL) {
         // a pool position past the reachable range (only in the newest block) is no candidate
+        if (KPT % 8 == 0 && a.block_shift == 3 && (c0 & 7) == 0) {
 #pragma unroll
-        for (int i = 0; i < KPT; i++) {
-            const int64_t c = c0 + i;
-            const int64_t pp = pool_position(s, a.block_shift, prow, c < lim ? c : 0);
-            key[i] = (pp >= R) ? 0u : key[i];
+            for (int b8 = 0; b8 < bid_slots(KPT); b8++) {
+                const int64_t c = c0 + 8 * b8;
+                bid[b8] = s.pool.blocks[(int64_t)prow * s.pool.max_blocks + ((c < lim ? c : 0) >> 3)];
+            }
+#pragma unroll
+            for (int i = 0; i < KPT; i++) {
+                const int64_t pp = ((int64_t)bid[i >> 3] << 3) + (i & 7);
+                key[i] = (pp >= R) ? 0u : key[i];
+            }
+            bid_ok = true;
+        } else {
+#pragma unroll
+            for (int i = 0; i < KPT; i++) {
+                const int64_t c = c0 + i;
+                const int64_t pp = pool_position(s, a.block_shift, prow, c < lim ? c : 0);
+                key[i] = (pp >= R) ? 0u : key[i];
+            }
         }
     }
 }
@@ -301,7 +323,9 @@ __global__ __launch_bounds__(kNT) void k_select(SelArgs a)
     const int64_t e0 = (int64_t)tid * KPT;  // blocked: thread t owns [t*KPT, (t+1)*KPT)
 
     uint32_t key[KPT];
-    load_keys<KPT, SRC>(a, row, R, ncol, prow, base, e0, key);
+    int32_t bid[bid_slots(KPT)];
+    bool bid_ok;
+    load_keys<KPT, SRC>(a, row, R, ncol, prow, base, e0, key, bid, bid_ok);
     int nvalid = 0;
     uint32_t kmax = 0, kmin = 0xFFFFFFFFu;
     uint64_t live = 0;
@@ -418,12 +442,15 @@ __global__ __launch_bounds__(kNT) void k_select(SelArgs a)
         selbits |= (uint64_t)isgt << i;
         eqbits |= (uint64_t)iseq << i;
     }
-    int eq_before, dummy_b, eq_tot, dummy_t;
+    // One scan of both counts: selected before this thread = keys above T before it plus
+    // the equal keys before it, capped at need_eq; of its own equal keys it takes the
+    // first need_eq - (equal keys before it).
+    int gt_before, eq_before, nsel_gt, eq_tot;
+    block_scan2(gt, eq, s_w, lane, wave, &gt_before, &eq_before, &nsel_gt, &eq_tot);
+    int take = 0;
     if (!ge_mode) {
-        block_scan2(eq, 0, s_w, lane, wave, &eq_before, &dummy_b, &eq_tot, &dummy_t);
-        int take = need_eq - eq_before;
+        take = need_eq - eq_before;
         take = take < 0 ? 0 : (take > eq ? eq : take);
-        // the first `take` equal keys of this thread
         int seen = 0;
 #pragma unroll
         for (int i = 0; i < KPT; i++) {
@@ -431,10 +458,9 @@ __global__ __launch_bounds__(kNT) void k_select(SelArgs a)
             selbits |= (uint64_t)(e && seen < take) << i;
             seen += e;
         }
-        gt += take;
     }
-    int off, nsel, d0, d1;
-    block_scan2(gt, 0, s_w, lane, wave, &off, &d0, &nsel, &d1);
+    int off = gt_before + (ge_mode ? 0 : (eq_before < need_eq ? eq_before : need_eq));
+    const int nsel = nsel_gt + (ge_mode ? 0 : (eq_tot < need_eq ? eq_tot : need_eq));
     const int64_t row_out = (int64_t)row * nseg + seg;
 #pragma unroll
     for (int i = 0; i < KPT; i++) {
@@ -444,7 +470,7 @@ __global__ __launch_bounds__(kNT) void k_select(SelArgs a)
             if (SRC == SRC_LIST)
                 pos = (int32_t)a.in[(int64_t)row * a.nlists_prev * k + base + e].y;
             else if (SRC == SRC_POOL || SRC == SRC_PGATHER)
-                pos = (int32_t)pool_position(s, a.block_shift, prow, base + e);
+                pos = bid_ok ? (bid[i >> 3] << 3) + (i & 7) : (int32_t)pool_position(s, a.block_shift, prow, base + e);
             else
                 pos = (int32_t)(base + e);
             if (a.out_mode == OUT_LIST)
