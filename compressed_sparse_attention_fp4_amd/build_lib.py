@@ -36,10 +36,15 @@ COMMON = [
 ]
 
 
+# Per-source flags.  The index-score kernel consumes every MFMA result with VALU
+# arithmetic at once, so its MFMAs write VGPRs (no AGPR round trip).
+EXTRA = {"k_score.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = [] if src.endswith(".hip") else ["-x", "hip"]
-    cmd = [hipcc()] + COMMON + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + COMMON + EXTRA.get(src, []) + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr[-6000:]))

@@ -21,6 +21,17 @@
 
 namespace csa2 {
 
+constexpr int kScoreMaxBlocks = 1024;  // pool blocks per workgroup chunk (block ids staged in LDS)
+
+// max(x, 0) for a float through its bit pattern: a signed-integer max with 0 keeps every
+// x >= +0 and maps negative values and -0 to +0, in one instruction (a float max would
+// first quiet possible signalling NaNs).
+__device__ __forceinline__ float relu_bits(float x)
+{
+    const int b = __float_as_int(x);
+    return __int_as_float(b > 0 ? b : 0);
+}
+
 __device__ __forceinline__ int64_t row_columns(const RowsArg& rows, const CacheArg& cache, const PoolArg& pool,
                                                int row, int64_t stride, int64_t* R_out, int* prow_out)
 {
@@ -100,6 +111,7 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
     constexpr int G = H / 4;
     __shared__ uint4 s_qa[NHT][64];
     __shared__ uint32_t s_qs[NHT][64];
+    __shared__ int32_t s_bid[kScoreMaxBlocks];
 
     const int row = blockIdx.x / nchunks;
     const int lane = threadIdx.x & 63;
@@ -111,6 +123,15 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
     if (c_begin >= ncol) return;
     const int64_t c_end = (c_begin + chunk < ncol) ? c_begin + chunk : ncol;
     const int64_t krow0 = cache.row_start[rows.req[row]];
+    // Pool rows: the chunk's block ids go to LDS (a chunk starts on a block boundary and
+    // spans at most kScoreMaxBlocks blocks; the block size is a power of two).
+    const int bshift = pool.blocks ? __builtin_ctz((unsigned)pool.block) : 0;
+    const int ncc = (int)(c_end - c_begin);  // columns of this chunk (<= 8192)
+    if (pool.blocks) {
+        const int nb = (ncc + pool.block - 1) >> bshift;
+        const int32_t* src = pool.blocks + (int64_t)prow * pool.max_blocks + (c_begin >> bshift);
+        for (int i = threadIdx.x; i < nb; i += 256) s_bid[i] = src[i];
+    }
 
     // quantize the row's index q into A operands
     for (int idx = threadIdx.x; idx < NHT * 64; idx += 256) {
@@ -154,42 +175,55 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
             for (int i = 0; i < 4; i++) wr[4 * t + i] = wrow[4 * t + i];
     }
 
-    // key tile loader: lane (g, c) of tile u takes position c's 32-element block g
-    auto load_b = [&](int64_t c0, uint4 (&kd)[4], int (&sk)[4]) {
+    // Position of chunk column `off` (0 <= off < ncc); R or beyond when the column lies
+    // past the row's reach.  Positions are below n_entries, so 32 bits hold them.
+    const int R32 = (int)R;
+    auto pos_of = [&](int off) -> int {
+        if (!pool.blocks) return (int)c_begin + off;
+        return (s_bid[off >> bshift] << bshift) | (off & (pool.block - 1));
+    };
+    const uint8_t* kd_base = kdata + krow0 * 64 + 16 * (lane >> 4);
+    const uint8_t* ks_base = kscale + krow0 * 4 + (lane >> 4);
+
+    // key tile loader: lane (g, c) of tile u takes position c's 32-element block g (an
+    // unreachable column reads position 0 and is masked when stored)
+    auto load_b = [&](int off0, uint4 (&kd)[4], int (&sk)[4]) {
 #pragma unroll
         for (int u = 0; u < 4; u++) {
-            const int64_t c = c0 + 16 * u + (lane & 15);
-            int64_t j = 0;
-            if (c < c_end) {
-                j = column_position(pool, prow, c);
-                if (j >= R) j = 0;
+            const int off = off0 + 16 * u + (lane & 15);
+            int j = 0;
+            if (off < ncc) {
+                j = pos_of(off);
+                if (j >= R32) j = 0;
             }
-            const int64_t krow = krow0 + j;
-            kd[u] = *reinterpret_cast<const uint4*>(kdata + krow * 64 + 16 * g);
-            sk[u] = (int)kscale[krow * 4 + g];
+            kd[u] = *reinterpret_cast<const uint4*>(kd_base + ((uint64_t)(uint32_t)j << 6));
+            sk[u] = (int)ks_base[(uint64_t)(uint32_t)j << 2];
         }
     };
 
     uint4 kd[4], kn[4];
     int sk[4], skn[4];
-    int64_t c0 = c_begin + 64 * wave;
-    if (c0 < c_end) load_b(c0, kd, sk);
-    for (; c0 < c_end; c0 += 256) {
+    int off0 = 64 * wave;
+    if (off0 < ncc) load_b(off0, kd, sk);
+    for (; off0 < ncc; off0 += 256) {
         // the next group's keys are in flight while this one is scored
-        if (c0 + 256 < c_end) load_b(c0 + 256, kn, skn);
+        if (off0 + 256 < ncc) load_b(off0 + 256, kn, skn);
+        // tiles one at a time: NHT products into separate registers, then the head sum
         float P[4];
 #pragma unroll
         for (int u = 0; u < 4; u++) {
+            f32x4 d[NHT];
             const i32x8 b = i32x8{(int)kd[u].x, (int)kd[u].y, (int)kd[u].z, (int)kd[u].w, 0, 0, 0, 0};
-            float pp = 0.0f;
 #pragma unroll
             for (int t = 0; t < NHT; t++) {
                 const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-                const f32x4 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[t], b, zero, 4, 4, 0, sa[t], 0,
-                                                                                 sk[u]);
-#pragma unroll
-                for (int i = 0; i < 4; i++) pp = __builtin_fmaf(wr[4 * t + i], fmaxf(d[i], 0.0f), pp);
+                d[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[t], b, zero, 4, 4, 0, sa[t], 0, sk[u]);
             }
+            float pp = 0.0f;
+#pragma unroll
+            for (int t = 0; t < NHT; t++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) pp = __builtin_fmaf(wr[4 * t + i], relu_bits(d[t][i]), pp);
             P[u] = pp;
         }
         // Lane group g holds P_g for tiles 0..3.  Pair groups (0,1) and (2,3) per tile,
@@ -201,10 +235,10 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
         auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(h01), __float_as_uint(h23), false, false);
         float score = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 
-        const int64_t c = c0 + lane;
-        if (c < c_end) {
-            if (pool.blocks && column_position(pool, prow, c) >= R) score = -INFINITY;
-            scores[(int64_t)row * stride + c] = score;
+        const int off = off0 + lane;
+        if (off < ncc) {
+            if (pool.blocks && pos_of(off) >= R32) score = -INFINITY;
+            scores[(int64_t)row * stride + c_begin + off] = score;
         }
 #pragma unroll
         for (int u = 0; u < 4; u++) {
@@ -214,12 +248,14 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
     }
 }
 
-static int pick_chunk(int n, int64_t cols)
+static int pick_chunk(int n, int64_t cols, int block)
 {
     // Each workgroup quantizes its row's index q once, so columns per workgroup should be
-    // many (1024..8192); shrink only while there are fewer than ~1024 workgroups.
+    // many (1024..8192); shrink only while there are fewer than ~1024 workgroups.  A pool
+    // chunk spans at most kScoreMaxBlocks blocks (1024 columns suffice for block 1).
     int64_t chunk = 8192;
     while (chunk > 1024 && (int64_t)n * ((cols + chunk - 1) / chunk) < 1024) chunk >>= 1;
+    while (block > 0 && chunk / block > kScoreMaxBlocks) chunk >>= 1;
     return (int)chunk;
 }
 
@@ -229,7 +265,7 @@ hipError_t launch_index_score_mxfp4(const RowsArg& rows, const CacheArg& cache, 
 {
     if (rows.n == 0) return hipSuccess;
     const int64_t cols = pool.blocks ? (int64_t)pool.block * pool.max_blocks : stride;
-    const int chunk = pick_chunk(rows.n, cols);
+    const int chunk = pick_chunk(rows.n, cols, pool.blocks ? pool.block : 0);
     const int nchunks = (int)((cols + chunk - 1) / chunk);
     dim3 grid((unsigned)((int64_t)nchunks * rows.n));
     switch (heads / 16) {
