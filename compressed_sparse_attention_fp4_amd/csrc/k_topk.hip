@@ -77,6 +77,26 @@ __device__ __forceinline__ int64_t pool_position(const SelSource& s, int shift, 
 
 constexpr int bid_slots(int kpt) { return kpt / 8 > 0 ? kpt / 8 : 1; }
 
+// Pin loaded values: an empty asm consumes them unconditionally, so the compiler cannot
+// sink a load into the branch of a later mask (which would serialize every load of a
+// thread behind a full memory round trip).
+__device__ __forceinline__ void pin(uint32_t x)
+{
+    asm volatile("" ::"v"(x));
+}
+__device__ __forceinline__ void pin(int32_t x)
+{
+    asm volatile("" ::"v"(x));
+}
+__device__ __forceinline__ void pin(float x)
+{
+    asm volatile("" ::"v"(x));
+}
+__device__ __forceinline__ void pin(const float4& v)
+{
+    asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w));
+}
+
 // Keys of candidates [e0, e0 + KPT) of this workgroup's slice (blocked layout), loaded
 // without per-element branches: addresses are clamped and invalid slots masked after.
 // Pool sources with whole blocks per thread (KPT % 8 == 0, slice start % 8 == 0) also
@@ -86,32 +106,45 @@ __device__ __forceinline__ void load_keys(const SelArgs& a, int row, int64_t R, 
                                           int64_t e0, uint32_t (&key)[KPT], int32_t (&bid)[bid_slots(KPT)],
                                           bool& bid_ok)
 {
+    // Every path issues all of the thread's loads first, with addresses clamped by bounds
+    // known without the row's geometry, then pins them (one wait) and masks afterwards.
     bid_ok = false;
     const SelSource& s = a.src;
     if (SRC == SRC_LIST) {
         const int64_t lim_e = (int64_t)a.seg_len * a.k;
         const int64_t lim_l = (int64_t)a.nlists_prev * a.k;
         const uint2* in = a.in + (int64_t)row * lim_l;
+        uint32_t v[KPT];
+#pragma unroll
+        for (int i = 0; i < KPT; i++) {
+            const int64_t li = base + e0 + i;
+            v[i] = in[li < lim_l ? li : 0].x;
+        }
+#pragma unroll
+        for (int i = 0; i < KPT; i++) pin(v[i]);
 #pragma unroll
         for (int i = 0; i < KPT; i++) {
             const int64_t e = e0 + i;
-            const int64_t li = base + e;
-            const bool ok = e < lim_e && li < lim_l;
-            const uint32_t v = in[ok ? li : 0].x;
-            key[i] = ok ? v : 0u;
+            key[i] = (e < lim_e && base + e < lim_l) ? v[i] : 0u;
         }
         return;
     }
     if (SRC == SRC_BMAX) {
         // every block but the newest (its key is 0 in the array, and it is past lim)
-        const int64_t lim = ((ncol + 7) >> 3) - 1;
         const uint32_t* kp = a.bmax + (int64_t)row * a.bstride;
+        uint32_t v[KPT];
 #pragma unroll
         for (int i = 0; i < KPT; i++) {
             const int64_t c = base + e0 + i;
-            const bool ok = (e0 + i < a.seg_len) && (c < lim);
-            const uint32_t v = kp[ok ? c : 0];
-            key[i] = ok ? v : 0u;
+            v[i] = kp[c < a.bstride ? c : 0];
+        }
+#pragma unroll
+        for (int i = 0; i < KPT; i++) pin(v[i]);
+        const int64_t lim = ((ncol + 7) >> 3) - 1;
+#pragma unroll
+        for (int i = 0; i < KPT; i++) {
+            const int64_t c = base + e0 + i;
+            key[i] = ((e0 + i < a.seg_len) && (c < lim)) ? v[i] : 0u;
         }
         return;
     }
@@ -120,27 +153,46 @@ __device__ __forceinline__ void load_keys(const SelArgs& a, int row, int64_t R, 
         // a thread's KPT candidates are KPT / 8 whole blocks
         static_assert(KPT % 8 == 0, "whole blocks per thread");
         const float* rowp = s.scores + (int64_t)row * s.stride;
-        const bool vec = ((reinterpret_cast<uintptr_t>(rowp) & 15) == 0);
+        const bool vec = ((reinterpret_cast<uintptr_t>(rowp) & 15) == 0) && (s.stride % 8 == 0);
+        int32_t bl[KPT / 8];
+#pragma unroll
+        for (int b8 = 0; b8 < KPT / 8; b8++) {
+            const int64_t cb = ((base + e0) >> 3) + b8;
+            bl[b8] = s.pool.blocks[(int64_t)prow * s.pool.max_blocks + (cb < s.pool.max_blocks ? cb : 0)];
+        }
+#pragma unroll
+        for (int b8 = 0; b8 < KPT / 8; b8++) pin(bl[b8]);
+        float f[KPT];
+#pragma unroll
+        for (int b8 = 0; b8 < KPT / 8; b8++) {
+            const int64_t p0 = (int64_t)bl[b8] * 8;
+            if (vec) {
+                const int64_t pc = (p0 >= 0 && p0 + 8 <= s.stride) ? p0 : 0;
+                const float4 u = reinterpret_cast<const float4*>(rowp + pc)[0];
+                const float4 v = reinterpret_cast<const float4*>(rowp + pc)[1];
+                f[8 * b8] = u.x; f[8 * b8 + 1] = u.y; f[8 * b8 + 2] = u.z; f[8 * b8 + 3] = u.w;
+                f[8 * b8 + 4] = v.x; f[8 * b8 + 5] = v.y; f[8 * b8 + 6] = v.z; f[8 * b8 + 7] = v.w;
+            } else {
+#pragma unroll
+                for (int q = 0; q < 8; q++) {
+                    const int64_t pq = p0 + q;
+                    f[8 * b8 + q] = rowp[(pq >= 0 && pq < s.stride) ? pq : 0];
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < KPT; i++) pin(f[i]);
         const int64_t lim = (a.seg_len < ncol - base) ? base + a.seg_len : ncol;
 #pragma unroll
         for (int b8 = 0; b8 < KPT / 8; b8++) {
             const int64_t c = base + e0 + 8 * b8;
             const bool okb = c < lim;
-            const int64_t blk = okb ? s.pool.blocks[(int64_t)prow * s.pool.max_blocks + (c >> 3)] : 0;
+            const int64_t blk = okb ? bl[b8] : 0;
             bid[b8] = (int32_t)blk;
-            float f[8];
-            if (vec && blk * 8 + 8 <= s.stride) {
-                const float4 u = reinterpret_cast<const float4*>(rowp + blk * 8)[0];
-                const float4 v = reinterpret_cast<const float4*>(rowp + blk * 8)[1];
-                f[0] = u.x; f[1] = u.y; f[2] = u.z; f[3] = u.w; f[4] = v.x; f[5] = v.y; f[6] = v.z; f[7] = v.w;
-            } else {
-#pragma unroll
-                for (int q = 0; q < 8; q++) f[q] = rowp[blk * 8 + q < s.stride ? blk * 8 + q : 0];
-            }
 #pragma unroll
             for (int q = 0; q < 8; q++) {
                 const bool ok = okb && (c + q < lim) && (blk * 8 + q < R);
-                key[8 * b8 + q] = ok ? order_key(f[q]) : 0u;
+                key[8 * b8 + q] = ok ? order_key(f[8 * b8 + q]) : 0u;
             }
         }
         bid_ok = ((base + e0) & 7) == 0;
@@ -148,58 +200,78 @@ __device__ __forceinline__ void load_keys(const SelArgs& a, int row, int64_t R, 
     }
     if (SRC == SRC_BLOCK) {
         // every block but the newest; all their members are reachable (block == 8)
-        const int64_t nblk = (ncol + 7) >> 3;
         const float* rowp = s.scores + (int64_t)row * s.stride;
         const bool vec = ((reinterpret_cast<uintptr_t>(rowp) & 15) == 0);
+        const int64_t nfull = s.stride >> 3;  // whole blocks inside the row
+        const int64_t nblk = (ncol + 7) >> 3;
+        constexpr int NB = KPT < 4 ? KPT : 4;  // blocks loaded together (registers)
 #pragma unroll
-        for (int i = 0; i < KPT; i++) {
-            const int64_t c = base + e0 + i;
-            const bool ok = (e0 + i < a.seg_len) && (c < nblk - 1);
-            const float* sp = rowp + ((ok ? c : 0) << 3);
-            uint32_t m;
-            if (vec) {
-                const float4 u = reinterpret_cast<const float4*>(sp)[0];
-                const float4 v = reinterpret_cast<const float4*>(sp)[1];
-                m = max(max(max(order_key(u.x), order_key(u.y)), max(order_key(u.z), order_key(u.w))),
-                        max(max(order_key(v.x), order_key(v.y)), max(order_key(v.z), order_key(v.w))));
-            } else {
-                m = 0;
+        for (int i0 = 0; i0 < KPT; i0 += NB) {
+            float f[NB][8];
 #pragma unroll
-                for (int q = 0; q < 8; q++) m = max(m, order_key(sp[q]));
+            for (int j = 0; j < NB; j++) {
+                const int64_t c = base + e0 + i0 + j;
+                const float* sp = rowp + ((c < nfull ? c : 0) << 3);
+                if (vec) {
+                    const float4 u = reinterpret_cast<const float4*>(sp)[0];
+                    const float4 v = reinterpret_cast<const float4*>(sp)[1];
+                    f[j][0] = u.x; f[j][1] = u.y; f[j][2] = u.z; f[j][3] = u.w;
+                    f[j][4] = v.x; f[j][5] = v.y; f[j][6] = v.z; f[j][7] = v.w;
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 8; q++) f[j][q] = sp[q];
+                }
             }
-            key[i] = ok ? m : 0u;
+#pragma unroll
+            for (int j = 0; j < NB; j++)
+#pragma unroll
+                for (int q = 0; q < 8; q++) pin(f[j][q]);
+#pragma unroll
+            for (int j = 0; j < NB; j++) {
+                const int64_t c = base + e0 + i0 + j;
+                const bool ok = (e0 + i0 + j < a.seg_len) && (c < nblk - 1);
+                uint32_t m = 0;
+#pragma unroll
+                for (int q = 0; q < 8; q++) m = max(m, order_key(f[j][q]));
+                key[i0 + j] = ok ? m : 0u;
+            }
         }
         return;
     }
     const float* rowp = s.scores + (int64_t)row * s.stride;
     const int64_t c0 = base + e0;
-    const int64_t lim = (a.seg_len < ncol - base) ? base + a.seg_len : ncol;  // columns of this slice
+    float v[KPT];
     if (KPT % 4 == 0 && c0 + KPT <= s.stride && ((reinterpret_cast<uintptr_t>(rowp + c0) & 15) == 0)) {
 #pragma unroll
         for (int i = 0; i < KPT; i += 4) {
-            const int64_t c = c0 + i;
-            const float4 v = *reinterpret_cast<const float4*>(rowp + c);
-            key[i] = (c < lim) ? order_key(v.x) : 0u;
-            key[i + 1] = (c + 1 < lim) ? order_key(v.y) : 0u;
-            key[i + 2] = (c + 2 < lim) ? order_key(v.z) : 0u;
-            key[i + 3] = (c + 3 < lim) ? order_key(v.w) : 0u;
+            const float4 u = *reinterpret_cast<const float4*>(rowp + c0 + i);
+            v[i] = u.x; v[i + 1] = u.y; v[i + 2] = u.z; v[i + 3] = u.w;
         }
     } else {
 #pragma unroll
         for (int i = 0; i < KPT; i++) {
             const int64_t c = c0 + i;
-            const float v = rowp[c < lim ? c : 0];
-            key[i] = (c < lim) ? order_key(v) : 0u;
+            v[i] = rowp[c < s.stride ? c : 0];
         }
     }
+    const bool pool_bids = SRC == SRC_POOL && KPT % 8 == 0 && a.block_shift == 3 && (c0 & 7) == 0;
+    if (pool_bids) {
+#pragma unroll
+        for (int b8 = 0; b8 < bid_slots(KPT); b8++) {
+            const int64_t cb = (c0 >> 3) + b8;
+            bid[b8] = s.pool.blocks[(int64_t)prow * s.pool.max_blocks + (cb < s.pool.max_blocks ? cb : 0)];
+        }
+#pragma unroll
+        for (int b8 = 0; b8 < bid_slots(KPT); b8++) pin(bid[b8]);
+    }
+#pragma unroll
+    for (int i = 0; i < KPT; i++) pin(v[i]);
+    const int64_t lim = (a.seg_len < ncol - base) ? base + a.seg_len : ncol;  // columns of this slice
+#pragma unroll
+    for (int i = 0; i < KPT; i++) key[i] = (c0 + i < lim) ? order_key(v[i]) : 0u;
     if (SRC == SRC_POOL) {
         // a pool position past the reachable range (only in the newest block) is no candidate
-        if (KPT % 8 == 0 && a.block_shift == 3 && (c0 & 7) == 0) {
-#pragma unroll
-            for (int b8 = 0; b8 < bid_slots(KPT); b8++) {
-                const int64_t c = c0 + 8 * b8;
-                bid[b8] = s.pool.blocks[(int64_t)prow * s.pool.max_blocks + ((c < lim ? c : 0) >> 3)];
-            }
+        if (pool_bids) {
 #pragma unroll
             for (int i = 0; i < KPT; i++) {
                 const int64_t pp = ((int64_t)bid[i >> 3] << 3) + (i & 7);
@@ -217,14 +289,53 @@ __device__ __forceinline__ void load_keys(const SelArgs& a, int row, int64_t R, 
     }
 }
 
-__device__ __forceinline__ int wave_incl_scan(int x, int lane)
+// Wave-wide scans and reductions on DPP (register-to-register lane moves, no LDS round
+// trip): Hillis-Steele shifts inside each 16-lane row (row_shr 1, 2, 4, 8), then row
+// broadcasts carry row 0's last lane into row 1, row 2's into row 3 (row_bcast:15) and
+// lane 31 into rows 2 and 3 (row_bcast:31).  Lanes a move does not reach read the
+// operation's identity.
+enum : int { kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118, kDppBcast15 = 0x142,
+             kDppBcast31 = 0x143 };
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t identity, uint32_t v)
 {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
-    return x;
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)v, CTRL, ROWS, 0xf, false);
+}
+
+// inclusive prefix of op over lanes 0..lane
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_incl(uint32_t v, uint32_t identity, Op op)
+{
+    v = op(v, dpp_move<kDppShr1, 0xf>(identity, v));
+    v = op(v, dpp_move<kDppShr2, 0xf>(identity, v));
+    v = op(v, dpp_move<kDppShr4, 0xf>(identity, v));
+    v = op(v, dpp_move<kDppShr8, 0xf>(identity, v));
+    v = op(v, dpp_move<kDppBcast15, 0xa>(identity, v));
+    v = op(v, dpp_move<kDppBcast31, 0xc>(identity, v));
+    return v;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int x, int)
+{
+    return (int)wave_incl((uint32_t)x, 0u, [](uint32_t p, uint32_t q) { return p + q; });
+}
+
+// wave-uniform reductions (the inclusive result of the last lane)
+__device__ __forceinline__ int wave_sum(int x)
+{
+    return __builtin_amdgcn_readlane((int)wave_incl((uint32_t)x, 0u, [](uint32_t p, uint32_t q) { return p + q; }),
+                                     63);
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_readlane(
+        (int)wave_incl(x, 0u, [](uint32_t p, uint32_t q) { return p > q ? p : q; }), 63);
+}
+__device__ __forceinline__ uint32_t wave_min(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_readlane(
+        (int)wave_incl(x, 0xFFFFFFFFu, [](uint32_t p, uint32_t q) { return p < q ? p : q; }), 63);
 }
 
 // Exclusive block scan of two counters at once (one barrier pair).
@@ -337,12 +448,9 @@ __global__ __launch_bounds__(kNT) void k_select(SelArgs a)
         kmax = max(kmax, key[i]);
         kmin = v ? min(kmin, key[i]) : kmin;
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        nvalid += __shfl_xor(nvalid, off, 64);
-        kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, 64));
-        kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, 64));
-    }
+    nvalid = wave_sum(nvalid);
+    kmax = wave_max(kmax);
+    kmin = wave_min(kmin);
     if (lane == 0) {
         s_red[0][wave] = (uint32_t)nvalid;
         s_red[1][wave] = kmax;
