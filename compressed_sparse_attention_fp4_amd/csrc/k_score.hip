@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256) void k_score_f32(RowsArg rows, CacheArg cache,
 // at a time: 4 key tiles of 16 positions, each scored against NHT head tiles with
 // v_mfma_scale_f32_16x16x128_f8f6f4 (E2M1 x E2M1, E8M0 block scales): key tile lane
 // (g, c) loads position c's 16-byte code block g (one 32-element block) and its scale.
-template <int NHT>
+template <int NHT, bool POOL>
 __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cache, const uint16_t* __restrict__ q,
                                                      const float* __restrict__ w, int64_t w_stride,
                                                      const uint8_t* __restrict__ kdata,
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
     constexpr int G = H / 4;
     __shared__ uint4 s_qa[NHT][64];
     __shared__ uint32_t s_qs[NHT][64];
-    __shared__ int32_t s_bid[kScoreMaxBlocks];
+    __shared__ int32_t s_bid[POOL ? kScoreMaxBlocks : 1];
 
     const int row = blockIdx.x / nchunks;
     const int lane = threadIdx.x & 63;
@@ -125,9 +125,9 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
     const int64_t krow0 = cache.row_start[rows.req[row]];
     // Pool rows: the chunk's block ids go to LDS (a chunk starts on a block boundary and
     // spans at most kScoreMaxBlocks blocks; the block size is a power of two).
-    const int bshift = pool.blocks ? __builtin_ctz((unsigned)pool.block) : 0;
+    const int bshift = POOL ? __builtin_ctz((unsigned)pool.block) : 0;
     const int ncc = (int)(c_end - c_begin);  // columns of this chunk (<= 8192)
-    if (pool.blocks) {
+    if (POOL) {
         const int nb = (ncc + pool.block - 1) >> bshift;
         const int32_t* src = pool.blocks + (int64_t)prow * pool.max_blocks + (c_begin >> bshift);
         for (int i = threadIdx.x; i < nb; i += 256) s_bid[i] = src[i];
@@ -179,15 +179,31 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
     // past the row's reach.  Positions are below n_entries, so 32 bits hold them.
     const int R32 = (int)R;
     auto pos_of = [&](int off) -> int {
-        if (!pool.blocks) return (int)c_begin + off;
+        if (!POOL) return (int)c_begin + off;
         return (s_bid[off >> bshift] << bshift) | (off & (pool.block - 1));
     };
     const uint8_t* kd_base = kdata + krow0 * 64 + 16 * (lane >> 4);
     const uint8_t* ks_base = kscale + krow0 * 4 + (lane >> 4);
+    // Full rows: the columns below `fast` are reachable positions c_begin + off, so a
+    // group that lies below it loads its four key tiles from one base address (tile u
+    // at +1 KiB u, its scales at +64 B u) without per-lane checks.
+    const int fast = POOL ? 0 : min(ncc, R32 - (int)c_begin);
+    const uint8_t* kd_lane = kd_base + (c_begin + (lane & 15)) * 64;
+    const uint8_t* ks_lane = ks_base + (c_begin + (lane & 15)) * 4;
 
     // key tile loader: lane (g, c) of tile u takes position c's 32-element block g (an
     // unreachable column reads position 0 and is masked when stored)
     auto load_b = [&](int off0, uint4 (&kd)[4], int (&sk)[4]) {
+        if (!POOL && off0 + 64 <= fast) {
+            const uint8_t* kp = kd_lane + (int64_t)off0 * 64;
+            const uint8_t* sp = ks_lane + (int64_t)off0 * 4;
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                kd[u] = *reinterpret_cast<const uint4*>(kp + 1024 * u);
+                sk[u] = (int)sp[64 * u];
+            }
+            return;
+        }
 #pragma unroll
         for (int u = 0; u < 4; u++) {
             const int off = off0 + 16 * u + (lane & 15);
@@ -200,14 +216,8 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
             sk[u] = (int)ks_base[(uint64_t)(uint32_t)j << 2];
         }
     };
-
-    uint4 kd[4], kn[4];
-    int sk[4], skn[4];
-    int off0 = 64 * wave;
-    if (off0 < ncc) load_b(off0, kd, sk);
-    for (; off0 < ncc; off0 += 256) {
-        // the next group's keys are in flight while this one is scored
-        if (off0 + 256 < ncc) load_b(off0 + 256, kn, skn);
+    // score the 64 columns off0 .. off0 + 63 from their key tiles
+    auto score_group = [&](int off0, const uint4 (&kd)[4], const int (&sk)[4]) {
         // tiles one at a time: NHT products into separate registers, then the head sum
         float P[4];
 #pragma unroll
@@ -237,14 +247,23 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
 
         const int off = off0 + lane;
         if (off < ncc) {
-            if (pool.blocks && pos_of(off) >= R32) score = -INFINITY;
+            if (POOL && pos_of(off) >= R32) score = -INFINITY;
             scores[(int64_t)row * stride + c_begin + off] = score;
         }
-#pragma unroll
-        for (int u = 0; u < 4; u++) {
-            kd[u] = kn[u];
-            sk[u] = skn[u];
-        }
+    };
+
+    // Groups 64 wave + 256 i, two key buffers alternating: the next group's keys are in
+    // flight while this one is scored.
+    uint4 ka[4], kb[4];
+    int sa4[4], sb4[4];
+    int off0 = 64 * wave;
+    if (off0 < ncc) load_b(off0, ka, sa4);
+    for (; off0 < ncc; off0 += 512) {
+        if (off0 + 256 < ncc) load_b(off0 + 256, kb, sb4);
+        score_group(off0, ka, sa4);
+        if (off0 + 256 >= ncc) break;
+        if (off0 + 512 < ncc) load_b(off0 + 512, ka, sa4);
+        score_group(off0 + 256, kb, sb4);
     }
 }
 
@@ -268,12 +287,16 @@ hipError_t launch_index_score_mxfp4(const RowsArg& rows, const CacheArg& cache, 
     const int chunk = pick_chunk(rows.n, cols, pool.blocks ? pool.block : 0);
     const int nchunks = (int)((cols + chunk - 1) / chunk);
     dim3 grid((unsigned)((int64_t)nchunks * rows.n));
-    switch (heads / 16) {
 #define CSA2_SCORE_CASE(T)                                                                                      \
     case T:                                                                                                     \
-        hipLaunchKernelGGL((k_score_mxfp4<T>), grid, dim3(256), 0, stream, rows, cache, q, w, w_stride, kdata, \
-                           kscale, pool, scores, stride, chunk, nchunks);                                               \
+        if (pool.blocks)                                                                                        \
+            hipLaunchKernelGGL((k_score_mxfp4<T, true>), grid, dim3(256), 0, stream, rows, cache, q, w, w_stride, \
+                               kdata, kscale, pool, scores, stride, chunk, nchunks);                            \
+        else                                                                                                    \
+            hipLaunchKernelGGL((k_score_mxfp4<T, false>), grid, dim3(256), 0, stream, rows, cache, q, w,         \
+                               w_stride, kdata, kscale, pool, scores, stride, chunk, nchunks);                  \
         break;
+    switch (heads / 16) {
         CSA2_SCORE_CASE(1)
         CSA2_SCORE_CASE(2)
         CSA2_SCORE_CASE(3)
@@ -282,10 +305,10 @@ hipError_t launch_index_score_mxfp4(const RowsArg& rows, const CacheArg& cache, 
         CSA2_SCORE_CASE(6)
         CSA2_SCORE_CASE(7)
         CSA2_SCORE_CASE(8)
-#undef CSA2_SCORE_CASE
         default:
             return hipErrorInvalidValue;
     }
+#undef CSA2_SCORE_CASE
     return hipGetLastError();
 }
 
