@@ -61,6 +61,9 @@ int check_device()
     return CSA2_OK;
 }
 
+// The kernels move element data in 8- and 16-byte vectors.
+bool misaligned(const void* p, uintptr_t bytes) { return (reinterpret_cast<uintptr_t>(p) & (bytes - 1)) != 0; }
+
 int check_rows(const csa2_rows* rows)
 {
     if (!rows) return fail(CSA2_E_ARG, "rows is NULL");
@@ -142,6 +145,8 @@ int csa2_index_score(const csa2_rows* rows, const csa2_cache* cache, const void*
         if (q_dtype != CSA2_BF16) return fail(CSA2_E_UNSUPPORTED, "MXFP4 keys need a BF16 index q");
         if (keys->dim != 128) return fail(CSA2_E_UNSUPPORTED, "MXFP4 keys: dim %d (128 supported)", keys->dim);
         if (!keys->scale) return fail(CSA2_E_ARG, "MXFP4 keys without a scale plane");
+        if (misaligned(q_idx, 16) || misaligned(keys->data, 16))
+            return fail(CSA2_E_ARG, "q_idx / keys->data must start on a 16-byte boundary");
         if (heads < 16 || heads > 128 || heads % 16)
             return fail(CSA2_E_UNSUPPORTED, "MXFP4 scoring: heads %d (multiple of 16, at most 128)", heads);
         if (w_row_stride != 0 && w_row_stride < heads) return fail(CSA2_E_ARG, "w_row_stride < heads");
@@ -242,6 +247,9 @@ int csa2_sparse_swa_attn(const csa2_rows* rows, const csa2_cache* cache, const v
         if (dim != 512) return fail(CSA2_E_UNSUPPORTED, "BF16 attention: dim %d (512 supported)", dim);
         if (heads % 16 || heads > 1024) return fail(CSA2_E_UNSUPPORTED, "BF16 attention: heads %d (multiple of 16)", heads);
         if (swa->dtype == CSA2_MXFP8_E4M3 && !swa->scale) return fail(CSA2_E_ARG, "MXFP8 window without scales");
+        if (misaligned(q, 16) || misaligned(kv, 16) || misaligned(out, 16) || misaligned(swa->data, 16) ||
+            (swa->scale && misaligned(swa->scale, 16)))
+            return fail(CSA2_E_ARG, "q / kv / out / swa->data / swa->scale must start on a 16-byte boundary");
     } else {
         return fail(CSA2_E_UNSUPPORTED, "attention dtypes (q %d, kv %d, window %d, out %d)", (int)q_dtype,
                     (int)kv_dtype, (int)swa->dtype, (int)out_dtype);
@@ -288,6 +296,7 @@ int csa2_quant_mx(csa2_dtype fmt, const void* x, csa2_dtype x_dtype, int64_t nbl
     if (x_dtype != CSA2_F32 && x_dtype != CSA2_BF16) return fail(CSA2_E_UNSUPPORTED, "x_dtype %d", (int)x_dtype);
     if (nblocks < 0) return fail(CSA2_E_ARG, "nblocks < 0");
     if (nblocks > 0 && (!x || !codes || !scales)) return fail(CSA2_E_ARG, "x / codes / scales is NULL");
+    if (misaligned(x, 16) || misaligned(codes, 16)) return fail(CSA2_E_ARG, "x / codes must start on a 16-byte boundary");
     if (nblocks == 0) return ok();
     int rc;
     if ((rc = check_device())) return rc;

@@ -119,17 +119,19 @@ __global__ __launch_bounds__(256) void k_attn_f32(RowsArg rows, CacheArg cache, 
 // entry is skipped) followed by the window positions.  Wave w takes tiles w, w+4, ...
 // with its own online-softmax state and output, double-buffering them in LDS: while it
 // computes on one tile, the next one is on its way (selected and bf16 window rows by
-// direct global-to-LDS copies, one 1 KiB row per instruction; FP8 window rows are
-// dequantized to bf16 through registers: E4M3 times a power of two is exact in bf16).
+// direct global-to-LDS copies with scalar row addresses, one 1 KiB row per instruction;
+// FP8 window rows are loaded into registers a tile ahead and dequantized to bf16 by the
+// scaled conversion: E4M3 times a power of two is exact in bf16).
 //   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16, 16 steps over the 512 dims: A = K rows
-//     from LDS (lane (g, c) holds key c, dims [32s+8g, +8)), B = Q^T in registers.
-//   * S^T output: lane (g, c) holds keys 4g..4g+3 of head c, which is the A operand of
-//     P V with v_mfma_f32_16x16x16_bf16 (keys are the contraction index).
-//   * The V operand (lane (g, c): keys 4g..4g+3 of dim c) comes straight from the row-
+//     from LDS (lane (g, c) holds key c, dims [32s+8g, +8)), B = Q^T in registers.  The
+//     next tile's K operand is read while this tile's P V products run.
+//   * S^T output: lane (g, c) holds keys 4g..4g+3 of head c, which is the B operand of
+//     O^T = V^T P^T with v_mfma_f32_16x16x16_bf16 (keys are the contraction index).
+//   * The V^T operand (lane (g, c): keys 4g..4g+3 of dim c) comes straight from the row-
 //     major tile with the LDS transpose read ds_read_b64_tr_b16: within a 16-lane group,
 //     element j of lane i comes from the 8-byte chunk that lane 4j + i/4 addresses, so
 //     lane (g, 4j+q) points at V[4g+j][16t+4q].
-//   * Output O: 32 tiles of 16 heads x 16 dims (lane (g, c): heads 4g..4g+3, dim 16t+c).
+//   * Output O^T: 32 tiles of 16 dims x 16 heads (lane (g, c): dims 16t+4g..+3, head c).
 // The four waves' partial results are merged in fixed order through LDS.
 // Blocks are mapped so that the head groups of one row share an XCD (and its L2): block
 // b serves row 8*(b / (8*NHG)) + b%8 and head group (b/8) % NHG.
@@ -138,10 +140,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kRowBytes = kAttnD * 2 + 48;           // LDS row pitch of a tile (48 B pad)
 constexpr int kTileBytes = 16 * kRowBytes;            // one tile of 16 keys
 constexpr int kWaveBytes = 2 * kTileBytes;            // double buffer per wave
-constexpr int kMergeWave = 512 * 64 + 64 * 16;        // one wave's output in the merge: [dim][16 heads] + pad
-constexpr int kLdsBytes = 4 * kMergeWave > 4 * kWaveBytes ? 4 * kMergeWave : 4 * kWaveBytes;
-
-typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p)
 {
@@ -149,35 +147,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p)
 }
 
 // Tiles are row-major in LDS with a pitch of 1072 B (1024 + 3 x 16): 16-byte chunk q of
-// key r starts at 67 r + q chunks, so the 16 keys of a K-operand read (same chunk) fall
-// on distinct banks, and so do the 4 keys x 4 chunks of a transposed V read.
-//
-// Copy 4 keys into LDS: key q (0..3) goes to byte address m0v + 1072 q (wave-uniform),
-// lane l passing the global address of the key's byte 16 l minus 1072 q (the immediate
-// offset moves both the global and the LDS address).  The copies are asynchronous: 4
-// vector-memory instructions, complete once s_waitcnt vmcnt has dropped past them.
-// Inline assembly, so the compiler adds no wait for them before unrelated LDS reads.
-__device__ __forceinline__ void dma_rows4(uint32_t m0v, const void* a0, const void* a1, const void* a2,
-                                          const void* a3)
-{
-    asm volatile("s_mov_b32 m0, %4\n\ts_nop 0\n\t"
-                 "global_load_lds_dwordx4 %0, off\n\t"
-                 "global_load_lds_dwordx4 %1, off offset:1072\n\t"
-                 "global_load_lds_dwordx4 %2, off offset:2144\n\t"
-                 "global_load_lds_dwordx4 %3, off offset:3216"
-                 :: "v"(a0), "v"(a1), "v"(a2), "v"(a3), "s"(m0v) : "memory", "m0");
-}
-static_assert(kRowBytes == 1072, "dma_rows4 encodes the row pitch");
+// key r starts at 67 r + q chunks, so the 8 keys of each 8-lane group of a K-operand read
+// (same chunk) fall on distinct bank quads, and a transposed V read conflicts at most
+// 2-way.
+static_assert(kRowBytes == 1072, "dma_rows4_s encodes the row pitch");
 
-// Reductions over the four 16-lane rows (lanes c, c+16, c+32, c+48).
-__device__ __forceinline__ float max_over_g(float x)
-{
-    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
+// Sum over the four 16-lane rows (lanes c, c+16, c+32, c+48).
 __device__ __forceinline__ float sum_over_g(float x)
 {
     const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -192,20 +167,44 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p)
     return __builtin_bit_cast(bf16x8, u);
 }
 
-__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 u, float scale)
+// Copy 4 keys into LDS: key u (0..3) goes to byte address m0v + 1072 u, its global row
+// address being au + 1072 u (au already holds the -1072 u that the immediate offset adds
+// back); every lane passes the same offset 16 lane.  The copies are asynchronous: 4
+// vector-memory instructions, complete once s_waitcnt vmcnt has dropped past them.
+// Inline assembly, so the compiler adds no wait for them before unrelated LDS reads.
+__device__ __forceinline__ void dma_rows4_s(uint32_t m0v, uint32_t voff, uint64_t a0, uint64_t a1, uint64_t a2,
+                                            uint64_t a3)
 {
-    bf16x8 r;
-#define CSA2_CVT(word, b, idx) r[idx] = (__bf16)(__builtin_amdgcn_cvt_f32_fp8((int)(word), b) * scale)
-    CSA2_CVT(u.x, 0, 0);
-    CSA2_CVT(u.x, 1, 1);
-    CSA2_CVT(u.x, 2, 2);
-    CSA2_CVT(u.x, 3, 3);
-    CSA2_CVT(u.y, 0, 4);
-    CSA2_CVT(u.y, 1, 5);
-    CSA2_CVT(u.y, 2, 6);
-    CSA2_CVT(u.y, 3, 7);
-#undef CSA2_CVT
-    return __builtin_bit_cast(uint4, r);
+    asm volatile("s_mov_b32 m0, %5\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %0, %1\n\t"
+                 "global_load_lds_dwordx4 %0, %2 offset:1072\n\t"
+                 "global_load_lds_dwordx4 %0, %3 offset:2144\n\t"
+                 "global_load_lds_dwordx4 %0, %4 offset:3216"
+                 :: "v"(voff), "s"(a0), "s"(a1), "s"(a2), "s"(a3), "s"(m0v) : "memory", "m0");
+}
+
+// Float max without the NaN quieting that fmaxf adds around lane-swapped values (the
+// operands here are logits or -inf, never NaN).
+__device__ __forceinline__ float vmax(float a, float b)
+{
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// 8 FP8 E4M3 codes times 2^(e - 127) to bf16 (exact: 3 mantissa bits fit in bf16's 7).
+// The scaled conversion takes the E8M0 exponent as the exponent field of an fp32 scale.
+__device__ __forceinline__ uint4 fp8x8_to_bf16x8_e(uint2 u, uint32_t e)
+{
+    const float sc = __builtin_bit_cast(float, e << 23);
+    const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u.x, sc, false);
+    const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u.x, sc, true);
+    const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u.y, sc, false);
+    const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u.y, sc, true);
+    return uint4{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, c),
+                 __builtin_bit_cast(uint32_t, d)};
 }
 
 __global__ __launch_bounds__(256) void k_attn_bf16(RowsArg rows, CacheArg cache, const uint16_t* __restrict__ q,
@@ -215,7 +214,7 @@ __global__ __launch_bounds__(256) void k_attn_bf16(RowsArg rows, CacheArg cache,
                                                    float sm_scale, const float* __restrict__ sink,
                                                    uint16_t* __restrict__ out, float* __restrict__ lse)
 {
-    __shared__ __attribute__((aligned(16))) char s_tiles[kLdsBytes];
+    __shared__ __attribute__((aligned(16))) char s_tiles[4 * kWaveBytes];
     __shared__ __attribute__((aligned(16))) int32_t s_sel[2048];
     __shared__ uint32_t s_vmask[128];
     __shared__ float s_m[4][16], s_l[4][16];
@@ -224,11 +223,30 @@ __global__ __launch_bounds__(256) void k_attn_bf16(RowsArg rows, CacheArg cache,
     const int row = 8 * (b / (8 * nhg)) + (b & 7);
     const int hg = (b >> 3) % nhg;
     if (row >= rows.n) return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c = lane & 15;
     const int h0 = 16 * hg;
 
-    // ---- Q^T as the B operand (lane (g, c): head h0+c, dims [32s+8g, +8)), issued first
+    // Wave w takes tiles w, w+4, ...: first its selected tiles (empty ones skipped),
+    // then its window tiles.  Each wave stages the slots of its own selected tiles, so no
+    // workgroup barrier precedes the tile loop.
+    const int sel_tiles = (k + 15) >> 4;
+    const int ntw = sel_tiles > wave ? (sel_tiles - wave + 3) >> 2 : 0;  // the wave's selected tiles (<= 32)
+    const int32_t* selrow = sel ? sel + (int64_t)(sel_row_map ? sel_row_map[row] : row) * sel_stride : nullptr;
+    // pass r, lane (g, c): slot c of the wave's tile 4r + g
+    int32_t jl[8];
+#pragma unroll
+    for (int r = 0; r < 8; r++) {
+        jl[r] = -1;
+        if (4 * r < ntw) {
+            const int i = 4 * r + g;
+            const int e = 16 * (wave + 4 * i) + c;
+            if (i < ntw && e < k) jl[r] = selrow[e];
+        }
+    }
+
+    // ---- Q^T as the B operand (lane (g, c): head h0+c, dims [32s+8g, +8))
     bf16x8 qb[16];
     {
         const uint16_t* qrow = q + ((int64_t)row * H + h0 + c) * kAttnD + 8 * g;
@@ -236,92 +254,123 @@ __global__ __launch_bounds__(256) void k_attn_bf16(RowsArg rows, CacheArg cache,
         for (int s = 0; s < 16; s++) qb[s] = load_bf16x8(qrow + 32 * s);
     }
     const RowKeys rk = row_keys(rows, cache, swa, sel, sel_stride, sel_row_map, row);
-
-    // ---- selected slots: indices into LDS (-1 replaced by the request's entry 0, which
-    // exists whenever the tile holds a valid entry) and a 16-bit validity mask per tile
-    const int sel_tiles = (k + 15) >> 4;
-    for (int base = 0; base < sel_tiles * 16; base += 256) {
-        const int i = base + tid;
-        const int32_t j = (i < k) ? rk.sel[i] : -1;
-        const unsigned long long bal = __ballot(j >= 0);
-        if (i < sel_tiles * 16) s_sel[i] = j >= 0 ? j : 0;
-        const int t0 = (base + 64 * wave) / 16 + lane;
-        if (lane < 4 && t0 < sel_tiles) s_vmask[t0] = (uint32_t)(bal >> (16 * lane)) & 0xffffu;
-    }
-    __syncthreads();
     const int ntiles = sel_tiles + ((rk.nwin + 15) >> 4);
+    const int64_t swa_base = swa.row_start[rk.r] - swa.pos_start[rk.r] + rk.t0;
+    const int win_first = wave + 4 * ntw;  // the wave's first window tile
+
+    // FP8 window tiles go through registers: the raw rows of the wave's next window tile
+    // are loaded one tile ahead (the first one here), so converting them into the LDS
+    // buffer does not wait on memory.
+    const bool win_fp8 = swa.dtype == 3;
+    uint2 wr[16];
+    uint32_t wsc[4];
+    auto load_win = [&](int tile) {
+        int wi = (tile - sel_tiles) * 16 + c;
+        wi = wi < rk.nwin ? wi : rk.nwin - 1;
+        const int64_t srow = swa_base + wi;
+        const uint8_t* sr = static_cast<const uint8_t*>(swa.data) + srow * kAttnD + 8 * g;
+#pragma unroll
+        for (int s = 0; s < 16; s++) wr[s] = *reinterpret_cast<const uint2*>(sr + 32 * s);
+        const uint4 sc4 = *reinterpret_cast<const uint4*>(swa.scale + srow * (kAttnD / 32));
+        wsc[0] = sc4.x;
+        wsc[1] = sc4.y;
+        wsc[2] = sc4.z;
+        wsc[3] = sc4.w;
+    };
+    auto prefetch_win = [&](int tile) {
+        if (win_fp8 && tile >= sel_tiles && tile < ntiles) load_win(tile);
+    };
+    prefetch_win(win_first);
+
+    // ---- the wave's selected slots into LDS (-1 replaced by the request's entry 0, which
+    // exists whenever the tile holds a valid entry), a 16-bit validity mask per tile, and
+    // one bit per wave tile that holds any valid slot
+    uint32_t nonempty = 0;
+#pragma unroll
+    for (int r = 0; r < 8; r++) {
+        if (4 * r < ntw) {
+            const int i = 4 * r + g;
+            const int t = wave + 4 * i;
+            const int32_t j = jl[r];
+            const uint64_t bal = __ballot(j >= 0);
+            if (i < ntw) {
+                s_sel[16 * t + c] = j >= 0 ? j : 0;
+                if (c == 0) s_vmask[t] = (uint32_t)(bal >> (16 * g)) & 0xffffu;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; u++)
+                if ((bal >> (16 * u)) & 0xffffull) nonempty |= 1u << (4 * r + u);
+        }
+    }
     // Make the compiler wait for the Q loads here, not inside the tile loop where the
     // wait would also hold back the next tile's copies.
 #pragma unroll
     for (int s = 0; s < 16; s++) asm volatile("" : "+v"(qb[s]));
 
-    const uint16_t* kv_r = kv + rk.kv0 * kAttnD;
-    const int64_t swa_base = swa.row_start[rk.r] - swa.pos_start[rk.r] + rk.t0;
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    char* my_tiles = s_tiles + wave_u * kWaveBytes;
+    char* my_tiles = s_tiles + wave * kWaveBytes;
     const uint32_t my_tiles_lds = lds_addr(my_tiles);
-    // Per-lane copy sources: byte 16 lane of a key, less q row pitches for key q of a group
-    // of 4 (the copy's immediate offset adds them back).  Window rows are addressed
-    // relative to the window cache (row swa_row0 + wi for window slot wi).
-    const int64_t swa_row0 = swa_base;
-    const uint64_t sel_lane0 = reinterpret_cast<uint64_t>(kv_r) + 16 * lane;
-    const uint64_t win_lane0 = reinterpret_cast<uint64_t>(swa.data) + 16 * lane;
-    uint32_t row_bytes;  // 1024, opaque to the compiler so the address is one v_mad_u64_u32
-    asm("s_mov_b32 %0, 1024" : "=s"(row_bytes));
+    const uint32_t voff = 16 * lane;
+    // Scalar row addresses: row j of the request's main KV (selected) or window row wi
+    // (bf16 window), less 1072 q for the q-th key of a group of 4.
+    const uint64_t kv_r = reinterpret_cast<uint64_t>(kv + rk.kv0 * kAttnD);
+    const uint64_t win_r = reinterpret_cast<uint64_t>(swa.data) + (uint64_t)swa_base * (kAttnD * 2);
     // tiles that arrive by direct copies: selected rows, and a bf16 window
-    const int dma_tiles = (swa.dtype == 3) ? sel_tiles : ntiles;
-    // the wave's next tile at or after t that holds a valid slot
-    auto next_tile = [&](int t) {
-        while (t < sel_tiles && s_vmask[t] == 0) t += 4;
-        return __builtin_amdgcn_readfirstlane(t);
+    const int dma_tiles = win_fp8 ? sel_tiles : ntiles;
+    // the wave's next tile at or after t (t = wave + 4 i) that holds a valid slot
+    auto next_tile = [&](int t) -> int {
+        if (t < sel_tiles) {
+            const int i = (t - wave) >> 2;
+            const uint32_t m = nonempty >> i;
+            return m ? t + 4 * (int)__builtin_ctz(m) : win_first;
+        }
+        return t;
     };
 
-    // Start the copy of tile `tile` into buffer `buf`.  Rows that arrive by direct copy
-    // are only issued here; FP8 window rows are loaded, dequantized and stored to LDS.
-    auto fetch = [&](int tile, int buf) {
+    // Start the copy of tile `tile` into buffer `buf`; returns the tile's 16-bit mask of
+    // valid slots.  Rows that arrive by direct copy are only issued here; FP8 window rows
+    // are converted from registers and stored to LDS.
+    auto fetch = [&](int tile, int buf) -> uint32_t {
         const uint32_t dst = my_tiles_lds + buf * kTileBytes;
-        if (tile < sel_tiles || swa.dtype != 3) {
-            uint32_t jr[16];  // the tile's rows, relative to the base of its source
-            const bool from_sel = tile < sel_tiles;
-            if (from_sel) {
-                int4 jv[4];
+        if (tile < sel_tiles) {
+            int4 jv[4];
 #pragma unroll
-                for (int u = 0; u < 4; u++) jv[u] = reinterpret_cast<const int4*>(s_sel + tile * 16)[u];
-#pragma unroll
-                for (int r = 0; r < 16; r++) jr[r] = (uint32_t)jv[r >> 2][r & 3];
-            } else {
-#pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    int wi = (tile - sel_tiles) * 16 + r;
-                    wi = wi < rk.nwin ? wi : rk.nwin - 1;
-                    jr[r] = (uint32_t)(swa_row0 + wi);
-                }
-            }
-            const uint64_t l0 = from_sel ? sel_lane0 : win_lane0;
+            for (int u = 0; u < 4; u++) jv[u] = reinterpret_cast<const int4*>(s_sel + tile * 16)[u];
+            const uint32_t vm = __builtin_amdgcn_readfirstlane(s_vmask[tile]);
 #pragma unroll
             for (int r4 = 0; r4 < 4; r4++) {
-                // one multiply-add per key: row * 1024 + lane base
-                const uint64_t a0 = (uint64_t)jr[4 * r4] * row_bytes + l0;
-                const uint64_t a1 = (uint64_t)jr[4 * r4 + 1] * row_bytes + (l0 - kRowBytes);
-                const uint64_t a2 = (uint64_t)jr[4 * r4 + 2] * row_bytes + (l0 - 2 * kRowBytes);
-                const uint64_t a3 = (uint64_t)jr[4 * r4 + 3] * row_bytes + (l0 - 3 * kRowBytes);
-                dma_rows4(dst + 4 * kRowBytes * r4, reinterpret_cast<const void*>(a0), reinterpret_cast<const void*>(a1),
-                          reinterpret_cast<const void*>(a2), reinterpret_cast<const void*>(a3));
+                uint64_t a[4];
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    const uint32_t j = __builtin_amdgcn_readfirstlane(jv[r4][u]);
+                    a[u] = kv_r + ((uint64_t)j << 10) - (uint64_t)(kRowBytes * u);
+                }
+                dma_rows4_s(dst + 4 * kRowBytes * r4, voff, a[0], a[1], a[2], a[3]);
+            }
+            return vm;
+        }
+        const int w0 = (tile - sel_tiles) * 16;
+        const int nv = rk.nwin - w0;
+        const uint32_t vm = nv >= 16 ? 0xffffu : (1u << nv) - 1u;
+        if (!win_fp8) {
+#pragma unroll
+            for (int r4 = 0; r4 < 4; r4++) {
+                uint64_t a[4];
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    const int wi = w0 + 4 * r4 + u < rk.nwin ? w0 + 4 * r4 + u : rk.nwin - 1;
+                    a[u] = win_r + ((uint64_t)(uint32_t)wi << 10) - (uint64_t)(kRowBytes * u);
+                }
+                dma_rows4_s(dst + 4 * kRowBytes * r4, voff, a[0], a[1], a[2], a[3]);
             }
         } else {
-            int wi = (tile - sel_tiles) * 16 + c;
-            wi = wi < rk.nwin ? wi : rk.nwin - 1;
-            const int64_t srow = swa_base + wi;
-            const uint8_t* sr = static_cast<const uint8_t*>(swa.data) + srow * kAttnD + 8 * g;
-            const uint8_t* sc = swa.scale + srow * (kAttnD / 32);
             char* dp = my_tiles + buf * kTileBytes + kRowBytes * c + 16 * g;
-            uint2 raw[16];
 #pragma unroll
-            for (int s = 0; s < 16; s++) raw[s] = *reinterpret_cast<const uint2*>(sr + 32 * s);
-#pragma unroll
-            for (int s = 0; s < 16; s++)
-                *reinterpret_cast<uint4*>(dp + 64 * s) = fp8x8_to_bf16x8(raw[s], __builtin_ldexpf(1.0f, (int)sc[s] - 127));
+            for (int s = 0; s < 16; s++) {
+                const uint32_t e = (wsc[s >> 2] >> (8 * (s & 3))) & 0xffu;
+                *reinterpret_cast<uint4*>(dp + 64 * s) = fp8x8_to_bf16x8_e(wr[s], e);
+            }
         }
+        return vm;
     };
 
     // State of head c (replicated over g).  Exponents are taken against a reference
@@ -342,31 +391,38 @@ __global__ __launch_bounds__(256) void k_attn_bf16(RowsArg rows, CacheArg cache,
         l_run = 0.0f;
         m_ref = (attempt == 0) ? -INFINITY : m_true;
         bool over = false;
+        // Two tiles in flight: the current one (operands being read) and the next one
+        // (arriving); the next tile's K operand is read while this tile's P V runs.
+        if (attempt == 1) prefetch_win(win_first);
         int buf = 0;
-        int tile = next_tile(wave_u);
-        if (tile < ntiles) fetch(tile, 0);
-        for (; tile < ntiles; buf ^= 1) {
-            const int nxt = next_tile(tile + 4);
-            const bool more = nxt < ntiles;
-            if (more) fetch(nxt, buf ^ 1);
-            // Wait for this tile's copies, issued one iteration ago.  When the next
-            // tile's 16 copies were just issued they may stay in flight.
-            if (more && nxt < dma_tiles)
+        int tile = next_tile(wave);
+        uint32_t vm_cur = 0, vm_nxt = 0;
+        int nxt = ntiles;
+        bf16x8 ka[16];
+        if (tile < ntiles) {
+            vm_cur = fetch(tile, 0);
+            if (tile >= sel_tiles) prefetch_win(tile + 4);
+            nxt = next_tile(tile + 4);
+            if (nxt < ntiles) vm_nxt = fetch(nxt, 1);
+            if (nxt < ntiles && nxt < dma_tiles)
                 asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
             else
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            const char* tb = my_tiles + buf * kTileBytes;
-
-            // S^T tile: lane (g, c) -> key slots 4g..4g+3, head c.  All operand reads are
-            // issued before the first product so their latencies overlap.
-            bf16x8 ka[16];
+            if (nxt < ntiles && nxt >= sel_tiles) prefetch_win(nxt + 4);
 #pragma unroll
             for (int s = 0; s < 16; s++)
-                ka[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(tb + k_off + 64 * s));
-            __builtin_amdgcn_sched_barrier(0);
-            f32x4 st = {0.0f, 0.0f, 0.0f, 0.0f};
+                ka[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(my_tiles + k_off + 64 * s));
+        }
+        for (; tile < ntiles; buf ^= 1) {
+            const char* tb = my_tiles + buf * kTileBytes;
+            // S^T tile: lane (g, c) -> key slots 4g..4g+3, head c; two accumulators halve
+            // the dependent chain
+            f32x4 st0 = {0.0f, 0.0f, 0.0f, 0.0f}, st1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int s = 0; s < 16; s++) st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s], qb[s], st, 0, 0, 0);
+            for (int s = 0; s < 16; s += 2) {
+                st0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s], qb[s], st0, 0, 0, 0);
+                st1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s + 1], qb[s + 1], st1, 0, 0, 0);
+            }
             // V operand, read transposed from the row-major tile (in flight during the
             // softmax arithmetic below)
             s16x4 vb[32];
@@ -376,87 +432,117 @@ __global__ __launch_bounds__(256) void k_attn_bf16(RowsArg rows, CacheArg cache,
                     (__attribute__((address_space(3))) s16x4*)(tb + v_off + 32 * t));
             __builtin_amdgcn_sched_barrier(0);
 
-            const uint32_t vmask = (tile < sel_tiles) ? __builtin_amdgcn_readfirstlane(s_vmask[tile]) : 0u;
             float lg[4];
-            float tmax = -INFINITY;
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const bool valid = (tile < sel_tiles) ? ((vmask >> (4 * g + i)) & 1u) != 0
-                                                      : (tile - sel_tiles) * 16 + 4 * g + i < rk.nwin;
-                lg[i] = valid ? st[i] * qk_scale : -INFINITY;
-                tmax = fmaxf(tmax, lg[i]);
+            for (int i = 0; i < 4; i++) lg[i] = (st0[i] + st1[i]) * qk_scale;
+            if (vm_cur != 0xffffu) {
+                const uint32_t bits = vm_cur >> (4 * g);
+#pragma unroll
+                for (int i = 0; i < 4; i++) lg[i] = (bits >> i) & 1u ? lg[i] : -INFINITY;
             }
-            tmax = max_over_g(tmax);
-            m_true = fmaxf(m_true, tmax);
+            float tmax = vmax(vmax(lg[0], lg[1]), vmax(lg[2], lg[3]));
+            {
+                const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+                tmax = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
+                const auto bb = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+                tmax = vmax(__uint_as_float(bb[0]), __uint_as_float(bb[1]));
+            }
+            m_true = vmax(m_true, tmax);
             if (m_ref == -INFINITY && tmax != -INFINITY) m_ref = tmax + 64.0f;  // the accumulator is still zero
             over |= tmax > m_ref;
             const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
-            float psum = 0.0f;
-            s16x4 pa;
+            float pv[4];
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const float pv = __builtin_amdgcn_exp2f(lg[i] - m_use);
-                psum += pv;
-                pa[i] = __builtin_bit_cast(short, (__bf16)pv);
-            }
+            for (int i = 0; i < 4; i++) pv[i] = __builtin_amdgcn_exp2f(lg[i] - m_use);
+            const float psum = (pv[0] + pv[1]) + (pv[2] + pv[3]);
+            const bf16x2_t p01 = bf16x2_t{(__bf16)pv[0], (__bf16)pv[1]};
+            const bf16x2_t p23 = bf16x2_t{(__bf16)pv[2], (__bf16)pv[3]};
+            const s16x4 pa = __builtin_bit_cast(s16x4, uint2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)});
             l_run += sum_over_g(psum);
             __builtin_amdgcn_sched_barrier(0);
 
-            // O += P V
+            // O^T += V^T P^T
 #pragma unroll
-            for (int t = 0; t < 32; t++) o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb[t], o[t], 0, 0, 0);
+            for (int t = 0; t < 32; t++) o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vb[t], pa, o[t], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+
+            // This buffer is free (its V operand is in registers): it takes the tile after
+            // next.  Then wait for the next tile and read its K operand while P V runs.
+            int n2 = ntiles;
+            uint32_t vm_n2 = 0;
+            if (nxt < ntiles) {
+                n2 = next_tile(nxt + 4);
+                if (n2 < ntiles) vm_n2 = fetch(n2, buf);
+                if (n2 < ntiles && n2 < dma_tiles)
+                    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+                else
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                if (n2 < ntiles && n2 >= sel_tiles) prefetch_win(n2 + 4);
+                const char* tn = my_tiles + (buf ^ 1) * kTileBytes;
+#pragma unroll
+                for (int s = 0; s < 16; s++)
+                    ka[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(tn + k_off + 64 * s));
+            }
             tile = nxt;
+            nxt = n2;
+            vm_cur = vm_nxt;
+            vm_nxt = vm_n2;
         }
         if (!__ballot(over)) break;
     }
-    __syncthreads();  // every wave is done with its tiles: the merge reuses them
 
     // ---- merge the four waves: out = sum_w O_w 2^(m_w - M) / L.  Each wave stores its
-    // scaled output as [dim][16 heads] (16 B per lane store; 16 B of padding every 8
-    // dims spreads the reads over the banks), then every thread sums 4 heads x 8 dims.
+    // unscaled O^T into its own tile area as [16 heads][512 dims] with a head pitch of
+    // 2064 B (516 dwords: the 8 lanes of each 8-lane group of a 16-byte store fall on
+    // distinct bank quads) as soon as its loop ends; after one barrier wave w combines
+    // dims [128 w, 128 w + 128) of the 16 heads, reading the four waves' values with the
+    // same lane pattern.
+    constexpr int kHeadPitch = 2064;
+    static_assert(16 * kHeadPitch <= kWaveBytes, "a wave's output fits its tile area");
+    {
+        char* ob = my_tiles + kHeadPitch * c + 16 * g;
+#pragma unroll
+        for (int t = 0; t < 32; t++) *reinterpret_cast<f32x4*>(ob + 64 * t) = o[t];
+    }
     if (g == 0) {
         s_m[wave][c] = m_ref;
         s_l[wave][c] = l_run;
     }
-    __syncthreads();  // also: every wave is done with its tiles, which the merge reuses
+    __syncthreads();
     float fac[4];
+    {
+        float mw[4], M = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int hh = 4 * g + i;
-        float M = -INFINITY;
-        for (int w = 0; w < 4; w++) M = fmaxf(M, s_m[w][hh]);
+        for (int w = 0; w < 4; w++) {
+            mw[w] = s_m[w][c];
+            M = fmaxf(M, mw[w]);
+        }
         const float Mu = (M == -INFINITY) ? 0.0f : M;
         float L = 0.0f;
-        for (int w = 0; w < 4; w++) L += s_l[w][hh] * __builtin_amdgcn_exp2f(s_m[w][hh] - Mu);
-        if (sink && M != -INFINITY) L += __builtin_amdgcn_exp2f(sink[h0 + hh] * kLog2e - Mu);
-        fac[i] = (L > 0.0f) ? __builtin_amdgcn_exp2f(s_m[wave][hh] - Mu) / L : 0.0f;
-        if (lse && wave == 0 && c == 0)
-            lse[(int64_t)row * H + h0 + hh] = (M == -INFINITY) ? -INFINITY : (M + __log2f(L)) * 0.69314718055994531f;
-    }
-    auto o_off = [](int w, int d, int quad) { return w * kMergeWave + d * 64 + (d >> 3) * 16 + quad * 16; };
 #pragma unroll
-    for (int t = 0; t < 32; t++)
-        *reinterpret_cast<f32x4*>(s_tiles + o_off(wave, 16 * t + c, g)) =
-            f32x4{o[t][0] * fac[0], o[t][1] * fac[1], o[t][2] * fac[2], o[t][3] * fac[3]};
-    __syncthreads();
-    {
-        const int quad = tid & 3, db = tid >> 2;  // heads 4 quad .. +3, dims 8 db .. +7
-        f32x4 acc[8];
-#pragma unroll
-        for (int e = 0; e < 8; e++) {
-            const int d = 8 * db + e;
-            const f32x4 v0 = *reinterpret_cast<const f32x4*>(s_tiles + o_off(0, d, quad));
-            const f32x4 v1 = *reinterpret_cast<const f32x4*>(s_tiles + o_off(1, d, quad));
-            const f32x4 v2 = *reinterpret_cast<const f32x4*>(s_tiles + o_off(2, d, quad));
-            const f32x4 v3 = *reinterpret_cast<const f32x4*>(s_tiles + o_off(3, d, quad));
-            acc[e] = ((v0 + v1) + v2) + v3;
+        for (int w = 0; w < 4; w++) {
+            fac[w] = __builtin_amdgcn_exp2f(mw[w] - Mu);
+            L += s_l[w][c] * fac[w];
         }
+        if (sink && M != -INFINITY) L += __builtin_amdgcn_exp2f(sink[h0 + c] * kLog2e - Mu);
+        const float rL = (L > 0.0f) ? 1.0f / L : 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            bf16x8 r;
+        for (int w = 0; w < 4; w++) fac[w] *= rL;
+        if (lse && wave == 0 && g == 0)
+            lse[(int64_t)row * H + h0 + c] = (M == -INFINITY) ? -INFINITY : (M + __log2f(L)) * 0.69314718055994531f;
+    }
+    {
+        const char* ib = s_tiles + kHeadPitch * c + 16 * g + 512 * wave;
+        uint16_t* orow = out + ((int64_t)row * H + h0 + c) * kAttnD + 128 * wave + 4 * g;
 #pragma unroll
-            for (int e = 0; e < 8; e++) r[e] = (__bf16)acc[e][i];
-            *reinterpret_cast<bf16x8*>(out + ((int64_t)row * H + h0 + 4 * quad + i) * kAttnD + 8 * db) = r;
+        for (int u = 0; u < 8; u++) {
+            f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int w = 0; w < 4; w++) a += *reinterpret_cast<const f32x4*>(ib + w * kWaveBytes + 64 * u) * fac[w];
+            const bf16x2_t r01 = bf16x2_t{(__bf16)a[0], (__bf16)a[1]};
+            const bf16x2_t r23 = bf16x2_t{(__bf16)a[2], (__bf16)a[3]};
+            *reinterpret_cast<uint2*>(orow + 16 * u) =
+                uint2{__builtin_bit_cast(uint32_t, r01), __builtin_bit_cast(uint32_t, r23)};
         }
     }
 }

@@ -30,6 +30,12 @@
  *     csa2_last_error() gives a message for the calling thread.
  *   - Device-array contents (positions, lengths, indices) are preconditions stated per
  *     call; they are not checked.
+ *   - Element arrays move in 16-byte vectors and must start on a 16-byte boundary (every
+ *     hipMalloc / torch allocation does): q_idx and keys->data of csa2_index_score (MXFP4);
+ *     q, kv, out, swa->data and swa->scale of csa2_sparse_swa_attn (BF16); x and codes of
+ *     csa2_quant_mx.  A misaligned pointer is CSA2_E_ARG.  Row pitches follow from the
+ *     shapes (64 + 4 bytes per MXFP4 key, 1 KiB per bf16 KV row), so aligned bases keep
+ *     every row aligned.
  *   - Results are deterministic: the same inputs give bitwise-identical outputs, and a
  *     row's outputs do not depend on the other rows of the batch.
  *   - Calls are reentrant; the library keeps no state between calls.

@@ -43,6 +43,7 @@ def _err():
 
 
 P = ctypes.c_void_p(4096)  # a non-null pointer that is never dereferenced on these paths
+M = ctypes.c_void_p(4104)  # the same, not on a 16-byte boundary
 
 
 def test_index_score_arg_errors():
@@ -67,6 +68,9 @@ def test_index_score_arg_errors():
     assert call(args(keys=ctypes.byref(no_scale))) == B.CSA2_E_ARG
     pool = B._Pool(8, 2048, P, P, None)
     assert call(args(pool=ctypes.byref(pool), stride=1000)) == B.CSA2_E_ARG and "score_stride" in _err()
+    assert call(args(q=M)) == B.CSA2_E_ARG and "16-byte" in _err()
+    odd_keys = B._IndexKeys(B.MXFP4, 128, M, P)
+    assert call(args(keys=ctypes.byref(odd_keys))) == B.CSA2_E_ARG and "16-byte" in _err()
     f32 = B._IndexKeys(B.F32, 64, P, None)
     assert call(args(keys=ctypes.byref(f32), qdt=B.F32, heads=6)) == B.CSA2_E_UNSUPPORTED
     # zero rows: valid and a no-op
@@ -108,11 +112,12 @@ def test_attn_arg_errors():
     L = B.lib()
     swa = B._Swa(B.MXFP8_E4M3, P, P, P, P, 128)
 
-    def call(qdt=B.BF16, kvdt=B.BF16, odt=B.BF16, heads=64, dim=512, k=512, stride=512, sel=P, w=None, scale=0.04):
+    def call(qdt=B.BF16, kvdt=B.BF16, odt=B.BF16, heads=64, dim=512, k=512, stride=512, sel=P, w=None, scale=0.04,
+             q=P, kv=P, out=P):
         s = w or swa
-        return L.csa2_sparse_swa_attn(ctypes.byref(_rows()), ctypes.byref(_cache()), P, qdt, ctypes.c_int32(heads),
-                                      ctypes.c_int32(dim), P, kvdt, sel, ctypes.c_int32(k), ctypes.c_int64(stride), None,
-                                      ctypes.byref(s), ctypes.c_float(scale), None, P, odt, None, None,
+        return L.csa2_sparse_swa_attn(ctypes.byref(_rows()), ctypes.byref(_cache()), q, qdt, ctypes.c_int32(heads),
+                                      ctypes.c_int32(dim), kv, kvdt, sel, ctypes.c_int32(k), ctypes.c_int64(stride), None,
+                                      ctypes.byref(s), ctypes.c_float(scale), None, out, odt, None, None,
                                       ctypes.c_size_t(0), None)
 
     assert call(dim=256) == B.CSA2_E_UNSUPPORTED
@@ -124,6 +129,9 @@ def test_attn_arg_errors():
     assert call(scale=0.0) == B.CSA2_E_ARG
     noscale = B._Swa(B.MXFP8_E4M3, P, None, P, P, 128)
     assert call(w=noscale) == B.CSA2_E_ARG
+    for kw in (dict(q=M), dict(kv=M), dict(out=M), dict(w=B._Swa(B.MXFP8_E4M3, M, P, P, P, 128)),
+               dict(w=B._Swa(B.MXFP8_E4M3, P, M, P, P, 128))):
+        assert call(**kw) == B.CSA2_E_ARG and "16-byte" in _err(), kw
     f32win = B._Swa(B.F32, P, None, P, P, 128)
     assert call(qdt=B.F32, kvdt=B.F32, odt=B.F32, dim=300, w=f32win) == B.CSA2_E_UNSUPPORTED
 
@@ -146,3 +154,5 @@ def test_quant_arg_errors():
     assert L.csa2_quant_mx(B.MXFP4, P, B.MXFP4, ctypes.c_int64(4), P, P, None) == B.CSA2_E_UNSUPPORTED
     assert L.csa2_quant_mx(B.MXFP4, None, B.F32, ctypes.c_int64(4), P, P, None) == B.CSA2_E_ARG
     assert L.csa2_quant_mx(B.MXFP4, None, B.F32, ctypes.c_int64(0), None, None, None) == B.CSA2_OK
+    assert L.csa2_quant_mx(B.MXFP4, M, B.F32, ctypes.c_int64(4), P, P, None) == B.CSA2_E_ARG and "16-byte" in _err()
+    assert L.csa2_quant_mx(B.MXFP4, P, B.F32, ctypes.c_int64(4), M, P, None) == B.CSA2_E_ARG

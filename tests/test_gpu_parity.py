@@ -363,6 +363,17 @@ def test_attn_bf16(orc, H, k, swa_fp8, tail):
     _check_bf16_attn(got, ref, lse_g, lse_r)
 
 
+@pytest.mark.parametrize("sm_scale", [1.0, 3.0])
+def test_attn_bf16_wide_logits(orc, sm_scale):
+    # Logits spread over far more than 64 (log2 units) between a wave's first tile and the
+    # row maximum, so the exponent reference taken from the first tile is exceeded and the
+    # wave redoes its tiles with the exact maximum.
+    say("case: bf16 attention with logits spread wider than the first-tile reference, scale %g" % sm_scale)
+    rows, cache, q, kv, win, swa_raw, sel = _attn_bf16_case(61, (2600, 700), 2, 16, 512, 6)
+    got, lse_g, ref, lse_r = _run_attn_bf16(orc, rows, cache, q, kv, win, swa_raw, sel, 16, sm_scale)
+    _check_bf16_attn(got, ref, lse_g, lse_r)
+
+
 def test_attn_bf16_dense_equivalence(orc):
     say("case: bf16 attention with every reachable entry selected equals dense brute force")
     rows, cache, q, kv, win, swa_raw, _ = _attn_bf16_case(77, (900,), 2, 16, 512, 8)
