@@ -302,10 +302,6 @@ __global__ __launch_bounds__(256) void k_attn_bf16(RowsArg rows, CacheArg cache,
                 if ((bal >> (16 * u)) & 0xffffull) nonempty |= 1u << (4 * r + u);
         }
     }
-    // Make the compiler wait for the Q loads here, not inside the tile loop where the
-    // wait would also hold back the next tile's copies.
-#pragma unroll
-    for (int s = 0; s < 16; s++) asm volatile("" : "+v"(qb[s]));
 
     char* my_tiles = s_tiles + wave * kWaveBytes;
     const uint32_t my_tiles_lds = lds_addr(my_tiles);
@@ -413,6 +409,11 @@ __global__ __launch_bounds__(256) void k_attn_bf16(RowsArg rows, CacheArg cache,
             for (int s = 0; s < 16; s++)
                 ka[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(my_tiles + k_off + 64 * s));
         }
+        // The first copies are on their way: make the compiler wait for the Q loads here
+        // (the wait above has already covered them), not inside the tile loop where its
+        // wait would also hold back copies.
+#pragma unroll
+        for (int s = 0; s < 16; s++) asm volatile("" : "+v"(qb[s]));
         for (; tile < ntiles; buf ^= 1) {
             const char* tb = my_tiles + buf * kTileBytes;
             // S^T tile: lane (g, c) -> key slots 4g..4g+3, head c; two accumulators halve
