@@ -128,4 +128,25 @@ __device__ __forceinline__ uint32_t order_key(float s)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Workgroups are dealt to the GPU's 8 XCDs (each with its own L2) round-robin by block
+// index.  A grid of nrows x nchunks workgroups keeps the chunks of row r on XCD r % 8, the
+// XCD every kernel of the path gives row r, so that a row's scores, selections and rows of
+// KV that one kernel writes or pulls in are in the L2 the next kernel reads from.  Block
+// b of each complete group of 8 rows serves row 8 (b / 8 / nchunks) + b % 8, chunk
+// (b / 8) % nchunks; the rows after the last complete group take the remaining blocks in
+// row-major order.  Any b below nrows x nchunks maps to one (row, chunk), and back.
+__device__ __forceinline__ void xcd_row_chunk(int b, int nrows, int nchunks, int* row, int* chunk)
+{
+    const int full = (nrows >> 3) * nchunks * 8;  // blocks of the complete groups
+    if (b < full) {
+        const int g = b >> 3;
+        *row = 8 * (g / nchunks) + (b & 7);
+        *chunk = g % nchunks;
+    } else {
+        const int rb = b - full;
+        *row = (nrows & ~7) + rb / nchunks;
+        *chunk = rb % nchunks;
+    }
+}
+
 }  // namespace csa2

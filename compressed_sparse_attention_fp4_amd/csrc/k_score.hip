@@ -63,11 +63,12 @@ __global__ __launch_bounds__(256) void k_score_f32(RowsArg rows, CacheArg cache,
                                                    const float* __restrict__ keys, PoolArg pool,
                                                    float* __restrict__ scores, int64_t stride, int nchunks)
 {
-    const int row = blockIdx.x / nchunks;
+    int row, chk;
+    xcd_row_chunk(blockIdx.x, rows.n, nchunks, &row, &chk);
     int64_t R;
     int prow;
     const int64_t ncol = row_columns(rows, cache, pool, row, stride, &R, &prow);
-    const int64_t c = (int64_t)(blockIdx.x % nchunks) * blockDim.x + threadIdx.x;
+    const int64_t c = (int64_t)chk * blockDim.x + threadIdx.x;
     if (c >= ncol) return;
     const int64_t j = column_position(pool, prow, c);
     float* dst = scores + (int64_t)row * stride + c;
@@ -113,13 +114,14 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
     __shared__ uint32_t s_qs[NHT][64];
     __shared__ int32_t s_bid[POOL ? kScoreMaxBlocks : 1];
 
-    const int row = blockIdx.x / nchunks;
+    int row, chk;
+    xcd_row_chunk(blockIdx.x, rows.n, nchunks, &row, &chk);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     int64_t R;
     int prow;
     const int64_t ncol = row_columns(rows, cache, pool, row, stride, &R, &prow);
-    const int64_t c_begin = (int64_t)(blockIdx.x % nchunks) * chunk;
+    const int64_t c_begin = (int64_t)chk * chunk;
     if (c_begin >= ncol) return;
     const int64_t c_end = (c_begin + chunk < ncol) ? c_begin + chunk : ncol;
     const int64_t krow0 = cache.row_start[rows.req[row]];

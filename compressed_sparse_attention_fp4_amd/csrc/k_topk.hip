@@ -421,8 +421,8 @@ __global__ __launch_bounds__(kNT) void k_select(SelArgs a)
     __shared__ int s_res[2][3];
 
     const int nseg = a.nseg;
-    const int row = blockIdx.x / nseg;
-    const int seg = blockIdx.x - row * nseg;
+    int row, seg;
+    xcd_row_chunk(blockIdx.x, a.src.rows.n, nseg, &row, &seg);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const SelSource& s = a.src;
     const int k = a.k;
@@ -761,8 +761,9 @@ hipError_t launch_topk(const SelSource& src, int k, int32_t* out, void* ws, size
 __global__ __launch_bounds__(256) void k_block_max(SelSource s, uint32_t* __restrict__ bmax, int64_t bstride,
                                                    int chunks)
 {
-    const int row = blockIdx.x / chunks;
-    const int64_t c = (int64_t)(blockIdx.x - row * chunks) * 256 + threadIdx.x;
+    int row, chk;
+    xcd_row_chunk(blockIdx.x, s.rows.n, chunks, &row, &chk);
+    const int64_t c = (int64_t)chk * 256 + threadIdx.x;
     if (c >= bstride) return;
     int64_t R, ncol;
     int prow;
