@@ -39,6 +39,7 @@ from compressed_sparse_attention_fp4_amd import binding as B  # noqa: E402
 from compressed_sparse_attention_fp4_amd import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+FP4_PEAK_TFLOPS = 10100.0  # dense FP4 MFMA, MI355X
 NREQ, SEQ, M = 64, 131072, 2
 C = SEQ // M
 HI, DI = 64, 128
@@ -241,6 +242,41 @@ def cpu_baseline(x: InputSet, nrows: int):
 
 
 # ---------------------------------------------------------------------- main
+def c1_scoring(steps: int, warmup: int, dev) -> dict:
+    """FP4 MFMA rate of the index scoring alone on the C1 prefill workload (8 requests x 8192
+    rows, m = 1: row p scores the p + 1 entries it reaches, 64 heads x 128 dims, MXFP4 keys).
+    Algorithmic work: 2 x 64 x 128 flop per (row, reachable entry)."""
+    cfg = synth.config(1)
+    g = cfg.geom
+    rows = synth.prefill_rows(g)
+    n = rows["req_of_row"].numel()
+    rd = B.Rows(rows["req_of_row"].to(dev), rows["pos_of_row"].to(dev))
+    cd = B.Cache(1, torch.tensor(g.n_entries, dtype=torch.int32, device=dev),
+                 torch.tensor(g.row_start, dtype=torch.int64, device=dev))
+    kd, ksd = B.quant_mx(B.MXFP4, synth.normal((g.total_entries, cfg.index_dim), cfg.seed, "index_keys", device=dev))
+    keys = B.IndexKeys(kd, ksd, cfg.index_dim)
+    qi = synth.normal_bf16((n, cfg.index_heads, cfg.index_dim), cfg.seed, "index_q", device=dev)
+    w = synth.uniform((n, cfg.index_heads), cfg.seed, "index_w", device=dev)
+    scores = torch.empty((n, max(g.seq_len)), dtype=torch.float32, device=dev)
+    reach = int(((rows["pos_of_row"].to(torch.int64) + 1) // g.ratio_m).clamp(max=max(g.n_entries)).sum())
+    flop = 2.0 * cfg.index_heads * cfg.index_dim * reach
+    for _ in range(max(1, warmup)):
+        B.index_score(rd, cd, qi, w, keys, scores=scores)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        B.index_score(rd, cd, qi, w, keys, scores=scores)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    tflops = flop / (ms * 1e-3) / 1e12
+    return {"measurement": "C1 prefill index scoring, MXFP4 x MXFP4 MFMA", "rows": n, "row_entries": reach,
+            "ms_per_launch": ms, "TFLOP/s": tflops, "peak_TFLOP/s": FP4_PEAK_TFLOPS,
+            "frac": tflops / FP4_PEAK_TFLOPS}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -248,6 +284,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=int(os.environ.get("OMP_NUM_THREADS", "0") or 16))
+    ap.add_argument("--c1-scoring", action="store_true",
+                    help="instead of the decode step: time the C1 prefill index scoring alone (FP4 MFMA rate)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the CSA2 path is built and timed on a single MI355X; "
@@ -257,6 +295,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     B.lib()
+    if args.c1_scoring:
+        print(json.dumps(c1_scoring(args.steps, args.warmup, dev)), flush=True)
+        return
     log("building %d input sets ..." % NSETS)
     sets = [InputSet(s, dev) for s in range(NSETS)]
     torch.cuda.synchronize()
