@@ -94,6 +94,42 @@ __global__ __launch_bounds__(256) void k_score_f32(RowsArg rows, CacheArg cache,
 }
 
 // ---------------------------------------------------------------------------- MXFP4
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// Key-tile loads in inline assembly: the compiler does not count them, so it adds no
+// conservative wait before the tile being scored; the loop waits explicitly with
+// s_waitcnt vmcnt(N), N = the loads issued after the ones it needs (loads return in
+// order, so stores in between cannot satisfy the wait early).  Every use of a loaded
+// register follows such a wait.
+template <int OFF>
+__device__ __forceinline__ u32x4_t gload_x4(const void* p)
+{
+    u32x4_t r;
+    asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=v"(r) : "v"(p), "i"(OFF) : "memory");
+    return r;
+}
+template <int OFF>
+__device__ __forceinline__ int gload_u8(const void* p)
+{
+    int r;
+    asm volatile("global_load_ubyte %0, %1, off offset:%2" : "=v"(r) : "v"(p), "i"(OFF) : "memory");
+    return r;
+}
+template <int OFF>
+__device__ __forceinline__ int gload_i32(const void* p)
+{
+    int r;
+    asm volatile("global_load_dword %0, %1, off offset:%2" : "=v"(r) : "v"(p), "i"(OFF) : "memory");
+    return r;
+}
+template <int OFF>
+__device__ __forceinline__ float gload_f32(const void* p)
+{
+    float r;
+    asm volatile("global_load_dword %0, %1, off offset:%2" : "=v"(r) : "v"(p), "i"(OFF) : "memory");
+    return r;
+}
+constexpr int kTileLoads = 8;  // vector-memory instructions per group of 4 key tiles
 // Workgroup = 4 waves on one query row and a chunk of columns.  The row's bf16 index q
 // is quantized once per workgroup into LDS (one 32-element block per lane, which is
 // exactly the lane's slice of the MFMA A operand).  Each wave then takes 64 columns
@@ -117,7 +153,7 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
     int row, chk;
     xcd_row_chunk(blockIdx.x, rows.n, nchunks, &row, &chk);
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar loop control
     int64_t R;
     int prow;
     const int64_t ncol = row_columns(rows, cache, pool, row, stride, &R, &prow);
@@ -129,33 +165,165 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
     // spans at most kScoreMaxBlocks blocks; the block size is a power of two).
     const int bshift = POOL ? __builtin_ctz((unsigned)pool.block) : 0;
     const int ncc = (int)(c_end - c_begin);  // columns of this chunk (<= 8192)
+
+    // Position of chunk column `off` (0 <= off < ncc); R or beyond when the column lies
+    // past the row's reach.  Positions are below n_entries, so 32 bits hold them.
+    const int R32 = (int)R;
+    auto pos_of = [&](int off) -> int {
+        if (!POOL) return (int)c_begin + off;
+        return (s_bid[off >> bshift] << bshift) | (off & (pool.block - 1));
+    };
+    const int32_t* bid_row = POOL ? pool.blocks + (int64_t)prow * pool.max_blocks + (c_begin >> bshift) : nullptr;
+    const uint8_t* kd_base = kdata + krow0 * 64 + 16 * (lane >> 4);
+    const uint8_t* ks_base = kscale + krow0 * 4 + (lane >> 4);
+    // Full rows: the columns below `fast` are reachable positions c_begin + off, so a
+    // group that lies below it loads its four key tiles from one base address (tile u
+    // at +1 KiB u, its scales at +64 B u) without per-lane checks.
+    const int fast = POOL ? 0 : min(ncc, R32 - (int)c_begin);
+    const uint8_t* kd_lane = kd_base + (c_begin + (lane & 15)) * 64;
+    const uint8_t* ks_lane = ks_base + (c_begin + (lane & 15)) * 4;
+
+    // key tile loader: lane (g, c) of tile u takes position c's 32-element block g (an
+    // unreachable column reads position 0 and is masked when stored).  Issues exactly
+    // kTileLoads loads.  General columns first get their row addresses (gather_b), then
+    // the loads are issued (issue_b).
+    // (positions are looked up without branches: a column past the chunk looks up column
+    // 0, so that all lookups are issued before the first wait)
+    auto lookup_b = [&](int off0, int (&jj)[4]) {
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const int off = off0 + 16 * u + (lane & 15);
+            jj[u] = pos_of(off < ncc ? off : 0);
+        }
+    };
+    auto address_b = [&](int off0, const int (&jj)[4], const uint8_t* (&kp)[4], const uint8_t* (&sp)[4]) {
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const int off = off0 + 16 * u + (lane & 15);
+            const int j = (off < ncc && jj[u] < R32) ? jj[u] : 0;
+            kp[u] = kd_base + ((uint64_t)(uint32_t)j << 6);
+            sp[u] = ks_base + ((uint64_t)(uint32_t)j << 2);
+        }
+    };
+    auto gather_b = [&](int off0, const uint8_t* (&kp)[4], const uint8_t* (&sp)[4]) {
+        int jj[4];
+        lookup_b(off0, jj);
+        address_b(off0, jj, kp, sp);
+    };
+    auto issue_b = [&](const uint8_t* const (&kp)[4], const uint8_t* const (&sp)[4], u32x4_t (&kd)[4], int (&sk)[4]) {
+#pragma unroll
+        for (int u = 0; u < 4; u++) kd[u] = gload_x4<0>(kp[u]);
+#pragma unroll
+        for (int u = 0; u < 4; u++) sk[u] = gload_u8<0>(sp[u]);
+    };
+    auto load_b = [&](int off0, u32x4_t (&kd)[4], int (&sk)[4]) {
+        if (!POOL && off0 + 64 <= fast) {
+            const uint8_t* kp = kd_lane + (int64_t)off0 * 64;
+            const uint8_t* sp = ks_lane + (int64_t)off0 * 4;
+            kd[0] = gload_x4<0>(kp);
+            kd[1] = gload_x4<1024>(kp);
+            kd[2] = gload_x4<2048>(kp);
+            kd[3] = gload_x4<3072>(kp);
+            sk[0] = gload_u8<0>(sp);
+            sk[1] = gload_u8<64>(sp);
+            sk[2] = gload_u8<128>(sp);
+            sk[3] = gload_u8<192>(sp);
+            return;
+        }
+        const uint8_t* kp[4];
+        const uint8_t* sp[4];
+        gather_b(off0, kp, sp);
+        issue_b(kp, sp, kd, sk);
+    };
+    // ---- loads, all issued before the first wait: the row's index q (one 32-element
+    // block per thread and pass), the head weights and the pool block ids (assembly
+    // loads), then (full rows) the wave's first two groups of key tiles, so that HBM is
+    // busy from the start.
+    constexpr int QP = (NHT * 64 + 255) / 256;
+    u32x4_t qraw[QP][4];
+#pragma unroll
+    for (int pp = 0; pp < QP; pp++) {
+        const int idx = threadIdx.x + 256 * pp;
+        if (idx < NHT * 64) {
+            const int t = idx >> 6, l = idx & 63;
+            const int m = l & 15, blk = l >> 4;
+            const int head = G * (m >> 2) + 4 * t + (m & 3);
+            const uint16_t* src = q + ((int64_t)row * H + head) * 128 + blk * 32;
+            qraw[pp][0] = gload_x4<0>(src);
+            qraw[pp][1] = gload_x4<16>(src);
+            qraw[pp][2] = gload_x4<32>(src);
+            qraw[pp][3] = gload_x4<48>(src);
+        }
+    }
+    const int g = lane >> 4;
+    float wr[NHT * 4];
+    {
+        const float* wrow = w + (int64_t)row * w_stride + G * g;
+#pragma unroll
+        for (int t = 0; t < NHT; t++) {
+            wr[4 * t + 0] = gload_f32<0>(wrow + 4 * t);
+            wr[4 * t + 1] = gload_f32<4>(wrow + 4 * t);
+            wr[4 * t + 2] = gload_f32<8>(wrow + 4 * t);
+            wr[4 * t + 3] = gload_f32<12>(wrow + 4 * t);
+        }
+    }
+    constexpr int BPT = POOL ? kScoreMaxBlocks / 256 : 1;  // pool block ids staged per thread
+    const int nb = POOL ? (ncc + pool.block - 1) >> bshift : 0;
+    int32_t bidv[BPT];
     if (POOL) {
-        const int nb = (ncc + pool.block - 1) >> bshift;
-        const int32_t* src = pool.blocks + (int64_t)prow * pool.max_blocks + (c_begin >> bshift);
-        for (int i = threadIdx.x; i < nb; i += 256) s_bid[i] = src[i];
+#pragma unroll
+        for (int i = 0; i < BPT; i++) {  // branch-free: past the chunk, block 0 is read again
+            const int idx = threadIdx.x + 256 * i;
+            bidv[i] = gload_i32<0>(bid_row + (idx < nb ? idx : 0));
+        }
+    }
+    u32x4_t ka[4], kb[4];
+    int sa4[4], sb4[4];
+    int off0 = 64 * wave;
+    const bool g0 = off0 < ncc, g1 = off0 + 256 < ncc;
+    if (POOL) {
+        // pool rows look their positions up in the staged block ids: the first key tiles
+        // follow the barrier below
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+        if (g0) load_b(off0, ka, sa4);
+        if (g1) load_b(off0 + 256, kb, sb4);
+        // q and the weights have arrived once at most the key tiles are in flight
+        if (g1)
+            asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * kTileLoads) : "memory");
+        else if (g0)
+            asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kTileLoads) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
 
-    // quantize the row's index q into A operands
-    for (int idx = threadIdx.x; idx < NHT * 64; idx += 256) {
-        const int t = idx >> 6, l = idx & 63;
-        const int m = l & 15, kb = l >> 4;
-        const int head = G * (m >> 2) + 4 * t + (m & 3);
-        const uint4* src = reinterpret_cast<const uint4*>(q + ((int64_t)row * H + head) * 128 + kb * 32);
-        float v[32];
+    // ---- pool block ids to LDS; the row's index q quantized into A operands
+    if (POOL) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const uint4 u = src[i];
-            const uint32_t ws[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-            for (int jj = 0; jj < 4; jj++) {
-                v[i * 8 + 2 * jj] = __uint_as_float(ws[jj] << 16);
-                v[i * 8 + 2 * jj + 1] = __uint_as_float(ws[jj] & 0xFFFF0000u);
-            }
+        for (int i = 0; i < BPT; i++) {
+            const int idx = threadIdx.x + 256 * i;
+            if (idx < nb) s_bid[idx] = bidv[i];
         }
-        uint32_t o[4], sb;
-        quant_block_e2m1(v, o, &sb);
-        s_qa[t][l] = make_uint4(o[0], o[1], o[2], o[3]);
-        s_qs[t][l] = sb;
+    }
+#pragma unroll
+    for (int pp = 0; pp < QP; pp++) {
+        const int idx = threadIdx.x + 256 * pp;
+        if (idx < NHT * 64) {
+            const int t = idx >> 6, l = idx & 63;
+            float v[32];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+#pragma unroll
+                for (int jj = 0; jj < 4; jj++) {
+                    v[i * 8 + 2 * jj] = __uint_as_float(qraw[pp][i][jj] << 16);
+                    v[i * 8 + 2 * jj + 1] = __uint_as_float(qraw[pp][i][jj] & 0xFFFF0000u);
+                }
+            }
+            uint32_t o[4], sb;
+            quant_block_e2m1(v, o, &sb);
+            s_qa[t][l] = make_uint4(o[0], o[1], o[2], o[3]);
+            s_qs[t][l] = sb;
+        }
     }
     __syncthreads();
 
@@ -167,65 +335,19 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
         a[t] = i32x8{(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
         sa[t] = (int)s_qs[t][lane];
     }
-    const int g = lane >> 4;
-    float wr[NHT * 4];
-    {
-        const float* wrow = w + (int64_t)row * w_stride + G * g;
-#pragma unroll
-        for (int t = 0; t < NHT; t++)
-#pragma unroll
-            for (int i = 0; i < 4; i++) wr[4 * t + i] = wrow[4 * t + i];
+    if (POOL) {
+        if (g0) load_b(off0, ka, sa4);
+        if (g1) load_b(off0 + 256, kb, sb4);
     }
 
-    // Position of chunk column `off` (0 <= off < ncc); R or beyond when the column lies
-    // past the row's reach.  Positions are below n_entries, so 32 bits hold them.
-    const int R32 = (int)R;
-    auto pos_of = [&](int off) -> int {
-        if (!POOL) return (int)c_begin + off;
-        return (s_bid[off >> bshift] << bshift) | (off & (pool.block - 1));
-    };
-    const uint8_t* kd_base = kdata + krow0 * 64 + 16 * (lane >> 4);
-    const uint8_t* ks_base = kscale + krow0 * 4 + (lane >> 4);
-    // Full rows: the columns below `fast` are reachable positions c_begin + off, so a
-    // group that lies below it loads its four key tiles from one base address (tile u
-    // at +1 KiB u, its scales at +64 B u) without per-lane checks.
-    const int fast = POOL ? 0 : min(ncc, R32 - (int)c_begin);
-    const uint8_t* kd_lane = kd_base + (c_begin + (lane & 15)) * 64;
-    const uint8_t* ks_lane = ks_base + (c_begin + (lane & 15)) * 4;
-
-    // key tile loader: lane (g, c) of tile u takes position c's 32-element block g (an
-    // unreachable column reads position 0 and is masked when stored)
-    auto load_b = [&](int off0, uint4 (&kd)[4], int (&sk)[4]) {
-        if (!POOL && off0 + 64 <= fast) {
-            const uint8_t* kp = kd_lane + (int64_t)off0 * 64;
-            const uint8_t* sp = ks_lane + (int64_t)off0 * 4;
-#pragma unroll
-            for (int u = 0; u < 4; u++) {
-                kd[u] = *reinterpret_cast<const uint4*>(kp + 1024 * u);
-                sk[u] = (int)sp[64 * u];
-            }
-            return;
-        }
-#pragma unroll
-        for (int u = 0; u < 4; u++) {
-            const int off = off0 + 16 * u + (lane & 15);
-            int j = 0;
-            if (off < ncc) {
-                j = pos_of(off);
-                if (j >= R32) j = 0;
-            }
-            kd[u] = *reinterpret_cast<const uint4*>(kd_base + ((uint64_t)(uint32_t)j << 6));
-            sk[u] = (int)ks_base[(uint64_t)(uint32_t)j << 2];
-        }
-    };
     // score the 64 columns off0 .. off0 + 63 from their key tiles
-    auto score_group = [&](int off0, const uint4 (&kd)[4], const int (&sk)[4]) {
+    auto score_group = [&](int off0, const u32x4_t (&kd)[4], const int (&sk)[4]) {
         // tiles one at a time: NHT products into separate registers, then the head sum
         float P[4];
 #pragma unroll
         for (int u = 0; u < 4; u++) {
             f32x4 d[NHT];
-            const i32x8 b = i32x8{(int)kd[u].x, (int)kd[u].y, (int)kd[u].z, (int)kd[u].w, 0, 0, 0, 0};
+            const i32x8 b = i32x8{(int)kd[u][0], (int)kd[u][1], (int)kd[u][2], (int)kd[u][3], 0, 0, 0, 0};
 #pragma unroll
             for (int t = 0; t < NHT; t++) {
                 const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -256,16 +378,20 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
 
     // Groups 64 wave + 256 i, two key buffers alternating: the next group's keys are in
     // flight while this one is scored.
-    uint4 ka[4], kb[4];
-    int sa4[4], sb4[4];
-    int off0 = 64 * wave;
-    if (off0 < ncc) load_b(off0, ka, sa4);
     for (; off0 < ncc; off0 += 512) {
-        if (off0 + 256 < ncc) load_b(off0 + 256, kb, sb4);
+        if (off0 + 256 < ncc)
+            asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kTileLoads) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         score_group(off0, ka, sa4);
-        if (off0 + 256 >= ncc) break;
         if (off0 + 512 < ncc) load_b(off0 + 512, ka, sa4);
+        if (off0 + 256 >= ncc) break;
+        if (off0 + 512 < ncc)
+            asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kTileLoads) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         score_group(off0 + 256, kb, sb4);
+        if (off0 + 768 < ncc) load_b(off0 + 768, kb, sb4);
     }
 }
 
