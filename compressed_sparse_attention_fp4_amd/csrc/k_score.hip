@@ -259,12 +259,23 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
     float wr[NHT * 4];
     {
         const float* wrow = w + (int64_t)row * w_stride + G * g;
+        if ((reinterpret_cast<uintptr_t>(w) & 15) == 0 && (w_stride & 3) == 0) {  // uniform
 #pragma unroll
-        for (int t = 0; t < NHT; t++) {
-            wr[4 * t + 0] = gload_f32<0>(wrow + 4 * t);
-            wr[4 * t + 1] = gload_f32<4>(wrow + 4 * t);
-            wr[4 * t + 2] = gload_f32<8>(wrow + 4 * t);
-            wr[4 * t + 3] = gload_f32<12>(wrow + 4 * t);
+            for (int t = 0; t < NHT; t++) {
+                const u32x4_t v = gload_x4<0>(wrow + 4 * t);
+                wr[4 * t + 0] = __uint_as_float(v[0]);
+                wr[4 * t + 1] = __uint_as_float(v[1]);
+                wr[4 * t + 2] = __uint_as_float(v[2]);
+                wr[4 * t + 3] = __uint_as_float(v[3]);
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < NHT; t++) {
+                wr[4 * t + 0] = gload_f32<0>(wrow + 4 * t);
+                wr[4 * t + 1] = gload_f32<4>(wrow + 4 * t);
+                wr[4 * t + 2] = gload_f32<8>(wrow + 4 * t);
+                wr[4 * t + 3] = gload_f32<12>(wrow + 4 * t);
+            }
         }
     }
     constexpr int BPT = POOL ? kScoreMaxBlocks / 256 : 1;  // pool block ids staged per thread
@@ -272,9 +283,9 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
     int32_t bidv[BPT];
     if (POOL) {
 #pragma unroll
-        for (int i = 0; i < BPT; i++) {  // branch-free: past the chunk, block 0 is read again
+        for (int i = 0; i < BPT; i++) {  // branch-free within a pass: past the chunk, block 0 again
             const int idx = threadIdx.x + 256 * i;
-            bidv[i] = gload_i32<0>(bid_row + (idx < nb ? idx : 0));
+            bidv[i] = 256 * i < nb ? gload_i32<0>(bid_row + (idx < nb ? idx : 0)) : 0;
         }
     }
     u32x4_t ka[4], kb[4];
@@ -302,7 +313,7 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
 #pragma unroll
         for (int i = 0; i < BPT; i++) {
             const int idx = threadIdx.x + 256 * i;
-            if (idx < nb) s_bid[idx] = bidv[i];
+            if (256 * i < nb && idx < nb) s_bid[idx] = bidv[i];
         }
     }
 #pragma unroll
