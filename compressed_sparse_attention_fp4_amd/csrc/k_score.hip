@@ -96,40 +96,32 @@ __global__ __launch_bounds__(256) void k_score_f32(RowsArg rows, CacheArg cache,
 // ---------------------------------------------------------------------------- MXFP4
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
-// Key-tile loads in inline assembly: the compiler does not count them, so it adds no
-// conservative wait before the tile being scored; the loop waits explicitly with
-// s_waitcnt vmcnt(N), N = the loads issued after the ones it needs (loads return in
-// order, so stores in between cannot satisfy the wait early).  Every use of a loaded
-// register follows such a wait.
+// Loads with a constant byte offset (the offset folds into the instruction).  They are
+// ordinary loads, so the compiler tracks them and waits for each register it reads; the
+// code issues them early and in a fixed order, so the compiler's waits let the next key
+// tiles stay in flight while the current ones are scored.
 template <int OFF>
 __device__ __forceinline__ u32x4_t gload_x4(const void* p)
 {
-    u32x4_t r;
-    asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=v"(r) : "v"(p), "i"(OFF) : "memory");
-    return r;
+    return *reinterpret_cast<const u32x4_t*>(static_cast<const uint8_t*>(p) + OFF);
 }
 template <int OFF>
 __device__ __forceinline__ int gload_u8(const void* p)
 {
-    int r;
-    asm volatile("global_load_ubyte %0, %1, off offset:%2" : "=v"(r) : "v"(p), "i"(OFF) : "memory");
-    return r;
+    return static_cast<const uint8_t*>(p)[OFF];
 }
 template <int OFF>
 __device__ __forceinline__ int gload_i32(const void* p)
 {
-    int r;
-    asm volatile("global_load_dword %0, %1, off offset:%2" : "=v"(r) : "v"(p), "i"(OFF) : "memory");
-    return r;
+    return *reinterpret_cast<const int32_t*>(static_cast<const uint8_t*>(p) + OFF);
 }
 template <int OFF>
 __device__ __forceinline__ float gload_f32(const void* p)
 {
-    float r;
-    asm volatile("global_load_dword %0, %1, off offset:%2" : "=v"(r) : "v"(p), "i"(OFF) : "memory");
-    return r;
+    return *reinterpret_cast<const float*>(static_cast<const uint8_t*>(p) + OFF);
 }
 constexpr int kTileLoads = 8;  // vector-memory instructions per group of 4 key tiles
+
 // Workgroup = 4 waves on one query row and a chunk of columns.  The row's bf16 index q
 // is quantized once per workgroup into LDS (one 32-element block per lane, which is
 // exactly the lane's slice of the MFMA A operand).  Each wave then takes 64 columns
@@ -164,11 +156,13 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
     // Pool rows: the chunk's block ids go to LDS (a chunk starts on a block boundary and
     // spans at most kScoreMaxBlocks blocks; the block size is a power of two).
     const int bshift = POOL ? __builtin_ctz((unsigned)pool.block) : 0;
-    const int ncc = (int)(c_end - c_begin);  // columns of this chunk (<= 8192)
+    // (the row's sizes are read through vector loads; readfirstlane makes the branches on
+    // them scalar, so that no wave runs both sides of one)
+    const int ncc = __builtin_amdgcn_readfirstlane((int)(c_end - c_begin));  // columns of this chunk (<= 8192)
 
     // Position of chunk column `off` (0 <= off < ncc); R or beyond when the column lies
     // past the row's reach.  Positions are below n_entries, so 32 bits hold them.
-    const int R32 = (int)R;
+    const int R32 = __builtin_amdgcn_readfirstlane((int)R);
     auto pos_of = [&](int off) -> int {
         if (!POOL) return (int)c_begin + off;
         return (s_bid[off >> bshift] << bshift) | (off & (pool.block - 1));
@@ -176,17 +170,20 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
     const int32_t* bid_row = POOL ? pool.blocks + (int64_t)prow * pool.max_blocks + (c_begin >> bshift) : nullptr;
     const uint8_t* kd_base = kdata + krow0 * 64 + 16 * (lane >> 4);
     const uint8_t* ks_base = kscale + krow0 * 4 + (lane >> 4);
-    // Full rows: the columns below `fast` are reachable positions c_begin + off, so a
-    // group that lies below it loads its four key tiles from one base address (tile u
-    // at +1 KiB u, its scales at +64 B u) without per-lane checks.
-    const int fast = POOL ? 0 : min(ncc, R32 - (int)c_begin);
+    // Full rows: every chunk column is a reachable position c_begin + off (the chunk ends
+    // at the row's reach), so a group of 64 columns inside the chunk loads its four key
+    // tiles from one base address (tile u at +1 KiB u, its scales at +64 B u) without
+    // per-lane checks.
     const uint8_t* kd_lane = kd_base + (c_begin + (lane & 15)) * 64;
     const uint8_t* ks_lane = ks_base + (c_begin + (lane & 15)) * 4;
 
-    // key tile loader: lane (g, c) of tile u takes position c's 32-element block g (an
-    // unreachable column reads position 0 and is masked when stored).  Issues exactly
-    // kTileLoads loads.  General columns first get their row addresses (gather_b), then
-    // the loads are issued (issue_b).
+    // Key tile loaders: lane (g, c) of tile u takes position c's 32-element block g (an
+    // unreachable column reads position 0 and is masked when stored); each issues exactly
+    // kTileLoads loads.  load_gen serves any group: the row addresses are looked up
+    // (gather_b), then the loads issued (issue_b).  load_fast serves a full-row group
+    // inside the chunk.  Neither branches, and a wave picks one of them for all its
+    // reloads, so that the compiler sees one sequence of loads per loop and waits for
+    // each key tile just before its products.
     // (positions are looked up without branches: a column past the chunk looks up column
     // 0, so that all lookups are issued before the first wait)
     auto lookup_b = [&](int off0, int (&jj)[4]) {
@@ -216,20 +213,19 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
 #pragma unroll
         for (int u = 0; u < 4; u++) sk[u] = gload_u8<0>(sp[u]);
     };
-    auto load_b = [&](int off0, u32x4_t (&kd)[4], int (&sk)[4]) {
-        if (!POOL && off0 + 64 <= fast) {
-            const uint8_t* kp = kd_lane + (int64_t)off0 * 64;
-            const uint8_t* sp = ks_lane + (int64_t)off0 * 4;
-            kd[0] = gload_x4<0>(kp);
-            kd[1] = gload_x4<1024>(kp);
-            kd[2] = gload_x4<2048>(kp);
-            kd[3] = gload_x4<3072>(kp);
-            sk[0] = gload_u8<0>(sp);
-            sk[1] = gload_u8<64>(sp);
-            sk[2] = gload_u8<128>(sp);
-            sk[3] = gload_u8<192>(sp);
-            return;
-        }
+    auto load_fast = [&](int off0, u32x4_t (&kd)[4], int (&sk)[4]) {
+        const uint8_t* kp = kd_lane + (int64_t)off0 * 64;
+        const uint8_t* sp = ks_lane + (int64_t)off0 * 4;
+        kd[0] = gload_x4<0>(kp);
+        kd[1] = gload_x4<1024>(kp);
+        kd[2] = gload_x4<2048>(kp);
+        kd[3] = gload_x4<3072>(kp);
+        sk[0] = gload_u8<0>(sp);
+        sk[1] = gload_u8<64>(sp);
+        sk[2] = gload_u8<128>(sp);
+        sk[3] = gload_u8<192>(sp);
+    };
+    auto load_gen = [&](int off0, u32x4_t (&kd)[4], int (&sk)[4]) {
         const uint8_t* kp[4];
         const uint8_t* sp[4];
         gather_b(off0, kp, sp);
@@ -259,23 +255,12 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
     float wr[NHT * 4];
     {
         const float* wrow = w + (int64_t)row * w_stride + G * g;
-        if ((reinterpret_cast<uintptr_t>(w) & 15) == 0 && (w_stride & 3) == 0) {  // uniform
 #pragma unroll
-            for (int t = 0; t < NHT; t++) {
-                const u32x4_t v = gload_x4<0>(wrow + 4 * t);
-                wr[4 * t + 0] = __uint_as_float(v[0]);
-                wr[4 * t + 1] = __uint_as_float(v[1]);
-                wr[4 * t + 2] = __uint_as_float(v[2]);
-                wr[4 * t + 3] = __uint_as_float(v[3]);
-            }
-        } else {
-#pragma unroll
-            for (int t = 0; t < NHT; t++) {
-                wr[4 * t + 0] = gload_f32<0>(wrow + 4 * t);
-                wr[4 * t + 1] = gload_f32<4>(wrow + 4 * t);
-                wr[4 * t + 2] = gload_f32<8>(wrow + 4 * t);
-                wr[4 * t + 3] = gload_f32<12>(wrow + 4 * t);
-            }
+        for (int t = 0; t < NHT; t++) {
+            wr[4 * t + 0] = gload_f32<0>(wrow + 4 * t);
+            wr[4 * t + 1] = gload_f32<4>(wrow + 4 * t);
+            wr[4 * t + 2] = gload_f32<8>(wrow + 4 * t);
+            wr[4 * t + 3] = gload_f32<12>(wrow + 4 * t);
         }
     }
     constexpr int BPT = POOL ? kScoreMaxBlocks / 256 : 1;  // pool block ids staged per thread
@@ -288,24 +273,19 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
             bidv[i] = 256 * i < nb ? gload_i32<0>(bid_row + (idx < nb ? idx : 0)) : 0;
         }
     }
+    // The wave scores groups 64 wave + 256 i, i < n, from two key buffers that alternate.
+    // Both first loads are issued even when the wave has fewer than two groups (load_gen
+    // then reads position 0 for their columns), so the loads in flight are the same on
+    // every path.
+    const int off0 = 64 * wave;
+    const int n = off0 < ncc ? (ncc - off0 + 255) >> 8 : 0;
     u32x4_t ka[4], kb[4];
     int sa4[4], sb4[4];
-    int off0 = 64 * wave;
-    const bool g0 = off0 < ncc, g1 = off0 + 256 < ncc;
-    if (POOL) {
-        // pool rows look their positions up in the staged block ids: the first key tiles
-        // follow the barrier below
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    } else {
-        if (g0) load_b(off0, ka, sa4);
-        if (g1) load_b(off0 + 256, kb, sb4);
-        // q and the weights have arrived once at most the key tiles are in flight
-        if (g1)
-            asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * kTileLoads) : "memory");
-        else if (g0)
-            asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kTileLoads) : "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (!POOL) {
+        // pool rows look their positions up in the staged block ids: their first key
+        // tiles follow the barrier below
+        load_gen(off0, ka, sa4);
+        load_gen(off0 + 256, kb, sb4);
     }
 
     // ---- pool block ids to LDS; the row's index q quantized into A operands
@@ -347,8 +327,8 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
         sa[t] = (int)s_qs[t][lane];
     }
     if (POOL) {
-        if (g0) load_b(off0, ka, sa4);
-        if (g1) load_b(off0 + 256, kb, sb4);
+        load_gen(off0, ka, sa4);
+        load_gen(off0 + 256, kb, sb4);
     }
 
     // score the 64 columns off0 .. off0 + 63 from their key tiles
@@ -387,23 +367,35 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
         }
     };
 
-    // Groups 64 wave + 256 i, two key buffers alternating: the next group's keys are in
-    // flight while this one is scored.
-    for (; off0 < ncc; off0 += 512) {
-        if (off0 + 256 < ncc)
-            asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kTileLoads) : "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        score_group(off0, ka, sa4);
-        if (off0 + 512 < ncc) load_b(off0 + 512, ka, sa4);
-        if (off0 + 256 >= ncc) break;
-        if (off0 + 512 < ncc)
-            asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kTileLoads) : "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        score_group(off0 + 256, kb, sb4);
-        if (off0 + 768 < ncc) load_b(off0 + 768, kb, sb4);
-    }
+    // Groups i and i + 1 are in flight while group i is scored.  The loop runs while both
+    // reloads are real groups; the last two or three groups follow, so that each wait
+    // (and the load count it assumes) is fixed along every path.
+    auto run = [&](auto&& load) {
+        int i = 0;
+        for (; i + 3 < n; i += 2) {
+            score_group(off0 + 256 * i, ka, sa4);
+            load(off0 + 256 * (i + 2), ka, sa4);
+            score_group(off0 + 256 * (i + 1), kb, sb4);
+            load(off0 + 256 * (i + 3), kb, sb4);
+        }
+        const int rest = n - i;  // 0 .. 3
+        if (rest == 3) {
+            score_group(off0 + 256 * i, ka, sa4);
+            load(off0 + 256 * (i + 2), ka, sa4);
+            score_group(off0 + 256 * (i + 1), kb, sb4);
+            score_group(off0 + 256 * (i + 2), ka, sa4);
+        } else if (rest == 2) {
+            score_group(off0 + 256 * i, ka, sa4);
+            score_group(off0 + 256 * (i + 1), kb, sb4);
+        } else {
+            if (rest == 1) score_group(off0 + 256 * i, ka, sa4);
+        }
+    };
+    // a full-row wave whose every group lies inside the chunk reloads through load_fast
+    if (!POOL && n > 0 && off0 + 256 * (n - 1) + 64 <= ncc)
+        run(load_fast);
+    else
+        run(load_gen);
 }
 
 static int pick_chunk(int n, int64_t cols, int block)
