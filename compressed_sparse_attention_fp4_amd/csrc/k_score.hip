@@ -170,20 +170,14 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
     const int32_t* bid_row = POOL ? pool.blocks + (int64_t)prow * pool.max_blocks + (c_begin >> bshift) : nullptr;
     const uint8_t* kd_base = kdata + krow0 * 64 + 16 * (lane >> 4);
     const uint8_t* ks_base = kscale + krow0 * 4 + (lane >> 4);
-    // Full rows: every chunk column is a reachable position c_begin + off (the chunk ends
-    // at the row's reach), so a group of 64 columns inside the chunk loads its four key
-    // tiles from one base address (tile u at +1 KiB u, its scales at +64 B u) without
-    // per-lane checks.
-    const uint8_t* kd_lane = kd_base + (c_begin + (lane & 15)) * 64;
-    const uint8_t* ks_lane = ks_base + (c_begin + (lane & 15)) * 4;
 
-    // Key tile loaders: lane (g, c) of tile u takes position c's 32-element block g (an
-    // unreachable column reads position 0 and is masked when stored); each issues exactly
-    // kTileLoads loads.  load_gen serves any group: the row addresses are looked up
-    // (gather_b), then the loads issued (issue_b).  load_fast serves a full-row group
-    // inside the chunk.  Neither branches, and a wave picks one of them for all its
-    // reloads, so that the compiler sees one sequence of loads per loop and waits for
-    // each key tile just before its products.
+    // Key tile loader: lane (g, c) of tile u takes position c's 32-element block g (an
+    // unreachable column reads position 0 and is masked when stored); it issues exactly
+    // kTileLoads loads, after looking the row addresses up (gather_b).  It has no branch,
+    // so the compiler sees one sequence of loads on every path and waits for each key
+    // tile just before its products.  (A second loader for full-row groups, one base
+    // address and immediate tile offsets, made the full-range launch slower: the two loops
+    // it needs raise the register count from 120 to 164.)
     // (positions are looked up without branches: a column past the chunk looks up column
     // 0, so that all lookups are issued before the first wait)
     auto lookup_b = [&](int off0, int (&jj)[4]) {
@@ -213,19 +207,7 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
 #pragma unroll
         for (int u = 0; u < 4; u++) sk[u] = gload_u8<0>(sp[u]);
     };
-    auto load_fast = [&](int off0, u32x4_t (&kd)[4], int (&sk)[4]) {
-        const uint8_t* kp = kd_lane + (int64_t)off0 * 64;
-        const uint8_t* sp = ks_lane + (int64_t)off0 * 4;
-        kd[0] = gload_x4<0>(kp);
-        kd[1] = gload_x4<1024>(kp);
-        kd[2] = gload_x4<2048>(kp);
-        kd[3] = gload_x4<3072>(kp);
-        sk[0] = gload_u8<0>(sp);
-        sk[1] = gload_u8<64>(sp);
-        sk[2] = gload_u8<128>(sp);
-        sk[3] = gload_u8<192>(sp);
-    };
-    auto load_gen = [&](int off0, u32x4_t (&kd)[4], int (&sk)[4]) {
+    auto load = [&](int off0, u32x4_t (&kd)[4], int (&sk)[4]) {
         const uint8_t* kp[4];
         const uint8_t* sp[4];
         gather_b(off0, kp, sp);
@@ -274,7 +256,7 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
         }
     }
     // The wave scores groups 64 wave + 256 i, i < n, from two key buffers that alternate.
-    // Both first loads are issued even when the wave has fewer than two groups (load_gen
+    // Both first loads are issued even when the wave has fewer than two groups (load
     // then reads position 0 for their columns), so the loads in flight are the same on
     // every path.
     const int off0 = 64 * wave;
@@ -284,8 +266,8 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
     if (!POOL) {
         // pool rows look their positions up in the staged block ids: their first key
         // tiles follow the barrier below
-        load_gen(off0, ka, sa4);
-        load_gen(off0 + 256, kb, sb4);
+        load(off0, ka, sa4);
+        load(off0 + 256, kb, sb4);
     }
 
     // ---- pool block ids to LDS; the row's index q quantized into A operands
@@ -327,8 +309,8 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
         sa[t] = (int)s_qs[t][lane];
     }
     if (POOL) {
-        load_gen(off0, ka, sa4);
-        load_gen(off0 + 256, kb, sb4);
+        load(off0, ka, sa4);
+        load(off0 + 256, kb, sb4);
     }
 
     // score the 64 columns off0 .. off0 + 63 from their key tiles
@@ -370,7 +352,7 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
     // Groups i and i + 1 are in flight while group i is scored.  The loop runs while both
     // reloads are real groups; the last two or three groups follow, so that each wait
     // (and the load count it assumes) is fixed along every path.
-    auto run = [&](auto&& load) {
+    {
         int i = 0;
         for (; i + 3 < n; i += 2) {
             score_group(off0 + 256 * i, ka, sa4);
@@ -390,21 +372,17 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
         } else {
             if (rest == 1) score_group(off0 + 256 * i, ka, sa4);
         }
-    };
-    // a full-row wave whose every group lies inside the chunk reloads through load_fast
-    if (!POOL && n > 0 && off0 + 256 * (n - 1) + 64 <= ncc)
-        run(load_fast);
-    else
-        run(load_gen);
+    }
 }
 
 static int pick_chunk(int n, int64_t cols, int block)
 {
     // Each workgroup quantizes its row's index q once, so columns per workgroup should be
-    // many (1024..8192); shrink only while there are fewer than ~1024 workgroups.  A pool
+    // many (1024..8192); shrink only while there are fewer than 2048 workgroups (about two
+    // rounds of the 256 CUs at 4 workgroups each, which evens out the finish).  A pool
     // chunk spans at most kScoreMaxBlocks blocks (1024 columns suffice for block 1).
     int64_t chunk = 8192;
-    while (chunk > 1024 && (int64_t)n * ((cols + chunk - 1) / chunk) < 1024) chunk >>= 1;
+    while (chunk > 1024 && (int64_t)n * ((cols + chunk - 1) / chunk) < 2048) chunk >>= 1;
     while (block > 0 && chunk / block > kScoreMaxBlocks) chunk >>= 1;
     return (int)chunk;
 }
