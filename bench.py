@@ -277,6 +277,92 @@ def c1_scoring(steps: int, warmup: int, dev) -> dict:
             "frac": tflops / FP4_PEAK_TFLOPS}
 
 
+C4_SEQ, C4_SETS = 524288, 24
+
+
+def c4_decode(steps: int, warmup: int, dev, nreq: int = 32) -> dict:
+    """C4 long-context decode: nreq requests x 1 query at S = 524,288, m = 2 (262,144
+    reachable entries per row): full-range index scores, hierarchical top-k (32,768 blocks
+    of 8 -> a pool of 2,048), attention over the top-512 and the 128-row window.  One KV
+    cache; C4_SETS layers of index q, weights, q and window, so the attention timing
+    rotates over C4_SETS different index sets (about 557 MB of gathered rows for 32
+    requests, more than the 256 MiB MALL holds).  Each stage's launches for all sets are
+    captured in one HIP graph and replayed between two HIP events."""
+    seed = 4 * 1000 + nreq
+    c = C4_SEQ // M
+    g = synth.Geometry([C4_SEQ] * nreq, M)
+    rows = B.Rows(torch.arange(nreq, dtype=torch.int32, device=dev),
+                  torch.full((nreq,), C4_SEQ - 1, dtype=torch.int32, device=dev))
+    cache = B.Cache(M, torch.tensor(g.n_entries, dtype=torch.int32, device=dev),
+                    torch.tensor(g.row_start, dtype=torch.int64, device=dev))
+    kcodes = torch.empty((g.total_entries, DI // 2), dtype=torch.uint8, device=dev)
+    kscale = torch.empty((g.total_entries, DI // 32), dtype=torch.uint8, device=dev)
+    for c0 in range(0, g.total_entries, 1 << 20):
+        raw = synth.normal((min(1 << 20, g.total_entries - c0), DI), seed, "index_keys/%d" % c0, device=dev)
+        kcodes[c0:c0 + raw.shape[0]], kscale[c0:c0 + raw.shape[0]] = B.quant_mx(B.MXFP4, raw)
+        del raw
+    keys = B.IndexKeys(kcodes, kscale, DI)
+    kv = synth.normal_bf16((g.total_entries, D), seed, "kv", device=dev, chunk_rows=1 << 19)
+    win = synth.window_cache_geometry(g, W)
+    lay = []
+    for l in range(C4_SETS):
+        sraw = synth.normal((win["rows"], D), seed, "swa/%d" % l, device=dev)
+        scd, ssd = B.quant_mx(B.MXFP8_E4M3, sraw)
+        del sraw
+        lay.append(dict(qi=synth.normal_bf16((nreq, HI, DI), seed, "index_q/%d" % l, device=dev),
+                        w=synth.uniform((nreq, HI), seed, "index_w/%d" % l, device=dev),
+                        q=synth.normal_bf16((nreq, H, D), seed, "q/%d" % l, device=dev),
+                        window=B.Window(scd, ssd, win["row_start"].to(dev), win["pos_start"].to(dev), W),
+                        idx=torch.empty((nreq, K), dtype=torch.int32, device=dev),
+                        out=torch.empty((nreq, H, D), dtype=torch.bfloat16, device=dev)))
+    scores = torch.empty((nreq, c), dtype=torch.float32, device=dev)
+    pool_blocks = torch.empty((nreq, NB), dtype=torch.int32, device=dev)
+    pool_n = torch.empty((nreq,), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(1, B.workspace_size(B.OP_TOPK_HIER, nreq, c, K, NB)), dtype=torch.uint8, device=dev)
+    sm = synth.sm_scale(D)
+    calls = {
+        "score_full": lambda L: B.index_score(rows, cache, L["qi"], L["w"], keys, scores=scores),
+        "topk_hier": lambda L: B.topk_hier(rows, cache, scores, K, BLK, NB, workspace=ws,
+                                           out=(L["idx"], pool_blocks, pool_n)),
+        "attn": lambda L: B.sparse_swa_attn(rows, cache, L["q"], kv, L["idx"], L["window"], sm, out=L["out"]),
+    }
+    for L in lay:  # eager pass: every set's index list
+        for f in calls.values():
+            f(L)
+    torch.cuda.synchronize()
+    nbytes = {
+        "score_full": nreq * c * (DI // 2 + DI // 32) + nreq * HI * DI * 2 + nreq * HI * 4 + nreq * c * 4,
+        "topk_hier": 2 * nreq * c * 4 + nreq * (K + NB + 1) * 4,
+        "attn": nreq * ATTN_BYTES_PER_QUERY,
+    }
+    stages = {}
+    for name, f in calls.items():
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for L in lay:
+                f(L)
+        for _ in range(max(1, warmup)):
+            gr.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            gr.replay()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / (steps * len(lay))
+        stages[name] = {"us_per_launch": round(us, 2), "alg_bytes": nbytes[name],
+                        "alg_GBs": round(nbytes[name] / (us * 1e-6) / 1e9, 1)}
+    step_us = sum(v["us_per_launch"] for v in stages.values())
+    att = stages["attn"]
+    return {"measurement": "C4 long-context decode, %d requests x 1 query, S=524288, m=2 (262144 entries), "
+                           "top-512 + hierarchical pool of 2048 blocks of 8" % nreq,
+            "queries_per_s": nreq / (step_us * 1e-6), "us_per_layer": round(step_us, 2), "stages": stages,
+            "attn_roofline": {"bound": "hbm", "achieved": att["alg_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": att["alg_GBs"] / HBM_PEAK_GBS}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -286,6 +372,9 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=int(os.environ.get("OMP_NUM_THREADS", "0") or 16))
     ap.add_argument("--c1-scoring", action="store_true",
                     help="instead of the decode step: time the C1 prefill index scoring alone (FP4 MFMA rate)")
+    ap.add_argument("--c4-decode", type=int, default=0, metavar="NREQ",
+                    help="instead of the decode step: time the C4 long-context decode stages for NREQ "
+                         "requests (1 or 32)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the CSA2 path is built and timed on a single MI355X; "
@@ -297,6 +386,9 @@ def main():
     B.lib()
     if args.c1_scoring:
         print(json.dumps(c1_scoring(args.steps, args.warmup, dev)), flush=True)
+        return
+    if args.c4_decode:
+        print(json.dumps(c4_decode(args.steps, args.warmup, dev, args.c4_decode)), flush=True)
         return
     log("building %d input sets ..." % NSETS)
     sets = [InputSet(s, dev) for s in range(NSETS)]
