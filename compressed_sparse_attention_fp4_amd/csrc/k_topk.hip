@@ -413,7 +413,7 @@ __device__ __forceinline__ void find_bin(const int* hist, int need, int* s_w, in
 template <int KPT, int SRC>
 __global__ __launch_bounds__(kNT) void k_select(SelArgs a)
 {
-    __shared__ int s_h1[kBins1 + 1];    // first pass (+1 dummy bin for masked slots)
+    __shared__ int s_h1[kBins1];        // first pass
     __shared__ int s_h[3][kBins];       // later passes, rotating (cleared one pass ahead)
     __shared__ uint32_t s_red[3][kNW];
     __shared__ int s_w[2 * kNW];
@@ -456,7 +456,7 @@ __global__ __launch_bounds__(kNT) void k_select(SelArgs a)
         s_red[1][wave] = kmax;
         s_red[2][wave] = kmin;
     }
-    for (int i = tid; i <= kBins1; i += kNT) s_h1[i] = 0;
+    for (int i = tid; i < kBins1; i += kNT) s_h1[i] = 0;
     if (tid < kBins) s_h[1][tid] = 0;  // pass 1's histogram
     __syncthreads();
     int nv = 0;
@@ -492,15 +492,16 @@ __global__ __launch_bounds__(kNT) void k_select(SelArgs a)
                 const int shift = sb + 1 - nbits;
                 const uint32_t dmask = (1u << nbits) - 1u;
                 int* hist = pass == 0 ? s_h1 : s_h[pass % 3];
-                const int dummy = kBins1;
                 // clear the next pass's buffer: its last readers were two passes back and
                 // finished before the previous pass's barrier
                 if (pass > 0 && tid < kBins) s_h[(pass + 1) % 3][tid] = 0;
                 if (pass == 0) {
-                    // every valid key shares the prefix above sb
+                    // every valid key shares the prefix above sb.  Empty slots add nothing
+                    // (a shared dummy bin for them serialized thousands of same-address
+                    // atomics when a row fills only part of the slots).
 #pragma unroll
                     for (int i = 0; i < KPT; i++)
-                        atomicAdd(&hist[key[i] ? (int)((key[i] >> shift) & dmask) : dummy], 1);
+                        if (key[i]) atomicAdd(&hist[(key[i] >> shift) & dmask], 1);
                 } else {
 #pragma unroll
                     for (int i = 0; i < KPT; i++)
