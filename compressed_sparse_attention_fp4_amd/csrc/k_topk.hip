@@ -496,12 +496,15 @@ __global__ __launch_bounds__(kNT) void k_select(SelArgs a)
                 // finished before the previous pass's barrier
                 if (pass > 0 && tid < kBins) s_h[(pass + 1) % 3][tid] = 0;
                 if (pass == 0) {
-                    // every valid key shares the prefix above sb.  Empty slots add nothing
-                    // (a shared dummy bin for them serialized thousands of same-address
-                    // atomics when a row fills only part of the slots).
+                    // every valid key shares the prefix above sb.  An empty slot adds 0 to
+                    // a bin picked by its slot number: no branch, and no pile-up of
+                    // same-address atomics (one shared dummy bin serialized thousands of
+                    // them when a row fills only part of the slots).
 #pragma unroll
-                    for (int i = 0; i < KPT; i++)
-                        if (key[i]) atomicAdd(&hist[(key[i] >> shift) & dmask], 1);
+                    for (int i = 0; i < KPT; i++) {
+                        const int bin = key[i] ? (int)((key[i] >> shift) & dmask) : (int)((e0 + i) & dmask);
+                        atomicAdd(&hist[bin], key[i] ? 1 : 0);
+                    }
                 } else {
 #pragma unroll
                     for (int i = 0; i < KPT; i++)
@@ -671,6 +674,8 @@ static void launch_level(dim3 grid, int64_t cap, const SelArgs& a, hipStream_t s
 {
     if (cap <= 4096)  // (pool gathers take whole blocks: at least 8 per thread)
         hipLaunchKernelGGL((k_select<SRC == SRC_PGATHER ? 16 : 4, SRC>), grid, dim3(kNT), 0, stream, a);
+    else if (cap <= 8192)  // e.g. the 8,192 block maxima of a 65,536-entry row: every slot used
+        hipLaunchKernelGGL((k_select<8, SRC>), grid, dim3(kNT), 0, stream, a);
     else if (cap <= 16384 || SRC != SRC_FULL)
         hipLaunchKernelGGL((k_select<16, SRC>), grid, dim3(kNT), 0, stream, a);
     else
