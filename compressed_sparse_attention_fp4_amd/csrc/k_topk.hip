@@ -419,6 +419,9 @@ __global__ __launch_bounds__(kNT) void k_select(SelArgs a)
     __shared__ int s_w[2 * kNW];
     __shared__ int s_fw[2][kNW];   // find_bin partial sums (alternating between passes)
     __shared__ int s_res[2][3];
+    __shared__ uint32_t s_cand[64];  // the threshold bin's keys once it holds at most 64
+    __shared__ int s_ncand;
+    __shared__ uint32_t s_fin[2];
 
     const int nseg = a.nseg;
     int row, seg;
@@ -457,6 +460,7 @@ __global__ __launch_bounds__(kNT) void k_select(SelArgs a)
         s_red[2][wave] = kmin;
     }
     for (int i = tid; i < kBins1; i += kNT) s_h1[i] = 0;
+    if (tid == 0) s_ncand = 0;
     if (tid < kBins) s_h[1][tid] = 0;  // pass 1's histogram
     __syncthreads();
     int nv = 0;
@@ -535,6 +539,35 @@ __global__ __launch_bounds__(kNT) void k_select(SelArgs a)
                     ge_mode = false;
                     T = prefix;
                     need_eq = need;
+                    break;
+                }
+                if (cnt <= 64) {
+                    // Few keys left in the threshold bin: gather them and let one wave
+                    // find the need-th largest, T, directly (no further histogram pass).
+                    // Then the selection is every key above T plus the first need - (keys
+                    // above T in the bin) keys equal to T, in candidate order.
+#pragma unroll
+                    for (int i = 0; i < KPT; i++)
+                        if ((live >> i) & 1) s_cand[atomicAdd(&s_ncand, 1)] = key[i];
+                    __syncthreads();
+                    if (wave == 0) {
+                        const uint32_t v = lane < cnt ? s_cand[lane] : 0u;
+                        int gt = 0, ge = 0;
+                        for (int j = 0; j < cnt; j++) {
+                            const uint32_t c = s_cand[j];
+                            gt += c > v;
+                            ge += c >= v;
+                        }
+                        // exactly the lanes holding T satisfy gt < need <= ge; they agree
+                        if (lane < cnt && gt < need && need <= ge) {
+                            s_fin[0] = v;
+                            s_fin[1] = (uint32_t)(need - gt);
+                        }
+                    }
+                    __syncthreads();
+                    ge_mode = false;
+                    T = s_fin[0];
+                    need_eq = (int)s_fin[1];
                     break;
                 }
                 sb = shift - 1;
