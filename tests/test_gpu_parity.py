@@ -205,6 +205,39 @@ def test_topk_flat(orc, k, ties):
         assert np.array_equal(got[i], ref[i]), (i, R_list[i])
 
 
+@pytest.mark.parametrize("stride", [8192, 16384])
+def test_topk_small_threshold_bin(orc, stride):
+    """Rows whose threshold falls among a few repeated values: after the first pass the
+    threshold bin holds at most 64 keys (the direct ranking path) or just more (another
+    histogram pass), with ties broken by the lowest index."""
+    say("case: topk small threshold bin, stride=%d" % stride)
+    rng = np.random.default_rng(31 + stride)
+    k = 512
+    R = stride
+    rows_scores = []
+    for above, groups in [(500, [(50.0, 30)]),             # 12 of 30 copies of the threshold value
+                          (505, [(50.0, 20), (50.5, 20)]),  # 7 of the 20 copies of 50.5
+                          (448, [(50.0, 64)]),              # exactly 64 keys in the bin
+                          (440, [(50.0, 65)]),              # one more than the direct path takes
+                          (511, [(50.0, 1), (49.0, 40)])]:  # the threshold is a single key
+        v = rng.uniform(0.0, 1.0, R).astype(np.float32)
+        pos = rng.permutation(R)
+        v[pos[:above]] = (100.0 + rng.permutation(above)).astype(np.float32)
+        at = above
+        for val, cnt in groups:
+            v[pos[at:at + cnt]] = np.float32(val)
+            at += cnt
+        rows_scores.append(v)
+    n = len(rows_scores)
+    scores = np.stack(rows_scores)
+    rows = dict(req_of_row=np.arange(n), pos_of_row=np.full(n, R - 1))
+    cache = dict(ratio_m=1, n_entries=np.full(n, R), row_start=np.arange(n, dtype=np.int64) * R)
+    got = B.topk(dev_rows(rows), dev_cache(cache), torch.from_numpy(scores).to(DEV), k).cpu().numpy()
+    ref = orc.topk(rows, cache, scores, k)
+    for i in range(n):
+        assert np.array_equal(got[i], ref[i]), i
+
+
 def test_topk_pool(orc):
     say("case: topk over a pool")
     rng = np.random.default_rng(7)
