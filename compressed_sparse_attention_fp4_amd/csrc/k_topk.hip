@@ -546,15 +546,22 @@ __global__ __launch_bounds__(kNT) void k_select(SelArgs a)
                     // find the need-th largest, T, directly (no further histogram pass).
                     // Then the selection is every key above T plus the first need - (keys
                     // above T in the bin) keys equal to T, in candidate order.
+                    // (one LDS atomic per thread that holds any of them)
+                    const int nlive = __builtin_popcountll(live);
+                    if (nlive) {
+                        int at = atomicAdd(&s_ncand, nlive);
 #pragma unroll
-                    for (int i = 0; i < KPT; i++)
-                        if ((live >> i) & 1) s_cand[atomicAdd(&s_ncand, 1)] = key[i];
+                        for (int i = 0; i < KPT; i++)
+                            if ((live >> i) & 1) s_cand[at++] = key[i];
+                    }
                     __syncthreads();
                     if (wave == 0) {
+                        // lane j holds candidate j; each lane counts the candidates above
+                        // and at or above its own through register reads of every lane
                         const uint32_t v = lane < cnt ? s_cand[lane] : 0u;
                         int gt = 0, ge = 0;
                         for (int j = 0; j < cnt; j++) {
-                            const uint32_t c = s_cand[j];
+                            const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, j);
                             gt += c > v;
                             ge += c >= v;
                         }
