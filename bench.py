@@ -363,6 +363,123 @@ def c4_decode(steps: int, warmup: int, dev, nreq: int = 32) -> dict:
                               "frac": att["alg_GBs"] / HBM_PEAK_GBS}}
 
 
+def _time_graph(fn, steps: int, warmup: int, per: int) -> float:
+    """Microseconds per call of fn's launches: captured once in a HIP graph, replayed
+    back to back between two HIP events (per = calls inside fn)."""
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        fn()
+    for _ in range(max(1, warmup)):
+        gr.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        gr.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / (steps * per)
+
+
+def c2_replay(steps: int, warmup: int, dev) -> dict:
+    """C2 decoder bounded replay: 8 requests of S = 8192 (m = 1) with extends
+    8192, 8192, 4096, 4096, 2048, 512, 128, 64.  A Full layer scores every extend row
+    (27,332 rows) and selects top-512 plus pools; the tail layout keeps each request's last
+    min(128, E) rows (960); a Reindex layer rescored over the source pools (through the
+    tail -> extend row map) with its own top-512 and attention; a Reuse layer attending to
+    the source layer's top-512 through the same map.  Each stage timed by graph replay."""
+    cfg = synth.config(2)
+    g = cfg.geom
+    E = synth.C2_EXTENDS
+    ext_req = torch.cat([torch.full((e,), r, dtype=torch.int32) for r, e in enumerate(E)])
+    ext_pos = torch.cat([torch.arange(sq - e, sq, dtype=torch.int32) for sq, e in zip(g.seq_len, E)])
+    n_ext = ext_req.numel()
+    cd = B.Cache(1, torch.tensor(g.n_entries, dtype=torch.int32, device=dev),
+                 torch.tensor(g.row_start, dtype=torch.int64, device=dev))
+    kd, ksd = B.quant_mx(B.MXFP4, synth.normal((g.total_entries, cfg.index_dim), cfg.seed, "index_keys", device=dev))
+    keys = B.IndexKeys(kd, ksd, cfg.index_dim)
+    c = g.n_entries[0]
+    re_d = B.Rows(ext_req.to(dev), ext_pos.to(dev))
+    qi_s = synth.normal_bf16((n_ext, cfg.index_heads, cfg.index_dim), cfg.seed, "index_q/src", device=dev)
+    w_s = synth.uniform((n_ext, cfg.index_heads), cfg.seed, "index_w/src", device=dev)
+    sc_s = torch.empty((n_ext, c), dtype=torch.float32, device=dev)
+    ws_h = torch.empty(max(1, B.workspace_size(B.OP_TOPK_HIER, n_ext, c, cfg.topk, cfg.max_blocks)),
+                       dtype=torch.uint8, device=dev)
+    idx_s = torch.empty((n_ext, cfg.topk), dtype=torch.int32, device=dev)
+    pb = torch.empty((n_ext, cfg.max_blocks), dtype=torch.int32, device=dev)
+    pn = torch.empty((n_ext,), dtype=torch.int32, device=dev)
+    ext_len = torch.tensor(E, dtype=torch.int32, device=dev)
+    seq_len = torch.tensor(g.seq_len, dtype=torch.int32, device=dev)
+    t = B.replay_tail_layout(ext_len, seq_len, 128)
+    torch.cuda.synchronize()
+    nt = int(t["tail_row_start"][-1])
+    rt_d = B.Rows(t["req_of_row"][:nt], t["abs_pos"][:nt], t["win_lo"][:nt])
+    src_map = t["src_row"][:nt].contiguous()
+    pool_d = B.Pool(pb, pn, cfg.block, src_map)
+    qi_t = synth.normal_bf16((nt, cfg.index_heads, cfg.index_dim), cfg.seed, "index_q/reindex", device=dev)
+    w_t = synth.uniform((nt, cfg.index_heads), cfg.seed, "index_w/reindex", device=dev)
+    sc_t = torch.empty((nt, cfg.max_blocks * cfg.block), dtype=torch.float32, device=dev)
+    idx_t = torch.empty((nt, cfg.topk), dtype=torch.int32, device=dev)
+    ws_t = torch.empty(max(1, B.workspace_size(B.OP_TOPK, nt, cfg.max_blocks * cfg.block, cfg.topk)),
+                       dtype=torch.uint8, device=dev)
+    kv = synth.normal_bf16((g.total_entries, cfg.dim), cfg.seed, "kv", device=dev)
+    win = synth.window_cache_geometry(g, 128)
+    lay = {}
+    for layer in ("reindex", "reuse"):
+        scd, ssd = B.quant_mx(B.MXFP8_E4M3, synth.normal((win["rows"], cfg.dim), cfg.seed, "swa/" + layer, device=dev))
+        lay[layer] = dict(q=synth.normal_bf16((nt, cfg.heads, cfg.dim), cfg.seed, "q/" + layer, device=dev),
+                          window=B.Window(scd, ssd, win["row_start"].to(dev), win["pos_start"].to(dev), 128),
+                          out=torch.empty((nt, cfg.heads, cfg.dim), dtype=torch.bfloat16, device=dev))
+    sm = synth.sm_scale(cfg.dim)
+    calls = {
+        "score_src": lambda: B.index_score(re_d, cd, qi_s, w_s, keys, scores=sc_s),
+        "topk_hier_src": lambda: B.topk_hier(re_d, cd, sc_s, cfg.topk, cfg.block, cfg.max_blocks, workspace=ws_h,
+                                             out=(idx_s, pb, pn)),
+        "tail_layout": lambda: B.replay_tail_layout(ext_len, seq_len, 128),
+        "score_reindex": lambda: B.index_score(rt_d, cd, qi_t, w_t, keys, pool=pool_d, scores=sc_t),
+        "topk_reindex": lambda: B.topk(rt_d, cd, sc_t, cfg.topk, pool=pool_d, out=idx_t, workspace=ws_t),
+        "attn_reindex": lambda: B.sparse_swa_attn(rt_d, cd, lay["reindex"]["q"], kv, idx_t, lay["reindex"]["window"],
+                                                  sm, out=lay["reindex"]["out"]),
+        "attn_reuse": lambda: B.sparse_swa_attn(rt_d, cd, lay["reuse"]["q"], kv, idx_s, lay["reuse"]["window"], sm,
+                                                sel_row_map=src_map, out=lay["reuse"]["out"]),
+    }
+    for f in calls.values():  # eager pass in flow order
+        f()
+    torch.cuda.synchronize()
+    reach = int((ext_pos.to(torch.int64) + 1).clamp(max=c).sum())
+    nbytes = {
+        "score_src": reach * (cfg.index_dim // 2 + cfg.index_dim // 32 + 4) + n_ext * cfg.index_heads * (cfg.index_dim * 2 + 4),
+        "topk_hier_src": 2 * reach * 4 + n_ext * (cfg.topk + cfg.max_blocks + 1) * 4,
+        "score_reindex": int(pn[src_map.long()].sum()) * cfg.block * (cfg.index_dim // 2 + cfg.index_dim // 32 + 4)
+        + nt * cfg.index_heads * (cfg.index_dim * 2 + 4),
+        "attn_reindex": nt * ATTN_BYTES_PER_QUERY,
+        "attn_reuse": nt * ATTN_BYTES_PER_QUERY,
+    }
+    # scoring: the keys of a request are shared by all its rows and stay in cache, so the
+    # FP4 MFMA rate (2 x heads x dim flop per scored pair) is the bound, not bytes
+    flop = {"score_src": 2.0 * cfg.index_heads * cfg.index_dim * reach,
+            "score_reindex": 2.0 * cfg.index_heads * cfg.index_dim * int(pn[src_map.long()].sum()) * cfg.block}
+    stages = {}
+    for name, f in calls.items():
+        us = _time_graph(f, steps, warmup, 1)
+        st = {"us_per_launch": round(us, 2)}
+        if name in nbytes:
+            st["alg_bytes"] = nbytes[name]
+            st["alg_GBs"] = round(nbytes[name] / (us * 1e-6) / 1e9, 1)
+        if name in flop:
+            st["TFLOP/s"] = round(flop[name] / (us * 1e-6) / 1e12, 1)
+            st["fp4_frac"] = round(flop[name] / (us * 1e-6) / 1e12 / FP4_PEAK_TFLOPS, 4)
+        stages[name] = st
+    total = sum(v["us_per_launch"] for v in stages.values())
+    att = stages["attn_reindex"]
+    return {"measurement": "C2 decoder bounded replay: Full layer over 27,332 extend rows, 960 tail rows through "
+                           "Reindex and Reuse (8 requests, S=8192, m=1, top-512, pools of 2048 blocks of 8)",
+            "us_per_flow": round(total, 2), "stages": stages,
+            "attn_roofline": {"bound": "hbm", "achieved": att["alg_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": att["alg_GBs"] / HBM_PEAK_GBS, "note": "nominal 724,992 B per tail row"}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -375,6 +492,8 @@ def main():
     ap.add_argument("--c4-decode", type=int, default=0, metavar="NREQ",
                     help="instead of the decode step: time the C4 long-context decode stages for NREQ "
                          "requests (1 or 32)")
+    ap.add_argument("--c2-replay", action="store_true",
+                    help="instead of the decode step: time the C2 bounded-replay flow stage by stage")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the CSA2 path is built and timed on a single MI355X; "
@@ -386,6 +505,9 @@ def main():
     B.lib()
     if args.c1_scoring:
         print(json.dumps(c1_scoring(args.steps, args.warmup, dev)), flush=True)
+        return
+    if args.c2_replay:
+        print(json.dumps(c2_replay(args.steps, args.warmup, dev)), flush=True)
         return
     if args.c4_decode:
         print(json.dumps(c4_decode(args.steps, args.warmup, dev, args.c4_decode)), flush=True)
