@@ -338,7 +338,8 @@ __device__ __forceinline__ uint32_t wave_min(uint32_t x)
         (int)wave_incl(x, 0xFFFFFFFFu, [](uint32_t p, uint32_t q) { return p < q ? p : q; }), 63);
 }
 
-// Exclusive block scan of two counters at once (one barrier pair).
+// Exclusive block scan of two counters at once (one barrier pair); NW waves.
+template <int NW>
 __device__ __forceinline__ void block_scan2(int a, int b, int* s_w, int lane, int wave, int* ea, int* eb, int* ta,
                                             int* tb)
 {
@@ -351,7 +352,7 @@ __device__ __forceinline__ void block_scan2(int a, int b, int* s_w, int lane, in
     __syncthreads();
     int pa = 0, pb = 0, sa = 0, sb = 0;
 #pragma unroll
-    for (int w = 0; w < kNW; w++) {
+    for (int w = 0; w < NW; w++) {
         const int va = s_w[2 * w], vb = s_w[2 * w + 1];
         pa += (w < wave) ? va : 0;
         pb += (w < wave) ? vb : 0;
@@ -370,14 +371,14 @@ constexpr int kBins = 256;    // later digits: 8 bits
 
 // Threshold bin of a histogram of NB bins, scanned from the top: the bin b where the
 // count of keys in bins above b is < need <= that count plus hist[b].  All threads
-// cooperate: thread t takes NB/kNT adjacent bins from the top (conflict-free reads),
+// cooperate: thread t of NT takes NB/NT adjacent bins from the top (conflict-free reads),
 // one block scan orders the partial sums, and the thread holding the crossing publishes
 // (bin, count above, bin count) through LDS.
-template <int NB>
+template <int NB, int NT>
 __device__ __forceinline__ void find_bin(const int* hist, int need, int* s_w, int* s_res, int tid, int lane,
                                          int wave, int* bin, int* above, int* cnt)
 {
-    constexpr int PER = NB / kNT > 0 ? NB / kNT : 1;
+    constexpr int PER = NB / NT > 0 ? NB / NT : 1;
     int c[PER], sum = 0;
     const bool act = tid * PER < NB;
 #pragma unroll
@@ -390,7 +391,7 @@ __device__ __forceinline__ void find_bin(const int* hist, int need, int* s_w, in
     __syncthreads();
     int before = 0;
 #pragma unroll
-    for (int w = 0; w < kNW; w++) before += (w < wave) ? s_w[w] : 0;
+    for (int w = 0; w < NT / 64; w++) before += (w < wave) ? s_w[w] : 0;
     int acc = before + incl - sum;
     if (act && acc < need && need <= acc + sum) {
 #pragma unroll
@@ -410,14 +411,15 @@ __device__ __forceinline__ void find_bin(const int* hist, int need, int* s_w, in
     *cnt = s_res[2];
 }
 
-template <int KPT, int SRC>
-__global__ __launch_bounds__(kNT) void k_select(SelArgs a)
+template <int KPT, int SRC, int NT = kNT>
+__global__ __launch_bounds__(NT) void k_select(SelArgs a)
 {
     __shared__ int s_h1[kBins1];        // first pass
     __shared__ int s_h[3][kBins];       // later passes, rotating (cleared one pass ahead)
-    __shared__ uint32_t s_red[3][kNW];
-    __shared__ int s_w[2 * kNW];
-    __shared__ int s_fw[2][kNW];   // find_bin partial sums (alternating between passes)
+    constexpr int NW = NT / 64;
+    __shared__ uint32_t s_red[3][NW];
+    __shared__ int s_w[2 * NW];
+    __shared__ int s_fw[2][NW];    // find_bin partial sums (alternating between passes)
     __shared__ int s_res[2][3];
     __shared__ uint32_t s_cand[64];  // the threshold bin's keys once it holds at most 64
     __shared__ int s_ncand;
@@ -459,7 +461,7 @@ __global__ __launch_bounds__(kNT) void k_select(SelArgs a)
         s_red[1][wave] = kmax;
         s_red[2][wave] = kmin;
     }
-    for (int i = tid; i < kBins1; i += kNT) s_h1[i] = 0;
+    for (int i = tid; i < kBins1; i += NT) s_h1[i] = 0;
     if (tid == 0) s_ncand = 0;
     if (tid < kBins) s_h[1][tid] = 0;  // pass 1's histogram
     __syncthreads();
@@ -467,7 +469,7 @@ __global__ __launch_bounds__(kNT) void k_select(SelArgs a)
     kmax = 0;
     kmin = 0xFFFFFFFFu;
 #pragma unroll
-    for (int w = 0; w < kNW; w++) {
+    for (int w = 0; w < NW; w++) {
         nv += (int)s_red[0][w];
         kmax = max(kmax, s_red[1][w]);
         kmin = min(kmin, s_red[2][w]);
@@ -517,10 +519,10 @@ __global__ __launch_bounds__(kNT) void k_select(SelArgs a)
                 __syncthreads();
                 int bsel, above, cnt;
                 if (pass == 0)
-                    find_bin<kBins1>(hist, need, s_fw[pass & 1], s_res[pass & 1], tid, lane, wave, &bsel, &above,
+                    find_bin<kBins1, NT>(hist, need, s_fw[pass & 1], s_res[pass & 1], tid, lane, wave, &bsel, &above,
                                      &cnt);
                 else
-                    find_bin<kBins>(hist, need, s_fw[pass & 1], s_res[pass & 1], tid, lane, wave, &bsel, &above,
+                    find_bin<kBins, NT>(hist, need, s_fw[pass & 1], s_res[pass & 1], tid, lane, wave, &bsel, &above,
                                     &cnt);
                 prefix |= (uint32_t)bsel << shift;
                 need -= above;
@@ -598,7 +600,7 @@ __global__ __launch_bounds__(kNT) void k_select(SelArgs a)
     // the equal keys before it, capped at need_eq; of its own equal keys it takes the
     // first need_eq - (equal keys before it).
     int gt_before, eq_before, nsel_gt, eq_tot;
-    block_scan2(gt, eq, s_w, lane, wave, &gt_before, &eq_before, &nsel_gt, &eq_tot);
+    block_scan2<NW>(gt, eq, s_w, lane, wave, &gt_before, &eq_before, &nsel_gt, &eq_tot);
     int take = 0;
     if (!ge_mode) {
         take = need_eq - eq_before;
@@ -634,9 +636,9 @@ __global__ __launch_bounds__(kNT) void k_select(SelArgs a)
     }
     // ---- padding (and the newest block of the hierarchical pool)
     if (a.out_mode == OUT_LIST) {
-        for (int i = nsel + tid; i < k; i += kNT) a.out_list[row_out * k + i] = make_uint2(0u, 0xFFFFFFFFu);
+        for (int i = nsel + tid; i < k; i += NT) a.out_list[row_out * k + i] = make_uint2(0u, 0xFFFFFFFFu);
     } else if (a.out_mode == OUT_IDX) {
-        for (int i = nsel + tid; i < a.out_stride; i += kNT) a.out_idx[(int64_t)row * a.out_stride + i] = -1;
+        for (int i = nsel + tid; i < a.out_stride; i += NT) a.out_idx[(int64_t)row * a.out_stride + i] = -1;
     } else {
         const int64_t nblk = (ncol + a.block - 1) >> a.block_shift;
         int tot = nsel;
@@ -644,7 +646,7 @@ __global__ __launch_bounds__(kNT) void k_select(SelArgs a)
             if (tid == 0) a.out_idx[(int64_t)row * a.out_stride + nsel] = (int32_t)(nblk - 1);
             tot = nsel + 1;
         }
-        for (int i = tot + tid; i < a.out_stride; i += kNT) a.out_idx[(int64_t)row * a.out_stride + i] = -1;
+        for (int i = tot + tid; i < a.out_stride; i += NT) a.out_idx[(int64_t)row * a.out_stride + i] = -1;
         if (tid == 0) a.out_nblocks[row] = tot;
     }
 }
@@ -709,9 +711,25 @@ static size_t plan_workspace(const Plan& p, int n, int k)
     return ((a + 255) & ~(size_t)255) + b;
 }
 
+// Launches over many rows (a prefill, a replay over thousands of extend rows) select
+// with 256-thread workgroups: a workgroup's passes are a chain of barriers whose cost
+// grows with its wave count, and four times as many of them fit on a CU, so rows per
+// second rise; few rows (a decode batch) keep 1024 threads, which finish one row
+// sooner.  The selection is exact either way.
+constexpr int kManyRows = 1024;
+
 template <int SRC>
-static void launch_level(dim3 grid, int64_t cap, const SelArgs& a, hipStream_t stream)
+static void launch_level(dim3 grid, int64_t cap, int nrows, const SelArgs& a, hipStream_t stream)
 {
+    if (nrows >= kManyRows && cap <= 8192) {
+        if (cap <= 2048)
+            hipLaunchKernelGGL((k_select<8, SRC, 256>), grid, dim3(256), 0, stream, a);
+        else if (cap <= 4096)
+            hipLaunchKernelGGL((k_select<16, SRC, 256>), grid, dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL((k_select<32, SRC, 256>), grid, dim3(256), 0, stream, a);
+        return;
+    }
     if (cap <= 4096)  // (pool gathers take whole blocks: at least 8 per thread)
         hipLaunchKernelGGL((k_select<SRC == SRC_PGATHER ? 16 : 4, SRC>), grid, dim3(kNT), 0, stream, a);
     else if (cap <= 8192)  // e.g. the 8,192 block maxima of a 65,536-entry row: every slot used
@@ -766,17 +784,17 @@ static hipError_t run_plan(const SelSource& src, int mode, int block, int k, int
         a.bstride = bstride;
         const dim3 grid((unsigned)((int64_t)n * p.nseg[l]));
         if (l > 0)
-            launch_level<SRC_LIST>(grid, p.cap[l], a, stream);
+            launch_level<SRC_LIST>(grid, p.cap[l], n, a, stream);
         else if (mode == SRC_FULL)
-            launch_level<SRC_FULL>(grid, p.cap[l], a, stream);
+            launch_level<SRC_FULL>(grid, p.cap[l], n, a, stream);
         else if (mode == SRC_POOL)
-            launch_level<SRC_POOL>(grid, p.cap[l], a, stream);
+            launch_level<SRC_POOL>(grid, p.cap[l], n, a, stream);
         else if (mode == SRC_BMAX)
-            launch_level<SRC_BMAX>(grid, p.cap[l], a, stream);
+            launch_level<SRC_BMAX>(grid, p.cap[l], n, a, stream);
         else if (mode == SRC_PGATHER)
-            launch_level<SRC_PGATHER>(grid, p.cap[l], a, stream);
+            launch_level<SRC_PGATHER>(grid, p.cap[l], n, a, stream);
         else
-            launch_level<SRC_BLOCK>(grid, p.cap[l], a, stream);
+            launch_level<SRC_BLOCK>(grid, p.cap[l], n, a, stream);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         prev = a.out_list;

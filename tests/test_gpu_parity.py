@@ -205,6 +205,28 @@ def test_topk_flat(orc, k, ties):
         assert np.array_equal(got[i], ref[i]), (i, R_list[i])
 
 
+@pytest.mark.parametrize("stride", [2048, 4096, 8192])
+@pytest.mark.parametrize("ties", [None, 4.0])
+def test_topk_many_rows(orc, stride, ties):
+    """At least 1024 rows select with 256-thread workgroups (8, 16 or 32 candidates per
+    thread by the row length): ragged reaches around k and the slice sizes, with and
+    without ties, checked row by row against the oracle; the same rows in a batch of
+    16 (1024-thread workgroups) give the same index sets."""
+    say("case: topk many rows stride=%d ties=%s" % (stride, ties))
+    base = [0, 1, 100, 511, 512, 513, 1000, 2047, 2048, 2049, 4095, 4096, 4097, 6000, 8191, 8192]
+    R_list = [min(base[i % len(base)], stride) for i in range(1024)]
+    rows, cache, scores = _topk_inputs(700 + stride, R_list, stride, ties)
+    sd = torch.from_numpy(scores).to(DEV)
+    got = B.topk(dev_rows(rows), dev_cache(cache), sd, 512).cpu().numpy()
+    ref = orc.topk(rows, cache, scores, 512)
+    for i in range(len(R_list)):
+        assert np.array_equal(got[i], ref[i]), (i, R_list[i])
+    few = {k: v[:16] for k, v in rows.items()}
+    fc = dict(ratio_m=1, n_entries=cache["n_entries"][:16], row_start=cache["row_start"][:16])
+    got16 = B.topk(dev_rows(few), dev_cache(fc), sd[:16].contiguous(), 512).cpu().numpy()
+    assert np.array_equal(got16, got[:16])
+
+
 @pytest.mark.parametrize("stride", [8192, 16384])
 def test_topk_small_threshold_bin(orc, stride):
     """Rows whose threshold falls among a few repeated values: after the first pass the
