@@ -565,6 +565,18 @@ def main():
     log(json.dumps(stages, indent=1))
     log("graph step %.3f ms; sum of stage launches %.3f ms" % (elapsed * 1e3 / args.steps, sum(per_step_ms.values())))
 
+    # spread of single steps: each replay alone between two HIP events (outside the timed
+    # region above, which is the reported value)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        graphs[i % NSETS].replay()
+        b.record()
+    torch.cuda.synchronize()
+    single = np.array([a.elapsed_time(b) for a, b in ev])
+    spread = {"p10": round(float(np.percentile(single, 10)), 4), "p50": round(float(np.percentile(single, 50)), 4),
+              "p90": round(float(np.percentile(single, 90)), 4)}
+
     queries = NREQ * LAYERS * args.steps
     value = queries / elapsed
     # one plain copy of known size, for scaling rocprof FETCH/WRITE counters
@@ -586,6 +598,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": elapsed * 1e3 / args.steps,
+        "step_ms_spread": spread,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
