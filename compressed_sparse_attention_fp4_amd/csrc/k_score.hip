@@ -120,7 +120,6 @@ __device__ __forceinline__ float gload_f32(const void* p)
 {
     return *reinterpret_cast<const float*>(static_cast<const uint8_t*>(p) + OFF);
 }
-constexpr int kTileLoads = 8;  // vector-memory instructions per group of 4 key tiles
 
 // Workgroup = 4 waves on one query row and a chunk of columns.  The row's bf16 index q
 // is quantized once per workgroup into LDS (one 32-element block per lane, which is
@@ -173,13 +172,12 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
 
     // Key tile loader: lane (g, c) of tile u takes position c's 32-element block g (an
     // unreachable column reads position 0 and is masked when stored); it issues exactly
-    // kTileLoads loads, after looking the row addresses up (gather_b).  It has no branch,
-    // so the compiler sees one sequence of loads on every path and waits for each key
+    // eight loads (four 16-byte code blocks, four scale bytes), after looking the row
+    // addresses up (gather_b).  It has no branch (a column past the chunk looks up column
+    // 0), so the compiler sees one sequence of loads on every path and waits for each key
     // tile just before its products.  (A second loader for full-row groups, one base
     // address and immediate tile offsets, made the full-range launch slower: the two loops
     // it needs raise the register count from 120 to 164.)
-    // (positions are looked up without branches: a column past the chunk looks up column
-    // 0, so that all lookups are issued before the first wait)
     auto lookup_b = [&](int off0, int (&jj)[4]) {
 #pragma unroll
         for (int u = 0; u < 4; u++) {
@@ -213,10 +211,9 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
         gather_b(off0, kp, sp);
         issue_b(kp, sp, kd, sk);
     };
-    // ---- loads, all issued before the first wait: the row's index q (one 32-element
-    // block per thread and pass), the head weights and the pool block ids (assembly
-    // loads), then (full rows) the wave's first two groups of key tiles, so that HBM is
-    // busy from the start.
+    // ---- loads, all issued before their first use: the row's index q (one 32-element
+    // block per thread and pass), the head weights and the pool block ids, then (full
+    // rows) the wave's first two groups of key tiles, so that HBM is busy from the start.
     constexpr int QP = (NHT * 64 + 255) / 256;
     u32x4_t qraw[QP][4];
 #pragma unroll
@@ -257,8 +254,8 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
     }
     // The wave scores groups 64 wave + 256 i, i < n, from two key buffers that alternate.
     // Both first loads are issued even when the wave has fewer than two groups (load
-    // then reads position 0 for their columns), so the loads in flight are the same on
-    // every path.
+    // then reads position 0 for their columns), so the same loads are in flight on every
+    // path and the compiler's waits need not depend on the group count.
     const int off0 = 64 * wave;
     const int n = off0 < ncc ? (ncc - off0 + 255) >> 8 : 0;
     u32x4_t ka[4], kb[4];
