@@ -9,15 +9,15 @@
 // position (the workload definition; the pages are silent).
 //
 // Method.  Candidates are mapped to order-preserving 32-bit keys (0 = no candidate).  One
-// workgroup of 1024 threads holds up to 1024*KPT candidates in registers, striped
-// (candidate e = i*1024 + t lives in register i of thread t, so loads are coalesced and
-// candidate order is (i, wave, lane)).  An MSB-first radix select over 8-bit digits finds
-// the threshold key T: the first digit starts at the highest bit where the largest and
-// smallest keys differ, and a pass whose threshold bin is taken whole ends the search
-// early.  Each pass costs one barrier: histograms rotate through three LDS buffers (the
-// next one is cleared while the current one fills) and every wave scans the finished
-// histogram itself.  The selection is every key above T plus the lowest-indexed keys
-// equal to T; ballots and one scan over per-(register, wave) counts give each selected
+// workgroup (1024 threads; 256 for launches over many rows) holds up to threads*KPT
+// candidates in registers, blocked: thread t owns candidates [t*KPT, (t+1)*KPT), so thread
+// order is candidate order.  An MSB-first radix select finds the threshold key T: the
+// first digit (11 bits) starts at the highest bit where the largest and smallest keys
+// differ, later digits take 8 bits of the keys still in the threshold bin; a pass whose
+// threshold bin is taken whole ends the search, and a threshold bin of at most 64 keys is
+// ranked directly by one wave.  Histograms are LDS atomics; the threshold bin is found by
+// a cooperative scan from the top.  The selection is every key above T plus the
+// lowest-indexed keys equal to T; one block scan of per-thread counts gives each selected
 // candidate its output slot in ascending candidate order.  Rows longer than one
 // workgroup are cut into segments whose top-k lists are merged by another pass (the
 // order is total, so the merge is exact).
