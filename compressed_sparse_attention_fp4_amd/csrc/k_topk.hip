@@ -616,8 +616,29 @@ __global__ __launch_bounds__(NT) void k_select(SelArgs a)
     int off = gt_before + (ge_mode ? 0 : (eq_before < need_eq ? eq_before : need_eq));
     const int nsel = nsel_gt + (ge_mode ? 0 : (eq_tot < need_eq ? eq_tot : need_eq));
     const int64_t row_out = (int64_t)row * nseg + seg;
+    // Index outputs whose positions follow from the slot alone (score rows, block maxima,
+    // pools with their block ids in registers) loop over the thread's selected slots only:
+    // a thread holds few of them, and the general loop below branches on every slot.
+    const bool slots_only = a.out_mode != OUT_LIST && SRC != SRC_LIST &&
+                            (!(SRC == SRC_POOL || SRC == SRC_PGATHER) || bid_ok);
+    if (slots_only) {
+        int32_t* orow = a.out_idx + (int64_t)row * a.out_stride;
+        for (uint64_t m = selbits; m; m &= m - 1) {
+            const int i = __builtin_ctzll(m);
+            int32_t pos;
+            if (SRC == SRC_POOL || SRC == SRC_PGATHER) {
+                int32_t blk = bid[0];
 #pragma unroll
-    for (int i = 0; i < KPT; i++) {
+                for (int b8 = 1; b8 < bid_slots(KPT); b8++) blk = ((i >> 3) == b8) ? bid[b8] : blk;
+                pos = (blk << 3) + (i & 7);
+            } else {
+                pos = (int32_t)(base + e0 + i);
+            }
+            orow[off++] = pos;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < KPT && !slots_only; i++) {
         if ((selbits >> i) & 1) {
             const int64_t e = e0 + i;
             int32_t pos;
