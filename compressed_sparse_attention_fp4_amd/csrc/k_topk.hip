@@ -338,7 +338,8 @@ __device__ __forceinline__ uint32_t wave_min(uint32_t x)
         (int)wave_incl(x, 0xFFFFFFFFu, [](uint32_t p, uint32_t q) { return p < q ? p : q; }), 63);
 }
 
-// Exclusive block scan of two counters at once (one barrier pair); NW waves.
+// Exclusive block scan of two counters at once (one barrier); NW waves.  s_w is not
+// protected afterwards: the caller must not write it again (k_select scans once).
 template <int NW>
 __device__ __forceinline__ void block_scan2(int a, int b, int* s_w, int lane, int wave, int* ea, int* eb, int* ta,
                                             int* tb)
@@ -359,7 +360,6 @@ __device__ __forceinline__ void block_scan2(int a, int b, int* s_w, int lane, in
         sa += va;
         sb += vb;
     }
-    __syncthreads();
     *ea = pa + ia - a;
     *eb = pb + ib - b;
     *ta = sa;
