@@ -128,10 +128,12 @@ def _is_vmem(op: str) -> bool:
 def _load_dst(insn: Insn) -> set[tuple[str, int]]:
     """Registers a vector memory instruction writes when its data returns."""
     op = insn.op
-    if "_lds" in op or "store" in op:
+    mods = set(insn.operands.replace(",", " ").split())
+    if "_lds" in op or "store" in op or "lds" in mods:  # LDS-DMA forms write LDS, not VGPRs
         return set()
     first = insn.operands.split(",", 1)[0]
-    if "atomic" in op and "glc" not in insn.operands.split():  # no return value
+    # an atomic returns the old value only with glc (gfx9) or sc0 (gfx940 and later)
+    if "atomic" in op and not ({"glc", "sc0"} & mods):
         return set()
     return regs_of(first)
 

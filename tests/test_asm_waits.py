@@ -105,6 +105,22 @@ def test_checker_branch_merge_and_lds_dma():
     assert len(hits) == 1 and "v2, v1" in hits[0]
 
 
+def test_checker_atomics_and_lds_modifier():
+    # gfx940-style returning atomic (sc0) writes its first operand; one without sc0 or glc
+    # does not; a buffer load with the lds modifier writes LDS only
+    asm = _kernel("""
+\tglobal_atomic_add v5, v[60:61], v6, off sc0
+\tv_mov_b32_e32 v1, v5
+\tglobal_atomic_add v[60:61], v7, off
+\tv_mov_b32_e32 v2, v7
+\tbuffer_load_dword v9, s[4:7], 0 offen lds
+\tv_mov_b32_e32 v3, v9
+\ts_waitcnt vmcnt(0)
+\ts_endpgm""")
+    (hits,) = W.check_asm(asm).values()
+    assert len(hits) == 1 and "v1, v5" in hits[0]
+
+
 def _device_asm(src: str, out_dir: str) -> str:
     out = os.path.join(out_dir, src + ".s")
     cmd = ([build_lib.hipcc()] + build_lib.COMMON + build_lib.EXTRA.get(src, [])
