@@ -242,12 +242,15 @@ def topk_hier(rows: Rows, cache: Cache, scores: torch.Tensor, k: int, block: int
 def sparse_swa_attn(rows: Rows, cache: Cache, q: torch.Tensor, kv: torch.Tensor, sel_idx: Optional[torch.Tensor],
                     window: Window, sm_scale: float, sel_row_map: Optional[torch.Tensor] = None,
                     sink: Optional[torch.Tensor] = None, want_lse: bool = False, out: Optional[torch.Tensor] = None,
-                    stream=None):
-    """csa2_sparse_swa_attn: out [n, heads, dim] (q's dtype), and lse [n, heads] if asked."""
+                    lse: Optional[torch.Tensor] = None, stream=None):
+    """csa2_sparse_swa_attn: out [n, heads, dim] (q's dtype), and lse [n, heads] if asked
+    (or given: a preallocated lse implies want_lse)."""
     n, heads, dim = q.shape
     if out is None:
         out = torch.empty_like(q)
-    lse = torch.empty((n, heads), dtype=torch.float32, device=q.device) if want_lse else None
+    want_lse = want_lse or lse is not None
+    if want_lse and lse is None:
+        lse = torch.empty((n, heads), dtype=torch.float32, device=q.device)
     k = 0 if sel_idx is None else sel_idx.shape[1]
     sel_stride = 0 if sel_idx is None else sel_idx.stride(0)
     rc = lib().csa2_sparse_swa_attn(ctypes.byref(rows.c()), ctypes.byref(cache.c()), _ptr(q),
@@ -260,15 +263,21 @@ def sparse_swa_attn(rows: Rows, cache: Cache, q: torch.Tensor, kv: torch.Tensor,
     return (out, lse) if want_lse else out
 
 
-def replay_tail_layout(ext_len: torch.Tensor, seq_len: torch.Tensor, budget: int = 128, stream=None) -> dict:
-    """csa2_replay_tail_layout; returns device tensors sized for budget * nreq rows."""
+def replay_tail_layout(ext_len: torch.Tensor, seq_len: torch.Tensor, budget: int = 128, out: Optional[dict] = None,
+                       stream=None) -> dict:
+    """csa2_replay_tail_layout; returns device tensors sized for budget * nreq rows (or
+    fills `out`, a dict of the same int32 tensors)."""
     nreq = ext_len.numel()
     dev = ext_len.device
     cap = budget * nreq
-    t = dict(tail_len=torch.empty(nreq, dtype=torch.int32, device=dev),
-             tail_row_start=torch.empty(nreq + 1, dtype=torch.int32, device=dev))
-    for name in ("src_row", "abs_pos", "win_lo", "req_of_row"):
-        t[name] = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    if out is not None:
+        t = out
+        cap = min(t[name].numel() for name in ("src_row", "abs_pos", "win_lo", "req_of_row"))
+    else:
+        t = dict(tail_len=torch.empty(nreq, dtype=torch.int32, device=dev),
+                 tail_row_start=torch.empty(nreq + 1, dtype=torch.int32, device=dev))
+        for name in ("src_row", "abs_pos", "win_lo", "req_of_row"):
+            t[name] = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
     rc = lib().csa2_replay_tail_layout(ctypes.c_int32(nreq), _ptr(ext_len), _ptr(seq_len), ctypes.c_int32(budget),
                                        _ptr(t["tail_len"]), _ptr(t["tail_row_start"]), _ptr(t["src_row"]),
                                        _ptr(t["abs_pos"]), _ptr(t["win_lo"]), _ptr(t["req_of_row"]),

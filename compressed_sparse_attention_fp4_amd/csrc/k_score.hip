@@ -48,6 +48,19 @@ __device__ __forceinline__ int64_t row_columns(const RowsArg& rows, const CacheA
     return ncol < stride ? ncol : stride;
 }
 
+// Columns a row's output covers: every position below score_stride (full range), or
+// the max_blocks * block columns of a pool row (score_stride is then its pitch).
+__device__ __forceinline__ int64_t output_columns(const PoolArg& pool, int64_t stride)
+{
+    return pool.blocks ? (int64_t)pool.block * pool.max_blocks : stride;
+}
+
+// -inf into columns [from, to) of a score row, by all threads of the workgroup.
+__device__ __forceinline__ void fill_neg_inf(float* rowp, int64_t from, int64_t to)
+{
+    for (int64_t c = from + threadIdx.x; c < to; c += blockDim.x) rowp[c] = -INFINITY;
+}
+
 __device__ __forceinline__ int64_t column_position(const PoolArg& pool, int prow, int64_t c)
 {
     if (!pool.blocks) return c;
@@ -69,9 +82,13 @@ __global__ __launch_bounds__(256) void k_score_f32(RowsArg rows, CacheArg cache,
     int prow;
     const int64_t ncol = row_columns(rows, cache, pool, row, stride, &R, &prow);
     const int64_t c = (int64_t)chk * blockDim.x + threadIdx.x;
-    if (c >= ncol) return;
-    const int64_t j = column_position(pool, prow, c);
     float* dst = scores + (int64_t)row * stride + c;
+    if (c >= ncol) {
+        // columns past the row's reach (or past its pool) hold -inf
+        if (c < output_columns(pool, stride)) *dst = -INFINITY;
+        return;
+    }
+    const int64_t j = column_position(pool, prow, c);
     if (j >= R) {
         *dst = -INFINITY;
         return;
@@ -149,8 +166,15 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
     int prow;
     const int64_t ncol = row_columns(rows, cache, pool, row, stride, &R, &prow);
     const int64_t c_begin = (int64_t)chk * chunk;
-    if (c_begin >= ncol) return;
+    // the chunk's columns past the row's reach (or its pool) hold -inf
+    const int64_t cover = output_columns(pool, stride) < c_begin + chunk ? output_columns(pool, stride)
+                                                                           : c_begin + chunk;
+    if (c_begin >= ncol) {
+        fill_neg_inf(scores + (int64_t)row * stride, c_begin, cover);
+        return;
+    }
     const int64_t c_end = (c_begin + chunk < ncol) ? c_begin + chunk : ncol;
+
     const int64_t krow0 = cache.row_start[rows.req[row]];
     // Pool rows: the chunk's block ids go to LDS (a chunk starts on a block boundary and
     // spans at most kScoreMaxBlocks blocks; the block size is a power of two).
@@ -370,6 +394,7 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
             if (rest == 1) score_group(off0 + 256 * i, ka, sa4);
         }
     }
+    if (c_end < cover) fill_neg_inf(scores + (int64_t)row * stride, c_end, cover);
 }
 
 static int pick_chunk(int n, int64_t cols, int block)

@@ -37,6 +37,7 @@ constexpr int kNT = 1024;
 constexpr int kNW = kNT / 64;
 constexpr int kMaxKPT = 32;
 constexpr int64_t kMaxCap = (int64_t)kNT * kMaxKPT;  // 32768 candidates per workgroup
+constexpr int64_t kListCap = (int64_t)kNT * 16;      // 16384 candidates per merge workgroup
 
 struct SelArgs {
     SelSource src;
@@ -183,6 +184,8 @@ __device__ __forceinline__ void load_keys(const SelArgs& a, int row, int64_t R, 
 #pragma unroll
         for (int i = 0; i < KPT; i++) pin(f[i]);
         const int64_t lim = (a.seg_len < ncol - base) ? base + a.seg_len : ncol;
+        // positions the block pass saw: reachable ones that lie inside the score row
+        const int64_t rlim = R < s.stride ? R : s.stride;
 #pragma unroll
         for (int b8 = 0; b8 < KPT / 8; b8++) {
             const int64_t c = base + e0 + 8 * b8;
@@ -191,7 +194,7 @@ __device__ __forceinline__ void load_keys(const SelArgs& a, int row, int64_t R, 
             bid[b8] = (int32_t)blk;
 #pragma unroll
             for (int q = 0; q < 8; q++) {
-                const bool ok = okb && (c + q < lim) && (blk * 8 + q < R);
+                const bool ok = okb && (c + q < lim) && (blk * 8 + q < rlim);
                 key[8 * b8 + q] = ok ? order_key(f[8 * b8 + q]) : 0u;
             }
         }
@@ -674,6 +677,7 @@ __global__ __launch_bounds__(NT) void k_select(SelArgs a)
 
 // ------------------------------------------------------------------------ host plans
 struct Plan {
+    bool ok;     // every level fits the workgroups that run it, and the last one leaves one list
     int levels;
     int64_t seg_len[8];  // candidates (level 0) or lists (merge) per workgroup
     int nseg[8];         // lists per row produced by each level
@@ -687,6 +691,7 @@ static int64_t first_cap(int mode) { return (mode == SRC_FULL) ? kMaxCap : 16384
 static Plan make_plan(int64_t cols, int k, int mode)
 {
     Plan p{};
+    p.ok = true;
     p.levels = 1;
     if (cols < 1) cols = 1;
     const int64_t cap0 = first_cap(mode);
@@ -703,7 +708,9 @@ static Plan make_plan(int64_t cols, int k, int mode)
     p.nseg[0] = (int)nseg;
     p.cap[0] = p.seg_len[0];
     int64_t cur = nseg;
-    const int64_t group = kMaxCap / k;  // lists merged per workgroup
+    // lists merged per workgroup: a merge level selects with at most 16 candidates per
+    // thread (launch_level), so a group holds at most kListCap candidates
+    const int64_t group = kListCap / k;
     while (cur > 1 && p.levels < 8) {
         const int64_t g = cur < group ? cur : group;
         const int64_t nxt = (cur + g - 1) / g;
@@ -713,6 +720,7 @@ static Plan make_plan(int64_t cols, int k, int mode)
         p.levels++;
         cur = nxt;
     }
+    p.ok = cur == 1;
     return p;
 }
 
@@ -739,8 +747,11 @@ static size_t plan_workspace(const Plan& p, int n, int k)
 // sooner.  The selection is exact either way.
 constexpr int kManyRows = 1024;
 
+// Launch one level; every variant holds threads x KPT candidates, and a level whose
+// workgroups would hold more (a plan the variants cannot take) is refused rather than
+// losing candidates.
 template <int SRC>
-static void launch_level(dim3 grid, int64_t cap, int nrows, const SelArgs& a, hipStream_t stream)
+static hipError_t launch_level(dim3 grid, int64_t cap, int nrows, const SelArgs& a, hipStream_t stream)
 {
     if (nrows >= kManyRows && cap <= 8192) {
         if (cap <= 2048)
@@ -749,17 +760,20 @@ static void launch_level(dim3 grid, int64_t cap, int nrows, const SelArgs& a, hi
             hipLaunchKernelGGL((k_select<16, SRC, 256>), grid, dim3(256), 0, stream, a);
         else
             hipLaunchKernelGGL((k_select<32, SRC, 256>), grid, dim3(256), 0, stream, a);
-        return;
+        return hipSuccess;
     }
     if (cap <= 4096)  // (pool gathers take whole blocks: at least 8 per thread)
         hipLaunchKernelGGL((k_select<SRC == SRC_PGATHER ? 16 : 4, SRC>), grid, dim3(kNT), 0, stream, a);
     else if (cap <= 8192)  // e.g. the 8,192 block maxima of a 65,536-entry row: every slot used
         hipLaunchKernelGGL((k_select<8, SRC>), grid, dim3(kNT), 0, stream, a);
-    else if (cap <= 16384 || SRC != SRC_FULL)
+    else if (cap <= kListCap)
         hipLaunchKernelGGL((k_select<16, SRC>), grid, dim3(kNT), 0, stream, a);
-    else
+    else if (SRC == SRC_FULL && cap <= kMaxCap)
         hipLaunchKernelGGL((k_select<SRC == SRC_FULL ? kMaxKPT : 16, SRC>), grid, dim3(kNT), 0,
                            stream, a);
+    else
+        return hipErrorInvalidValue;
+    return hipSuccess;
 }
 
 static int ilog2(int x)
@@ -776,6 +790,7 @@ static hipError_t run_plan(const SelSource& src, int mode, int block, int k, int
     const int n = src.rows.n;
     if (n == 0) return hipSuccess;
     const Plan p = make_plan(cols, k, mode);
+    if (!p.ok) return hipErrorInvalidValue;
     size_t sza = 0;
     for (int l = 0; l + 1 < p.levels; l += 2) {
         const size_t sz = level_bytes(p, l, n, k);
@@ -804,19 +819,20 @@ static hipError_t run_plan(const SelSource& src, int mode, int block, int k, int
         a.bmax = bmax;
         a.bstride = bstride;
         const dim3 grid((unsigned)((int64_t)n * p.nseg[l]));
+        hipError_t e;
         if (l > 0)
-            launch_level<SRC_LIST>(grid, p.cap[l], n, a, stream);
+            e = launch_level<SRC_LIST>(grid, p.cap[l], n, a, stream);
         else if (mode == SRC_FULL)
-            launch_level<SRC_FULL>(grid, p.cap[l], n, a, stream);
+            e = launch_level<SRC_FULL>(grid, p.cap[l], n, a, stream);
         else if (mode == SRC_POOL)
-            launch_level<SRC_POOL>(grid, p.cap[l], n, a, stream);
+            e = launch_level<SRC_POOL>(grid, p.cap[l], n, a, stream);
         else if (mode == SRC_BMAX)
-            launch_level<SRC_BMAX>(grid, p.cap[l], n, a, stream);
+            e = launch_level<SRC_BMAX>(grid, p.cap[l], n, a, stream);
         else if (mode == SRC_PGATHER)
-            launch_level<SRC_PGATHER>(grid, p.cap[l], n, a, stream);
+            e = launch_level<SRC_PGATHER>(grid, p.cap[l], n, a, stream);
         else
-            launch_level<SRC_BLOCK>(grid, p.cap[l], n, a, stream);
-        const hipError_t e = hipGetLastError();
+            e = launch_level<SRC_BLOCK>(grid, p.cap[l], n, a, stream);
+        if (e == hipSuccess) e = hipGetLastError();
         if (e != hipSuccess) return e;
         prev = a.out_list;
     }

@@ -38,7 +38,9 @@
  *     every row aligned.
  *   - Results are deterministic: the same inputs give bitwise-identical outputs, and a
  *     row's outputs do not depend on the other rows of the batch.
- *   - Calls are reentrant; the library keeps no state between calls.
+ *   - Calls are reentrant.  The only state kept between calls is a per-device flag,
+ *     filled on a device's first call, that records whether it is a gfx950 (guarded by
+ *     a mutex); nothing else persists.
  */
 #ifndef CSA2_H
 #define CSA2_H
@@ -96,7 +98,7 @@ typedef struct csa2_cache {
 /* Index keys of the owner ([MOD] "Mixed precision": MXFP4 with 32-element groups, 68 B
  * per 128-d entry = 64 B codes + 4 B scales, stored as two planes). */
 typedef struct csa2_index_keys {
-    csa2_dtype dtype;     /* CSA2_MXFP4 (dim 128) or CSA2_F32 (dim 16..256, multiple of 4) */
+    csa2_dtype dtype;     /* CSA2_MXFP4 (dim 128) or CSA2_F32 (dim 1..1024) */
     int32_t dim;
     const void* data;     /* MXFP4: uint8[rows][dim/2]; F32: float[rows][dim] */
     const uint8_t* scale; /* MXFP4: uint8[rows][dim/32] E8M0; F32: NULL */
@@ -143,11 +145,13 @@ typedef struct csa2_swa {
  * q_idx   [n][heads][keys->dim]: BF16 for MXFP4 keys, F32 for F32 keys (q_dtype says which).
  * heads   MXFP4: a multiple of 16, at most 128; F32: a multiple of 4, at most 128.
  * w       float [n][heads] with row stride w_row_stride (0: one row shared by all).
- * pool    NULL: column j of row q is compressed position j, written for j < min(R(q),
- *         score_stride).  Non-NULL: column c is position blocks[c/block]*block + c%block
- *         of the row's pool, written for c < block*nblocks, -inf where the position is
- *         not reachable; requires block*max_blocks <= score_stride.
- * scores  float [n][score_stride]; columns beyond those listed are not written.
+ * pool    NULL: column j of row q is compressed position j; every column j < score_stride
+ *         is written, the score for j < R(q) and -inf from R(q) on.  Non-NULL: column c
+ *         is position blocks[c/block]*block + c%block of the row's pool; the columns
+ *         c < block*max_blocks are written, -inf where the position is not reachable and
+ *         from block*nblocks on; requires block*max_blocks <= score_stride, and the
+ *         columns from block*max_blocks to score_stride are row padding, not written.
+ * scores  float [n][score_stride].
  * Errors: E_ARG (null pointers, n < 0, bad strides), E_UNSUPPORTED (dtype/dim/heads).
  * ------------------------------------------------------------------------------- */
 int csa2_index_score(const csa2_rows* rows, const csa2_cache* cache, const void* q_idx, csa2_dtype q_dtype,
@@ -177,7 +181,8 @@ int csa2_topk(const csa2_rows* rows, const csa2_cache* cache, const float* score
  * when ceil(R/block) <= max_blocks every block is kept, otherwise the block holding
  * the newest reachable position plus the max_blocks-1 best other blocks by (block
  * score desc, block id asc).  out_pool_blocks [n][max_blocks] ascending ids, -1 padded;
- * out_pool_nblocks [n].  block 1..64, max_blocks 1..4096, k 1..2048.
+ * out_pool_nblocks [n].  block 8 (the pages' block; other sizes are CSA2_E_UNSUPPORTED),
+ * max_blocks 1..4096, k 1..2048.
  * ------------------------------------------------------------------------------- */
 int csa2_topk_hier(const csa2_rows* rows, const csa2_cache* cache, const float* scores, int64_t score_stride,
                    int32_t k, int32_t block, int32_t max_blocks, int32_t* out_idx, int32_t* out_pool_blocks,

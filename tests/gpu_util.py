@@ -57,3 +57,14 @@ def allclose_report(got, ref, atol, rtol):
     err = np.abs(got - ref)
     bad = err > atol + rtol * np.abs(ref)
     return int(bad.sum()), float(err.max(initial=0.0)), float((err / (np.abs(ref) + 1e-30)).max(initial=0.0))
+
+
+POISON_I32 = 0x7FFFFFFF
+
+
+def poison(shape, dtype, device=DEV):
+    """An output buffer filled with a sentinel no kernel writes (NaN for floating point,
+    0x7fffffff for int32), so that elements a kernel leaves unwritten are caught."""
+    if dtype == torch.int32:
+        return torch.full(shape, POISON_I32, dtype=dtype, device=device)
+    return torch.full(shape, float("nan"), dtype=dtype, device=device)

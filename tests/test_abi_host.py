@@ -156,3 +156,38 @@ def test_quant_arg_errors():
     assert L.csa2_quant_mx(B.MXFP4, None, B.F32, ctypes.c_int64(0), None, None, None) == B.CSA2_OK
     assert L.csa2_quant_mx(B.MXFP4, M, B.F32, ctypes.c_int64(4), P, P, None) == B.CSA2_E_ARG and "16-byte" in _err()
     assert L.csa2_quant_mx(B.MXFP4, P, B.F32, ctypes.c_int64(4), M, P, None) == B.CSA2_E_ARG
+
+
+def test_topk_hier_block_is_8_only():
+    """The header documents block 8 only; every other block size is refused before launch."""
+    L = B.lib()
+    for block in (1, 2, 4, 16, 64, 0, -8):
+        rc = L.csa2_topk_hier(ctypes.byref(_rows()), ctypes.byref(_cache()), P, ctypes.c_int64(1024),
+                              ctypes.c_int32(512), ctypes.c_int32(block), ctypes.c_int32(2048), P, P, P, None,
+                              ctypes.c_size_t(0), None)
+        assert rc == B.CSA2_E_UNSUPPORTED and "block" in _err(), block
+
+
+def test_f32_index_dim_range():
+    """F32 index keys take dim 1..1024 (the header's range); 0 and 1025 are refused."""
+    L = B.lib()
+
+    def call(dim):
+        keys = B._IndexKeys(B.F32, dim, P, None)
+        return L.csa2_index_score(ctypes.byref(_rows()), ctypes.byref(_cache()), P, B.F32, 8, P, ctypes.c_int64(8),
+                                  ctypes.byref(keys), None, P, ctypes.c_int64(512), None)
+
+    for dim in (0, 1025):
+        assert call(dim) == B.CSA2_E_UNSUPPORTED and "dim" in _err()
+    for dim in (1, 7, 1024):
+        rc = call(dim)
+        assert not (rc == B.CSA2_E_UNSUPPORTED and "dim" in _err()), dim
+
+
+def test_workspace_grows_with_merge_levels():
+    """Rows long enough for several merge levels need workspace for each level's lists
+    (k = 2048 at 524,288 columns: 32 segments of 16,384, then groups of 8 lists)."""
+    a = B.workspace_size(B.OP_TOPK, 3, 262152, 2048)
+    b = B.workspace_size(B.OP_TOPK, 3, 524288, 2048)
+    assert 0 < a < b
+    assert B.workspace_size(B.OP_TOPK_HIER, 2, 600000, 512, 4096) > 0

@@ -12,7 +12,7 @@ import torch
 from compressed_sparse_attention_fp4_amd import binding as B
 from compressed_sparse_attention_fp4_amd import synth
 
-from gpu_util import DEV, allclose_report, dev_cache, dev_rows, i32, i64, quant_both, say
+from gpu_util import DEV, POISON_I32, allclose_report, dev_cache, dev_rows, i32, i64, poison, quant_both, say
 
 pytestmark = pytest.mark.gpu
 
@@ -22,6 +22,19 @@ def _gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     B.lib()
+
+
+def _topk(rows_d, cache_d, scores_d, k, pool=None):
+    """csa2_topk into a poisoned output (every slot must be written: positions or -1)."""
+    out = poison((rows_d.n, k), torch.int32)
+    return B.topk(rows_d, cache_d, scores_d, k, pool=pool, out=out)
+
+
+def _hier(rows_d, cache_d, scores_d, k, block, max_blocks):
+    """csa2_topk_hier into poisoned outputs."""
+    n = rows_d.n
+    out = (poison((n, k), torch.int32), poison((n, max_blocks), torch.int32), poison((n,), torch.int32))
+    return B.topk_hier(rows_d, cache_d, scores_d, k, block, max_blocks, out=out)
 
 
 # ------------------------------------------------------------------ quantizer
@@ -66,7 +79,12 @@ def test_replay_tail_layout(orc):
     e = rng.integers(0, 400, size=700)
     cases.append((e.tolist(), (e + rng.integers(0, 1000, size=700)).tolist()))
     for ext, seq in cases:
-        t = B.replay_tail_layout(i32(ext).to(DEV), i32(seq).to(DEV), 128)
+        nreq = len(ext)
+        cap = 128 * nreq
+        t = dict(tail_len=poison((nreq,), torch.int32), tail_row_start=poison((nreq + 1,), torch.int32))
+        for name in ("src_row", "abs_pos", "win_lo", "req_of_row"):
+            t[name] = poison((cap,), torch.int32)
+        B.replay_tail_layout(i32(ext).to(DEV), i32(seq).to(DEV), 128, out=t)
         o = orc.replay_tail_layout(ext, seq, 128)
         tot = int(o["tail_row_start"][-1])
         assert t["tail_len"].cpu().numpy().tolist() == o["tail_len"].tolist()
@@ -104,8 +122,9 @@ def test_index_score_mxfp4_full_range(orc, H):
     rows, cache, keys, q, w = _score_case(10 + H, (3000, 1234, 77), 2, H, 128, 12)
     stride = 1536
     (kd, ksd), (ko, kso) = quant_both(orc, B.MXFP4, orc.E2M1, keys)
+    n = len(rows["req_of_row"])
     s_d = B.index_score(dev_rows(rows), dev_cache(cache), q.to(DEV), w.to(DEV), B.IndexKeys(kd, ksd, 128),
-                        score_stride=stride)
+                        scores=poison((n, stride), torch.float32))
     s_o, bad = orc.index_score(rows, cache, q.float().numpy(), w.numpy(), ko, key_scales=kso, heads=H, dim=128,
                                score_stride=stride)
     assert bad == 0
@@ -113,6 +132,7 @@ def test_index_score_mxfp4_full_range(orc, H):
     for i in range(len(rows["req_of_row"])):
         r, p = rows["req_of_row"][i], rows["pos_of_row"][i]
         R = min((p + 1) // 2, cache["n_entries"][r])
+        assert np.all(got[i, R:] == -np.inf), "row %d: columns past R=%d not -inf" % (i, R)
         if not np.array_equal(got[i, :R], s_o[i, :R]):
             bad_cols = np.nonzero(got[i, :R] != s_o[i, :R])[0]
             raise AssertionError("row %d (p=%d R=%d): %d columns differ, first %s: gpu %r oracle %r" % (
@@ -145,8 +165,10 @@ def test_index_score_mxfp4_pool(orc):
     pool_d = B.Pool(i32(pool_blocks).to(DEV), i32(pool_n).to(DEV), B_, i32(perm).to(DEV))
     stride = NB * B_
     (kd, ksd), (ko, kso) = quant_both(orc, B.MXFP4, orc.E2M1, keys)
+    # score_stride is the pool width plus padding that the call must leave alone
+    pad = poison((n, stride + 24), torch.float32)
     s_d = B.index_score(dev_rows(rows), dev_cache(cache), q.to(DEV), w.to(DEV), B.IndexKeys(kd, ksd, 128),
-                        pool=pool_d, score_stride=stride)
+                        pool=pool_d, scores=pad)
     s_o, bad = orc.index_score(rows, cache, q.float().numpy(), w.numpy(), ko, key_scales=kso, heads=64, dim=128,
                                score_stride=stride, pool=pool_o)
     assert bad == 0
@@ -154,6 +176,8 @@ def test_index_score_mxfp4_pool(orc):
     for i in range(n):
         ncol = nblocks[i] * B_
         assert np.array_equal(got[i, :ncol], s_o[i, :ncol]), i
+        assert np.all(got[i, ncol:stride] == -np.inf), i
+        assert np.all(np.isnan(got[i, stride:])), i
 
 
 def test_index_score_f32_c0(orc):
@@ -169,12 +193,13 @@ def test_index_score_f32_c0(orc):
     w = synth.uniform((n, cfg.index_heads), 0, "index_w")
     stride = 512
     s_d = B.index_score(dev_rows(rows), dev_cache(cache), q.to(DEV), w.to(DEV), B.IndexKeys(keys.to(DEV), None, 64),
-                        score_stride=stride)
+                        scores=poison((n, stride), torch.float32))
     s_o, _ = orc.index_score(rows, cache, q.numpy(), w.numpy(), keys.numpy(), heads=8, dim=64, score_stride=stride)
     got = s_d.cpu().numpy()
     for i in range(n):
         R = min((rows["pos_of_row"][i] + 1) // 2, 512)
         assert np.array_equal(got[i, :R], s_o[i, :R]), i
+        assert np.all(got[i, R:] == -np.inf), i
 
 
 # ---------------------------------------------------------------------- top-k
@@ -199,7 +224,7 @@ def test_topk_flat(orc, k, ties):
     R_list = [0, 1, 511, 512, 513, 2047, 2048, 2049, 5000, 8191, 8192, 8193, 16385, 40000]
     stride = 40960
     rows, cache, scores = _topk_inputs(100 + k, R_list, stride, ties)
-    got = B.topk(dev_rows(rows), dev_cache(cache), torch.from_numpy(scores).to(DEV), k).cpu().numpy()
+    got = _topk(dev_rows(rows), dev_cache(cache), torch.from_numpy(scores).to(DEV), k).cpu().numpy()
     ref = orc.topk(rows, cache, scores, k)
     for i in range(len(R_list)):
         assert np.array_equal(got[i], ref[i]), (i, R_list[i])
@@ -217,13 +242,13 @@ def test_topk_many_rows(orc, stride, ties):
     R_list = [min(base[i % len(base)], stride) for i in range(1024)]
     rows, cache, scores = _topk_inputs(700 + stride, R_list, stride, ties)
     sd = torch.from_numpy(scores).to(DEV)
-    got = B.topk(dev_rows(rows), dev_cache(cache), sd, 512).cpu().numpy()
+    got = _topk(dev_rows(rows), dev_cache(cache), sd, 512).cpu().numpy()
     ref = orc.topk(rows, cache, scores, 512)
     for i in range(len(R_list)):
         assert np.array_equal(got[i], ref[i]), (i, R_list[i])
     few = {k: v[:16] for k, v in rows.items()}
     fc = dict(ratio_m=1, n_entries=cache["n_entries"][:16], row_start=cache["row_start"][:16])
-    got16 = B.topk(dev_rows(few), dev_cache(fc), sd[:16].contiguous(), 512).cpu().numpy()
+    got16 = _topk(dev_rows(few), dev_cache(fc), sd[:16].contiguous(), 512).cpu().numpy()
     assert np.array_equal(got16, got[:16])
 
 
@@ -254,7 +279,7 @@ def test_topk_small_threshold_bin(orc, stride):
     scores = np.stack(rows_scores)
     rows = dict(req_of_row=np.arange(n), pos_of_row=np.full(n, R - 1))
     cache = dict(ratio_m=1, n_entries=np.full(n, R), row_start=np.arange(n, dtype=np.int64) * R)
-    got = B.topk(dev_rows(rows), dev_cache(cache), torch.from_numpy(scores).to(DEV), k).cpu().numpy()
+    got = _topk(dev_rows(rows), dev_cache(cache), torch.from_numpy(scores).to(DEV), k).cpu().numpy()
     ref = orc.topk(rows, cache, scores, k)
     for i in range(n):
         assert np.array_equal(got[i], ref[i]), i
@@ -284,7 +309,7 @@ def test_topk_pool(orc):
             scores[i, c] = -np.inf if j >= R else np.float32(rng.standard_normal() * 20 + 100)
     pool_o = dict(blocks=blocks, nblocks=nb_, block=B_, max_blocks=NB)
     pool_d = B.Pool(i32(blocks).to(DEV), i32(nb_).to(DEV), B_)
-    got = B.topk(dev_rows(rows), dev_cache(cache), torch.from_numpy(scores).to(DEV), 512, pool=pool_d).cpu().numpy()
+    got = _topk(dev_rows(rows), dev_cache(cache), torch.from_numpy(scores).to(DEV), 512, pool=pool_d).cpu().numpy()
     ref = orc.topk(rows, cache, scores, 512, pool=pool_o)
     assert np.array_equal(got, ref)
 
@@ -295,7 +320,7 @@ def test_topk_hier(orc, ties):
     R_list = [1, 9, 100, 16383, 16384, 16385, 16392, 16393, 30000, 65536]
     stride = 65536
     rows, cache, scores = _topk_inputs(55, R_list, stride, ties)
-    idx, blocks, nblocks = B.topk_hier(dev_rows(rows), dev_cache(cache), torch.from_numpy(scores).to(DEV), 512, 8, 2048)
+    idx, blocks, nblocks = _hier(dev_rows(rows), dev_cache(cache), torch.from_numpy(scores).to(DEV), 512, 8, 2048)
     ri, rb, rn = orc.topk_hier(rows, cache, scores, 512, 8, 2048)
     assert np.array_equal(nblocks.cpu().numpy(), rn)
     assert np.array_equal(blocks.cpu().numpy(), rb)
@@ -326,7 +351,7 @@ def test_attn_f32_c0(orc):
     wo = dict(data=swa_data.numpy(), dtype=0, scale=None, row_start=win["row_start"].numpy(),
               pos_start=win["pos_start"].numpy(), window=128)
     out_d, lse_d = B.sparse_swa_attn(dev_rows(rows), dev_cache(cache), q.to(DEV), kv.to(DEV), i32(sel).to(DEV), wd,
-                                     scale, want_lse=True)
+                                     scale, out=poison((n, 8, 64), torch.float32), lse=poison((n, 8), torch.float32))
     out_o, lse_o = orc.sparse_swa_attn(rows, cache, q.numpy(), 0, kv.numpy(), 0, sel, wo, heads=8, dim=64,
                                        sm_scale=scale)
     nb, emax, _ = allclose_report(out_d.cpu().numpy(), out_o, 1e-4, 1e-4)
@@ -337,7 +362,8 @@ def test_attn_f32_c0(orc):
     for i in range(n):
         R = min((rows["pos_of_row"][i] + 1) // 2, 512)
         sel_all[i, :R] = np.arange(R)
-    out_d2 = B.sparse_swa_attn(dev_rows(rows), dev_cache(cache), q.to(DEV), kv.to(DEV), i32(sel_all).to(DEV), wd, scale)
+    out_d2 = B.sparse_swa_attn(dev_rows(rows), dev_cache(cache), q.to(DEV), kv.to(DEV), i32(sel_all).to(DEV), wd, scale,
+                               out=poison((n, 8, 64), torch.float32))
     dense, _ = orc.sparse_swa_attn(rows, cache, q.numpy(), 0, kv.numpy(), 0, None, wo, heads=8, dim=64, sm_scale=scale,
                                    dense=True)
     nb, emax, _ = allclose_report(out_d2.cpu().numpy(), dense, 1e-4, 1e-4)
@@ -375,7 +401,8 @@ def _attn_bf16_case(seed, S, m, H, k, nrows_per_req, win_lo_tail=False, swa_fp8=
     return rows, cache, q, kv, win, swa_raw, sel
 
 
-def _run_attn_bf16(orc, rows, cache, q, kv, win, swa_raw, sel, H, sm_scale, swa_fp8=True, sel_row_map=None):
+def _run_attn_bf16(orc, rows, cache, q, kv, win, swa_raw, sel, H, sm_scale, swa_fp8=True, sel_row_map=None,
+                   sink=None):
     n = len(rows["req_of_row"])
     if swa_fp8:
         (cd, sd), (co, so) = quant_both(orc, B.MXFP8_E4M3, orc.E4M3, swa_raw)
@@ -389,11 +416,12 @@ def _run_attn_bf16(orc, rows, cache, q, kv, win, swa_raw, sel, H, sm_scale, swa_
                   row_start=win["row_start"].numpy(), pos_start=win["pos_start"].numpy(), window=128)
     out_d, lse_d = B.sparse_swa_attn(dev_rows(rows), dev_cache(cache), q.to(DEV), kv.to(DEV), i32(sel).to(DEV), wd,
                                      sm_scale, sel_row_map=None if sel_row_map is None else i32(sel_row_map).to(DEV),
-                                     want_lse=True)
+                                     sink=None if sink is None else torch.from_numpy(sink).to(DEV),
+                                     out=poison(tuple(q.shape), torch.bfloat16), lse=poison((n, H), torch.float32))
     qb = q.view(torch.int16).numpy().view(np.uint16)
     kvb = kv.view(torch.int16).numpy().view(np.uint16)
     out_o, lse_o = orc.sparse_swa_attn(rows, cache, qb, 1, kvb, 1, sel, wo, heads=H, dim=512, sm_scale=sm_scale,
-                                       sel_row_map=sel_row_map)
+                                       sel_row_map=sel_row_map, sink=sink)
     return out_d.float().cpu().numpy(), lse_d.cpu().numpy(), out_o, lse_o
 
 
@@ -466,7 +494,8 @@ def test_attn_bf16_reuse_row_map(orc):
 def test_determinism_and_batch_invariance(orc):
     say("case: run twice bitwise equal; a row alone equals the row inside a batch")
     rows, cache, q, kv, win, swa_raw, sel = _attn_bf16_case(99, (1200, 800), 2, 32, 512, 6)
-    a, _, _, _ = _run_attn_bf16(orc, rows, cache, q, kv, win, swa_raw, sel, 32, 0.04)
+    a, la, ref, lref = _run_attn_bf16(orc, rows, cache, q, kv, win, swa_raw, sel, 32, 0.04)
+    _check_bf16_attn(a, ref, la, lref)
     b, _, _, _ = _run_attn_bf16(orc, rows, cache, q, kv, win, swa_raw, sel, 32, 0.04)
     assert np.array_equal(a, b)
     i = 3
@@ -480,12 +509,12 @@ def test_topk_multilevel(orc, k):
     say("case: topk over rows longer than one workgroup (segments + merge), k=%d" % k)
     R_list = [70000, 131072, 262144, 200001, 65536, 65537]
     rows, cache, scores = _topk_inputs(300 + k, R_list, 262144, ties=None)
-    got = B.topk(dev_rows(rows), dev_cache(cache), torch.from_numpy(scores).to(DEV), k).cpu().numpy()
+    got = _topk(dev_rows(rows), dev_cache(cache), torch.from_numpy(scores).to(DEV), k).cpu().numpy()
     ref = orc.topk(rows, cache, scores, k)
     assert np.array_equal(got, ref)
     # and with heavy ties, where the merge must keep the lowest positions
     rows, cache, scores = _topk_inputs(301 + k, R_list, 262144, ties=50.0)
-    got = B.topk(dev_rows(rows), dev_cache(cache), torch.from_numpy(scores).to(DEV), k).cpu().numpy()
+    got = _topk(dev_rows(rows), dev_cache(cache), torch.from_numpy(scores).to(DEV), k).cpu().numpy()
     ref = orc.topk(rows, cache, scores, k)
     assert np.array_equal(got, ref)
 
@@ -494,8 +523,162 @@ def test_topk_hier_long(orc):
     say("case: topk_hier on 262144-entry rows (C4 shape)")
     R_list = [262144, 100000]
     rows, cache, scores = _topk_inputs(400, R_list, 262144)
-    idx, blocks, nblocks = B.topk_hier(dev_rows(rows), dev_cache(cache), torch.from_numpy(scores).to(DEV), 512, 8, 2048)
+    idx, blocks, nblocks = _hier(dev_rows(rows), dev_cache(cache), torch.from_numpy(scores).to(DEV), 512, 8, 2048)
     ri, rb, rn = orc.topk_hier(rows, cache, scores, 512, 8, 2048)
     assert np.array_equal(nblocks.cpu().numpy(), rn)
     assert np.array_equal(blocks.cpu().numpy(), rb)
     assert np.array_equal(idx.cpu().numpy(), ri)
+
+
+# ------------------------------------------------ hierarchy: single-stage path, ties
+@pytest.mark.parametrize("max_blocks", [64, 512])
+def test_topk_hier_single_stage(orc, max_blocks):
+    """k >= max_blocks takes the single-stage path (flat top-k over the score row, then the
+    block pass with maxima taken on the fly)."""
+    say("case: topk_hier k=512, max_blocks=%d (single-stage path)" % max_blocks)
+    R_list = [1, 8, 9, 500, 511, 512, 513, 8 * max_blocks - 1, 8 * max_blocks, 8 * max_blocks + 1, 20000, 65536]
+    stride = 65536
+    for ties in (None, 2.0):
+        rows, cache, scores = _topk_inputs(57 + max_blocks, R_list, stride, ties)
+        idx, blocks, nblocks = _hier(dev_rows(rows), dev_cache(cache), torch.from_numpy(scores).to(DEV), 512, 8,
+                                     max_blocks)
+        ri, rb, rn = orc.topk_hier(rows, cache, scores, 512, 8, max_blocks)
+        assert np.array_equal(nblocks.cpu().numpy(), rn)
+        assert np.array_equal(blocks.cpu().numpy(), rb)
+        assert np.array_equal(idx.cpu().numpy(), ri)
+
+
+@pytest.mark.parametrize("max_blocks", [2048, 64])
+def test_topk_hier_all_equal(orc, max_blocks):
+    """Every score equal: the pool is the lowest block ids plus the newest block, and the
+    flat top-k is the k lowest positions (ties go to the lowest index)."""
+    say("case: topk_hier with all scores equal, max_blocks=%d" % max_blocks)
+    R_list = [5, 16384, 16385, 30001, 65536]
+    stride = 65536
+    n = len(R_list)
+    rows = dict(req_of_row=np.arange(n), pos_of_row=np.array([R - 1 for R in R_list]))
+    cache = dict(ratio_m=1, n_entries=np.array(R_list), row_start=np.zeros(n, np.int64))
+    scores = np.full((n, stride), 3.0, np.float32)
+    idx, blocks, nblocks = _hier(dev_rows(rows), dev_cache(cache), torch.from_numpy(scores).to(DEV), 512, 8,
+                                 max_blocks)
+    ri, rb, rn = orc.topk_hier(rows, cache, scores, 512, 8, max_blocks)
+    assert np.array_equal(nblocks.cpu().numpy(), rn)
+    assert np.array_equal(blocks.cpu().numpy(), rb)
+    assert np.array_equal(idx.cpu().numpy(), ri)
+    for i, R in enumerate(R_list):
+        nb = (R + 7) // 8
+        want = list(range(nb)) if nb <= max_blocks else list(range(max_blocks - 1)) + [nb - 1]
+        assert rb[i, :len(want)].tolist() == want
+        assert ri[i, :min(R, 512)].tolist() == list(range(min(R, 512)))
+
+
+def test_topk_hier_stride_below_reach(orc):
+    """score_stride smaller than R and not a multiple of 8: only the columns that exist are
+    candidates, and the newest block is the one holding column score_stride - 1."""
+    say("case: topk_hier with score_stride < R, stride % 8 != 0")
+    stride = 40003
+    R_list = [50000, 40003, 40001, 39999, 16390]
+    rows, cache, scores = _topk_inputs(59, R_list, stride)
+    for mb in (2048, 64):
+        idx, blocks, nblocks = _hier(dev_rows(rows), dev_cache(cache), torch.from_numpy(scores).to(DEV), 512, 8, mb)
+        ri, rb, rn = orc.topk_hier(rows, cache, scores, 512, 8, mb)
+        assert np.array_equal(nblocks.cpu().numpy(), rn)
+        assert np.array_equal(blocks.cpu().numpy(), rb)
+        assert np.array_equal(idx.cpu().numpy(), ri)
+
+
+# ----------------------------------------- merge levels at their largest candidate counts
+@pytest.mark.parametrize("stride", [262152, 524288])
+def test_topk_merge_capacity_k2048(orc, stride):
+    """k = 2048 over rows long enough that a merge level gathers more than 8 lists: every
+    merge workgroup must hold all of its lists' candidates."""
+    say("case: topk k=2048 at score_stride %d (merge-level capacity)" % stride)
+    R_list = [stride, stride - 5, 300001 if stride > 300001 else 200001]
+    rows, cache, scores = _topk_inputs(61 + stride % 97, R_list, stride)
+    got = _topk(dev_rows(rows), dev_cache(cache), torch.from_numpy(scores).to(DEV), 2048).cpu().numpy()
+    ref = orc.topk(rows, cache, scores, 2048)
+    assert np.array_equal(got, ref)
+
+
+def test_topk_pool_merge_capacity(orc):
+    """Pool top-k with k = 2048 over a pool of 32,768 blocks of 8 (262,144 candidates)."""
+    say("case: pool topk k=2048 over 262144 pool columns")
+    rng = np.random.default_rng(63)
+    B_, NB = 8, 32768
+    R_list = [400000, 262144]
+    n = len(R_list)
+    rows = dict(req_of_row=np.arange(n), pos_of_row=np.array([R - 1 for R in R_list]))
+    cache = dict(ratio_m=1, n_entries=np.array(R_list), row_start=np.zeros(n, np.int64))
+    blocks = np.full((n, NB), -1, np.int32)
+    nb_ = np.zeros(n, np.int32)
+    for i, R in enumerate(R_list):
+        nb = (R + B_ - 1) // B_
+        pick = sorted(set(rng.choice(nb - 1, NB - 1, replace=False).tolist()) | {nb - 1}) if nb > NB \
+            else list(range(nb))
+        blocks[i, :len(pick)] = pick
+        nb_[i] = len(pick)
+    scores = rng.standard_normal((n, NB * B_)).astype(np.float32)
+    pool_o = dict(blocks=blocks, nblocks=nb_, block=B_, max_blocks=NB)
+    pool_d = B.Pool(i32(blocks).to(DEV), i32(nb_).to(DEV), B_)
+    got = _topk(dev_rows(rows), dev_cache(cache), torch.from_numpy(scores).to(DEV), 2048, pool=pool_d).cpu().numpy()
+    ref = orc.topk(rows, cache, scores, 2048, pool=pool_o)
+    assert np.array_equal(got, ref)
+
+
+def test_topk_hier_4096_blocks_long_row(orc):
+    """max_blocks = 4096 on rows of more than 524,288 entries (block maxima merged over
+    several levels with 4,095 kept per list)."""
+    say("case: topk_hier max_blocks=4096 on 600000-entry rows")
+    R_list = [600000, 590001]
+    rows, cache, scores = _topk_inputs(65, R_list, 600000)
+    idx, blocks, nblocks = _hier(dev_rows(rows), dev_cache(cache), torch.from_numpy(scores).to(DEV), 512, 8, 4096)
+    ri, rb, rn = orc.topk_hier(rows, cache, scores, 512, 8, 4096)
+    assert np.array_equal(nblocks.cpu().numpy(), rn)
+    assert np.array_equal(blocks.cpu().numpy(), rb)
+    assert np.array_equal(idx.cpu().numpy(), ri)
+
+
+# ----------------------------------------------------------------- attention sink
+@pytest.mark.parametrize("shift", [0.0, 6.0])
+def test_attn_bf16_sink(orc, shift):
+    """The sink adds exp(sink_h - max) to each head's denominator (one more key of value
+    zero); sinks around and above the logits, bf16 path."""
+    say("case: bf16 attention with a sink, shift %g" % shift)
+    rows, cache, q, kv, win, swa_raw, sel = _attn_bf16_case(71, (2600, 700), 2, 32, 512, 6)
+    sink = (np.random.default_rng(72).standard_normal(32) * 2.0 + shift).astype(np.float32)
+    got, lse_g, ref, lse_r = _run_attn_bf16(orc, rows, cache, q, kv, win, swa_raw, sel, 32, 1 / math.sqrt(512),
+                                            sink=sink)
+    _check_bf16_attn(got, ref, lse_g, lse_r)
+
+
+def test_attn_f32_sink(orc):
+    say("case: fp32 attention (C0 shapes) with a sink")
+    cfg = synth.config(0)
+    g = cfg.geom
+    rows_t = synth.prefill_rows(g)
+    rows = {k: v.numpy() for k, v in rows_t.items()}
+    n = len(rows["req_of_row"])
+    cache = dict(ratio_m=2, n_entries=np.array(g.n_entries), row_start=np.array(g.row_start))
+    q = synth.normal((n, 8, 64), 0, "q") * 3.0   # logits spread wide: the max shift matters
+    kv = synth.normal((g.total_entries, 64), 0, "kv")
+    win = synth.window_cache_geometry(g, 128, rows_held=g.seq_len)
+    swa_data = synth.normal((win["rows"], 64), 0, "swa")
+    rng = np.random.default_rng(5)
+    sel = np.full((n, 64), -1, np.int32)
+    for i in range(n):
+        R = min((rows["pos_of_row"][i] + 1) // 2, 512)
+        take = min(R, 64)
+        sel[i, :take] = np.sort(rng.choice(R, size=take, replace=False)) if take else []
+    sink = (rng.standard_normal(8) * 3.0 + 4.0).astype(np.float32)
+    scale = 1.0 / 8.0
+    wd = B.Window(swa_data.to(DEV), None, win["row_start"].to(DEV), win["pos_start"].to(DEV), 128)
+    wo = dict(data=swa_data.numpy(), dtype=0, scale=None, row_start=win["row_start"].numpy(),
+              pos_start=win["pos_start"].numpy(), window=128)
+    out_d, lse_d = B.sparse_swa_attn(dev_rows(rows), dev_cache(cache), q.to(DEV), kv.to(DEV), i32(sel).to(DEV), wd,
+                                     scale, sink=torch.from_numpy(sink).to(DEV), out=poison((n, 8, 64), torch.float32),
+                                     lse=poison((n, 8), torch.float32))
+    out_o, lse_o = orc.sparse_swa_attn(rows, cache, q.numpy(), 0, kv.numpy(), 0, sel, wo, heads=8, dim=64,
+                                       sm_scale=scale, sink=sink)
+    nb, emax, _ = allclose_report(out_d.cpu().numpy(), out_o, 1e-4, 1e-4)
+    assert nb == 0, (nb, emax)
+    assert allclose_report(lse_d.cpu().numpy(), lse_o, 1e-4, 1e-4)[0] == 0

@@ -153,3 +153,38 @@ def test_fp8_window_and_bf16_operands(orc):
     b, _ = orc.sparse_swa_attn(rows, cache, q_bf.float().numpy(), 0, kv_bf.float().numpy(), 0, None, swaf,
                                heads=H, dim=D, sm_scale=0.1, dense=True)
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("shift", [0.0, 40.0])
+def test_sink_is_an_extra_zero_value_key(orc, shift):
+    """A sink of logit sink_h is one more key whose value is the zero vector: torch SDPA over
+    the key set with a zero row appended (its logit set to sink_h through an additive mask)
+    gives the output, and log-sum-exp over the logits together with sink_h gives lse.  With
+    shift 40 every logit is moved 40 up (one extra dimension: 1 in every key, shift/scale in
+    q), so that a sink added without the max shift, or added to the numerator, fails."""
+    rng = np.random.default_rng(46)
+    H, D = 4, 32
+    rows, cache, kv, q, swa = _case(rng, H=H, D=D)
+    n = len(rows["req_of_row"])
+    scale = 0.3
+    kv = np.concatenate([kv, np.ones((kv.shape[0], 1), np.float32)], axis=1)
+    swa = dict(swa, data=np.concatenate([swa["data"], np.ones((swa["data"].shape[0], 1), np.float32)], axis=1))
+    q = np.concatenate([q, np.full((n, H, 1), shift / scale, np.float32)], axis=2)
+    D += 1
+    sink = (rng.standard_normal(H) * 2.0 + shift).astype(np.float32)
+    out, lse = orc.sparse_swa_attn(rows, cache, q, 0, kv, 0, None, swa, heads=H, dim=D, sm_scale=scale, sink=sink,
+                                   dense=True)
+    for i in range(n):
+        keys = _keyset(rows, cache, kv, swa, i)
+        nk = keys.shape[0]
+        aug = np.concatenate([keys, np.zeros((1, D))], axis=0)
+        qt = torch.from_numpy(q[i].astype(np.float64)).reshape(1, H, 1, D)
+        kt = torch.from_numpy(aug).reshape(1, 1, nk + 1, D).expand(1, H, nk + 1, D)
+        bias = torch.zeros(1, H, 1, nk + 1, dtype=torch.float64)
+        bias[0, :, 0, nk] = torch.from_numpy(sink.astype(np.float64))
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, kt, attn_mask=bias, scale=scale)
+        assert np.allclose(out[i], ref[0, :, 0].numpy(), rtol=1e-12, atol=1e-13)
+        logits = scale * (q[i].astype(np.float64) @ keys.T)
+        lref = torch.logsumexp(torch.from_numpy(np.concatenate([logits, sink[:, None].astype(np.float64)], axis=1)),
+                               dim=1).numpy()
+        assert np.allclose(lse[i], lref, rtol=1e-12, atol=1e-12)

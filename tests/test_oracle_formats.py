@@ -9,7 +9,9 @@ groups; the window cache stays FP8).  Pins:
   * E2M1 element rounding against a brute-force nearest search, ties to even code;
   * the shared exponent against its defining property (amax / 2^e in [2^emax, 2^(emax+1))).
 """
+import json
 import math
+import os
 
 import numpy as np
 import pytest
@@ -159,8 +161,14 @@ def test_mx_quant_error_bound(orc):
         assert np.all(np.abs(deq - x)[ok] <= 0.5 * q[ok] + 1e-30)
 
 
-def test_index_entry_is_68_bytes(orc):
-    """[P1] "Mixed precision": an index K entry is 128 x (0.5 + 1/32) = 68 B."""
-    x = np.random.default_rng(1).standard_normal((3, 128)).astype(np.float32)
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "cache_bytes.json")
+
+
+def test_index_entry_bytes_golden(orc):
+    """[P1] "Mixed precision": an index K entry is 128 x (0.5 + 1/32) = 68 B (the page's
+    number, tests/golden/cache_bytes.json); the oracle's MXFP4 quantizer writes exactly
+    that many bytes per 128-d entry."""
+    g = json.load(open(GOLDEN))["index_entry_bytes"]
+    x = np.random.default_rng(1).standard_normal((3, g["dim"])).astype(np.float32)
     codes, scales = orc.mx_quant(orc.E2M1, x)
-    assert codes.shape[1] + scales.shape[1] == 68
+    assert codes.shape[1] + scales.shape[1] == g["bytes"] == 68
