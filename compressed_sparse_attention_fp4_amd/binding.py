@@ -21,8 +21,8 @@ F32, BF16, MXFP4, MXFP8_E4M3 = 0, 1, 2, 3
 OP_TOPK, OP_TOPK_HIER, OP_ATTN = 1, 2, 3
 
 # Every symbol include/csa2.h declares.
-EXPORTS = ["csa2_index_score", "csa2_topk", "csa2_topk_hier", "csa2_sparse_swa_attn", "csa2_replay_tail_layout",
-           "csa2_workspace_size", "csa2_last_error", "csa2_version", "csa2_quant_mx"]
+EXPORTS = ["csa2_index_score", "csa2_topk", "csa2_topk_hier", "csa2_topk_hier_noalloc", "csa2_sparse_swa_attn",
+           "csa2_replay_tail_layout", "csa2_workspace_size", "csa2_last_error", "csa2_version", "csa2_quant_mx"]
 
 
 class Csa2Error(RuntimeError):
@@ -235,6 +235,25 @@ def topk_hier(rows: Rows, cache: Cache, scores: torch.Tensor, k: int, block: int
                               ctypes.c_int64(scores.stride(0)), ctypes.c_int32(k), ctypes.c_int32(block),
                               ctypes.c_int32(max_blocks), _ptr(idx), _ptr(blocks), _ptr(nblocks), _ptr(workspace),
                               ctypes.c_size_t(workspace.numel()), _stream(stream))
+    _check(rc)
+    return idx, blocks, nblocks
+
+
+def topk_hier_noalloc(rows: Rows, cache: Cache, scores: torch.Tensor, k: int, block: int = 8,
+                      max_blocks: int = 2048, out=None, stream=None):
+    """csa2_topk_hier_noalloc: csa2_topk_hier with the library's own per-device scratch (no
+    workspace argument).  out: optional preallocated (idx, blocks, nblocks)."""
+    n = rows.n
+    dev = scores.device
+    if out is None:
+        out = (torch.empty((n, k), dtype=torch.int32, device=dev),
+               torch.empty((n, max_blocks), dtype=torch.int32, device=dev),
+               torch.empty((n,), dtype=torch.int32, device=dev))
+    idx, blocks, nblocks = out
+    rc = lib().csa2_topk_hier_noalloc(ctypes.byref(rows.c()), ctypes.byref(cache.c()), _ptr(scores),
+                                      ctypes.c_int64(scores.stride(0)), ctypes.c_int32(k), ctypes.c_int32(block),
+                                      ctypes.c_int32(max_blocks), _ptr(idx), _ptr(blocks), _ptr(nblocks),
+                                      _stream(stream))
     _check(rc)
     return idx, blocks, nblocks
 

@@ -105,6 +105,39 @@ csa2::PoolArg pool_arg(const csa2_pool* p)
     return csa2::PoolArg{p->blocks, p->nblocks, p->row_map, p->block, p->max_blocks};
 }
 
+// Scratch of csa2_topk_hier_noalloc: one array per device, held until the process ends.
+// Its name is a host-side stand-in for the device copy, so host code never passes it to
+// a kernel: the device address comes from hipGetSymbolAddress, taken once per device
+// with that device current.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {nullptr};
+
+int scratch_address(void** out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(CSA2_E_LAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 64) return fail(CSA2_E_UNSUPPORTED, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(CSA2_E_LAUNCH, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return CSA2_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -217,6 +250,34 @@ int csa2_topk_hier(const csa2_rows* rows, const csa2_cache* cache, const float* 
     return launch_result(csa2::launch_topk_hier(src, k, block, max_blocks, out_idx, out_pool_blocks, out_pool_nblocks,
                                                 workspace, workspace_bytes, static_cast<hipStream_t>(stream)),
                          "csa2_topk_hier");
+}
+
+int csa2_topk_hier_noalloc(const csa2_rows* rows, const csa2_cache* cache, const float* scores,
+                           int64_t score_stride, int32_t k, int32_t block, int32_t max_blocks, int32_t* out_idx,
+                           int32_t* out_pool_blocks, int32_t* out_pool_nblocks, void* stream)
+{
+    int rc;
+    if ((rc = check_rows(rows)) || (rc = check_cache(cache))) return rc;
+    if (!scores || !out_idx || !out_pool_blocks || !out_pool_nblocks)
+        return fail(CSA2_E_ARG, "scores / out_idx / out_pool_blocks / out_pool_nblocks is NULL");
+    if (k < 1 || k > 2048) return fail(CSA2_E_ARG, "k = %d (1..2048)", k);
+    if (block != 8) return fail(CSA2_E_UNSUPPORTED, "block = %d (8 supported)", block);
+    if (max_blocks < 1 || max_blocks > 4096) return fail(CSA2_E_ARG, "max_blocks = %d (1..4096)", max_blocks);
+    if (score_stride < 1) return fail(CSA2_E_ARG, "score_stride = %lld < 1", (long long)score_stride);
+    const size_t need = csa2::topk_hier_workspace(rows->n, score_stride, k, block, max_blocks);
+    if (need > kScratchBytes)
+        return fail(CSA2_E_WORKSPACE,
+                    "csa2_topk_hier_noalloc: %d rows x %lld columns need %zu scratch bytes, more than its %zu; "
+                    "use csa2_topk_hier with a workspace",
+                    rows->n, (long long)score_stride, need, kScratchBytes);
+    if (rows->n == 0) return ok();
+    if ((rc = check_device())) return rc;
+    void* ws = nullptr;
+    if (need > 0 && (rc = scratch_address(&ws))) return rc;
+    csa2::SelSource src{scores, score_stride, rows_arg(rows), cache_arg(cache), pool_arg(nullptr)};
+    return launch_result(csa2::launch_topk_hier(src, k, block, max_blocks, out_idx, out_pool_blocks, out_pool_nblocks,
+                                                ws, need, static_cast<hipStream_t>(stream)),
+                         "csa2_topk_hier_noalloc");
 }
 
 int csa2_sparse_swa_attn(const csa2_rows* rows, const csa2_cache* cache, const void* q, csa2_dtype q_dtype,

@@ -189,6 +189,26 @@ int csa2_topk_hier(const csa2_rows* rows, const csa2_cache* cache, const float* 
                    int32_t* out_pool_nblocks, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * csa2_topk_hier_noalloc -- csa2_topk_hier for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same selection, the same outputs, with its scratch taken from a library-owned
+ * 32 MiB array per device instead of a caller workspace.  Arguments as csa2_topk_hier.
+ *   - Allocates nothing: no hipMalloc / hipFree; the array is static device memory that
+ *     each device holds until the process ends; its address is looked up once per
+ *     device (the first call on it).
+ *   - Sizes whose scratch exceeds 32 MiB (csa2_workspace_size(CSA2_OP_TOPK_HIER, ...) >
+ *     33554432, e.g. more than about 1,000 rows of 65,536 columns) are refused with
+ *     CSA2_E_WORKSPACE before anything is enqueued.
+ *   - Every call on one device shares that device's array: calls that may overlap on one
+ *     device (different streams, or different host threads) race and must be ordered by
+ *     the caller.  Nothing in the array needs to start at zero; each call writes what it
+ *     reads.
+ * ------------------------------------------------------------------------------- */
+int csa2_topk_hier_noalloc(const csa2_rows* rows, const csa2_cache* cache, const float* scores,
+                           int64_t score_stride, int32_t k, int32_t block, int32_t max_blocks, int32_t* out_idx,
+                           int32_t* out_pool_blocks, int32_t* out_pool_nblocks, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * csa2_sparse_swa_attn -- each query row attends, per head, to its selected compressed
  * entries together with its own sliding window, in one softmax ([DAY0] section 1;
  * [MOD] "CSA2": Full, Reindex and Reuse layers all keep their own attention; Reuse

@@ -191,3 +191,17 @@ def test_workspace_grows_with_merge_levels():
     b = B.workspace_size(B.OP_TOPK, 3, 524288, 2048)
     assert 0 < a < b
     assert B.workspace_size(B.OP_TOPK_HIER, 2, 600000, 512, 4096) > 0
+
+
+def test_topk_hier_noalloc_refuses_oversized_scratch():
+    """The allocation-free hierarchy holds at most 32 MiB of scratch per device; a size that
+    needs more is refused before anything touches the device."""
+    L = B.lib()
+    need = B.workspace_size(B.OP_TOPK_HIER, 2048, 65536, 512, 2048)
+    assert need > (32 << 20)
+    rc = L.csa2_topk_hier_noalloc(ctypes.byref(_rows(2048)), ctypes.byref(_cache()), P, ctypes.c_int64(65536),
+                                  ctypes.c_int32(512), ctypes.c_int32(8), ctypes.c_int32(2048), P, P, P, None)
+    assert rc == B.CSA2_E_WORKSPACE and "scratch" in _err()
+    rc = L.csa2_topk_hier_noalloc(ctypes.byref(_rows()), ctypes.byref(_cache()), P, ctypes.c_int64(1024),
+                                  ctypes.c_int32(512), ctypes.c_int32(16), ctypes.c_int32(2048), P, P, P, None)
+    assert rc == B.CSA2_E_UNSUPPORTED

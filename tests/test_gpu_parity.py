@@ -213,7 +213,7 @@ def _topk_inputs(seed, R_list, stride, ties=None):
         v = (rng.standard_normal(R) * 30 + 150).astype(np.float32)
         if ties is not None:
             v = np.floor(v / ties).astype(np.float32) * ties
-        scores[i, :R] = v
+        scores[i, :min(R, stride)] = v[:stride]
     return rows, cache, scores
 
 
