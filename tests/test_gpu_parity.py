@@ -436,7 +436,8 @@ def _check_bf16_attn(got, ref, lse_g, lse_r):
 
 
 @pytest.mark.parametrize("H,k,swa_fp8,tail", [(64, 512, True, False), (16, 64, True, True), (32, 512, False, False),
-                                              (64, 0, True, False), (16, 2048, True, False)])
+                                              (64, 0, True, False), (16, 2048, True, False), (128, 512, True, True),
+                                              (80, 96, False, True)])
 def test_attn_bf16(orc, H, k, swa_fp8, tail):
     say("case: sparse+window attention bf16 H=%d k=%d fp8=%s tail=%s" % (H, k, swa_fp8, tail))
     rows, cache, q, kv, win, swa_raw, sel = _attn_bf16_case(30 + H + k, (2600, 700), 2 if k != 2048 else 1, H, k, 6,
