@@ -157,6 +157,54 @@ static double mx_elem(int fmt, const uint8_t* data, const uint8_t* scales, int64
 }
 
 /* ------------------------------------------------------------------------- */
+/* Main KV storage format ([P1] "Mixed precision", the table of per-entry bytes): */
+/* E2M1 elements with one E4M3 scale per 16 channels and no second-level global   */
+/* scale (the NVFP4 block layout without its tensor-wide scale); 512 channels make */
+/* 256 code bytes + 32 scale bytes = 288 B per entry.  Element 2i is the low      */
+/* nibble.  The pages fix the format, not the rounding; the reading taken is the  */
+/* NVFP4 rule with the global scale removed: s = E4M3 nearest-even rounding of    */
+/* amax / 6 (saturating at 448); element = E2M1 nearest-even rounding of |x| / s  */
+/* (saturating at 6) with the sign bit of x; a block whose s rounds to zero       */
+/* stores zero magnitudes.                                                        */
+/* ------------------------------------------------------------------------- */
+void orc_fp4s16_quant_block(const double* x, uint8_t* codes, uint8_t* scale)
+{
+    double amax = 0.0;
+    for (int i = 0; i < 16; i++)
+        if (fabs(x[i]) > amax) amax = fabs(x[i]);
+    double s = round_to_format(amax / 6.0, 3, -6, 448.0);
+    *scale = (uint8_t)encode_magnitude(s, ORC_E4M3);
+    for (int i = 0; i < 16; i++) {
+        int c = 0;
+        if (s > 0.0) c = encode_magnitude(round_to_format(fabs(x[i]) / s, 1, 0, 6.0), ORC_E2M1);
+        if (signbit(x[i])) c |= 8;
+        codes[i] = (uint8_t)c;
+    }
+}
+
+/* Quantize nblocks consecutive 16-element blocks of x: 8 packed code bytes and one
+ * E4M3 scale byte per block. */
+void orc_fp4s16_quant(const float* x, int64_t nblocks, uint8_t* out, uint8_t* scales)
+{
+    for (int64_t b = 0; b < nblocks; b++) {
+        double xb[16];
+        uint8_t codes[16];
+        for (int i = 0; i < 16; i++) xb[i] = x[b * 16 + i];
+        orc_fp4s16_quant_block(xb, codes, &scales[b]);
+        for (int i = 0; i < 8; i++) out[b * 8 + i] = (uint8_t)(codes[2 * i] | (codes[2 * i + 1] << 4));
+    }
+}
+
+/* Value of element i of a row in the main KV format: E2M1 code times its block's
+ * E4M3 scale. */
+static double fp4s16_elem(const uint8_t* data, const uint8_t* scales, int64_t row, int dim, int i)
+{
+    uint8_t byte = data[row * (dim / 2) + i / 2];
+    int code = (i & 1) ? (byte >> 4) : (byte & 15);
+    return orc_e2m1_value(code) * orc_e4m3_value(scales[row * (dim / 16) + i / 16]);
+}
+
+/* ------------------------------------------------------------------------- */
 /* Reachability: [P1] "CSA2" (non-overlapping compression; only complete groups   */
 /* are entries) and "Mixed precision" (incomplete groups are separate state);    */
 /* causal visibility "position i sees nothing later than i" ([P1] "CED").         */
@@ -446,7 +494,8 @@ void orc_topk_hier(int n, const int32_t* req_of_row, const int32_t* pos_of_row, 
 /* sets, computed in double.  The window of query p is [max(lo, p-W+1), p] where */
 /* lo is the replay lower bound ([P2] section 2.3) and the first cached window   */
 /* position.  A sink, when given, adds exp(sink_h - max) to the denominator.     */
-/* Data types: 0 = f32, 1 = bf16 (raw 16-bit patterns), 3 = MXFP8 E4M3 (+E8M0).  */
+/* Data types: 0 = f32, 1 = bf16 (raw 16-bit patterns), 3 = MXFP8 E4M3 (+E8M0),  */
+/* 4 = the main KV storage format (E2M1 + one E4M3 scale per 16, defined above).  */
 /* ------------------------------------------------------------------------- */
 static double load_val(const void* base, int dt, const uint8_t* scales, int64_t row, int dim, int i)
 {
@@ -457,6 +506,7 @@ static double load_val(const void* base, int dt, const uint8_t* scales, int64_t 
         memcpy(&f, &bits, 4);
         return f;
     }
+    if (dt == 4) return fp4s16_elem((const uint8_t*)base, scales, row, dim, i);
     return mx_elem(ORC_E4M3, (const uint8_t*)base, scales, row, dim, i);
 }
 
@@ -492,7 +542,7 @@ static void attend_set(const double* qh, int D, const double* keys, int64_t nk, 
 /* Gathers the key/value set of one row: selected entries (if sel != NULL) or
  * all reachable entries (dense mode), then the window rows. */
 static int64_t gather_row(int row, int r, int p, int64_t R, int D, const void* kv, int kv_dt,
-                          const int64_t* row_start, const int32_t* sel, int k, const void* swa, int swa_dt,
+                          const uint8_t* kv_scale, const int64_t* row_start, const int32_t* sel, int k, const void* swa, int swa_dt,
                           const uint8_t* swa_scale, const int64_t* swa_row_start, const int32_t* swa_pos_start,
                           int window, int lo, double* keys)
 {
@@ -501,12 +551,12 @@ static int64_t gather_row(int row, int r, int p, int64_t R, int D, const void* k
         for (int i = 0; i < k; i++) {
             int32_t j = sel[i];
             if (j < 0) continue;
-            for (int d = 0; d < D; d++) keys[nk * D + d] = load_val(kv, kv_dt, NULL, row_start[r] + j, D, d);
+            for (int d = 0; d < D; d++) keys[nk * D + d] = load_val(kv, kv_dt, kv_scale, row_start[r] + j, D, d);
             nk++;
         }
     } else {
         for (int64_t j = 0; j < R; j++) {
-            for (int d = 0; d < D; d++) keys[nk * D + d] = load_val(kv, kv_dt, NULL, row_start[r] + j, D, d);
+            for (int d = 0; d < D; d++) keys[nk * D + d] = load_val(kv, kv_dt, kv_scale, row_start[r] + j, D, d);
             nk++;
         }
     }
@@ -524,7 +574,8 @@ static int64_t gather_row(int row, int r, int p, int64_t R, int D, const void* k
 
 static void attn_common(int dense, int n, const int32_t* req_of_row, const int32_t* pos_of_row,
                         const int32_t* win_lo, int m, const int32_t* n_entries, const int64_t* row_start,
-                        const void* q, int q_dt, int H, int D, const void* kv, int kv_dt, const int32_t* sel_idx,
+                        const void* q, int q_dt, int H, int D, const void* kv, int kv_dt,
+                        const uint8_t* kv_scale, const int32_t* sel_idx,
                         int k, int64_t sel_stride, const int32_t* sel_row_map, const void* swa, int swa_dt,
                         const uint8_t* swa_scale, const int64_t* swa_row_start, const int32_t* swa_pos_start,
                         int window, double sm_scale, const float* sink, double* out, double* lse)
@@ -539,7 +590,7 @@ static void attn_common(int dense, int n, const int32_t* req_of_row, const int32
         double* keys = (double*)malloc(sizeof(double) * (size_t)(cap > 0 ? cap : 1) * D);
         const int32_t* sel = NULL;
         if (!dense) sel = sel_idx + (int64_t)(sel_row_map ? sel_row_map[row] : row) * sel_stride;
-        int64_t nk = gather_row(row, r, p, R, D, kv, kv_dt, row_start, sel, k, swa, swa_dt, swa_scale,
+        int64_t nk = gather_row(row, r, p, R, D, kv, kv_dt, kv_scale, row_start, sel, k, swa, swa_dt, swa_scale,
                                 swa_row_start, swa_pos_start, window, lo, keys);
         double* qh = (double*)malloc(sizeof(double) * D);
         for (int h = 0; h < H; h++) {
@@ -555,25 +606,25 @@ static void attn_common(int dense, int n, const int32_t* req_of_row, const int32
 
 void orc_sparse_swa_attn(int n, const int32_t* req_of_row, const int32_t* pos_of_row, const int32_t* win_lo, int m,
                          const int32_t* n_entries, const int64_t* row_start, const void* q, int q_dt, int H, int D,
-                         const void* kv, int kv_dt, const int32_t* sel_idx, int k, int64_t sel_stride,
-                         const int32_t* sel_row_map, const void* swa, int swa_dt, const uint8_t* swa_scale,
+                         const void* kv, int kv_dt, const uint8_t* kv_scale, const int32_t* sel_idx, int k,
+                         int64_t sel_stride, const int32_t* sel_row_map, const void* swa, int swa_dt, const uint8_t* swa_scale,
                          const int64_t* swa_row_start, const int32_t* swa_pos_start, int window, double sm_scale,
                          const float* sink, double* out, double* lse)
 {
-    attn_common(0, n, req_of_row, pos_of_row, win_lo, m, n_entries, row_start, q, q_dt, H, D, kv, kv_dt, sel_idx,
-                k, sel_stride, sel_row_map, swa, swa_dt, swa_scale, swa_row_start, swa_pos_start, window, sm_scale,
+    attn_common(0, n, req_of_row, pos_of_row, win_lo, m, n_entries, row_start, q, q_dt, H, D, kv, kv_dt, kv_scale,
+                sel_idx, k, sel_stride, sel_row_map, swa, swa_dt, swa_scale, swa_row_start, swa_pos_start, window, sm_scale,
                 sink, out, lse);
 }
 
 /* Dense brute force: every reachable compressed entry plus the window, no index set. */
 void orc_dense_attn(int n, const int32_t* req_of_row, const int32_t* pos_of_row, const int32_t* win_lo, int m,
                     const int32_t* n_entries, const int64_t* row_start, const void* q, int q_dt, int H, int D,
-                    const void* kv, int kv_dt, const void* swa, int swa_dt, const uint8_t* swa_scale,
-                    const int64_t* swa_row_start, const int32_t* swa_pos_start, int window, double sm_scale,
+                    const void* kv, int kv_dt, const uint8_t* kv_scale, const void* swa, int swa_dt,
+                    const uint8_t* swa_scale, const int64_t* swa_row_start, const int32_t* swa_pos_start, int window, double sm_scale,
                     const float* sink, double* out, double* lse)
 {
-    attn_common(1, n, req_of_row, pos_of_row, win_lo, m, n_entries, row_start, q, q_dt, H, D, kv, kv_dt, NULL, 0, 0,
-                NULL, swa, swa_dt, swa_scale, swa_row_start, swa_pos_start, window, sm_scale, sink, out, lse);
+    attn_common(1, n, req_of_row, pos_of_row, win_lo, m, n_entries, row_start, q, q_dt, H, D, kv, kv_dt, kv_scale,
+                NULL, 0, 0, NULL, swa, swa_dt, swa_scale, swa_row_start, swa_pos_start, window, sm_scale, sink, out, lse);
 }
 
 /* ------------------------------------------------------------------------- */

@@ -23,7 +23,7 @@ _lib = None
 E2M1 = 0
 E4M3 = 1
 # attention data-type codes understood by the C oracle
-DT_F32, DT_BF16, DT_MXFP8 = 0, 1, 3
+DT_F32, DT_BF16, DT_MXFP8, DT_FP4S16 = 0, 1, 3, 4
 
 
 def build(force: bool = False) -> str:
@@ -116,6 +116,30 @@ def mx_dequant(fmt: int, codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     v = table[c]
     s = np.array([e8m0_value(i) for i in range(256)])[scales]
     return v * np.repeat(s, 32, axis=-1)
+
+
+def fp4s16_quant(x: np.ndarray):
+    """Main KV storage format ([P1] "Mixed precision", per-entry bytes table): E2M1
+    elements, one E4M3 scale per 16 channels, no global scale.  Rounding reading:
+    s = RNE_E4M3(amax / 6), element = RNE_E2M1(|x| / s) with x's sign bit.
+
+    Returns (codes packed two per byte, element 2i low nibble; scales, one E4M3 byte
+    per 16 elements)."""
+    x = _f32(x)
+    assert x.shape[-1] % 16 == 0
+    d = x.shape[-1]
+    codes = np.empty(x.shape[:-1] + (d // 2,), dtype=np.uint8)
+    scales = np.empty(x.shape[:-1] + (d // 16,), dtype=np.uint8)
+    _load().orc_fp4s16_quant(_p(x), ctypes.c_int64(x.size // 16), _p(codes), _p(scales))
+    return codes, scales
+
+
+def fp4s16_dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Value of every element of a main-KV-format tensor, in float64."""
+    c = np.stack([codes & 15, codes >> 4], axis=-1).reshape(codes.shape[:-1] + (codes.shape[-1] * 2,))
+    v = np.array([e2m1_value(i) for i in range(16)])[c]
+    s = np.array([e4m3_value(i) for i in range(256)])[scales]
+    return v * np.repeat(s, 16, axis=-1)
 
 
 # ----------------------------------------------------------------------- reachability
@@ -217,10 +241,12 @@ def _attn_operand(x, dt):
 
 
 def sparse_swa_attn(rows, cache, q, q_dt, kv, kv_dt, sel_idx, swa, *, heads, dim, sm_scale,
-                    sel_row_map=None, sink=None, dense=False):
+                    sel_row_map=None, sink=None, dense=False, kv_scale=None):
     """Joint softmax over selected compressed entries and the row's window, in float64.
 
-    q: [n, heads, dim] (f32 values or bf16 bit patterns); kv: [rows, dim];
+    q: [n, heads, dim] (f32 values or bf16 bit patterns); kv: [rows, dim] (f32, bf16
+    bits) or, with kv_dt = DT_FP4S16, packed codes [rows, dim / 2] with kv_scale
+    [rows, dim / 16];
     sel_idx: [*, k] int32 (-1 skipped); swa = dict(data, dtype, scale, row_start,
     pos_start, window).  Returns (out float64 [n, heads, dim], lse float64 [n, heads]).
     dense=True ignores sel_idx and attends to every reachable entry."""
@@ -236,9 +262,11 @@ def sparse_swa_attn(rows, cache, q, q_dt, kv, kv_dt, sel_idx, swa, *, heads, dim
     out = np.empty((n, heads, dim), dtype=np.float64)
     lse = np.empty((n, heads), dtype=np.float64)
     sk = _f32(sink)
+    ks = None if kv_scale is None else np.ascontiguousarray(kv_scale, dtype=np.uint8)
+    assert (kv_dt == DT_FP4S16) == (ks is not None), "kv_scale goes with the main KV storage format only"
     common = [ctypes.c_int(n), _p(req), _p(pos), _p(lo), ctypes.c_int(cache["ratio_m"]),
               _p(_i32(cache["n_entries"])), _p(_i64(cache["row_start"])), _p(qa), ctypes.c_int(q_dt),
-              ctypes.c_int(heads), ctypes.c_int(dim), _p(kva), ctypes.c_int(kv_dt)]
+              ctypes.c_int(heads), ctypes.c_int(dim), _p(kva), ctypes.c_int(kv_dt), _p(ks)]
     swa_args = [_p(sw), ctypes.c_int(swa["dtype"]), _p(ss), _p(_i64(swa["row_start"])),
                 _p(_i32(swa["pos_start"])), ctypes.c_int(swa["window"]), ctypes.c_double(sm_scale), _p(sk),
                 _p(out), _p(lse)]

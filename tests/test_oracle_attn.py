@@ -188,3 +188,33 @@ def test_sink_is_an_extra_zero_value_key(orc, shift):
         lref = torch.logsumexp(torch.from_numpy(np.concatenate([logits, sink[:, None].astype(np.float64)], axis=1)),
                                dim=1).numpy()
         assert np.allclose(lse[i], lref, rtol=1e-12, atol=1e-12)
+
+
+def test_fp4_main_kv_attends_like_its_dequantized_values(orc):
+    """Main KV in its storage format ("DeepSeek V4.1 Flash modeling", section "Mixed
+    precision": dequantized before attention): the oracle's result with FP4 entries is
+    the same as with the fp32 values that the format's decode gives (exactly: each
+    decoded value is an E2M1 value times an E4M3 scale, representable in fp32), and
+    both match torch's SDPA on the dequantized key sets."""
+    rng = np.random.default_rng(47)
+    H, D = 4, 32
+    rows, cache, kv, q, swa = _case(rng, H=H, D=D)
+    codes, scales = orc.fp4s16_quant(kv)
+    deq = orc.fp4s16_dequant(codes, scales)
+    assert np.array_equal(deq.astype(np.float32).astype(np.float64), deq)
+    n = len(rows["req_of_row"])
+    sel = np.full((n, 6), -1, np.int32)
+    for i in range(n):
+        r, p = int(rows["req_of_row"][i]), int(rows["pos_of_row"][i])
+        R = min((p + 1) // 2, int(cache["n_entries"][r]))
+        sel[i, :min(R, 6)] = rng.permutation(R)[:6]
+    a, la = orc.sparse_swa_attn(rows, cache, q, 0, codes, orc.DT_FP4S16, sel, swa, heads=H, dim=D, sm_scale=0.2,
+                                kv_scale=scales)
+    b, lb = orc.sparse_swa_attn(rows, cache, q, 0, deq.astype(np.float32), 0, sel, swa, heads=H, dim=D, sm_scale=0.2)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+    for i in range(n):
+        keys = _keyset(rows, cache, deq, swa, i, sel[i])
+        assert np.allclose(a[i], _sdpa(q[i].astype(np.float64), keys, 0.2), rtol=1e-12, atol=1e-12)
+    # and the FP4 result differs from the unquantized one (the format is lossy)
+    c, _ = orc.sparse_swa_attn(rows, cache, q, 0, kv, 0, sel, swa, heads=H, dim=D, sm_scale=0.2)
+    assert not np.allclose(a, c, atol=1e-6)
