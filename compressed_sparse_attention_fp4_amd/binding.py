@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcsa2.so")
 
 CSA2_OK, CSA2_E_ARG, CSA2_E_UNSUPPORTED, CSA2_E_WORKSPACE, CSA2_E_LAUNCH = 0, 1, 2, 3, 4
-F32, BF16, MXFP4, MXFP8_E4M3 = 0, 1, 2, 3
+F32, BF16, MXFP4, MXFP8_E4M3, FP4_S16 = 0, 1, 2, 3, 4
 OP_TOPK, OP_TOPK_HIER, OP_ATTN = 1, 2, 3
 
 # Every symbol include/csa2.h declares.
@@ -261,9 +261,11 @@ def topk_hier_noalloc(rows: Rows, cache: Cache, scores: torch.Tensor, k: int, bl
 def sparse_swa_attn(rows: Rows, cache: Cache, q: torch.Tensor, kv: torch.Tensor, sel_idx: Optional[torch.Tensor],
                     window: Window, sm_scale: float, sel_row_map: Optional[torch.Tensor] = None,
                     sink: Optional[torch.Tensor] = None, want_lse: bool = False, out: Optional[torch.Tensor] = None,
-                    lse: Optional[torch.Tensor] = None, stream=None):
+                    lse: Optional[torch.Tensor] = None, kv_scale: Optional[torch.Tensor] = None, stream=None):
     """csa2_sparse_swa_attn: out [n, heads, dim] (q's dtype), and lse [n, heads] if asked
-    (or given: a preallocated lse implies want_lse)."""
+    (or given: a preallocated lse implies want_lse).  kv is float32 / bfloat16 [rows, dim],
+    or with kv_scale the FP4 main KV format: uint8 codes [rows, dim / 2] and E4M3 scales
+    uint8 [rows, dim / 16]."""
     n, heads, dim = q.shape
     if out is None:
         out = torch.empty_like(q)
@@ -274,7 +276,8 @@ def sparse_swa_attn(rows: Rows, cache: Cache, q: torch.Tensor, kv: torch.Tensor,
     sel_stride = 0 if sel_idx is None else sel_idx.stride(0)
     rc = lib().csa2_sparse_swa_attn(ctypes.byref(rows.c()), ctypes.byref(cache.c()), _ptr(q),
                                     ctypes.c_int(_dtype_code(q)), ctypes.c_int32(heads), ctypes.c_int32(dim), _ptr(kv),
-                                    ctypes.c_int(_dtype_code(kv)), _ptr(sel_idx), ctypes.c_int32(k),
+                                    ctypes.c_int(FP4_S16 if kv_scale is not None else _dtype_code(kv)),
+                                    _ptr(kv_scale), _ptr(sel_idx), ctypes.c_int32(k),
                                     ctypes.c_int64(sel_stride), _ptr(sel_row_map), ctypes.byref(window.c()),
                                     ctypes.c_float(sm_scale), _ptr(sink), _ptr(out), ctypes.c_int(_dtype_code(out)),
                                     _ptr(lse), None, ctypes.c_size_t(0), _stream(stream))
@@ -306,12 +309,15 @@ def replay_tail_layout(ext_len: torch.Tensor, seq_len: torch.Tensor, budget: int
 
 
 def quant_mx(fmt: int, x: torch.Tensor, stream=None):
-    """csa2_quant_mx over the last axis of x (multiple of 32): (codes uint8, scales uint8)."""
-    assert x.shape[-1] % 32 == 0
+    """csa2_quant_mx over the last axis of x: (codes uint8, scales uint8).  MXFP4 / MXFP8_E4M3
+    take 32-element blocks; FP4_S16 (the main KV format) takes 16-element blocks."""
+    blk = 16 if fmt == FP4_S16 else 32
+    assert x.shape[-1] % blk == 0
     d = x.shape[-1]
-    nblocks = x.numel() // 32
-    codes = torch.empty(x.shape[:-1] + ((d // 2) if fmt == MXFP4 else d,), dtype=torch.uint8, device=x.device)
-    scales = torch.empty(x.shape[:-1] + (d // 32,), dtype=torch.uint8, device=x.device)
+    nblocks = x.numel() // blk
+    codes = torch.empty(x.shape[:-1] + ((d // 2) if fmt in (MXFP4, FP4_S16) else d,), dtype=torch.uint8,
+                        device=x.device)
+    scales = torch.empty(x.shape[:-1] + (d // blk,), dtype=torch.uint8, device=x.device)
     rc = lib().csa2_quant_mx(ctypes.c_int(fmt), _ptr(x), ctypes.c_int(_dtype_code(x)), ctypes.c_int64(nblocks),
                              _ptr(codes), _ptr(scales), _stream(stream))
     _check(rc)

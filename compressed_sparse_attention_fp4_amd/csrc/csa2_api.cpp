@@ -281,10 +281,10 @@ int csa2_topk_hier_noalloc(const csa2_rows* rows, const csa2_cache* cache, const
 }
 
 int csa2_sparse_swa_attn(const csa2_rows* rows, const csa2_cache* cache, const void* q, csa2_dtype q_dtype,
-                         int32_t heads, int32_t dim, const void* kv, csa2_dtype kv_dtype, const int32_t* sel_idx,
-                         int32_t k, int64_t sel_stride, const int32_t* sel_row_map, const csa2_swa* swa,
-                         float sm_scale, const float* sink, void* out, csa2_dtype out_dtype, float* lse,
-                         void* workspace, size_t workspace_bytes, void* stream)
+                         int32_t heads, int32_t dim, const void* kv, csa2_dtype kv_dtype, const uint8_t* kv_scale,
+                         const int32_t* sel_idx, int32_t k, int64_t sel_stride, const int32_t* sel_row_map,
+                         const csa2_swa* swa, float sm_scale, const float* sink, void* out, csa2_dtype out_dtype,
+                         float* lse, void* workspace, size_t workspace_bytes, void* stream)
 {
     (void)workspace;
     (void)workspace_bytes;
@@ -299,8 +299,11 @@ int csa2_sparse_swa_attn(const csa2_rows* rows, const csa2_cache* cache, const v
     if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return fail(CSA2_E_ARG, "sm_scale must be positive and finite");
     if (heads < 1 || dim < 1) return fail(CSA2_E_ARG, "heads / dim < 1");
     const bool f32 = q_dtype == CSA2_F32 && kv_dtype == CSA2_F32 && swa->dtype == CSA2_F32 && out_dtype == CSA2_F32;
-    const bool bf = q_dtype == CSA2_BF16 && kv_dtype == CSA2_BF16 &&
+    const bool kv_fp4 = kv_dtype == CSA2_FP4_S16;
+    const bool bf = q_dtype == CSA2_BF16 && (kv_dtype == CSA2_BF16 || kv_fp4) &&
                     (swa->dtype == CSA2_MXFP8_E4M3 || swa->dtype == CSA2_BF16) && out_dtype == CSA2_BF16;
+    if (kv_fp4 != (kv_scale != nullptr))
+        return fail(CSA2_E_ARG, kv_fp4 ? "FP4_S16 kv without kv_scale" : "kv_scale given for a kv dtype without scales");
     if (f32) {
         if (dim > 256) return fail(CSA2_E_UNSUPPORTED, "F32 attention: dim %d > 256", dim);
         if (heads > 1024) return fail(CSA2_E_UNSUPPORTED, "F32 attention: heads %d > 1024", heads);
@@ -309,8 +312,9 @@ int csa2_sparse_swa_attn(const csa2_rows* rows, const csa2_cache* cache, const v
         if (heads % 16 || heads > 1024) return fail(CSA2_E_UNSUPPORTED, "BF16 attention: heads %d (multiple of 16)", heads);
         if (swa->dtype == CSA2_MXFP8_E4M3 && !swa->scale) return fail(CSA2_E_ARG, "MXFP8 window without scales");
         if (misaligned(q, 16) || misaligned(kv, 16) || misaligned(out, 16) || misaligned(swa->data, 16) ||
-            (swa->scale && misaligned(swa->scale, 16)))
-            return fail(CSA2_E_ARG, "q / kv / out / swa->data / swa->scale must start on a 16-byte boundary");
+            (swa->scale && misaligned(swa->scale, 16)) || (kv_scale && misaligned(kv_scale, 16)))
+            return fail(CSA2_E_ARG,
+                        "q / kv / kv_scale / out / swa->data / swa->scale must start on a 16-byte boundary");
     } else {
         return fail(CSA2_E_UNSUPPORTED, "attention dtypes (q %d, kv %d, window %d, out %d)", (int)q_dtype,
                     (int)kv_dtype, (int)swa->dtype, (int)out_dtype);
@@ -325,8 +329,8 @@ int csa2_sparse_swa_attn(const csa2_rows* rows, const csa2_cache* cache, const v
                                                    sel_row_map, sa, sm_scale, sink, static_cast<float*>(out), lse, s),
                              "csa2_sparse_swa_attn");
     return launch_result(csa2::launch_attn_bf16(rows_arg(rows), cache_arg(cache), static_cast<const uint16_t*>(q), heads,
-                                                static_cast<const uint16_t*>(kv), sel_idx, k, sel_stride, sel_row_map,
-                                                sa, sm_scale, sink, static_cast<uint16_t*>(out), lse, s),
+                                                kv, kv_scale, sel_idx, k, sel_stride, sel_row_map, sa, sm_scale, sink,
+                                                static_cast<uint16_t*>(out), lse, s),
                          "csa2_sparse_swa_attn");
 }
 
@@ -353,7 +357,8 @@ int csa2_replay_tail_layout(int32_t nreq, const int32_t* ext_len, const int32_t*
 int csa2_quant_mx(csa2_dtype fmt, const void* x, csa2_dtype x_dtype, int64_t nblocks, uint8_t* codes,
                   uint8_t* scales, void* stream)
 {
-    if (fmt != CSA2_MXFP4 && fmt != CSA2_MXFP8_E4M3) return fail(CSA2_E_UNSUPPORTED, "fmt %d", (int)fmt);
+    if (fmt != CSA2_MXFP4 && fmt != CSA2_MXFP8_E4M3 && fmt != CSA2_FP4_S16)
+        return fail(CSA2_E_UNSUPPORTED, "fmt %d", (int)fmt);
     if (x_dtype != CSA2_F32 && x_dtype != CSA2_BF16) return fail(CSA2_E_UNSUPPORTED, "x_dtype %d", (int)x_dtype);
     if (nblocks < 0) return fail(CSA2_E_ARG, "nblocks < 0");
     if (nblocks > 0 && (!x || !codes || !scales)) return fail(CSA2_E_ARG, "x / codes / scales is NULL");
@@ -361,8 +366,11 @@ int csa2_quant_mx(csa2_dtype fmt, const void* x, csa2_dtype x_dtype, int64_t nbl
     if (nblocks == 0) return ok();
     int rc;
     if ((rc = check_device())) return rc;
-    return launch_result(csa2::launch_quant_mx(fmt == CSA2_MXFP4, x_dtype == CSA2_BF16, x, nblocks, codes, scales,
-                                               static_cast<hipStream_t>(stream)),
+    const bool bf16_in = x_dtype == CSA2_BF16;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (fmt == CSA2_FP4_S16)
+        return launch_result(csa2::launch_quant_fp4s16(bf16_in, x, nblocks, codes, scales, s), "csa2_quant_mx");
+    return launch_result(csa2::launch_quant_mx(fmt == CSA2_MXFP4, bf16_in, x, nblocks, codes, scales, s),
                          "csa2_quant_mx");
 }
 

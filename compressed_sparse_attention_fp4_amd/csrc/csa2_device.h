@@ -74,6 +74,31 @@ __device__ __forceinline__ uint32_t e4m3_code(float y)
 
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
+// Value of a positive finite E4M3 ("fn") code c < 127: (8 + m) 2^(e-10) for a biased
+// exponent e > 0, m 2^-9 below.
+__device__ __forceinline__ float e4m3_value(uint32_t c)
+{
+    const uint32_t e = c >> 3, m = c & 7u;
+    return e == 0 ? (float)m * 0.001953125f : __builtin_ldexpf((float)(8u + m), (int)e - 10);
+}
+
+// E2M1 magnitude code of a / s for a >= 0 and an E4M3 scale s > 0, without dividing:
+// a is compared with the grid midpoints times s.  Those products have at most 7
+// significant bits and lie in fp32's normal range, so every comparison is exact and the
+// decision is the one the real quotient gives (ties to the even code, saturating at 6).
+__device__ __forceinline__ uint32_t e2m1_code_scaled(float a, float s)
+{
+    uint32_t c = 0;
+    c = (a > 0.25f * s) ? 1u : c;
+    c = (a >= 0.75f * s) ? 2u : c;
+    c = (a > 1.25f * s) ? 3u : c;
+    c = (a >= 1.75f * s) ? 4u : c;
+    c = (a > 2.5f * s) ? 5u : c;
+    c = (a >= 3.5f * s) ? 6u : c;
+    c = (a > 5.0f * s) ? 7u : c;
+    return c;
+}
+
 // Quantize one 32-element block to MXFP4: 16 packed bytes (element 2i in the low
 // nibble) returned as 4 dwords, and the E8M0 byte.  The sign bit follows x.
 __device__ __forceinline__ void quant_block_e2m1(const float* x, uint32_t out[4], uint32_t* scale_byte)

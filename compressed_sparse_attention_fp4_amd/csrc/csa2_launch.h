@@ -35,6 +35,9 @@ hipError_t launch_replay_tail_layout(int nreq, const int32_t* ext_len, const int
 
 hipError_t launch_quant_mx(bool fp4, bool bf16_in, const void* x, int64_t nblocks, uint8_t* codes,
                            uint8_t* scales, hipStream_t stream);
+// Main KV storage format: 16-element blocks, E2M1 codes + one E4M3 scale per block.
+hipError_t launch_quant_fp4s16(bool bf16_in, const void* x, int64_t nblocks, uint8_t* codes, uint8_t* scales,
+                               hipStream_t stream);
 
 // Index scores.  MXFP4 path: q bf16 [n][heads][128]; F32 path: q, keys fp32.
 hipError_t launch_index_score_mxfp4(const RowsArg& rows, const CacheArg& cache, const uint16_t* q, int heads,
@@ -75,8 +78,9 @@ hipError_t launch_attn_f32(const RowsArg& rows, const CacheArg& cache, const flo
                            const float* kv, const int32_t* sel, int k, int64_t sel_stride, const int32_t* sel_row_map,
                            const SwaArg& swa, float sm_scale, const float* sink, float* out, float* lse,
                            hipStream_t stream);
+// kv: bf16 [rows][512] (kv_scale null) or FP4_S16 codes [rows][256] with E4M3 scales [rows][32].
 hipError_t launch_attn_bf16(const RowsArg& rows, const CacheArg& cache, const uint16_t* q, int heads,
-                            const uint16_t* kv, const int32_t* sel, int k, int64_t sel_stride,
+                            const void* kv, const uint8_t* kv_scale, const int32_t* sel, int k, int64_t sel_stride,
                             const int32_t* sel_row_map, const SwaArg& swa, float sm_scale, const float* sink,
                             uint16_t* out, float* lse, hipStream_t stream);
 

@@ -121,7 +121,11 @@ __global__ __launch_bounds__(256) void k_attn_f32(RowsArg rows, CacheArg cache, 
 // computes on one tile, the next one is on its way (selected and bf16 window rows by
 // direct global-to-LDS copies with scalar row addresses, one 1 KiB row per instruction;
 // FP8 window rows are loaded into registers a tile ahead and dequantized to bf16 by the
-// scaled conversion: E4M3 times a power of two is exact in bf16).
+// scaled conversion: E4M3 times a power of two is exact in bf16).  Main KV in the FP4
+// storage format ("DeepSeek V4.1 Flash modeling", section "Mixed precision": dequantized
+// before attention) takes the register route too: E2M1 times its E4M3 block scale has
+// at most 6 significant bits, so the decoded bf16 tile is exact and the MFMAs see the
+// same operands as for a bf16 cache holding the decoded values.
 //   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16, 16 steps over the 512 dims: A = K rows
 //     from LDS (lane (g, c) holds key c, dims [32s+8g, +8)), B = Q^T in registers.  The
 //     next tile's K operand is read while this tile's P V products run.
@@ -193,6 +197,7 @@ __device__ __forceinline__ float vmax(float a, float b)
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // 8 FP8 E4M3 codes times 2^(e - 127) to bf16 (exact: 3 mantissa bits fit in bf16's 7).
 // The scaled conversion takes the E8M0 exponent as the exponent field of an fp32 scale.
@@ -207,8 +212,24 @@ __device__ __forceinline__ uint4 fp8x8_to_bf16x8_e(uint2 u, uint32_t e)
                  __builtin_bit_cast(uint32_t, d)};
 }
 
+// 8 E2M1 codes (one dword; element 2i in the low nibble of byte i) times the block scale s
+// to bf16.  The fp32 products are exact, and so is their bf16 rounding.
+__device__ __forceinline__ uint4 fp4x8_to_bf16x8(uint32_t w, float s)
+{
+    const f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    const f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    const f32x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    const f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    auto pack = [s](f32x2 f) {
+        return __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)(f[0] * s), (__bf16)(f[1] * s)});
+    };
+    return uint4{pack(f0), pack(f1), pack(f2), pack(f3)};
+}
+
+template <bool kKvFp4>
 __global__ __launch_bounds__(256) void k_attn_bf16(RowsArg rows, CacheArg cache, const uint16_t* __restrict__ q,
-                                                   int H, int nhg, const uint16_t* __restrict__ kv,
+                                                   int H, int nhg, const void* __restrict__ kv,
+                                                   const uint8_t* __restrict__ kv_scale,
                                                    const int32_t* __restrict__ sel, int k, int64_t sel_stride,
                                                    const int32_t* __restrict__ sel_row_map, SwaArg swa,
                                                    float sm_scale, const float* __restrict__ sink,
@@ -308,10 +329,8 @@ __global__ __launch_bounds__(256) void k_attn_bf16(RowsArg rows, CacheArg cache,
     const uint32_t voff = 16 * lane;
     // Scalar row addresses: row j of the request's main KV (selected) or window row wi
     // (bf16 window), less 1072 q for the q-th key of a group of 4.
-    const uint64_t kv_r = reinterpret_cast<uint64_t>(kv + rk.kv0 * kAttnD);
+    const uint64_t kv_r = reinterpret_cast<uint64_t>(static_cast<const uint16_t*>(kv) + rk.kv0 * kAttnD);
     const uint64_t win_r = reinterpret_cast<uint64_t>(swa.data) + (uint64_t)swa_base * (kAttnD * 2);
-    // tiles that arrive by direct copies: selected rows, and a bf16 window
-    const int dma_tiles = win_fp8 ? sel_tiles : ntiles;
     // the wave's next tile at or after t (t = wave + 4 i) that holds a valid slot
     auto next_tile = [&](int t) -> int {
         if (t < sel_tiles) {
@@ -322,11 +341,55 @@ __global__ __launch_bounds__(256) void k_attn_bf16(RowsArg rows, CacheArg cache,
         return t;
     };
 
+    // FP4 main KV: the raw rows of the wave's next selected tile are loaded one tile ahead,
+    // like FP8 window rows.  Lane (g, c) holds code bytes [64 g, 64 g + 64) of slot c, i.e.
+    // dims [128 g, 128 g + 128), and the 8 E4M3 scales of those dims.
+    uint4 kr[4];
+    uint2 ksc;
+    auto prefetch_sel = [&](int tile) {
+        if (!kKvFp4 || tile >= sel_tiles) return;
+        const int64_t j = rk.kv0 + s_sel[16 * tile + c];
+        const uint4* cp = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(kv) + j * (kAttnD / 2) + 64 * g);
+#pragma unroll
+        for (int i = 0; i < 4; i++) kr[i] = cp[i];
+        ksc = *reinterpret_cast<const uint2*>(kv_scale + j * (kAttnD / 16) + 8 * g);
+    };
+    // whether tile t arrives by direct copies (else through registers)
+    auto by_dma = [&](int t) -> bool { return t < sel_tiles ? !kKvFp4 : !win_fp8; };
+    // after tile t has been fetched: load the registers of the wave's next tile of its kind
+    auto prefetch_after = [&](int t) {
+        if (t < sel_tiles)
+            prefetch_sel(next_tile(t + 4));
+        else
+            prefetch_win(t + 4);
+    };
+
     // Start the copy of tile `tile` into buffer `buf`; returns the tile's 16-bit mask of
     // valid slots.  Rows that arrive by direct copy are only issued here; FP8 window rows
-    // are converted from registers and stored to LDS.
+    // and FP4 main rows are converted from registers and stored to LDS.
     auto fetch = [&](int tile, int buf) -> uint32_t {
         const uint32_t dst = my_tiles_lds + buf * kTileBytes;
+        if (kKvFp4 && tile < sel_tiles) {
+            // lane (g, c): slot c, dims [128 g + 8 i, +8) share scale i / 2 of the lane's 8
+            char* dp = my_tiles + buf * kTileBytes + kRowBytes * c + 256 * g;
+            float sv[8];
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                const uint32_t sw = h ? ksc.y : ksc.x;
+                const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw, 1.0f, false);
+                const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw, 1.0f, true);
+                sv[4 * h] = lo[0];
+                sv[4 * h + 1] = lo[1];
+                sv[4 * h + 2] = hi[0];
+                sv[4 * h + 3] = hi[1];
+            }
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                const uint32_t w = kr[i >> 2][i & 3];
+                *reinterpret_cast<uint4*>(dp + 16 * i) = fp4x8_to_bf16x8(w, sv[i >> 1]);
+            }
+            return __builtin_amdgcn_readfirstlane(s_vmask[tile]);
+        }
         if (tile < sel_tiles) {
             int4 jv[4];
 #pragma unroll
@@ -392,19 +455,20 @@ __global__ __launch_bounds__(256) void k_attn_bf16(RowsArg rows, CacheArg cache,
         if (attempt == 1) prefetch_win(win_first);
         int buf = 0;
         int tile = next_tile(wave);
+        prefetch_sel(tile);
         uint32_t vm_cur = 0, vm_nxt = 0;
         int nxt = ntiles;
         bf16x8 ka[16];
         if (tile < ntiles) {
             vm_cur = fetch(tile, 0);
-            if (tile >= sel_tiles) prefetch_win(tile + 4);
+            prefetch_after(tile);
             nxt = next_tile(tile + 4);
             if (nxt < ntiles) vm_nxt = fetch(nxt, 1);
-            if (nxt < ntiles && nxt < dma_tiles)
+            if (nxt < ntiles && by_dma(nxt))
                 asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
             else
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            if (nxt < ntiles && nxt >= sel_tiles) prefetch_win(nxt + 4);
+            if (nxt < ntiles) prefetch_after(nxt);
 #pragma unroll
             for (int s = 0; s < 16; s++)
                 ka[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(my_tiles + k_off + 64 * s));
@@ -474,11 +538,11 @@ __global__ __launch_bounds__(256) void k_attn_bf16(RowsArg rows, CacheArg cache,
             if (nxt < ntiles) {
                 n2 = next_tile(nxt + 4);
                 if (n2 < ntiles) vm_n2 = fetch(n2, buf);
-                if (n2 < ntiles && n2 < dma_tiles)
+                if (n2 < ntiles && by_dma(n2))
                     asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
                 else
                     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                if (n2 < ntiles && n2 >= sel_tiles) prefetch_win(n2 + 4);
+                if (n2 < ntiles) prefetch_after(n2);
                 const char* tn = my_tiles + (buf ^ 1) * kTileBytes;
 #pragma unroll
                 for (int s = 0; s < 16; s++)
@@ -562,15 +626,19 @@ hipError_t launch_attn_f32(const RowsArg& rows, const CacheArg& cache, const flo
 }
 
 hipError_t launch_attn_bf16(const RowsArg& rows, const CacheArg& cache, const uint16_t* q, int heads,
-                            const uint16_t* kv, const int32_t* sel, int k, int64_t sel_stride,
+                            const void* kv, const uint8_t* kv_scale, const int32_t* sel, int k, int64_t sel_stride,
                             const int32_t* sel_row_map, const SwaArg& swa, float sm_scale, const float* sink,
                             uint16_t* out, float* lse, hipStream_t stream)
 {
     if (rows.n == 0) return hipSuccess;
     const int nhg = heads / 16;
     const int64_t nblocks = (int64_t)((rows.n + 7) / 8) * 8 * nhg;
-    hipLaunchKernelGGL(k_attn_bf16, dim3((unsigned)nblocks), dim3(256), 0, stream, rows, cache, q, heads, nhg, kv, sel,
-                       k, sel_stride, sel_row_map, swa, sm_scale, sink, out, lse);
+    if (kv_scale)
+        hipLaunchKernelGGL((k_attn_bf16<true>), dim3((unsigned)nblocks), dim3(256), 0, stream, rows, cache, q, heads,
+                           nhg, kv, kv_scale, sel, k, sel_stride, sel_row_map, swa, sm_scale, sink, out, lse);
+    else
+        hipLaunchKernelGGL((k_attn_bf16<false>), dim3((unsigned)nblocks), dim3(256), 0, stream, rows, cache, q, heads,
+                           nhg, kv, kv_scale, sel, k, sel_stride, sel_row_map, swa, sm_scale, sink, out, lse);
     return hipGetLastError();
 }
 

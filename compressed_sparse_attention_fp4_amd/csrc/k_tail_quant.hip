@@ -1,4 +1,5 @@
-// Decoder bounded-replay tail layout and the MX quantization kernel.
+// Decoder bounded-replay tail layout and the block quantization kernels (OCP MX, and the
+// FP4 main KV storage format).
 #include "csa2_device.h"
 #include "csa2_launch.h"
 
@@ -142,6 +143,60 @@ __global__ __launch_bounds__(256) void k_quant_mx(const void* __restrict__ x, in
     scales[b] = (uint8_t)sb;
 }
 
+// Main KV storage format ("DeepSeek V4.1 Flash modeling", section "Mixed precision": E2M1
+// data with one E4M3 scale per 16 channels and no tensor-wide scale), one thread per
+// 16-element block.  The scale is the E4M3 rounding of amax / 6 (nearest, ties to even,
+// saturating at 448).  The quotient is formed by a correctly rounded fp32 division, which
+// decides every rounding exactly as the real quotient does: a tie point t of the E4M3
+// grid has at most 5 significant bits, so 6 t lies on amax's fp32 grid, and an amax other
+// than 6 t puts the real quotient at least ulp(amax) / 6 from t, further than the
+// division's error of at most ulp(amax) / 8.  Elements are rounded by e2m1_code_scaled.
+template <bool kBf16In>
+__global__ __launch_bounds__(256) void k_quant_fp4s16(const void* __restrict__ x, int64_t nblocks,
+                                                      uint8_t* __restrict__ codes, uint8_t* __restrict__ scales)
+{
+    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= nblocks) return;
+    float v[16];
+    if (kBf16In) {
+        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + b * 16);
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const uint4 w = p[i];
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                v[i * 8 + 2 * j] = __uint_as_float(ws[j] << 16);
+                v[i * 8 + 2 * j + 1] = __uint_as_float(ws[j] & 0xFFFF0000u);
+            }
+        }
+    } else {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + b * 16);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const float4 w = p[i];
+            v[4 * i] = w.x;
+            v[4 * i + 1] = w.y;
+            v[4 * i + 2] = w.z;
+            v[4 * i + 3] = w.w;
+        }
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i++) amax = fmaxf(amax, fabsf(v[i]));
+    const uint32_t sc = e4m3_code(__fdiv_rn(amax, 6.0f));
+    const float s = e4m3_value(sc);
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        uint32_t c = s > 0.0f ? e2m1_code_scaled(fabsf(v[i]), s) : 0u;
+        c |= (__float_as_uint(v[i]) >> 28) & 8u;
+        w[i >> 3] |= c << (4 * (i & 7));
+    }
+    reinterpret_cast<uint2*>(codes)[b] = make_uint2(w[0], w[1]);
+    scales[b] = (uint8_t)sc;
+}
+
 hipError_t launch_replay_tail_layout(int nreq, const int32_t* ext_len, const int32_t* seq_len, int budget,
                                      int32_t* tail_len, int32_t* tail_row_start, int32_t* src_row,
                                      int32_t* abs_pos, int32_t* win_lo, int32_t* req_of_row, hipStream_t stream)
@@ -164,6 +219,18 @@ hipError_t launch_quant_mx(bool fp4, bool bf16_in, const void* x, int64_t nblock
         hipLaunchKernelGGL((k_quant_mx<true, false>), grid, dim3(256), 0, stream, x, nblocks, codes, scales);
     else
         hipLaunchKernelGGL((k_quant_mx<false, false>), grid, dim3(256), 0, stream, x, nblocks, codes, scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_fp4s16(bool bf16_in, const void* x, int64_t nblocks, uint8_t* codes, uint8_t* scales,
+                               hipStream_t stream)
+{
+    if (nblocks == 0) return hipSuccess;
+    dim3 grid((unsigned)((nblocks + 255) / 256));
+    if (bf16_in)
+        hipLaunchKernelGGL((k_quant_fp4s16<true>), grid, dim3(256), 0, stream, x, nblocks, codes, scales);
+    else
+        hipLaunchKernelGGL((k_quant_fp4s16<false>), grid, dim3(256), 0, stream, x, nblocks, codes, scales);
     return hipGetLastError();
 }
 

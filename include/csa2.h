@@ -32,10 +32,10 @@
  *     call; they are not checked.
  *   - Element arrays move in 16-byte vectors and must start on a 16-byte boundary (every
  *     hipMalloc / torch allocation does): q_idx and keys->data of csa2_index_score (MXFP4);
- *     q, kv, out, swa->data and swa->scale of csa2_sparse_swa_attn (BF16); x and codes of
- *     csa2_quant_mx.  A misaligned pointer is CSA2_E_ARG.  Row pitches follow from the
- *     shapes (64 + 4 bytes per MXFP4 key, 1 KiB per bf16 KV row), so aligned bases keep
- *     every row aligned.
+ *     q, kv, kv_scale, out, swa->data and swa->scale of csa2_sparse_swa_attn (BF16); x and
+ *     codes of csa2_quant_mx.  A misaligned pointer is CSA2_E_ARG.  Row pitches follow from
+ *     the shapes (64 + 4 bytes per MXFP4 key, 1 KiB per bf16 KV row, 256 + 32 bytes per
+ *     FP4_S16 KV row), so aligned bases keep every row aligned.
  *   - Results are deterministic: the same inputs give bitwise-identical outputs, and a
  *     row's outputs do not depend on the other rows of the batch.
  *   - Calls are reentrant.  The only state kept between calls is a per-device flag,
@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CSA2_VERSION 1
+#define CSA2_VERSION 2
 
 enum {
     CSA2_OK = 0,
@@ -67,7 +67,11 @@ typedef enum csa2_dtype {
     CSA2_BF16 = 1,       /* bfloat16 */
     CSA2_MXFP4 = 2,      /* OCP MX: E2M1 codes, two per byte (element 2i in the low nibble),
                             one E8M0 scale byte per 32 elements in a separate plane */
-    CSA2_MXFP8_E4M3 = 3  /* OCP MX: E4M3 ("fn") codes, one per byte, one E8M0 scale per 32 */
+    CSA2_MXFP8_E4M3 = 3, /* OCP MX: E4M3 ("fn") codes, one per byte, one E8M0 scale per 32 */
+    CSA2_FP4_S16 = 4     /* main KV storage format ([MOD] "Mixed precision"): E2M1 codes, two per
+                            byte (element 2i in the low nibble), one E4M3 ("fn") scale byte per
+                            16 elements in a separate plane, no tensor-wide scale; a 512-d entry
+                            is 256 + 32 = 288 bytes */
 } csa2_dtype;
 
 /* Query rows of one call.  Row q belongs to request req_of_row[q] and sits at
@@ -223,13 +227,19 @@ int csa2_topk_hier_noalloc(const csa2_rows* rows, const csa2_cache* cache, const
  * Selected indices must be < R(q) (or -1); k = 0 gives window-only attention.
  *
  * q [n][heads][dim] and out [n][heads][dim]; lse float [n][heads] or NULL.
+ * kv: F32 / BF16 [rows][dim] (kv_scale NULL), or CSA2_FP4_S16 codes uint8 [rows][dim/2]
+ * with kv_scale uint8 [rows][dim/16] E4M3 ([MOD] "Mixed precision": the main KV is stored
+ * in 4 bits and dequantized before attention; each element is its E2M1 value times its
+ * block's scale, exact in bf16, so the result is attention over the decoded values).
+ * Scale bytes must be finite E4M3 codes (not 0x7F / 0xFF), as csa2_quant_mx writes them.
  * Supported: (q, kv, window, out) = (F32, F32, F32, F32) with dim <= 256 and any heads;
- *            (BF16, BF16, MXFP8_E4M3 or BF16, BF16) with dim = 512 and heads % 16 == 0.
+ *            (BF16, BF16 or FP4_S16, MXFP8_E4M3 or BF16, BF16) with dim = 512 and
+ *            heads % 16 == 0.
  * sel_idx [*][sel_stride] int32, k <= sel_stride, k 0..2048.
  * ------------------------------------------------------------------------------- */
 int csa2_sparse_swa_attn(const csa2_rows* rows, const csa2_cache* cache, const void* q, csa2_dtype q_dtype,
-                         int32_t heads, int32_t dim, const void* kv, csa2_dtype kv_dtype, const int32_t* sel_idx,
-                         int32_t k, int64_t sel_stride, const int32_t* sel_row_map, const csa2_swa* swa,
+                         int32_t heads, int32_t dim, const void* kv, csa2_dtype kv_dtype, const uint8_t* kv_scale,
+                         const int32_t* sel_idx, int32_t k, int64_t sel_stride, const int32_t* sel_row_map, const csa2_swa* swa,
                          float sm_scale, const float* sink, void* out, csa2_dtype out_dtype, float* lse,
                          void* workspace, size_t workspace_bytes, void* stream);
 
@@ -263,12 +273,19 @@ const char* csa2_last_error(void);
 
 int csa2_version(void);
 
-/* OCP MX quantization of nblocks 32-element blocks of x (F32 or BF16, contiguous) into
- * codes (MXFP4: 16 B per block, MXFP8_E4M3: 32 B per block) and one E8M0 scale byte
- * per block: shared exponent floor(log2(max|x|)) - emax (emax 2 for E2M1, 8 for E4M3;
- * -127 for an all-zero block), elements rounded to nearest even and saturated, the
- * sign bit copied from x.  This is the same quantizer csa2_index_score applies to the
- * BF16 index q; it also prepares index keys and window KV.  Inputs must be finite. */
+/* Block quantization of x (F32 or BF16, contiguous), nblocks blocks, into codes and one
+ * scale byte per block.  Inputs must be finite.
+ *   fmt CSA2_MXFP4 / CSA2_MXFP8_E4M3 (OCP MX): 32-element blocks, codes 16 / 32 B per
+ *     block, E8M0 scale = shared exponent floor(log2(max|x|)) - emax (emax 2 for E2M1, 8
+ *     for E4M3; -127 for an all-zero block), elements rounded to nearest even and
+ *     saturated, the sign bit copied from x.  This is the quantizer csa2_index_score
+ *     applies to the BF16 index q; it also prepares index keys and window KV.
+ *   fmt CSA2_FP4_S16 (the main KV format, [MOD] "Mixed precision"; applied after RoPE):
+ *     16-element blocks, codes 8 B per block, E4M3 scale s = max|x| / 6 rounded to the
+ *     nearest E4M3 value (ties to even, saturating at 448); element = |x| / s rounded to
+ *     the nearest E2M1 value (ties to even, saturating at 6) with x's sign bit; a block
+ *     whose s rounds to 0 stores zero magnitudes.  (The pages fix the format, not its
+ *     rounding; this is the NVFP4 rule without the tensor-wide scale.) */
 int csa2_quant_mx(csa2_dtype fmt, const void* x, csa2_dtype x_dtype, int64_t nblocks, uint8_t* codes,
                   uint8_t* scales, void* stream);
 

@@ -51,6 +51,29 @@ def quant_both(orc, fmt_hip, fmt_orc, x_f32: torch.Tensor):
     return (codes_d, scales_d), (codes_o, scales_o)
 
 
+def quant_fp4_both(orc, x: torch.Tensor):
+    """Main KV storage format on both sides (x float32 or bfloat16, host): the device
+    quantizer takes x as it is, the oracle its float32 values; identical bytes asserted."""
+    codes_d, scales_d = B.quant_mx(B.FP4_S16, x.to(DEV))
+    codes_o, scales_o = orc.fp4s16_quant(x.float().numpy())
+    cd, sd = codes_d.cpu().numpy(), scales_d.cpu().numpy()
+    assert np.array_equal(sd, scales_o), ("E4M3 scale bytes differ", int((sd != scales_o).sum()))
+    assert np.array_equal(cd, codes_o), ("E2M1 code bytes differ", int((cd != codes_o).sum()))
+    return (codes_d, scales_d), (codes_o, scales_o)
+
+
+E2M1_VALUES = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+
+
+def fp4_decode_torch(codes: torch.Tensor, scales: torch.Tensor) -> torch.Tensor:
+    """Decoded values of main-KV-format rows (host tensors), from the E2M1 value table and
+    torch's float8_e4m3fn decode of the scale bytes; float32 (every value is exact)."""
+    table = torch.tensor(E2M1_VALUES, dtype=torch.float32)
+    c = torch.stack([codes & 15, codes >> 4], dim=-1).reshape(codes.shape[0], -1).long()
+    s = scales.view(torch.float8_e4m3fn).float().repeat_interleave(16, dim=-1)
+    return table[c] * s
+
+
 def allclose_report(got, ref, atol, rtol):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)

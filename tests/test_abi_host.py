@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     L = B.lib()
     for name in _declared():
         assert hasattr(L, name), name
-    assert L.csa2_version() == 1
+    assert L.csa2_version() == 2
 
 
 def _rows(n=4):
@@ -113,10 +113,11 @@ def test_attn_arg_errors():
     swa = B._Swa(B.MXFP8_E4M3, P, P, P, P, 128)
 
     def call(qdt=B.BF16, kvdt=B.BF16, odt=B.BF16, heads=64, dim=512, k=512, stride=512, sel=P, w=None, scale=0.04,
-             q=P, kv=P, out=P):
+             q=P, kv=P, out=P, kvs=None):
         s = w or swa
         return L.csa2_sparse_swa_attn(ctypes.byref(_rows()), ctypes.byref(_cache()), q, qdt, ctypes.c_int32(heads),
-                                      ctypes.c_int32(dim), kv, kvdt, sel, ctypes.c_int32(k), ctypes.c_int64(stride), None,
+                                      ctypes.c_int32(dim), kv, kvdt, kvs, sel, ctypes.c_int32(k),
+                                      ctypes.c_int64(stride), None,
                                       ctypes.byref(s), ctypes.c_float(scale), None, out, odt, None, None,
                                       ctypes.c_size_t(0), None)
 
@@ -134,6 +135,12 @@ def test_attn_arg_errors():
         assert call(**kw) == B.CSA2_E_ARG and "16-byte" in _err(), kw
     f32win = B._Swa(B.F32, P, None, P, P, 128)
     assert call(qdt=B.F32, kvdt=B.F32, odt=B.F32, dim=300, w=f32win) == B.CSA2_E_UNSUPPORTED
+    # FP4 main KV: codes with their E4M3 scale plane, bf16 q / out, dim 512 only
+    assert call(kvdt=B.FP4_S16) == B.CSA2_E_ARG and "kv_scale" in _err()
+    assert call(kvdt=B.BF16, kvs=P) == B.CSA2_E_ARG and "kv_scale" in _err()
+    assert call(kvdt=B.FP4_S16, kvs=M) == B.CSA2_E_ARG and "16-byte" in _err()
+    assert call(kvdt=B.FP4_S16, kvs=P, dim=256) == B.CSA2_E_UNSUPPORTED
+    assert call(kvdt=B.FP4_S16, kvs=P, qdt=B.F32, odt=B.F32, w=f32win, dim=64) == B.CSA2_E_UNSUPPORTED
 
 
 def test_tail_layout_arg_errors():
@@ -156,6 +163,8 @@ def test_quant_arg_errors():
     assert L.csa2_quant_mx(B.MXFP4, None, B.F32, ctypes.c_int64(0), None, None, None) == B.CSA2_OK
     assert L.csa2_quant_mx(B.MXFP4, M, B.F32, ctypes.c_int64(4), P, P, None) == B.CSA2_E_ARG and "16-byte" in _err()
     assert L.csa2_quant_mx(B.MXFP4, P, B.F32, ctypes.c_int64(4), M, P, None) == B.CSA2_E_ARG
+    assert L.csa2_quant_mx(B.FP4_S16, M, B.BF16, ctypes.c_int64(4), P, P, None) == B.CSA2_E_ARG
+    assert L.csa2_quant_mx(B.FP4_S16, None, B.BF16, ctypes.c_int64(0), None, None, None) == B.CSA2_OK
 
 
 def test_topk_hier_block_is_8_only():

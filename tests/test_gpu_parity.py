@@ -12,7 +12,8 @@ import torch
 from compressed_sparse_attention_fp4_amd import binding as B
 from compressed_sparse_attention_fp4_amd import synth
 
-from gpu_util import DEV, POISON_I32, allclose_report, dev_cache, dev_rows, i32, i64, poison, quant_both, say
+from gpu_util import (DEV, POISON_I32, allclose_report, dev_cache, dev_rows, fp4_decode_torch, i32, i64, poison,
+                      quant_both, quant_fp4_both, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -402,7 +403,9 @@ def _attn_bf16_case(seed, S, m, H, k, nrows_per_req, win_lo_tail=False, swa_fp8=
 
 
 def _run_attn_bf16(orc, rows, cache, q, kv, win, swa_raw, sel, H, sm_scale, swa_fp8=True, sel_row_map=None,
-                   sink=None):
+                   sink=None, kv_fp4=False):
+    """kv_fp4: the main KV goes in the FP4 storage format, quantized on each side from
+    the same bf16 rows (identical bytes asserted)."""
     n = len(rows["req_of_row"])
     if swa_fp8:
         (cd, sd), (co, so) = quant_both(orc, B.MXFP8_E4M3, orc.E4M3, swa_raw)
@@ -414,14 +417,20 @@ def _run_attn_bf16(orc, rows, cache, q, kv, win, swa_raw, sel, H, sm_scale, swa_
         wd = B.Window(sb.to(DEV), None, win["row_start"].to(DEV), win["pos_start"].to(DEV), 128)
         wo = dict(data=sb.view(torch.int16).numpy().view(np.uint16), dtype=1, scale=None,
                   row_start=win["row_start"].numpy(), pos_start=win["pos_start"].numpy(), window=128)
-    out_d, lse_d = B.sparse_swa_attn(dev_rows(rows), dev_cache(cache), q.to(DEV), kv.to(DEV), i32(sel).to(DEV), wd,
+    if kv_fp4:
+        (kv_d, kvs_d), (kv_o, kvs_o) = quant_fp4_both(orc, kv)
+        kv_dt_o = orc.DT_FP4S16
+    else:
+        kv_d, kvs_d = kv.to(DEV), None
+        kv_o, kvs_o, kv_dt_o = kv.view(torch.int16).numpy().view(np.uint16), None, 1
+    out_d, lse_d = B.sparse_swa_attn(dev_rows(rows), dev_cache(cache), q.to(DEV), kv_d, i32(sel).to(DEV), wd,
                                      sm_scale, sel_row_map=None if sel_row_map is None else i32(sel_row_map).to(DEV),
                                      sink=None if sink is None else torch.from_numpy(sink).to(DEV),
-                                     out=poison(tuple(q.shape), torch.bfloat16), lse=poison((n, H), torch.float32))
+                                     out=poison(tuple(q.shape), torch.bfloat16), lse=poison((n, H), torch.float32),
+                                     kv_scale=kvs_d)
     qb = q.view(torch.int16).numpy().view(np.uint16)
-    kvb = kv.view(torch.int16).numpy().view(np.uint16)
-    out_o, lse_o = orc.sparse_swa_attn(rows, cache, qb, 1, kvb, 1, sel, wo, heads=H, dim=512, sm_scale=sm_scale,
-                                       sel_row_map=sel_row_map, sink=sink)
+    out_o, lse_o = orc.sparse_swa_attn(rows, cache, qb, 1, kv_o, kv_dt_o, sel, wo, heads=H, dim=512,
+                                       sm_scale=sm_scale, sel_row_map=sel_row_map, sink=sink, kv_scale=kvs_o)
     return out_d.float().cpu().numpy(), lse_d.cpu().numpy(), out_o, lse_o
 
 
@@ -683,3 +692,102 @@ def test_attn_f32_sink(orc):
     nb, emax, _ = allclose_report(out_d.cpu().numpy(), out_o, 1e-4, 1e-4)
     assert nb == 0, (nb, emax)
     assert allclose_report(lse_d.cpu().numpy(), lse_o, 1e-4, 1e-4)[0] == 0
+
+
+# ------------------------------------------------------------- FP4 main KV
+def test_quant_fp4s16_all_bf16_patterns(orc):
+    say("case: main KV FP4 quantizer over every finite bf16 pattern, bf16 and fp32 input")
+    bits = torch.arange(65536, dtype=torch.int32).to(torch.int16)
+    vals = bits.view(torch.bfloat16).float()
+    vals = vals[torch.isfinite(vals)]
+    vals = vals[: (vals.numel() // 16) * 16]
+    g = torch.Generator().manual_seed(5)
+    for rep in range(3):
+        x = vals[torch.randperm(vals.numel(), generator=g)].reshape(-1, 16).contiguous()
+        quant_fp4_both(orc, x)
+        quant_fp4_both(orc, x.to(torch.bfloat16))
+    # blocks of similar magnitude (sorted patterns), where every element matters
+    x = vals[torch.argsort(vals.abs())].reshape(-1, 16).contiguous()
+    quant_fp4_both(orc, x)
+
+
+def test_quant_fp4s16_ties_and_ranges(orc):
+    say("case: main KV FP4 quantizer at E4M3 / E2M1 tie points, saturation, underflow, zeros")
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((4096, 16)).astype(np.float32)
+    x *= (2.0 ** rng.integers(-40, 20, size=(4096, 1))).astype(np.float32)
+    e4 = torch.arange(127, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    # amax / 6 exactly at every E4M3 tie point (midpoints of consecutive codes)
+    mids = (e4[1:] + e4[:-1]) / 2.0
+    for i, t in enumerate(mids):
+        x[i] = 0.0
+        x[i, i % 16] = 6.0 * t
+        x[i, (i + 1) % 16] = -6.0 * t * 0.5
+    row = len(mids)
+    # elements exactly at the E2M1 midpoints times the scale, for a few scales
+    for sc in (0x38, 0x01, 0x07, 0x4B, 0x7E):
+        s = e4[sc]
+        x[row] = 0.0
+        x[row, 0] = 6.0 * s
+        x[row, 1:8] = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]) * s
+        x[row, 8:15] = -x[row, 1:8]
+        row += 1
+    x[row] = 0.0
+    x[row + 1] = -0.0
+    x[row + 2, :] = 6.0 * 2.0 ** -11          # scale rounds to zero
+    x[row + 3, 0] = 6.0 * 500.0                # scale saturates at 448
+    x[row + 4, :] = 6.0 * 2.0 ** -10           # exactly half the smallest subnormal: ties to 0
+    x[row + 5, :] = 6.0 * 2.0 ** -10 * 1.0001  # just above: the smallest subnormal
+    quant_fp4_both(orc, torch.from_numpy(x))
+
+
+@pytest.mark.parametrize("H,k,swa_fp8,tail", [(64, 512, True, False), (16, 64, True, True), (32, 512, False, False),
+                                              (64, 0, True, False), (16, 2048, True, False), (128, 512, True, True),
+                                              (80, 96, False, True)])
+def test_attn_fp4_kv(orc, H, k, swa_fp8, tail):
+    say("case: sparse+window attention, FP4 main KV, H=%d k=%d fp8=%s tail=%s" % (H, k, swa_fp8, tail))
+    rows, cache, q, kv, win, swa_raw, sel = _attn_bf16_case(130 + H + k, (2600, 700), 2 if k != 2048 else 1, H, k, 6,
+                                                            win_lo_tail=tail)
+    got, lse_g, ref, lse_r = _run_attn_bf16(orc, rows, cache, q, kv, win, swa_raw, sel, H, 1 / math.sqrt(512),
+                                            swa_fp8=swa_fp8, kv_fp4=True)
+    _check_bf16_attn(got, ref, lse_g, lse_r)
+
+
+def test_attn_fp4_kv_equals_bf16_path_on_decoded_values(orc):
+    """Every decoded FP4 value is exact in bf16, so the FP4 path must give bit for bit what
+    the bf16 path gives on a cache holding the decoded values (same MFMA operands, same
+    order); the decode here is torch's (E2M1 table times float8_e4m3fn)."""
+    say("case: FP4 main KV path == bf16 path on the decoded cache, bitwise")
+    rows, cache, q, kv, win, swa_raw, sel = _attn_bf16_case(141, (2600, 700), 2, 32, 512, 6, win_lo_tail=True)
+    n = len(rows["req_of_row"])
+    codes, scales = B.quant_mx(B.FP4_S16, kv.to(DEV))
+    dec = fp4_decode_torch(codes.cpu(), scales.cpu())
+    assert torch.equal(dec.to(torch.bfloat16).float(), dec)
+    (cd, sd), _ = quant_both(orc, B.MXFP8_E4M3, orc.E4M3, swa_raw)
+    wd = B.Window(cd, sd, win["row_start"].to(DEV), win["pos_start"].to(DEV), 128)
+    args = (dev_rows(rows), dev_cache(cache), q.to(DEV))
+    a, la = B.sparse_swa_attn(*args, codes, i32(sel).to(DEV), wd, 0.044, want_lse=True, kv_scale=scales)
+    b, lb = B.sparse_swa_attn(*args, dec.to(torch.bfloat16).to(DEV), i32(sel).to(DEV), wd, 0.044, want_lse=True)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16)) and torch.equal(la, lb)
+    assert a.shape == (n, 32, 512)
+
+
+@pytest.mark.parametrize("sm_scale", [1.0, 3.0])
+def test_attn_fp4_kv_wide_logits(orc, sm_scale):
+    say("case: FP4 main KV attention with the redo pass (logits wider than the reference), scale %g" % sm_scale)
+    rows, cache, q, kv, win, swa_raw, sel = _attn_bf16_case(161, (2600, 700), 2, 16, 512, 6)
+    got, lse_g, ref, lse_r = _run_attn_bf16(orc, rows, cache, q, kv, win, swa_raw, sel, 16, sm_scale, kv_fp4=True)
+    _check_bf16_attn(got, ref, lse_g, lse_r)
+
+
+def test_attn_fp4_kv_reuse_row_map(orc):
+    say("case: FP4 main KV, Reuse layer through sel_row_map, bf16 window")
+    rows, cache, q, kv, win, swa_raw, sel = _attn_bf16_case(188, (1500,), 2, 16, 512, 10)
+    n = len(rows["req_of_row"])
+    rng = np.random.default_rng(2)
+    table = np.full((3 * n, 512), -1, np.int32)
+    row_map = rng.permutation(3 * n)[:n].astype(np.int32)
+    table[row_map] = sel
+    got, lse_g, ref, lse_r = _run_attn_bf16(orc, rows, cache, q, kv, win, swa_raw, table, 16, 0.05,
+                                            sel_row_map=row_map, swa_fp8=False, kv_fp4=True)
+    _check_bf16_attn(got, ref, lse_g, lse_r)
