@@ -74,6 +74,8 @@ class InputSet:
             del raw
         self.keys = B.IndexKeys(self.kcodes, self.kscale, DI)
         self.kv = synth.normal_bf16((g.total_entries, D), seed, "kv", device=dev, chunk_rows=1 << 19)
+        # the same main KV in the pages' FP4 storage format (E2M1 + one E4M3 scale per 16)
+        self.kv4, self.kv4s = B.quant_mx(B.FP4_S16, self.kv)
         win = synth.window_cache_geometry(g, W)
         self.layers = []
         for l in range(LAYERS):
@@ -130,6 +132,34 @@ def step(x: InputSet, only: str | None = None):
 STAGE_LAUNCHES = {"score_full": 1, "topk_hier": 1, "attn": LAYERS, "score_pool": LAYERS - 1, "topk_pool": LAYERS - 1}
 
 
+def attn_fp4kv(x: InputSet):
+    """The step's 8 attention launches with the main KV in the FP4 storage format (same
+    index sets, q and windows as the bf16 step)."""
+    sm = synth.sm_scale(D)
+    for l in range(LAYERS):
+        Ll = x.layers[l]
+        B.sparse_swa_attn(x.rows, x.cache, Ll["q"], x.kv4, x.idx[l], Ll["window"], sm, out=x.out[l],
+                          kv_scale=x.kv4s)
+
+
+def launch_ms_of(fn, sets, reps: int, per: int) -> float:
+    """Average launch duration of fn's calls over every input set, as in stage_launch_ms."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for x in sets:
+            fn(x)
+    g.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / (reps * len(sets) * per)
+
+
 def stage_launch_ms(sets, reps: int) -> dict:
     """Average duration of one launch of each stage: the stage's calls for every input set
     captured in one HIP graph, replayed back to back between two HIP events on the stream
@@ -155,6 +185,7 @@ def stage_launch_ms(sets, reps: int) -> dict:
 
 # Algorithmic bytes per launch (what the step must move at least once).
 ATTN_BYTES_PER_QUERY = K * D * 2 + W * (D + D // 32) + H * D * 2 * 2 + K * 4     # 724,992
+ATTN_FP4KV_BYTES_PER_QUERY = K * (D // 2 + D // 16) + W * (D + D // 32) + H * D * 2 * 2 + K * 4  # 348,160
 STAGE_BYTES = {
     "score_full": NREQ * C * (DI // 2 + DI // 32) + NREQ * HI * DI * 2 + NREQ * HI * 4 + NREQ * C * 4,
     "topk_hier": 2 * NREQ * C * 4 + NREQ * (K + NB + 1) * 4,
@@ -184,17 +215,36 @@ def measured_traffic(stage: str):
     return None
 
 
+# The 7 Reindex launches of a step rescore the same 71 MB of pool keys, which the 256 MiB
+# last-level cache holds: their rate is cache-served, not HBM bandwidth.
+STAGE_NOTES = {"score_pool": {"served_from": "last-level cache (pool keys reread by 7 launches)"},
+               "topk_pool": {"served_from": "L2 / last-level cache (scores written by the previous launch)"}}
+
 STAGE_KERNEL = {"score_full": "k_score_mxfp4", "topk_hier": "k_select (2 launches)", "attn": "k_attn_bf16",
                 "score_pool": "k_score_mxfp4 (pool)", "topk_pool": "k_select"}
 
 
 # ------------------------------------------------------------------ cpu baseline
+def _host():
+    """What the host offers: CPUs this process may run on, all CPUs, and the CPU model."""
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return len(os.sched_getaffinity(0)), os.cpu_count(), model
+
+
 def cpu_baseline(x: InputSet, nrows: int):
     """The oracle on a bounded sample: nrows requests through the source layer and one
     Reindex layer, timed per layer; the rate is scaled to the step's mix (1 source +
-    7 Reindex layers per query row)."""
+    7 Reindex layers per query row).  Then the same for one row on one thread (the
+    per-core rate)."""
     import oracle as orc
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count() or 1
+    threads = orc.max_threads()
     nrows = max(1, min(nrows, NREQ))
     rows = dict(req_of_row=np.arange(nrows), pos_of_row=np.full(nrows, SEQ - 1))
     cache = dict(ratio_m=M, n_entries=np.full(nrows, C), row_start=np.arange(nrows, dtype=np.int64) * C)
@@ -220,25 +270,39 @@ def cpu_baseline(x: InputSet, nrows: int):
                                  row_start=wn.row_start[:nrows].cpu().numpy(),
                                  pos_start=wn.pos_start[:nrows].cpu().numpy(), window=W)))
     sm = synth.sm_scale(D)
-    t0 = time.perf_counter()
-    s, _ = orc.index_score(rows, cache, lay[0]["qi"], lay[0]["w"], kc, key_scales=ks, heads=HI, dim=DI,
-                           score_stride=C)
-    idx, pb, pn = orc.topk_hier(rows, cache, s, K, BLK, NB)
-    orc.sparse_swa_attn(rows, cache, lay[0]["q"], 1, kv, 1, idx, lay[0]["swa"], heads=H, dim=D, sm_scale=sm)
-    t_src = time.perf_counter() - t0
-    pool = dict(blocks=pb, nblocks=pn, block=BLK, max_blocks=NB)
-    t0 = time.perf_counter()
-    s2, _ = orc.index_score(rows, cache, lay[1]["qi"], lay[1]["w"], kc, key_scales=ks, heads=HI, dim=DI,
-                            score_stride=NB * BLK, pool=pool)
-    idx2 = orc.topk(rows, cache, s2, K, pool=pool)
-    orc.sparse_swa_attn(rows, cache, lay[1]["q"], 1, kv, 1, idx2, lay[1]["swa"], heads=H, dim=D, sm_scale=sm)
-    t_re = time.perf_counter() - t0
-    step_time = t_src + (LAYERS - 1) * t_re
-    rate = nrows * LAYERS / step_time
+
+    def layers(nr):
+        """Seconds of the source layer and of one Reindex layer for the first nr rows."""
+        rw = {k: v[:nr] for k, v in rows.items()}
+        ly = [{k: (v[:nr] if k in ("qi", "w", "q") else v) for k, v in L.items()} for L in lay]
+        t0 = time.perf_counter()
+        s, _ = orc.index_score(rw, cache, ly[0]["qi"], ly[0]["w"], kc, key_scales=ks, heads=HI, dim=DI,
+                               score_stride=C)
+        idx, pb, pn = orc.topk_hier(rw, cache, s, K, BLK, NB)
+        orc.sparse_swa_attn(rw, cache, ly[0]["q"], 1, kv, 1, idx, ly[0]["swa"], heads=H, dim=D, sm_scale=sm)
+        t_src = time.perf_counter() - t0
+        pool = dict(blocks=pb, nblocks=pn, block=BLK, max_blocks=NB)
+        t0 = time.perf_counter()
+        s2, _ = orc.index_score(rw, cache, ly[1]["qi"], ly[1]["w"], kc, key_scales=ks, heads=HI, dim=DI,
+                                score_stride=NB * BLK, pool=pool)
+        idx2 = orc.topk(rw, cache, s2, K, pool=pool)
+        orc.sparse_swa_attn(rw, cache, ly[1]["q"], 1, kv, 1, idx2, ly[1]["swa"], heads=H, dim=D, sm_scale=sm)
+        return t_src, time.perf_counter() - t0
+
+    t_src, t_re = layers(nrows)
+    rate = nrows * LAYERS / (t_src + (LAYERS - 1) * t_re)
     used = min(threads, nrows)  # the oracle parallelizes over query rows
-    return {"value": rate, "unit": "queries/s", "cores": used, "kind": "oracle",
+    orc.set_threads(1)
+    t1_src, t1_re = layers(1)
+    orc.set_threads(threads)
+    rate1 = LAYERS / (t1_src + (LAYERS - 1) * t1_re)
+    avail, ncpu, model = _host()
+    return {"value": rate, "unit": "queries/s", "cores": used, "threads_used": used, "kind": "oracle",
+            "host_cpus_available": avail, "host_cpus_total": ncpu, "cpu_model": model,
+            "single_thread_value": rate1,
             "sample": "%d of 64 query rows through the source layer (%.1f s) and one Reindex layer (%.1f s) on "
-                      "%d host threads; rate = rows x 8 layers / (source + 7 x Reindex)" % (nrows, t_src, t_re, used)}
+                      "%d host threads; rate = rows x 8 layers / (source + 7 x Reindex); single-thread rate from "
+                      "1 row (%.2f s + %.2f s)" % (nrows, t_src, t_re, used, t1_src, t1_re)}
 
 
 # ---------------------------------------------------------------------- main
@@ -486,6 +550,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-c2", action="store_true", help="skip the C2 replay-tail prefill stages")
     ap.add_argument("--cpu-rows", type=int, default=int(os.environ.get("OMP_NUM_THREADS", "0") or 16))
     ap.add_argument("--c1-scoring", action="store_true",
                     help="instead of the decode step: time the C1 prefill index scoring alone (FP4 MFMA rate)")
@@ -553,6 +618,13 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     log("timed %d steps in %.3f ms" % (args.steps, elapsed * 1e3))
+    # A/A: the same timed region again, for the run-to-run noise band (not the value)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % NSETS].replay()
+    torch.cuda.synchronize()
+    elapsed_aa = time.perf_counter() - t0
 
     # per-launch durations of each stage (HIP events around back-to-back graph replays)
     launch_ms = stage_launch_ms(sets, reps=max(3, args.steps // 4))
@@ -564,6 +636,16 @@ def main():
                   "alg_GBs": STAGE_BYTES[s] / (launch_ms[s] * 1e-3) / 1e9} for s in STAGES}
     log(json.dumps(stages, indent=1))
     log("graph step %.3f ms; sum of stage launches %.3f ms" % (elapsed * 1e3 / args.steps, sum(per_step_ms.values())))
+
+    # the FP4 main KV variant of the attention launches (the pages' storage format)
+    fp4_ms = launch_ms_of(attn_fp4kv, sets, max(3, args.steps // 4), LAYERS)
+    fp4_bytes = NREQ * ATTN_FP4KV_BYTES_PER_QUERY
+    fp4_gbs = fp4_bytes / (fp4_ms * 1e-3) / 1e9
+    fp4 = {"kernel": "k_attn_bf16<FP4 main KV>", "us_per_launch": round(fp4_ms * 1e3, 2),
+           "alg_bytes_per_launch": fp4_bytes, "achieved": round(fp4_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": fp4_gbs / HBM_PEAK_GBS,
+           "step_ms_with_fp4_kv": (sum(per_step_ms.values()) - per_step_ms["attn"] + LAYERS * fp4_ms)}
+    log("FP4 main KV attention: %.2f us per launch (%.1f GB/s algorithmic)" % (fp4_ms * 1e3, fp4_gbs))
 
     # spread of single steps: each replay alone between two HIP events (outside the timed
     # region above, which is the reported value)
@@ -585,6 +667,11 @@ def main():
     dst.copy_(src)
     torch.cuda.synchronize()
 
+    c2 = None
+    if not args.no_c2:
+        log("C2 replay-tail prefill flow ...")
+        c2 = c2_replay(max(5, args.steps // 2), args.warmup, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) on %d rows ..." % args.cpu_rows)
@@ -599,6 +686,8 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": elapsed * 1e3 / args.steps,
         "step_ms_spread": spread,
+        "aa_repeat": {"value": NREQ * LAYERS * args.steps / elapsed_aa, "ms_per_step": elapsed_aa * 1e3 / args.steps,
+                      "rel_diff": (elapsed_aa - elapsed) / elapsed},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -613,9 +702,12 @@ def main():
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(dominant), "alg_bytes_per_launch": STAGE_BYTES[dominant],
                      "avg_launch_us": avg_launch_ms * 1e3},
-        "stages": {s: {"us_per_launch": round(v["ms_per_launch"] * 1e3, 2),
-                       "launches_per_step": v["launches_per_step"], "alg_GBs": round(v["alg_GBs"], 1)}
+        "stages": {s: dict({"us_per_launch": round(v["ms_per_launch"] * 1e3, 2),
+                            "launches_per_step": v["launches_per_step"], "alg_GBs": round(v["alg_GBs"], 1)},
+                           **STAGE_NOTES.get(s, {}))
                    for s, v in stages.items()},
+        "c2_replay_tail_prefill": c2,
+        "fp4_main_kv_attn": fp4,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

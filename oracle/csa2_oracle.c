@@ -29,8 +29,14 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <omp.h>
+
 #define ORC_E2M1 0
 #define ORC_E4M3 1
+
+/* Host threads of the OpenMP loops (timing the oracle at a stated thread count). */
+void orc_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+int orc_max_threads(void) { return omp_get_max_threads(); }
 
 /* ------------------------------------------------------------------------- */
 /* Element formats (OCP MX v1.0).                                             */

@@ -73,6 +73,15 @@ def _f32(a):
     return None if a is None else np.ascontiguousarray(a, dtype=np.float32)
 
 
+def set_threads(n: int) -> None:
+    """Host threads used by the oracle's OpenMP loops."""
+    _load().orc_set_threads(ctypes.c_int(n))
+
+
+def max_threads() -> int:
+    return int(_load().orc_max_threads())
+
+
 # --------------------------------------------------------------------------- formats
 def e2m1_value(code: int) -> float:
     return _load().orc_e2m1_value(ctypes.c_int(code))
