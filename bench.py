@@ -196,7 +196,8 @@ STAGE_BYTES = {
 }
 # Kernel (as rocprofv3 names it, with its workgroup count) and source file behind each
 # stage, for the measured HBM traffic recorded under profiles/.
-STAGE_PROFILE = {"attn": ("csa2::k_attn_bf16", 256, "compressed_sparse_attention_fp4_amd/csrc/k_attn.hip")}
+STAGE_PROFILE = {"attn": ("csa2::k_attn_bf16<false>", 256, "compressed_sparse_attention_fp4_amd/csrc/k_attn.hip"),
+                 "attn_fp4kv": ("csa2::k_attn_bf16<true>", 256, "compressed_sparse_attention_fp4_amd/csrc/k_attn.hip")}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "c3_decode_hbm_traffic.txt")
 
 
@@ -643,7 +644,7 @@ def main():
     fp4_gbs = fp4_bytes / (fp4_ms * 1e-3) / 1e9
     fp4 = {"kernel": "k_attn_bf16<FP4 main KV>", "us_per_launch": round(fp4_ms * 1e3, 2),
            "alg_bytes_per_launch": fp4_bytes, "achieved": round(fp4_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-           "frac": fp4_gbs / HBM_PEAK_GBS,
+           "frac": fp4_gbs / HBM_PEAK_GBS, "traffic": measured_traffic("attn_fp4kv"),
            "step_ms_with_fp4_kv": (sum(per_step_ms.values()) - per_step_ms["attn"] + LAYERS * fp4_ms)}
     log("FP4 main KV attention: %.2f us per launch (%.1f GB/s algorithmic)" % (fp4_ms * 1e3, fp4_gbs))
 
