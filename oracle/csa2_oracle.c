@@ -635,32 +635,84 @@ void orc_dense_attn(int n, const int32_t* req_of_row, const int32_t* pos_of_row,
 
 /* ------------------------------------------------------------------------- */
 /* Decoder bounded-replay tail layout ([P2] sections 2.1 and 2.3, restated in the */
-/* rule block after the window table): per request, T = min(budget, E); the    */
+/* rule block after the window table): per request, T = min(budget, E); the     */
 /* late layers keep the absolute positions [S - T, S); the window lower bound is */
 /* S - T; the tail row u of request r is row (start of r in the extend) + E - T + u */
 /* of the original extend.  Computed per request, never per batch.               */
+/* Mixed batches ([P1] "Decoder Bounded Replay": in a mixed batch the new tokens */
+/* of decode requests still pass through the whole trunk): a request flagged as  */
+/* decode keeps all of its E rows (E <= budget) and no window cut (lower bound   */
+/* 0; the window cache's own first position still bounds what exists).          */
+/* flags bit 0 (reading of the short-extend proposal in [P2] section 2.6, which */
+/* lets the late layers see the cached prefix's window): the lower bound of a   */
+/* prefill request becomes max(0, S - budget) instead of S - T; it differs only */
+/* when E < budget.                                                              */
 /* ------------------------------------------------------------------------- */
-int orc_replay_tail_layout(int nreq, const int32_t* ext_len, const int32_t* seq_len, int budget, int32_t* tail_len,
-                           int32_t* tail_row_start, int32_t* src_row, int32_t* abs_pos, int32_t* win_lo,
-                           int32_t* req_of_row, int capacity)
+int orc_replay_tail_layout(int nreq, const int32_t* ext_len, const int32_t* seq_len, const int32_t* is_decode,
+                           int budget, int flags, int32_t* tail_len, int32_t* tail_row_start, int32_t* src_row,
+                           int32_t* abs_pos, int32_t* win_lo, int32_t* req_of_row, int capacity)
 {
     int64_t ext_start = 0, out = 0;
     for (int r = 0; r < nreq; r++) {
         int E = ext_len[r], S = seq_len[r];
+        int decode = is_decode && is_decode[r];
         if (E < 0 || E > S) return -1;
-        int T = E < budget ? E : budget;
+        if (decode && E > budget) return -3;
+        int T = (decode || E < budget) ? E : budget;
+        int lo;
+        if (decode)
+            lo = 0;
+        else if (flags & 1)
+            lo = S - budget > 0 ? S - budget : 0;
+        else
+            lo = S - T;
         tail_len[r] = T;
         tail_row_start[r] = (int32_t)out;
         for (int u = 0; u < T; u++) {
             if (out >= capacity) return -2;
             src_row[out] = (int32_t)(ext_start + E - T + u);
             abs_pos[out] = S - T + u;
-            win_lo[out] = S - T;
+            win_lo[out] = lo;
             req_of_row[out] = r;
             out++;
         }
         ext_start += E;
     }
     tail_row_start[nreq] = (int32_t)out;
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Encoder-side bounded replay layout ([P4] section 4.1; [P4] section 4.3: both */
+/* replay modes cut local attention at the rebuild boundary).  Request r has a  */
+/* cached prefix of P tokens (its compressed KV and indexer keys are kept, its  */
+/* window is not) and an extend of E new tokens.  The rows of the call are the  */
+/* last min(P, budget) prefix positions, recomputed to rebuild the window, then */
+/* the E extend positions: absolute positions [R0, P + E) with R0 =             */
+/* max(0, P - budget), all with window lower bound R0.  src_row is the row of   */
+/* the extend input for extend rows and -1 for replayed prefix rows (whose      */
+/* tokens come from the cache).  row_start[r] is the first row of request r.    */
+/* ------------------------------------------------------------------------- */
+int orc_encoder_replay_layout(int nreq, const int32_t* prefix_len, const int32_t* ext_len, int budget,
+                              int32_t* row_start, int32_t* src_row, int32_t* abs_pos, int32_t* win_lo,
+                              int32_t* req_of_row, int capacity)
+{
+    int64_t ext_start = 0, out = 0;
+    for (int r = 0; r < nreq; r++) {
+        int P = prefix_len[r], E = ext_len[r];
+        if (P < 0 || E < 0) return -1;
+        int R0 = P - budget > 0 ? P - budget : 0;
+        row_start[r] = (int32_t)out;
+        for (int t = R0; t < P + E; t++) {
+            if (out >= capacity) return -2;
+            src_row[out] = t < P ? -1 : (int32_t)(ext_start + (t - P));
+            abs_pos[out] = t;
+            win_lo[out] = R0;
+            req_of_row[out] = r;
+            out++;
+        }
+        ext_start += E;
+    }
+    row_start[nreq] = (int32_t)out;
     return 0;
 }

@@ -290,22 +290,47 @@ def sparse_swa_attn(rows, cache, q, q_dt, kv, kv_dt, sel_idx, swa, *, heads, dim
 
 
 # ------------------------------------------------------------------------- tail layout
-def replay_tail_layout(ext_len, seq_len, budget=128, capacity=None):
-    """Decoder bounded-replay tail layout ([P2] sections 2.1, 2.3)."""
+def replay_tail_layout(ext_len, seq_len, budget=128, capacity=None, is_decode=None, borrow_prefix_window=False):
+    """Decoder bounded-replay tail layout ([P2] sections 2.1, 2.3); decode requests of a
+    mixed batch keep all their rows uncut ([P1] "Decoder Bounded Replay"); the optional
+    short-extend reading of [P2] section 2.6 lowers the window bound to S - budget."""
     lib = _load()
     e = _i32(ext_len)
     s = _i32(seq_len)
     nreq = len(e)
+    dec = None if is_decode is None else _i32(is_decode)
     if capacity is None:
         capacity = budget * nreq
     tail_len = np.empty(nreq, np.int32)
     start = np.empty(nreq + 1, np.int32)
     bufs = [np.full(max(capacity, 1), -1, np.int32) for _ in range(4)]
-    rc = lib.orc_replay_tail_layout(ctypes.c_int(nreq), _p(e), _p(s), ctypes.c_int(budget), _p(tail_len),
-                                    _p(start), *[_p(b) for b in bufs], ctypes.c_int(capacity))
+    rc = lib.orc_replay_tail_layout(ctypes.c_int(nreq), _p(e), _p(s), _p(dec), ctypes.c_int(budget),
+                                    ctypes.c_int(1 if borrow_prefix_window else 0), _p(tail_len), _p(start),
+                                    *[_p(b) for b in bufs], ctypes.c_int(capacity))
     if rc != 0:
         raise ValueError("tail layout precondition violated (rc=%d)" % rc)
     tot = int(start[nreq])
     src_row, abs_pos, win_lo, req_of_row = (b[:tot] for b in bufs)
     return dict(tail_len=tail_len, tail_row_start=start, src_row=src_row, abs_pos=abs_pos, win_lo=win_lo,
                 req_of_row=req_of_row)
+
+
+def encoder_replay_layout(prefix_len, ext_len, budget=128, capacity=None):
+    """Encoder-side bounded replay ([P4] sections 4.1, 4.3): per request the last
+    min(P, budget) cached prefix positions are recomputed before the extend; every row's
+    window stops at R0 = max(0, P - budget); src_row is -1 for replayed prefix rows."""
+    lib = _load()
+    p = _i32(prefix_len)
+    e = _i32(ext_len)
+    nreq = len(e)
+    if capacity is None:
+        capacity = budget * nreq + int(e.sum())
+    start = np.empty(nreq + 1, np.int32)
+    bufs = [np.full(max(capacity, 1), -7, np.int32) for _ in range(4)]
+    rc = lib.orc_encoder_replay_layout(ctypes.c_int(nreq), _p(p), _p(e), ctypes.c_int(budget), _p(start),
+                                       *[_p(b) for b in bufs], ctypes.c_int(capacity))
+    if rc != 0:
+        raise ValueError("encoder replay layout precondition violated (rc=%d)" % rc)
+    tot = int(start[nreq])
+    src_row, abs_pos, win_lo, req_of_row = (b[:tot] for b in bufs)
+    return dict(row_start=start, src_row=src_row, abs_pos=abs_pos, win_lo=win_lo, req_of_row=req_of_row)
