@@ -22,7 +22,9 @@ OP_TOPK, OP_TOPK_HIER, OP_ATTN = 1, 2, 3
 
 # Every symbol include/csa2.h declares.
 EXPORTS = ["csa2_index_score", "csa2_topk", "csa2_topk_hier", "csa2_topk_hier_noalloc", "csa2_sparse_swa_attn",
-           "csa2_replay_tail_layout", "csa2_workspace_size", "csa2_last_error", "csa2_version", "csa2_quant_mx"]
+           "csa2_replay_tail_layout", "csa2_encoder_replay_layout", "csa2_workspace_size", "csa2_last_error",
+           "csa2_version", "csa2_quant_mx"]
+TAIL_BORROW_PREFIX_WINDOW = 1
 
 
 class Csa2Error(RuntimeError):
@@ -286,9 +288,11 @@ def sparse_swa_attn(rows: Rows, cache: Cache, q: torch.Tensor, kv: torch.Tensor,
 
 
 def replay_tail_layout(ext_len: torch.Tensor, seq_len: torch.Tensor, budget: int = 128, out: Optional[dict] = None,
+                       is_decode: Optional[torch.Tensor] = None, borrow_prefix_window: bool = False,
                        stream=None) -> dict:
     """csa2_replay_tail_layout; returns device tensors sized for budget * nreq rows (or
-    fills `out`, a dict of the same int32 tensors)."""
+    fills `out`, a dict of the same int32 tensors).  is_decode (int32 [nreq]) marks the
+    decode requests of a mixed batch."""
     nreq = ext_len.numel()
     dev = ext_len.device
     cap = budget * nreq
@@ -300,10 +304,34 @@ def replay_tail_layout(ext_len: torch.Tensor, seq_len: torch.Tensor, budget: int
                  tail_row_start=torch.empty(nreq + 1, dtype=torch.int32, device=dev))
         for name in ("src_row", "abs_pos", "win_lo", "req_of_row"):
             t[name] = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
-    rc = lib().csa2_replay_tail_layout(ctypes.c_int32(nreq), _ptr(ext_len), _ptr(seq_len), ctypes.c_int32(budget),
-                                       _ptr(t["tail_len"]), _ptr(t["tail_row_start"]), _ptr(t["src_row"]),
-                                       _ptr(t["abs_pos"]), _ptr(t["win_lo"]), _ptr(t["req_of_row"]),
-                                       ctypes.c_int32(cap), _stream(stream))
+    flags = TAIL_BORROW_PREFIX_WINDOW if borrow_prefix_window else 0
+    rc = lib().csa2_replay_tail_layout(ctypes.c_int32(nreq), _ptr(ext_len), _ptr(seq_len), _ptr(is_decode),
+                                       ctypes.c_int32(budget), ctypes.c_int32(flags), _ptr(t["tail_len"]),
+                                       _ptr(t["tail_row_start"]), _ptr(t["src_row"]), _ptr(t["abs_pos"]),
+                                       _ptr(t["win_lo"]), _ptr(t["req_of_row"]), ctypes.c_int32(cap),
+                                       _stream(stream))
+    _check(rc)
+    return t
+
+
+def encoder_replay_layout(prefix_len: torch.Tensor, ext_len: torch.Tensor, n_ext: int, budget: int = 128,
+                          out: Optional[dict] = None, stream=None) -> dict:
+    """csa2_encoder_replay_layout; device tensors sized for budget * nreq + n_ext rows (or
+    fills `out`).  n_ext must equal ext_len.sum()."""
+    nreq = ext_len.numel()
+    dev = ext_len.device
+    cap = budget * nreq + n_ext
+    if out is not None:
+        t = out
+        cap = min(t[name].numel() for name in ("src_row", "abs_pos", "win_lo", "req_of_row"))
+    else:
+        t = dict(row_start=torch.empty(nreq + 1, dtype=torch.int32, device=dev))
+        for name in ("src_row", "abs_pos", "win_lo", "req_of_row"):
+            t[name] = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    rc = lib().csa2_encoder_replay_layout(ctypes.c_int32(nreq), _ptr(prefix_len), _ptr(ext_len),
+                                          ctypes.c_int64(n_ext), ctypes.c_int32(budget), _ptr(t["row_start"]),
+                                          _ptr(t["src_row"]), _ptr(t["abs_pos"]), _ptr(t["win_lo"]),
+                                          _ptr(t["req_of_row"]), ctypes.c_int32(cap), _stream(stream))
     _check(rc)
     return t
 

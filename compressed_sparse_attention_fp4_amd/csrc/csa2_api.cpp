@@ -334,12 +334,14 @@ int csa2_sparse_swa_attn(const csa2_rows* rows, const csa2_cache* cache, const v
                          "csa2_sparse_swa_attn");
 }
 
-int csa2_replay_tail_layout(int32_t nreq, const int32_t* ext_len, const int32_t* seq_len, int32_t budget,
-                            int32_t* tail_len, int32_t* tail_row_start, int32_t* src_row, int32_t* abs_pos,
-                            int32_t* win_lo, int32_t* req_of_row, int32_t capacity, void* stream)
+int csa2_replay_tail_layout(int32_t nreq, const int32_t* ext_len, const int32_t* seq_len, const int32_t* is_decode,
+                            int32_t budget, int32_t flags, int32_t* tail_len, int32_t* tail_row_start,
+                            int32_t* src_row, int32_t* abs_pos, int32_t* win_lo, int32_t* req_of_row,
+                            int32_t capacity, void* stream)
 {
     if (nreq < 0) return fail(CSA2_E_ARG, "nreq = %d < 0", nreq);
     if (budget < 1) return fail(CSA2_E_ARG, "budget = %d < 1", budget);
+    if (flags & ~CSA2_TAIL_BORROW_PREFIX_WINDOW) return fail(CSA2_E_ARG, "unknown flags 0x%x", flags);
     if (!tail_row_start) return fail(CSA2_E_ARG, "tail_row_start is NULL");
     if (nreq > 0 && (!ext_len || !seq_len || !tail_len || !src_row || !abs_pos || !win_lo || !req_of_row))
         return fail(CSA2_E_ARG, "a tail-layout array is NULL");
@@ -348,10 +350,33 @@ int csa2_replay_tail_layout(int32_t nreq, const int32_t* ext_len, const int32_t*
     if ((int64_t)budget * nreq > 0x7FFFFFFF) return fail(CSA2_E_ARG, "budget x nreq overflows int32");
     int rc;
     if ((rc = check_device())) return rc;
-    return launch_result(csa2::launch_replay_tail_layout(nreq, ext_len, seq_len, budget, tail_len, tail_row_start,
-                                                         src_row, abs_pos, win_lo, req_of_row,
+    return launch_result(csa2::launch_replay_tail_layout(nreq, ext_len, seq_len, is_decode, budget, flags, tail_len,
+                                                         tail_row_start, src_row, abs_pos, win_lo, req_of_row,
                                                          static_cast<hipStream_t>(stream)),
                          "csa2_replay_tail_layout");
+}
+
+int csa2_encoder_replay_layout(int32_t nreq, const int32_t* prefix_len, const int32_t* ext_len, int64_t n_ext,
+                               int32_t budget, int32_t* row_start, int32_t* src_row, int32_t* abs_pos,
+                               int32_t* win_lo, int32_t* req_of_row, int32_t capacity, void* stream)
+{
+    if (nreq < 0) return fail(CSA2_E_ARG, "nreq = %d < 0", nreq);
+    if (budget < 1) return fail(CSA2_E_ARG, "budget = %d < 1", budget);
+    if (n_ext < 0) return fail(CSA2_E_ARG, "n_ext = %lld < 0", (long long)n_ext);
+    if (!row_start) return fail(CSA2_E_ARG, "row_start is NULL");
+    if (nreq > 0 && (!prefix_len || !ext_len || !src_row || !abs_pos || !win_lo || !req_of_row))
+        return fail(CSA2_E_ARG, "an encoder-replay layout array is NULL");
+    const int64_t bound = (int64_t)budget * nreq + n_ext;
+    if (bound > 0x7FFFFFFF) return fail(CSA2_E_ARG, "budget x nreq + n_ext overflows int32");
+    if ((int64_t)capacity < bound)
+        return fail(CSA2_E_ARG, "capacity %d < budget %d x nreq %d + n_ext %lld", capacity, budget, nreq,
+                    (long long)n_ext);
+    int rc;
+    if ((rc = check_device())) return rc;
+    return launch_result(csa2::launch_encoder_replay_layout(nreq, prefix_len, ext_len, budget, row_start, src_row,
+                                                            abs_pos, win_lo, req_of_row,
+                                                            static_cast<hipStream_t>(stream)),
+                         "csa2_encoder_replay_layout");
 }
 
 int csa2_quant_mx(csa2_dtype fmt, const void* x, csa2_dtype x_dtype, int64_t nblocks, uint8_t* codes,

@@ -29,9 +29,13 @@ struct PoolArg {
     int max_blocks;
 };
 
-hipError_t launch_replay_tail_layout(int nreq, const int32_t* ext_len, const int32_t* seq_len, int budget,
-                                     int32_t* tail_len, int32_t* tail_row_start, int32_t* src_row,
-                                     int32_t* abs_pos, int32_t* win_lo, int32_t* req_of_row, hipStream_t stream);
+hipError_t launch_replay_tail_layout(int nreq, const int32_t* ext_len, const int32_t* seq_len,
+                                     const int32_t* is_decode, int budget, int flags, int32_t* tail_len,
+                                     int32_t* tail_row_start, int32_t* src_row, int32_t* abs_pos, int32_t* win_lo,
+                                     int32_t* req_of_row, hipStream_t stream);
+hipError_t launch_encoder_replay_layout(int nreq, const int32_t* prefix_len, const int32_t* ext_len, int budget,
+                                        int32_t* row_start, int32_t* src_row, int32_t* abs_pos, int32_t* win_lo,
+                                        int32_t* req_of_row, hipStream_t stream);
 
 hipError_t launch_quant_mx(bool fp4, bool bf16_in, const void* x, int64_t nblocks, uint8_t* codes,
                            uint8_t* scales, hipStream_t stream);

@@ -8,6 +8,7 @@
  *   4. csa2_sparse_swa_attn  attention over the selected compressed entries and the
  *                            query's own sliding window, one joint softmax
  *   5. csa2_replay_tail_layout  per-request tail rows of the decoder bounded replay
+ *      csa2_encoder_replay_layout  rows of an extend under the encoder-side replay
  *
  * Pages (cited by title and section):
  *   [MOD]  "DeepSeek V4.1 Flash modeling" (pages.haorui.li): sections "CSA2",
@@ -251,13 +252,39 @@ int csa2_sparse_swa_attn(const csa2_rows* rows, const csa2_cache* cache, const v
  *   the window lower bound of those rows is S - T (also for E < budget, [TAIL] 2.6);
  *   tail row u of r is row ext_start(r) + E - T + u of the original extend, where
  *   ext_start(r) = sum of ext_len over the requests before r.
+ * Mixed batches ([MOD] "Decoder Bounded Replay": the new tokens of decode requests still
+ * pass through the whole trunk): is_decode[r] != 0 marks a decode request, whose E rows
+ * (E <= budget) are all kept, with window lower bound 0.  is_decode NULL = all prefill.
+ * flags: CSA2_TAIL_BORROW_PREFIX_WINDOW sets the lower bound of prefill requests to
+ * max(0, S - budget), so a short extend sees the cached prefix's window (a reading of
+ * the proposal discussed in [TAIL] 2.6; off reproduces the page's pinned behaviour).
  * Outputs: tail_len [nreq]; tail_row_start [nreq+1] (exclusive prefix sum of tail_len);
  * per tail row (at most capacity): src_row, abs_pos, win_lo, req_of_row.
  * Precondition 0 <= E <= S.  capacity >= budget*nreq (host-checked), budget >= 1.
  * ------------------------------------------------------------------------------- */
-int csa2_replay_tail_layout(int32_t nreq, const int32_t* ext_len, const int32_t* seq_len, int32_t budget,
-                            int32_t* tail_len, int32_t* tail_row_start, int32_t* src_row, int32_t* abs_pos,
-                            int32_t* win_lo, int32_t* req_of_row, int32_t capacity, void* stream);
+enum { CSA2_TAIL_BORROW_PREFIX_WINDOW = 1 };
+
+int csa2_replay_tail_layout(int32_t nreq, const int32_t* ext_len, const int32_t* seq_len, const int32_t* is_decode,
+                            int32_t budget, int32_t flags, int32_t* tail_len, int32_t* tail_row_start,
+                            int32_t* src_row, int32_t* abs_pos, int32_t* win_lo, int32_t* req_of_row,
+                            int32_t capacity, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * csa2_encoder_replay_layout -- rows of an extend batch under encoder-side bounded replay
+ * ([DAY0] section 4.1: on a prefix-cache hit the last 128 tokens of the cached prefix
+ * are recomputed to rebuild the window, the cached compressed KV and indexer keys stay;
+ * section 4.3: local attention is cut at the rebuild boundary).
+ * Request r has P = prefix_len[r] cached tokens and E = ext_len[r] new ones.  Its rows
+ * are the absolute positions [R0, P + E) with R0 = max(0, P - budget): first the
+ * min(P, budget) replayed prefix positions, then the extend.  Every row's window lower
+ * bound is R0.  src_row is the extend input row (ext_start(r) + t - P) of an extend row
+ * and -1 for a replayed prefix row.  row_start [nreq+1] is the exclusive prefix sum of
+ * the per-request row counts min(P, budget) + E.
+ * n_ext = sum of ext_len (a precondition); capacity >= budget*nreq + n_ext (host-checked).
+ * ------------------------------------------------------------------------------- */
+int csa2_encoder_replay_layout(int32_t nreq, const int32_t* prefix_len, const int32_t* ext_len, int64_t n_ext,
+                               int32_t budget, int32_t* row_start, int32_t* src_row, int32_t* abs_pos,
+                               int32_t* win_lo, int32_t* req_of_row, int32_t capacity, void* stream);
 
 /* ---------------------------------------------------------------------------------
  * Helpers.

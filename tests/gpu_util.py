@@ -82,6 +82,29 @@ def allclose_report(got, ref, atol, rtol):
     return int(bad.sum()), float(err.max(initial=0.0)), float((err / (np.abs(ref) + 1e-30)).max(initial=0.0))
 
 
+def bits(t):
+    """bf16 tensor -> its 16-bit patterns as a host uint16 array (the oracle's bf16 input)."""
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def check_scores(got, ref, ncols):
+    """Scores bit for bit on the first ncols[i] columns of every sampled row."""
+    for i, n in enumerate(ncols):
+        if not np.array_equal(got[i, :n], ref[i, :n]):
+            bad = np.nonzero(got[i, :n] != ref[i, :n])[0]
+            raise AssertionError("sample row %d: %d of %d score columns differ, first %s" % (i, len(bad), n, bad[:6]))
+
+
+def check_attn(got, ref):
+    """bf16 attention tolerance: |g - r| <= 2e-2 + 1e-2 |r| and a row relative L2 error <= 1e-2."""
+    nb, emax, _ = allclose_report(got, ref, 2e-2, 1e-2)
+    assert nb == 0, ("attention elements out of tolerance", nb, emax)
+    n, h, d = ref.shape
+    rel = np.linalg.norm((got - ref).reshape(n * h, d), axis=1) / (np.linalg.norm(ref.reshape(n * h, d), axis=1)
+                                                                   + 1e-30)
+    assert rel.max() <= 1e-2, ("row relative L2", rel.max())
+
+
 POISON_I32 = 0x7FFFFFFF
 
 

@@ -146,13 +146,27 @@ def test_attn_arg_errors():
 def test_tail_layout_arg_errors():
     L = B.lib()
 
-    def call(nreq=8, budget=128, cap=1024):
-        return L.csa2_replay_tail_layout(ctypes.c_int32(nreq), P, P, ctypes.c_int32(budget), P, P, P, P, P, P,
-                                         ctypes.c_int32(cap), None)
+    def call(nreq=8, budget=128, cap=1024, flags=0):
+        return L.csa2_replay_tail_layout(ctypes.c_int32(nreq), P, P, None, ctypes.c_int32(budget),
+                                         ctypes.c_int32(flags), P, P, P, P, P, P, ctypes.c_int32(cap), None)
 
     assert call(cap=1023) == B.CSA2_E_ARG and "capacity" in _err()
     assert call(budget=0) == B.CSA2_E_ARG
     assert call(nreq=-1) == B.CSA2_E_ARG
+    assert call(flags=2) == B.CSA2_E_ARG and "flags" in _err()
+
+
+def test_encoder_replay_layout_arg_errors():
+    L = B.lib()
+
+    def call(nreq=8, budget=128, cap=1024 + 500, n_ext=500, pre=P):
+        return L.csa2_encoder_replay_layout(ctypes.c_int32(nreq), pre, P, ctypes.c_int64(n_ext),
+                                            ctypes.c_int32(budget), P, P, P, P, P, ctypes.c_int32(cap), None)
+
+    assert call(cap=1024 + 499) == B.CSA2_E_ARG and "capacity" in _err()
+    assert call(n_ext=-1) == B.CSA2_E_ARG
+    assert call(budget=0) == B.CSA2_E_ARG
+    assert call(pre=None) == B.CSA2_E_ARG
 
 
 def test_quant_arg_errors():

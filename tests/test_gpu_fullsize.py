@@ -17,7 +17,7 @@ import torch
 from compressed_sparse_attention_fp4_amd import binding as B
 from compressed_sparse_attention_fp4_amd import synth
 
-from gpu_util import DEV, allclose_report, dev_cache, dev_rows, i32, i64, say
+from gpu_util import DEV, bits, check_attn, check_scores, dev_cache, dev_rows, i32, i64, say
 
 pytestmark = pytest.mark.gpu
 
@@ -27,26 +27,6 @@ def _gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     B.lib()
-
-
-def bits(t):
-    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-
-
-def check_scores(got, ref, ncols):
-    for i, n in enumerate(ncols):
-        if not np.array_equal(got[i, :n], ref[i, :n]):
-            bad = np.nonzero(got[i, :n] != ref[i, :n])[0]
-            raise AssertionError("sample row %d: %d of %d score columns differ, first %s" % (i, len(bad), n, bad[:6]))
-
-
-def check_attn(got, ref):
-    nb, emax, _ = allclose_report(got, ref, 2e-2, 1e-2)
-    assert nb == 0, ("attention elements out of tolerance", nb, emax)
-    n, h, d = ref.shape
-    rel = np.linalg.norm((got - ref).reshape(n * h, d), axis=1) / (np.linalg.norm(ref.reshape(n * h, d), axis=1)
-                                                                   + 1e-30)
-    assert rel.max() <= 1e-2, ("row relative L2", rel.max())
 
 
 def oracle_window(orc, raw_rows, nreq_rows, pos_start, window=128):
