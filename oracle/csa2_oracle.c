@@ -634,6 +634,132 @@ void orc_dense_attn(int n, const int32_t* req_of_row, const int32_t* pos_of_row,
 }
 
 /* ------------------------------------------------------------------------- */
+/* Index-K producer, the step that fills the caches the path reads ([P1] "CSA2":   */
+/* non-overlapping compression, index K projected from the compressed main KV;    */
+/* [P4] section 1: pairwise compression keeps incomplete pairs across decode      */
+/* steps; [P4] section 5: compressor projection with BF16 weights and FP32        */
+/* accumulation and output, ratio-2 pooling merging each completed pair, RoPE and */
+/* FP4 quantization/pack/cache write fused while keeping the intermediate        */
+/* rounding; [P1] "Mixed precision": main KV quantized after RoPE).              */
+/* Readings (the pages name the steps, not their arithmetic):                    */
+/*  - input: the compressor's per-token fp32 outputs (512-d); m tokens pool into  */
+/*    one entry by their mean, (a + b) * 0.5 in fp32 for m = 2, the token itself  */
+/*    for m = 1; entry j covers tokens [j m, j m + m - 1] and is produced when   */
+/*    its last token arrives; a lone first token waits in `pending` [nreq][512]. */
+/*  - RoPE: the last 64 dims of the 512-d latent and of the 128-d index key,     */
+/*    rotated in interleaved pairs (2i, 2i+1) at the entry's last token position */
+/*    P = j m + m - 1, with cos / sin taken from a caller table [pos][2][32]:     */
+/*    x' = x c - y s, y' = x s + y c, each product and sum rounded to fp32.      */
+/*  - index K: k_o = sum_i W[o][i] * bf16(latent_i) over the pre-RoPE latent,    */
+/*    accumulated in fp32 by one fma per term in ascending i (a fixed order, so  */
+/*    that the MXFP4 codes it decides are reproducible), then RoPE, then MXFP4.  */
+/*  - main KV: the RoPE'd latent, stored bf16 (nearest even) or in the FP4       */
+/*    storage format above.                                                      */
+/* Rows of one request in a call are consecutive ascending positions.  Reads of   */
+/* `pending` see its state before the call.                                      */
+/* ------------------------------------------------------------------------- */
+#define ORC_KV_DIM 512
+#define ORC_IDX_DIM 128
+#define ORC_ROPE_DIM 64
+
+static float orc_bf16_round(float x)
+{
+    uint32_t u;
+    memcpy(&u, &x, 4);
+    u = (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u;
+    float r;
+    memcpy(&r, &u, 4);
+    return r;
+}
+
+static void orc_rope(float* x, const float* rope, int64_t P)
+{
+    const float* c = rope + P * ORC_ROPE_DIM;
+    const float* sn = c + ORC_ROPE_DIM / 2;
+    for (int i = 0; i < ORC_ROPE_DIM / 2; i++) {
+        float a = x[2 * i], b = x[2 * i + 1];
+        float t1 = a * c[i], t2 = b * sn[i], t3 = a * sn[i], t4 = b * c[i];
+        x[2 * i] = t1 - t2;
+        x[2 * i + 1] = t3 + t4;
+    }
+}
+
+static void orc_produce_entry(const float* latent, int64_t P, int64_t erow, const uint16_t* w_index,
+                              const float* rope, int kv_dt, void* kv, uint8_t* kv_scale, uint8_t* idx_codes,
+                              uint8_t* idx_scales)
+{
+    float x[ORC_KV_DIM], k[ORC_IDX_DIM], y[ORC_KV_DIM];
+    for (int i = 0; i < ORC_KV_DIM; i++) {
+        x[i] = latent[i];
+        y[i] = orc_bf16_round(latent[i]);
+    }
+    /* index key */
+    for (int o = 0; o < ORC_IDX_DIM; o++) {
+        float acc = 0.0f;
+        for (int i = 0; i < ORC_KV_DIM; i++) {
+            uint32_t wb = (uint32_t)w_index[(int64_t)o * ORC_KV_DIM + i] << 16;
+            float wf;
+            memcpy(&wf, &wb, 4);
+            acc = fmaf(wf, y[i], acc);
+        }
+        k[o] = acc;
+    }
+    orc_rope(k + ORC_IDX_DIM - ORC_ROPE_DIM, rope, P);
+    orc_mx_quant(ORC_E2M1, k, ORC_IDX_DIM / 32, idx_codes + erow * (ORC_IDX_DIM / 2), idx_scales + erow * (ORC_IDX_DIM / 32));
+    /* main KV */
+    orc_rope(x + ORC_KV_DIM - ORC_ROPE_DIM, rope, P);
+    if (kv_dt == 4) {
+        orc_fp4s16_quant(x, ORC_KV_DIM / 16, (uint8_t*)kv + erow * (ORC_KV_DIM / 2), kv_scale + erow * (ORC_KV_DIM / 16));
+    } else {
+        uint16_t* o = (uint16_t*)kv + erow * ORC_KV_DIM;
+        for (int i = 0; i < ORC_KV_DIM; i++) {
+            float r = orc_bf16_round(x[i]);
+            uint32_t u;
+            memcpy(&u, &r, 4);
+            o[i] = (uint16_t)(u >> 16);
+        }
+    }
+}
+
+/* Returns 0, or -1 for an argument the producer does not take. */
+int orc_kv_produce(int n, const int32_t* req_of_row, const int32_t* pos_of_row, int m, const int64_t* row_start,
+                   const float* comp, float* pending, const uint16_t* w_index, const float* rope, int64_t max_pos,
+                   int kv_dt, void* kv, uint8_t* kv_scale, uint8_t* idx_codes, uint8_t* idx_scales)
+{
+    if (m != 1 && m != 2) return -1;
+    if (kv_dt != 1 && kv_dt != 4) return -1;
+    /* entries first (they read `pending` as it was before the call), then the new lone tokens */
+    for (int t = 0; t < n; t++) {
+        int r = req_of_row[t];
+        int64_t p = pos_of_row[t];
+        if ((p + 1) % m != 0) continue;
+        int64_t j = (p + 1) / m - 1;
+        int64_t P = j * m + m - 1;
+        if (P >= max_pos) return -1;
+        float latent[ORC_KV_DIM];
+        const float* b = comp + (int64_t)t * ORC_KV_DIM;
+        if (m == 1) {
+            for (int i = 0; i < ORC_KV_DIM; i++) latent[i] = b[i];
+        } else {
+            int prev_here = t > 0 && req_of_row[t - 1] == r && pos_of_row[t - 1] == p - 1;
+            const float* a = prev_here ? comp + (int64_t)(t - 1) * ORC_KV_DIM : pending + (int64_t)r * ORC_KV_DIM;
+            for (int i = 0; i < ORC_KV_DIM; i++) latent[i] = (a[i] + b[i]) * 0.5f;
+        }
+        orc_produce_entry(latent, P, row_start[r] + j, w_index, rope, kv_dt, kv, kv_scale, idx_codes, idx_scales);
+    }
+    if (m == 2) {
+        for (int t = 0; t < n; t++) {
+            int r = req_of_row[t];
+            int64_t p = pos_of_row[t];
+            int next_here = t + 1 < n && req_of_row[t + 1] == r && pos_of_row[t + 1] == p + 1;
+            if (p % 2 == 0 && !next_here)
+                memcpy(pending + (int64_t)r * ORC_KV_DIM, comp + (int64_t)t * ORC_KV_DIM, sizeof(float) * ORC_KV_DIM);
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
 /* Decoder bounded-replay tail layout ([P2] sections 2.1 and 2.3, restated in the */
 /* rule block after the window table): per request, T = min(budget, E); the     */
 /* late layers keep the absolute positions [S - T, S); the window lower bound is */

@@ -289,6 +289,46 @@ def sparse_swa_attn(rows, cache, q, q_dt, kv, kv_dt, sel_idx, swa, *, heads, dim
     return out, lse
 
 
+# ------------------------------------------------------------------------ KV producer
+KV_DIM, IDX_DIM, ROPE_DIM = 512, 128, 64
+
+
+def kv_produce(rows, ratio_m, row_start, n_rows_cache, comp, pending, w_index_bits, rope, kv_dt=DT_FP4S16,
+               fill=0xEE):
+    """Index-K / main-KV producer ([P1] "CSA2"; [P4] sections 1 and 5; readings in
+    csa2_oracle.c).  comp: float32 [n, 512] compressor outputs of the rows; pending:
+    float32 [nreq, 512] (copied, the updated copy is returned); w_index_bits: uint16
+    [128, 512] bf16 patterns; rope: float32 [max_pos, 2, 32] (cos, sin).  Cache buffers of
+    n_rows_cache rows are created filled with `fill` (bf16: the pattern fill * 0x101), so
+    rows the call does not produce keep it.  Returns a dict of the caches and the state."""
+    lib = _load()
+    req = _i32(rows["req_of_row"])
+    pos = _i32(rows["pos_of_row"])
+    n = len(req)
+    comp = _f32(comp)
+    assert comp.shape == (n, KV_DIM)
+    pend = np.array(pending, dtype=np.float32, copy=True, order="C")
+    w = np.ascontiguousarray(w_index_bits, dtype=np.uint16)
+    assert w.shape == (IDX_DIM, KV_DIM)
+    rope = _f32(rope)
+    max_pos = rope.shape[0]
+    assert rope.shape[1:] == (2, ROPE_DIM // 2)
+    if kv_dt == DT_FP4S16:
+        kv = np.full((n_rows_cache, KV_DIM // 2), fill, np.uint8)
+        kvs = np.full((n_rows_cache, KV_DIM // 16), fill, np.uint8)
+    else:
+        kv = np.full((n_rows_cache, KV_DIM), fill * 0x101, np.uint16)
+        kvs = None
+    ic = np.full((n_rows_cache, IDX_DIM // 2), fill, np.uint8)
+    isc = np.full((n_rows_cache, IDX_DIM // 32), fill, np.uint8)
+    rc = lib.orc_kv_produce(ctypes.c_int(n), _p(req), _p(pos), ctypes.c_int(ratio_m), _p(_i64(row_start)), _p(comp),
+                            _p(pend), _p(w), _p(rope), ctypes.c_int64(max_pos), ctypes.c_int(kv_dt), _p(kv), _p(kvs),
+                            _p(ic), _p(isc))
+    if rc != 0:
+        raise ValueError("kv producer argument not supported (rc=%d)" % rc)
+    return dict(kv=kv, kv_scale=kvs, index_codes=ic, index_scales=isc, pending=pend)
+
+
 # ------------------------------------------------------------------------- tail layout
 def replay_tail_layout(ext_len, seq_len, budget=128, capacity=None, is_decode=None, borrow_prefix_window=False):
     """Decoder bounded-replay tail layout ([P2] sections 2.1, 2.3); decode requests of a
