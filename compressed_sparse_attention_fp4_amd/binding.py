@@ -23,7 +23,7 @@ OP_TOPK, OP_TOPK_HIER, OP_ATTN = 1, 2, 3
 # Every symbol include/csa2.h declares.
 EXPORTS = ["csa2_index_score", "csa2_topk", "csa2_topk_hier", "csa2_topk_hier_noalloc", "csa2_sparse_swa_attn",
            "csa2_replay_tail_layout", "csa2_encoder_replay_layout", "csa2_workspace_size", "csa2_last_error",
-           "csa2_version", "csa2_quant_mx"]
+           "csa2_version", "csa2_quant_mx", "csa2_kv_produce"]
 TAIL_BORROW_PREFIX_WINDOW = 1
 
 
@@ -350,3 +350,18 @@ def quant_mx(fmt: int, x: torch.Tensor, stream=None):
                              _ptr(codes), _ptr(scales), _stream(stream))
     _check(rc)
     return codes, scales
+
+
+def kv_produce(rows: Rows, cache: Cache, comp: torch.Tensor, pending: Optional[torch.Tensor], w_index: torch.Tensor,
+               rope: torch.Tensor, kv: torch.Tensor, index_codes: torch.Tensor, index_scales: torch.Tensor,
+               kv_scale: Optional[torch.Tensor] = None, stream=None) -> None:
+    """csa2_kv_produce: writes the entries the rows complete into kv (bf16 [rows, 512], or
+    FP4 codes uint8 [rows, 256] with kv_scale [rows, 32]) and the MXFP4 index caches; updates
+    pending (float32 [nreq, 512], m = 2).  comp float32 [n, 512]; w_index bf16 [128, 512];
+    rope float32 [max_pos, 2, 32]."""
+    kv_dt = FP4_S16 if kv_scale is not None else BF16
+    rc = lib().csa2_kv_produce(ctypes.byref(rows.c()), ctypes.byref(cache.c()), _ptr(comp), _ptr(pending),
+                               _ptr(w_index), _ptr(rope), ctypes.c_int64(rope.shape[0]), ctypes.c_int(kv_dt),
+                               _ptr(kv), _ptr(kv_scale), _ptr(index_codes), _ptr(index_scales), _stream(stream))
+    _check(rc)
+

@@ -379,6 +379,32 @@ int csa2_encoder_replay_layout(int32_t nreq, const int32_t* prefix_len, const in
                          "csa2_encoder_replay_layout");
 }
 
+int csa2_kv_produce(const csa2_rows* rows, const csa2_cache* cache, const float* comp, float* pending,
+                    const uint16_t* w_index, const float* rope, int64_t max_pos, csa2_dtype kv_dtype, void* kv,
+                    uint8_t* kv_scale, uint8_t* index_codes, uint8_t* index_scales, void* stream)
+{
+    int rc;
+    if ((rc = check_rows(rows)) || (rc = check_cache(cache))) return rc;
+    if (!comp || !w_index || !rope || !kv || !index_codes || !index_scales)
+        return fail(CSA2_E_ARG, "comp / w_index / rope / kv / index_codes / index_scales is NULL");
+    if (cache->ratio_m == 2 && !pending) return fail(CSA2_E_ARG, "pending is NULL with ratio_m = 2");
+    if (max_pos < 1) return fail(CSA2_E_ARG, "max_pos = %lld < 1", (long long)max_pos);
+    if (kv_dtype != CSA2_FP4_S16 && kv_dtype != CSA2_BF16)
+        return fail(CSA2_E_UNSUPPORTED, "kv_dtype %d (FP4_S16 or BF16)", (int)kv_dtype);
+    if ((kv_dtype == CSA2_FP4_S16) != (kv_scale != nullptr))
+        return fail(CSA2_E_ARG, "kv_scale goes with FP4_S16 main KV only");
+    if (misaligned(comp, 16) || misaligned(pending, 16) || misaligned(w_index, 16) || misaligned(kv, 16) ||
+        misaligned(index_codes, 16))
+        return fail(CSA2_E_ARG, "comp / pending / w_index / kv / index_codes must start on a 16-byte boundary");
+    if (rows->n == 0) return ok();
+    if ((rc = check_device())) return rc;
+    return launch_result(csa2::launch_kv_produce(rows->n, rows->req_of_row, rows->pos_of_row, cache->ratio_m,
+                                                 cache->row_start, comp, pending, w_index, rope, max_pos,
+                                                 kv_dtype == CSA2_FP4_S16, kv, kv_scale, index_codes, index_scales,
+                                                 static_cast<hipStream_t>(stream)),
+                         "csa2_kv_produce");
+}
+
 int csa2_quant_mx(csa2_dtype fmt, const void* x, csa2_dtype x_dtype, int64_t nblocks, uint8_t* codes,
                   uint8_t* scales, void* stream)
 {

@@ -122,6 +122,31 @@ __device__ __forceinline__ void quant_block_e2m1(const float* x, uint32_t out[4]
     }
 }
 
+// Quantize one 16-element block to the FP4 main KV storage format: E2M1 codes (element 2i
+// in the low nibble of byte i, 8 bytes as 2 dwords) and the E4M3 scale byte s = RNE(amax / 6)
+// (saturating at 448).  The quotient is a correctly rounded fp32 division, which decides
+// every rounding as the real quotient does: a tie point t of the E4M3 grid has at most 5
+// significant bits, so 6 t lies on amax's fp32 grid, and an amax other than 6 t puts the
+// real quotient at least ulp(amax) / 6 from t, further than the division's error of at
+// most ulp(amax) / 8.  Elements are rounded by e2m1_code_scaled; a zero scale stores
+// zero magnitudes (sign bits kept).
+__device__ __forceinline__ void quant_block_fp4s16(const float* v, uint32_t out[2], uint32_t* scale_byte)
+{
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i++) amax = fmaxf(amax, fabsf(v[i]));
+    const uint32_t sc = e4m3_code(__fdiv_rn(amax, 6.0f));
+    const float s = e4m3_value(sc);
+    out[0] = out[1] = 0u;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        uint32_t c = s > 0.0f ? e2m1_code_scaled(fabsf(v[i]), s) : 0u;
+        c |= (__float_as_uint(v[i]) >> 28) & 8u;
+        out[i >> 3] |= c << (4 * (i & 7));
+    }
+    *scale_byte = sc;
+}
+
 // Quantize one 32-element block to MXFP8 E4M3: 32 code bytes as 8 dwords, E8M0 byte.
 __device__ __forceinline__ void quant_block_e4m3(const float* x, uint32_t out[8], uint32_t* scale_byte)
 {

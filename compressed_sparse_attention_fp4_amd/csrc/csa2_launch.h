@@ -88,4 +88,10 @@ hipError_t launch_attn_bf16(const RowsArg& rows, const CacheArg& cache, const ui
                             const int32_t* sel_row_map, const SwaArg& swa, float sm_scale, const float* sink,
                             uint16_t* out, float* lse, hipStream_t stream);
 
+// Index-K / main-KV producer (m = 1 or 2; main KV bf16 or FP4_S16).
+hipError_t launch_kv_produce(int n, const int32_t* req_of_row, const int32_t* pos_of_row, int m,
+                             const int64_t* row_start, const float* comp, float* pending, const uint16_t* w_index,
+                             const float* rope, int64_t max_pos, bool fp4_kv, void* kv, uint8_t* kv_scale,
+                             uint8_t* idx_codes, uint8_t* idx_scales, hipStream_t stream);
+
 }  // namespace csa2

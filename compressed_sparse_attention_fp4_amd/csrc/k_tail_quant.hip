@@ -189,12 +189,7 @@ __global__ __launch_bounds__(256) void k_quant_mx(const void* __restrict__ x, in
 
 // Main KV storage format ("DeepSeek V4.1 Flash modeling", section "Mixed precision": E2M1
 // data with one E4M3 scale per 16 channels and no tensor-wide scale), one thread per
-// 16-element block.  The scale is the E4M3 rounding of amax / 6 (nearest, ties to even,
-// saturating at 448).  The quotient is formed by a correctly rounded fp32 division, which
-// decides every rounding exactly as the real quotient does: a tie point t of the E4M3
-// grid has at most 5 significant bits, so 6 t lies on amax's fp32 grid, and an amax other
-// than 6 t puts the real quotient at least ulp(amax) / 6 from t, further than the
-// division's error of at most ulp(amax) / 8.  Elements are rounded by e2m1_code_scaled.
+// 16-element block (quant_block_fp4s16).
 template <bool kBf16In>
 __global__ __launch_bounds__(256) void k_quant_fp4s16(const void* __restrict__ x, int64_t nblocks,
                                                       uint8_t* __restrict__ codes, uint8_t* __restrict__ scales)
@@ -225,18 +220,8 @@ __global__ __launch_bounds__(256) void k_quant_fp4s16(const void* __restrict__ x
             v[4 * i + 3] = w.w;
         }
     }
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; i++) amax = fmaxf(amax, fabsf(v[i]));
-    const uint32_t sc = e4m3_code(__fdiv_rn(amax, 6.0f));
-    const float s = e4m3_value(sc);
-    uint32_t w[2] = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 16; i++) {
-        uint32_t c = s > 0.0f ? e2m1_code_scaled(fabsf(v[i]), s) : 0u;
-        c |= (__float_as_uint(v[i]) >> 28) & 8u;
-        w[i >> 3] |= c << (4 * (i & 7));
-    }
+    uint32_t w[2], sc;
+    quant_block_fp4s16(v, w, &sc);
     reinterpret_cast<uint2*>(codes)[b] = make_uint2(w[0], w[1]);
     scales[b] = (uint8_t)sc;
 }

@@ -9,6 +9,7 @@
  *                            query's own sliding window, one joint softmax
  *   5. csa2_replay_tail_layout  per-request tail rows of the decoder bounded replay
  *      csa2_encoder_replay_layout  rows of an extend under the encoder-side replay
+ *   0. csa2_kv_produce      the step before: pooled main KV and index keys into the caches
  *
  * Pages (cited by title and section):
  *   [MOD]  "DeepSeek V4.1 Flash modeling" (pages.haorui.li): sections "CSA2",
@@ -285,6 +286,40 @@ int csa2_replay_tail_layout(int32_t nreq, const int32_t* ext_len, const int32_t*
 int csa2_encoder_replay_layout(int32_t nreq, const int32_t* prefix_len, const int32_t* ext_len, int64_t n_ext,
                                int32_t budget, int32_t* row_start, int32_t* src_row, int32_t* abs_pos,
                                int32_t* win_lo, int32_t* req_of_row, int32_t capacity, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * csa2_kv_produce -- the index-K / main-KV producer that fills the caches the path reads
+ * ([MOD] "CSA2": non-overlapping compression, the index key projected from the
+ * compressed main KV; [MOD] "Mixed precision": main KV quantized after RoPE; [DAY0]
+ * section 1: pairwise compression keeps incomplete pairs across decode steps; section 5:
+ * BF16 weights with FP32 accumulation, ratio-2 pooling of each completed pair, RoPE, FP4
+ * quantization and cache write fused with the intermediate rounding kept).
+ *
+ * rows: the call's token rows (win_lo unused); rows of one request are consecutive and
+ * at ascending consecutive positions.  comp float [n][512]: the compressor's fp32 output
+ * of each token.  Row t at position p closes entry j = (p + 1) / m - 1 when (p + 1) % m
+ * == 0 (m = cache->ratio_m, 1 or 2); that entry, at row cache->row_start[r] + j of every
+ * cache buffer, is
+ *   latent = comp[t] (m = 1), or (first + comp[t]) * 0.5 in fp32 (m = 2), where first is
+ *            the previous row of the call when it holds position p - 1, else pending[r]
+ *   main   = latent with dims [448, 512) rotated (RoPE) at position P = j m + m - 1, in
+ *            interleaved pairs (2i, 2i+1): x' = x c - y s, y' = x s + y c, each product
+ *            and sum rounded to fp32, c = rope[P][0][i], s = rope[P][1][i]; stored to kv
+ *            as bf16 (nearest even) [rows][512], or as FP4_S16 codes [rows][256] with
+ *            kv_scale [rows][32]
+ *   index  = k_o = sum_i w_index[o][i] * bf16(latent_i) (fp32, one fma per term in
+ *            ascending i), dims [64, 128) rotated the same way, then MXFP4 into
+ *            index_codes [rows][64] and index_scales [rows][4] (csa2_quant_mx's rule).
+ * pending float [nreq][512] (m = 2; may be NULL for m = 1): a request whose rows in the
+ * call end at an even position leaves that token's comp row there; entries read pending
+ * as it was before the call.  Rows that close no entry write no cache row.
+ * w_index bf16 [128][512]; rope float [max_pos][2][32]; entries with P >= max_pos are
+ * not written (a precondition violation).  Buffers: comp, pending, w_index, kv and
+ * index_codes start on a 16-byte boundary.
+ * ------------------------------------------------------------------------------- */
+int csa2_kv_produce(const csa2_rows* rows, const csa2_cache* cache, const float* comp, float* pending,
+                    const uint16_t* w_index, const float* rope, int64_t max_pos, csa2_dtype kv_dtype, void* kv,
+                    uint8_t* kv_scale, uint8_t* index_codes, uint8_t* index_scales, void* stream);
 
 /* ---------------------------------------------------------------------------------
  * Helpers.

@@ -228,3 +228,22 @@ def test_topk_hier_noalloc_refuses_oversized_scratch():
     rc = L.csa2_topk_hier_noalloc(ctypes.byref(_rows()), ctypes.byref(_cache()), P, ctypes.c_int64(1024),
                                   ctypes.c_int32(512), ctypes.c_int32(16), ctypes.c_int32(2048), P, P, P, None)
     assert rc == B.CSA2_E_UNSUPPORTED
+
+
+def test_kv_produce_arg_errors():
+    L = B.lib()
+
+    def call(m=2, pend=P, kvdt=B.FP4_S16, kvs=P, comp=P, max_pos=1000, kv=P):
+        c = B._Cache(1, m, ctypes.c_void_p(64), ctypes.c_void_p(128))
+        return L.csa2_kv_produce(ctypes.byref(_rows()), ctypes.byref(c), comp, pend, P, P, ctypes.c_int64(max_pos),
+                                 kvdt, kv, kvs, P, P, None)
+
+    assert call(pend=None) == B.CSA2_E_ARG and "pending" in _err()
+    assert call(kvdt=B.MXFP8_E4M3) == B.CSA2_E_UNSUPPORTED
+    assert call(kvdt=B.BF16) == B.CSA2_E_ARG and "kv_scale" in _err()
+    assert call(kvs=None) == B.CSA2_E_ARG and "kv_scale" in _err()
+    assert call(comp=None) == B.CSA2_E_ARG
+    assert call(max_pos=0) == B.CSA2_E_ARG
+    assert call(comp=M) == B.CSA2_E_ARG and "16-byte" in _err()
+    assert call(kv=M) == B.CSA2_E_ARG and "16-byte" in _err()
+    assert call(m=3) == B.CSA2_E_UNSUPPORTED
