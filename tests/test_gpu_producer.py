@@ -2,8 +2,8 @@
 
 Every cache byte (main KV in bf16 or the FP4 storage format, MXFP4 index codes and
 scales, rows the call leaves alone included) and the pending state must match bit for
-bit: the producer's rounding is fixed step by step (readings in the design doc's table, the
-same on both sides), so the quantized codes it decides are reproducible.  Then the caches
+bit: the producer's rounding is fixed step by step (as include/csa2.h states it, the same
+on both sides), so the quantized codes it decides are reproducible.  Then the caches
 a decode sequence builds one token at a time must equal those of one prefill call, and a
 Full layer reading the produced caches must match the oracle reading its own."""
 import math
