@@ -40,6 +40,7 @@ from compressed_sparse_attention_fp4_amd import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 FP4_PEAK_TFLOPS = 10100.0  # dense FP4 MFMA, MI355X
+FP32_VALU_TFLOPS = 157.3   # fp32 vector, MI355X
 NREQ, SEQ, M = 64, 131072, 2
 C = SEQ // M
 HI, DI = 64, 128
@@ -428,6 +429,47 @@ def c4_decode(steps: int, warmup: int, dev, nreq: int = 32) -> dict:
                               "frac": att["alg_GBs"] / HBM_PEAK_GBS}}
 
 
+def kv_produce_rates(steps: int, warmup: int, dev) -> dict:
+    """The index-K / main-KV producer (csa2_kv_produce, m = 2, FP4 main KV) on two shapes:
+    the decode step's 64 new tokens (each closing a pair) and an 8 x 8192-token prefill
+    chunk (32,768 entries).  Algorithmic bytes: compressor rows read (2 KiB per token, plus
+    the pending row of a decode token) and 356 B of cache written per entry; work: the
+    128 x 512 fma projection per entry on fp32 VALU (the bound of the prefill shape)."""
+    out = {}
+    rope_rows = SEQ + 2
+    i = torch.arange(32, device=dev, dtype=torch.float64)
+    ang = torch.arange(rope_rows, device=dev, dtype=torch.float64)[:, None] * 10000.0 ** (-2.0 * i / 64)[None, :]
+    rope = torch.stack([ang.cos(), ang.sin()], dim=1).to(torch.float32).contiguous()
+    del ang
+    w_index = (synth.normal_bf16((128, D), 7, "w_index", device=dev) * 0.05).to(torch.bfloat16)
+    for name, nreq, ntok in (("decode_64", NREQ, 1), ("prefill_8x8192", 8, 8192)):
+        n = nreq * ntok
+        pos0 = SEQ - ntok
+        req = torch.arange(nreq, dtype=torch.int32, device=dev).repeat_interleave(ntok)
+        pos = (torch.arange(ntok, dtype=torch.int32, device=dev) + pos0).repeat(nreq)
+        rows = B.Rows(req, pos)
+        cache = B.Cache(M, torch.full((nreq,), SEQ // M, dtype=torch.int32, device=dev),
+                        torch.arange(nreq, dtype=torch.int64, device=dev) * (SEQ // M))
+        comp = synth.normal((n, D), 7, "comp/" + name, device=dev)
+        pending = synth.normal((nreq, D), 7, "pending/" + name, device=dev)
+        nrows = nreq * (SEQ // M)
+        kv = torch.empty((nrows, D // 2), dtype=torch.uint8, device=dev)
+        kvs = torch.empty((nrows, D // 16), dtype=torch.uint8, device=dev)
+        ic = torch.empty((nrows, DI // 2), dtype=torch.uint8, device=dev)
+        isc = torch.empty((nrows, DI // 32), dtype=torch.uint8, device=dev)
+        fn = lambda: B.kv_produce(rows, cache, comp, pending, w_index, rope, kv, ic, isc, kv_scale=kvs)  # noqa: E731
+        us = _time_graph(fn, steps, warmup, 1)
+        entries = n // M if ntok > 1 else nreq
+        nbytes = n * D * 4 + (nreq * D * 4 if ntok == 1 else 0) + entries * (D // 2 + D // 16 + DI // 2 + DI // 32)
+        flop = 2.0 * entries * DI * D
+        out[name] = {"us_per_launch": round(us, 2), "entries": entries, "alg_bytes": nbytes,
+                     "alg_GBs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                     "projection_TFLOP/s": round(flop / (us * 1e-6) / 1e12, 2),
+                     "fp32_valu_frac": round(flop / (us * 1e-6) / 1e12 / FP32_VALU_TFLOPS, 4)}
+        del comp, kv, kvs, ic, isc
+    return out
+
+
 def _time_graph(fn, steps: int, warmup: int, per: int) -> float:
     """Microseconds per call of fn's launches: captured once in a HIP graph, replayed
     back to back between two HIP events (per = calls inside fn)."""
@@ -668,6 +710,9 @@ def main():
     dst.copy_(src)
     torch.cuda.synchronize()
 
+    log("kv producer ...")
+    producer = kv_produce_rates(max(5, args.steps // 2), args.warmup, dev)
+
     c2 = None
     if not args.no_c2:
         log("C2 replay-tail prefill flow ...")
@@ -709,6 +754,7 @@ def main():
                    for s, v in stages.items()},
         "c2_replay_tail_prefill": c2,
         "fp4_main_kv_attn": fp4,
+        "kv_produce": producer,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -90,10 +90,15 @@ def _compare(caches, o, fp4):
     assert np.array_equal(isc.cpu().numpy(), o["index_scales"]), "index scales"
 
 
-@pytest.mark.parametrize("m,fp4", [(2, True), (2, False), (1, True), (1, False)])
-def test_kv_produce_one_call(orc, m, fp4):
-    say("case: kv producer, one call, m=%d fp4=%s" % (m, fp4))
+@pytest.mark.parametrize("m,fp4,wide", [(2, True, False), (2, False, False), (1, True, False), (1, False, False),
+                                        (2, True, True), (2, False, True), (1, True, True), (1, False, True)])
+def test_kv_produce_one_call(orc, m, fp4, wide):
+    """Short calls give each workgroup one row; calls of more than 4096 rows give it 8 m
+    rows, processed in rounds of 8 closing rows."""
+    say("case: kv producer, one call, m=%d fp4=%s wide=%s" % (m, fp4, wide))
     lens, prefix = [37, 20, 1, 300, 64, 9], [0, 5, 100, 2048, 7, 1001]
+    if wide:
+        lens, prefix = [3001, 20, 1, 1500, 64, 9], [0, 5, 100, 2049, 7, 1001]
     st = _Stream(600 + m, lens, prefix, m)
     caches = _dev_caches(st.rows_cache, fp4)
     pend = st.pending.clone().to(DEV)
