@@ -23,7 +23,7 @@ OP_TOPK, OP_TOPK_HIER, OP_ATTN = 1, 2, 3
 # Every symbol include/csa2.h declares.
 EXPORTS = ["csa2_index_score", "csa2_topk", "csa2_topk_hier", "csa2_topk_hier_noalloc", "csa2_sparse_swa_attn",
            "csa2_replay_tail_layout", "csa2_encoder_replay_layout", "csa2_workspace_size", "csa2_last_error",
-           "csa2_version", "csa2_quant_mx", "csa2_kv_produce"]
+           "csa2_version", "csa2_quant_mx", "csa2_kv_produce", "csa2_index_topk_pool"]
 TAIL_BORROW_PREFIX_WINDOW = 1
 
 
@@ -193,6 +193,22 @@ def index_score(rows: Rows, cache: Cache, q_idx: torch.Tensor, w: torch.Tensor, 
                                 ctypes.c_int64(scores.stride(0)), _stream(stream))
     _check(rc)
     return scores
+
+
+def index_topk_pool(rows: Rows, cache: Cache, q_idx: torch.Tensor, w: torch.Tensor, keys: IndexKeys, pool: Pool,
+                    k: int, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """csa2_index_topk_pool: the pool top-k of csa2_index_score + csa2_topk in one launch;
+    int32 [n, k] ascending positions, -1 padded."""
+    n, heads = q_idx.shape[0], q_idx.shape[1]
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.int32, device=q_idx.device)
+    w_stride = 0 if w.dim() == 1 else w.stride(0)
+    rc = lib().csa2_index_topk_pool(ctypes.byref(rows.c()), ctypes.byref(cache.c()), _ptr(q_idx),
+                                    ctypes.c_int(_dtype_code(q_idx)), ctypes.c_int32(heads), _ptr(w),
+                                    ctypes.c_int64(w_stride), ctypes.byref(keys.c()), ctypes.byref(pool.c()),
+                                    ctypes.c_int32(k), _ptr(out), _stream(stream))
+    _check(rc)
+    return out
 
 
 def workspace_size(op: int, n: int, cols: int, k: int, max_blocks: int = 0) -> int:

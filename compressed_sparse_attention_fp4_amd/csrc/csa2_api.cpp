@@ -208,6 +208,37 @@ int csa2_index_score(const csa2_rows* rows, const csa2_cache* cache, const void*
                          "csa2_index_score");
 }
 
+int csa2_index_topk_pool(const csa2_rows* rows, const csa2_cache* cache, const void* q_idx, csa2_dtype q_dtype,
+                         int32_t heads, const float* w, int64_t w_row_stride, const csa2_index_keys* keys,
+                         const csa2_pool* pool, int32_t k, int32_t* out_idx, void* stream)
+{
+    int rc;
+    if ((rc = check_rows(rows)) || (rc = check_cache(cache))) return rc;
+    if (!keys || !pool) return fail(CSA2_E_ARG, "keys / pool is NULL");
+    if (!q_idx || !w || !out_idx || !keys->data) return fail(CSA2_E_ARG, "q_idx / w / out_idx / keys->data is NULL");
+    if (w_row_stride < 0) return fail(CSA2_E_ARG, "w_row_stride < 0");
+    if (k < 1 || k > 2048) return fail(CSA2_E_ARG, "k = %d (1..2048)", k);
+    if (pool->block != 8) return fail(CSA2_E_UNSUPPORTED, "pool block %d (8 supported)", pool->block);
+    if (pool->max_blocks < 1 || pool->max_blocks > 2048)
+        return fail(CSA2_E_UNSUPPORTED, "pool max_blocks %d (1..2048: the pool fits one workgroup)", pool->max_blocks);
+    if ((rc = check_pool(pool, (int64_t)pool->block * pool->max_blocks))) return rc;
+    if (keys->dtype != CSA2_MXFP4 || keys->dim != 128 || !keys->scale)
+        return fail(CSA2_E_UNSUPPORTED, "fused pool top-k: MXFP4 keys of dim 128 with a scale plane");
+    if (q_dtype != CSA2_BF16) return fail(CSA2_E_UNSUPPORTED, "fused pool top-k: BF16 index q");
+    if (heads != 16 && heads != 32 && heads != 64)
+        return fail(CSA2_E_UNSUPPORTED, "fused pool top-k: heads %d (16, 32 or 64)", heads);
+    if (w_row_stride != 0 && w_row_stride < heads) return fail(CSA2_E_ARG, "w_row_stride < heads");
+    if (misaligned(q_idx, 16) || misaligned(keys->data, 16))
+        return fail(CSA2_E_ARG, "q_idx / keys->data must start on a 16-byte boundary");
+    if (rows->n == 0) return ok();
+    if ((rc = check_device())) return rc;
+    return launch_result(csa2::launch_score_topk_pool(rows_arg(rows), cache_arg(cache),
+                                                      static_cast<const uint16_t*>(q_idx), heads, w, w_row_stride,
+                                                      static_cast<const uint8_t*>(keys->data), keys->scale,
+                                                      pool_arg(pool), k, out_idx, static_cast<hipStream_t>(stream)),
+                         "csa2_index_topk_pool");
+}
+
 int csa2_topk(const csa2_rows* rows, const csa2_cache* cache, const float* scores, int64_t score_stride,
               const csa2_pool* pool, int32_t k, int32_t* out_idx, void* workspace, size_t workspace_bytes,
               void* stream)

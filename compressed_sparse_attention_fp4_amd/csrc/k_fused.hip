@@ -1,0 +1,226 @@
+// Fused pool scoring + top-k: the restricted scoring and the selection of a Reindex
+// layer in one kernel, with no score written to memory.
+//
+// Pages: "DeepSeek V4.1 Flash modeling", section "Hierarchical Sparse Indexer" (later index
+// layers rescore only the shared candidate pool and take their own top-k inside it; the
+// section's measurement notes ask for the fused module of restricted scoring and
+// selection and its data movement); "SGLang and Miles Day-0 support for DeepSeek-V4.1",
+// section 5 (the indexer scores the FP4 cache directly, MQA form).
+//
+// One workgroup of 1024 threads per query row.  Its 16 waves score the row's pool
+// columns (at most 2048 blocks of 8 = 16384) exactly as csa2_index_score does for a pool
+// (the same MXFP4 MFMA tiles, head permutation and fixed head-sum order, so every score
+// is bit for bit the same), turn each score into its order key in LDS (a column past the
+// pool, or a pool position past the row's reach, is no candidate), and then run the
+// radix selection of csa2_topk over those keys: thread t takes keys [16 t, 16 t + 16),
+// two whole pool blocks, so positions follow from the block ids in LDS.  The result is
+// the index set csa2_index_score + csa2_topk give, without the 64 KiB score row per query
+// going to memory and back.
+#include "csa2_device.h"
+#include "csa2_launch.h"
+#include "csa2_score.h"
+#include "csa2_select.h"
+
+#pragma clang fp contract(off)
+
+namespace csa2 {
+
+constexpr int kFusedNT = 1024;
+constexpr int kFusedKPT = 16;
+constexpr int kFusedCap = kFusedNT * kFusedKPT;  // 16384 pool columns
+
+template <int NHT>
+__global__ __launch_bounds__(1024) void k_score_topk_pool(RowsArg rows, CacheArg cache, const uint16_t* __restrict__ q,
+                                                          const float* __restrict__ w, int64_t w_stride,
+                                                          const uint8_t* __restrict__ kdata,
+                                                          const uint8_t* __restrict__ kscale, PoolArg pool, int k,
+                                                          int32_t* __restrict__ out_idx)
+{
+    constexpr int H = NHT * 16;
+    constexpr int G = H / 4;
+    constexpr int NW = kFusedNT / 64;
+    __shared__ uint4 s_qa[NHT][64];
+    __shared__ uint32_t s_qs[NHT][64];
+    __shared__ int32_t s_bid[kFusedCap / 8];
+    __shared__ __attribute__((aligned(16))) uint32_t s_key[kFusedCap];
+
+    int row, unused;
+    xcd_row_chunk(blockIdx.x, rows.n, 1, &row, &unused);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = rows.req[row];
+    const int64_t R = reach(rows.pos[row], cache.ratio_m, cache.n_entries[r]);
+    const int prow = pool.row_map ? pool.row_map[row] : row;
+    const int nb = R > 0 ? pool.nblocks[prow] : 0;  // <= max_blocks <= 2048 (host-checked)
+    const int ncol = __builtin_amdgcn_readfirstlane(nb * 8);
+    const int R32 = __builtin_amdgcn_readfirstlane((int)R);  // positions < n_entries fit 32 bits
+
+    // ---- the row's index q quantized into A operands (one 32-element block per thread),
+    // the pool's block ids and the lane group's head weights
+    if (tid < NHT * 64) {
+        const int t = tid >> 6, l = tid & 63;
+        const int m = l & 15, blk = l >> 4;
+        const int head = G * (m >> 2) + 4 * t + (m & 3);
+        const uint16_t* src = q + ((int64_t)row * H + head) * 128 + blk * 32;
+        u32x4_t x[4] = {gload_x4<0>(src), gload_x4<16>(src), gload_x4<32>(src), gload_x4<48>(src)};
+        float v[32];
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++) {
+                v[i * 8 + 2 * jj] = __uint_as_float(x[i][jj] << 16);
+                v[i * 8 + 2 * jj + 1] = __uint_as_float(x[i][jj] & 0xFFFF0000u);
+            }
+        uint32_t o[4], sb;
+        quant_block_e2m1(v, o, &sb);
+        s_qa[t][l] = make_uint4(o[0], o[1], o[2], o[3]);
+        s_qs[t][l] = sb;
+    }
+    {
+        const int32_t* bid_row = pool.blocks + (int64_t)prow * pool.max_blocks;
+        for (int i = tid; i < kFusedCap / 8; i += kFusedNT) s_bid[i] = i < nb ? bid_row[i] : 0;
+    }
+    const int g = lane >> 4;
+    float wr[NHT * 4];
+    {
+        const float* wrow = w + (int64_t)row * w_stride + G * g;
+#pragma unroll
+        for (int t = 0; t < NHT; t++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) wr[4 * t + i] = wrow[4 * t + i];
+    }
+    __syncthreads();
+    i32x8 a[NHT];
+    int sa[NHT];
+#pragma unroll
+    for (int t = 0; t < NHT; t++) {
+        const uint4 u = s_qa[t][lane];
+        a[t] = i32x8{(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
+        sa[t] = (int)s_qs[t][lane];
+    }
+
+    // ---- scores of 64 columns per wave and group; wave w takes groups w, w + 16, ...,
+    // loading the next group's key tiles while it scores the current one
+    const int64_t krow0 = cache.row_start[r];
+    const uint8_t* kd_base = kdata + krow0 * 64 + 16 * (lane >> 4);
+    const uint8_t* ks_base = kscale + krow0 * 4 + (lane >> 4);
+    auto load = [&](int off0, u32x4_t (&kd)[4], int (&sk)[4]) {
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const int off = off0 + 16 * u + (lane & 15);
+            const int oc = off < ncol ? off : 0;
+            const int pos = (s_bid[oc >> 3] << 3) | (oc & 7);
+            const int j = (off < ncol && pos < R32) ? pos : 0;
+            kd[u] = gload_x4<0>(kd_base + ((uint64_t)(uint32_t)j << 6));
+            sk[u] = gload_u8<0>(ks_base + ((uint64_t)(uint32_t)j << 2));
+        }
+    };
+    auto score_group = [&](int off0, const u32x4_t (&kd)[4], const int (&sk)[4]) {
+        float P[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            f32x4 d[NHT];
+            const i32x8 b = i32x8{(int)kd[u][0], (int)kd[u][1], (int)kd[u][2], (int)kd[u][3], 0, 0, 0, 0};
+#pragma unroll
+            for (int t = 0; t < NHT; t++) {
+                const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+                d[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[t], b, zero, 4, 4, 0, sa[t], 0, sk[u]);
+            }
+            float pp = 0.0f;
+#pragma unroll
+            for (int t = 0; t < NHT; t++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) pp = __builtin_fmaf(wr[4 * t + i], relu_bits(d[t][i]), pp);
+            P[u] = pp;
+        }
+        // lane group g holds P_g of tiles 0..3; after the swaps lane (g, c) holds the score
+        // of tile g, position c, i.e. column off0 + lane
+        auto s01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(P[0]), __float_as_uint(P[1]), false, false);
+        auto s23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(P[2]), __float_as_uint(P[3]), false, false);
+        const float h01 = __uint_as_float(s01[0]) + __uint_as_float(s01[1]);
+        const float h23 = __uint_as_float(s23[0]) + __uint_as_float(s23[1]);
+        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(h01), __float_as_uint(h23), false, false);
+        const float score = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        const int off = off0 + lane;
+        uint32_t key = 0u;
+        if (off < ncol) {
+            const int pos = (s_bid[off >> 3] << 3) | (off & 7);
+            key = pos < R32 ? order_key(score) : 0u;
+        }
+        s_key[off] = key;
+    };
+    const int ngrp = (ncol + 63) >> 6;
+    const int mine = wave < ngrp ? (ngrp - wave + NW - 1) / NW : 0;  // groups of this wave
+    {
+        u32x4_t ka[4], kb[4];
+        int sa4[4], sb4[4];
+        if (mine > 0) load(64 * wave, ka, sa4);
+        int i = 0;
+        for (; i + 1 < mine; i += 2) {
+            load(64 * (wave + NW * (i + 1)), kb, sb4);
+            score_group(64 * (wave + NW * i), ka, sa4);
+            if (i + 2 < mine) load(64 * (wave + NW * (i + 2)), ka, sa4);
+            score_group(64 * (wave + NW * (i + 1)), kb, sb4);
+        }
+        if (i < mine) score_group(64 * (wave + NW * i), ka, sa4);
+    }
+    // groups past the pool hold no candidate
+    for (int c = 64 * ngrp + tid; c < kFusedCap; c += kFusedNT) s_key[c] = 0u;
+    __syncthreads();
+
+    // ---- selection over the LDS keys
+    uint32_t key[kFusedKPT];
+    {
+        const uint4* kp = reinterpret_cast<const uint4*>(s_key + kFusedKPT * tid);
+#pragma unroll
+        for (int v4 = 0; v4 < kFusedKPT / 4; v4++) {
+            const uint4 u = kp[v4];
+            key[4 * v4] = u.x;
+            key[4 * v4 + 1] = u.y;
+            key[4 * v4 + 2] = u.z;
+            key[4 * v4 + 3] = u.w;
+        }
+    }
+    int32_t bid[bid_slots(kFusedKPT)];
+#pragma unroll
+    for (int b8 = 0; b8 < bid_slots(kFusedKPT); b8++) bid[b8] = s_bid[bid_slots(kFusedKPT) * tid + b8];
+    SelArgs sel{};
+    sel.src.rows = rows;
+    sel.src.cache = cache;
+    sel.src.pool = pool;
+    sel.src.stride = kFusedCap;
+    sel.block = 8;
+    sel.block_shift = 3;
+    sel.k = k;
+    sel.nseg = 1;
+    sel.seg_len = kFusedCap;
+    sel.out_idx = out_idx;
+    sel.out_stride = k;
+    sel.out_mode = OUT_IDX;
+    select_core<kFusedKPT, SRC_POOL, kFusedNT>(sel, row, 0, R, ncol, prow, 0, (int64_t)kFusedKPT * tid, key, bid,
+                                               true);
+}
+
+hipError_t launch_score_topk_pool(const RowsArg& rows, const CacheArg& cache, const uint16_t* q, int heads,
+                                  const float* w, int64_t w_stride, const uint8_t* kdata, const uint8_t* kscale,
+                                  const PoolArg& pool, int k, int32_t* out_idx, hipStream_t stream)
+{
+    if (rows.n == 0) return hipSuccess;
+    const dim3 grid((unsigned)rows.n);
+#define CSA2_FUSED_CASE(T)                                                                                     \
+    case T:                                                                                                    \
+        hipLaunchKernelGGL((k_score_topk_pool<T>), grid, dim3(kFusedNT), 0, stream, rows, cache, q, w, w_stride, \
+                           kdata, kscale, pool, k, out_idx);                                                   \
+        break;
+    switch (heads / 16) {
+        CSA2_FUSED_CASE(1)
+        CSA2_FUSED_CASE(2)
+        CSA2_FUSED_CASE(4)
+        default:
+            return hipErrorInvalidValue;
+    }
+#undef CSA2_FUSED_CASE
+    return hipGetLastError();
+}
+
+}  // namespace csa2

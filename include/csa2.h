@@ -180,6 +180,20 @@ int csa2_topk(const csa2_rows* rows, const csa2_cache* cache, const float* score
               void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * csa2_index_topk_pool -- csa2_index_score over a candidate pool and csa2_topk over its
+ * scores in one call, with no score written to memory ([MOD] "Hierarchical Sparse
+ * Indexer": Reindex layers rescore only the shared pool and select inside it; the
+ * section's measurement notes name the fused module of restricted scoring and selection).
+ * out_idx [n][k] is exactly what csa2_index_score (pool) followed by csa2_topk (pool) give:
+ * the k best pool positions below the row's reach, ascending, -1 padded (ties to the lower
+ * position).  Supported: MXFP4 keys of dim 128, BF16 index q, heads 16 / 32 / 64, pool
+ * block 8 with max_blocks <= 2048 (the pages' 16,384-position pool), k 1..2048.
+ * ------------------------------------------------------------------------------- */
+int csa2_index_topk_pool(const csa2_rows* rows, const csa2_cache* cache, const void* q_idx, csa2_dtype q_dtype,
+                         int32_t heads, const float* w, int64_t w_row_stride, const csa2_index_keys* keys,
+                         const csa2_pool* pool, int32_t k, int32_t* out_idx, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * csa2_topk_hier -- the source pass of the hierarchical indexer ([MOD] "Hierarchical
  * Sparse Indexer"; [DAY0] section 2, "two-level selection"): the flat top-k over all
  * reachable positions (as csa2_topk without a pool) AND the candidate pool: blocks
