@@ -143,6 +143,14 @@ def attn_fp4kv(x: InputSet):
                           kv_scale=x.kv4s)
 
 
+def reindex_fused(x: InputSet):
+    """The step's 7 Reindex selections through the fused pool scoring + top-k (same index
+    sets as score_pool + topk_pool, no score row written)."""
+    for l in range(1, LAYERS):
+        Ll = x.layers[l]
+        B.index_topk_pool(x.rows, x.cache, Ll["qi"], Ll["w"], x.keys, x.pool, K, out=x.idx[l])
+
+
 def launch_ms_of(fn, sets, reps: int, per: int) -> float:
     """Average launch duration of fn's calls over every input set, as in stage_launch_ms."""
     g = torch.cuda.CUDAGraph()
@@ -689,6 +697,12 @@ def main():
            "frac": fp4_gbs / HBM_PEAK_GBS, "traffic": measured_traffic("attn_fp4kv"),
            "step_ms_with_fp4_kv": (sum(per_step_ms.values()) - per_step_ms["attn"] + LAYERS * fp4_ms)}
     log("FP4 main KV attention: %.2f us per launch (%.1f GB/s algorithmic)" % (fp4_ms * 1e3, fp4_gbs))
+    fused_ms = launch_ms_of(reindex_fused, sets, max(3, args.steps // 4), LAYERS - 1)
+    fused = {"kernel": "k_score_topk_pool", "us_per_launch": round(fused_ms * 1e3, 2),
+             "replaces_us": round((launch_ms["score_pool"] + launch_ms["topk_pool"]) * 1e3, 2),
+             "step_ms_with_fused_reindex": sum(per_step_ms.values()) - (LAYERS - 1) * (
+                 launch_ms["score_pool"] + launch_ms["topk_pool"] - fused_ms)}
+    log("fused pool scoring + top-k: %.2f us per launch" % (fused_ms * 1e3))
 
     # spread of single steps: each replay alone between two HIP events (outside the timed
     # region above, which is the reported value)
@@ -754,6 +768,7 @@ def main():
                    for s, v in stages.items()},
         "c2_replay_tail_prefill": c2,
         "fp4_main_kv_attn": fp4,
+        "fused_reindex_select": fused,
         "kv_produce": producer,
         "cpu_baseline": cpu,
     }

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libcsa2.so")
 
 CSA2_OK, CSA2_E_ARG, CSA2_E_UNSUPPORTED, CSA2_E_WORKSPACE, CSA2_E_LAUNCH = 0, 1, 2, 3, 4
 F32, BF16, MXFP4, MXFP8_E4M3, FP4_S16 = 0, 1, 2, 3, 4
-OP_TOPK, OP_TOPK_HIER, OP_ATTN = 1, 2, 3
+OP_TOPK, OP_TOPK_HIER, OP_ATTN, OP_TOPK_POOL_FUSED = 1, 2, 3, 4
 
 # Every symbol include/csa2.h declares.
 EXPORTS = ["csa2_index_score", "csa2_topk", "csa2_topk_hier", "csa2_topk_hier_noalloc", "csa2_sparse_swa_attn",
@@ -196,17 +196,21 @@ def index_score(rows: Rows, cache: Cache, q_idx: torch.Tensor, w: torch.Tensor, 
 
 
 def index_topk_pool(rows: Rows, cache: Cache, q_idx: torch.Tensor, w: torch.Tensor, keys: IndexKeys, pool: Pool,
-                    k: int, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """csa2_index_topk_pool: the pool top-k of csa2_index_score + csa2_topk in one launch;
-    int32 [n, k] ascending positions, -1 padded."""
+                    k: int, out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """csa2_index_topk_pool: the pool top-k of csa2_index_score + csa2_topk without the score
+    rows; int32 [n, k] ascending positions, -1 padded."""
     n, heads = q_idx.shape[0], q_idx.shape[1]
     if out is None:
         out = torch.empty((n, k), dtype=torch.int32, device=q_idx.device)
+    if workspace is None:
+        workspace = _workspace(workspace_size(OP_TOPK_POOL_FUSED, n, pool.block * pool.max_blocks, k), q_idx.device)
     w_stride = 0 if w.dim() == 1 else w.stride(0)
     rc = lib().csa2_index_topk_pool(ctypes.byref(rows.c()), ctypes.byref(cache.c()), _ptr(q_idx),
                                     ctypes.c_int(_dtype_code(q_idx)), ctypes.c_int32(heads), _ptr(w),
                                     ctypes.c_int64(w_stride), ctypes.byref(keys.c()), ctypes.byref(pool.c()),
-                                    ctypes.c_int32(k), _ptr(out), _stream(stream))
+                                    ctypes.c_int32(k), _ptr(out), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+                                    _stream(stream))
     _check(rc)
     return out
 

@@ -158,6 +158,9 @@ size_t csa2_workspace_size(int op, int32_t n, int64_t cols, int32_t k, int32_t m
             return csa2::topk_hier_workspace(n, cols, k, 8, max_blocks > 0 ? max_blocks : 1);
         case CSA2_OP_ATTN:
             return 0;
+        case CSA2_OP_TOPK_POOL_FUSED:
+            // cols = block * max_blocks of the pool
+            return csa2::score_topk_pool_workspace(n, cols, k);
         default:
             return 0;
     }
@@ -210,7 +213,8 @@ int csa2_index_score(const csa2_rows* rows, const csa2_cache* cache, const void*
 
 int csa2_index_topk_pool(const csa2_rows* rows, const csa2_cache* cache, const void* q_idx, csa2_dtype q_dtype,
                          int32_t heads, const float* w, int64_t w_row_stride, const csa2_index_keys* keys,
-                         const csa2_pool* pool, int32_t k, int32_t* out_idx, void* stream)
+                         const csa2_pool* pool, int32_t k, int32_t* out_idx, void* workspace,
+                         size_t workspace_bytes, void* stream)
 {
     int rc;
     if ((rc = check_rows(rows)) || (rc = check_cache(cache))) return rc;
@@ -231,11 +235,15 @@ int csa2_index_topk_pool(const csa2_rows* rows, const csa2_cache* cache, const v
     if (misaligned(q_idx, 16) || misaligned(keys->data, 16))
         return fail(CSA2_E_ARG, "q_idx / keys->data must start on a 16-byte boundary");
     if (rows->n == 0) return ok();
+    const size_t need = csa2::score_topk_pool_workspace(rows->n, (int64_t)pool->block * pool->max_blocks, k);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(CSA2_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
     if ((rc = check_device())) return rc;
     return launch_result(csa2::launch_score_topk_pool(rows_arg(rows), cache_arg(cache),
                                                       static_cast<const uint16_t*>(q_idx), heads, w, w_row_stride,
                                                       static_cast<const uint8_t*>(keys->data), keys->scale,
-                                                      pool_arg(pool), k, out_idx, static_cast<hipStream_t>(stream)),
+                                                      pool_arg(pool), k, out_idx, workspace,
+                                                      static_cast<hipStream_t>(stream)),
                          "csa2_index_topk_pool");
 }
 

@@ -62,10 +62,16 @@ struct SelSource {
 
 size_t topk_workspace(int n, int64_t stride, int k, bool pool);
 
-// Fused pool scoring + top-k (block 8, at most 2048 blocks; heads 16, 32 or 64).
+// Exact merge of nlists (key, position) lists of k per row into the row's top-k indices.
+hipError_t launch_list_merge(const SelSource& src, int k, int nlists, const uint2* lists, int32_t* out,
+                             hipStream_t stream);
+
+// Fused pool scoring + top-k (block 8, at most 2048 blocks; heads 16, 32 or 64); pools
+// of more than 4096 columns need the segment lists' workspace.
+size_t score_topk_pool_workspace(int n, int64_t cols, int k);
 hipError_t launch_score_topk_pool(const RowsArg& rows, const CacheArg& cache, const uint16_t* q, int heads,
                                   const float* w, int64_t w_stride, const uint8_t* kdata, const uint8_t* kscale,
-                                  const PoolArg& pool, int k, int32_t* out_idx, hipStream_t stream);
+                                  const PoolArg& pool, int k, int32_t* out_idx, void* ws, hipStream_t stream);
 hipError_t launch_topk(const SelSource& src, int k, int32_t* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 size_t topk_hier_workspace(int n, int64_t stride, int k, int block, int max_blocks);

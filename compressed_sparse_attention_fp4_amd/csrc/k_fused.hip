@@ -7,15 +7,17 @@
 // selection and its data movement); "SGLang and Miles Day-0 support for DeepSeek-V4.1",
 // section 5 (the indexer scores the FP4 cache directly, MQA form).
 //
-// One workgroup of 1024 threads per query row.  Its 16 waves score the row's pool
-// columns (at most 2048 blocks of 8 = 16384) exactly as csa2_index_score does for a pool
-// (the same MXFP4 MFMA tiles, head permutation and fixed head-sum order, so every score
-// is bit for bit the same), turn each score into its order key in LDS (a column past the
-// pool, or a pool position past the row's reach, is no candidate), and then run the
-// radix selection of csa2_topk over those keys: thread t takes keys [16 t, 16 t + 16),
-// two whole pool blocks, so positions follow from the block ids in LDS.  The result is
-// the index set csa2_index_score + csa2_topk give, without the 64 KiB score row per query
-// going to memory and back.
+// One workgroup of 512 threads per query row and segment of 4096 pool columns (512
+// blocks of 8; a pool of 2048 blocks has 4 segments).  Its 8 waves score the segment
+// exactly as csa2_index_score does for a pool (the same MXFP4 MFMA tiles, head
+// permutation and fixed head-sum order, so every score is bit for bit the same), turn
+// each score into its order key in LDS (a column past the pool, or a pool position past
+// the row's reach, is no candidate), and run the radix selection of csa2_topk over those
+// keys: thread t takes keys [8 t, 8 t + 8), one whole pool block, so positions follow
+// from the block ids in LDS.  A one-segment pool writes the index set directly; longer
+// pools write each segment's top-k as (key, position) lists, which csa2_topk's exact list
+// merge reduces to the index set.  The result is what csa2_index_score + csa2_topk give,
+// without the 64 KiB score row per query going to memory and back.
 #include "csa2_device.h"
 #include "csa2_launch.h"
 #include "csa2_score.h"
@@ -25,16 +27,17 @@
 
 namespace csa2 {
 
-constexpr int kFusedNT = 1024;
-constexpr int kFusedKPT = 16;
-constexpr int kFusedCap = kFusedNT * kFusedKPT;  // 16384 pool columns
+constexpr int kFusedNT = 512;
+constexpr int kFusedKPT = 8;
+constexpr int kFusedCap = kFusedNT * kFusedKPT;  // 4096 pool columns per segment
 
 template <int NHT>
-__global__ __launch_bounds__(1024) void k_score_topk_pool(RowsArg rows, CacheArg cache, const uint16_t* __restrict__ q,
-                                                          const float* __restrict__ w, int64_t w_stride,
-                                                          const uint8_t* __restrict__ kdata,
-                                                          const uint8_t* __restrict__ kscale, PoolArg pool, int k,
-                                                          int32_t* __restrict__ out_idx)
+__global__ __launch_bounds__(512) void k_score_topk_pool(RowsArg rows, CacheArg cache, const uint16_t* __restrict__ q,
+                                                         const float* __restrict__ w, int64_t w_stride,
+                                                         const uint8_t* __restrict__ kdata,
+                                                         const uint8_t* __restrict__ kscale, PoolArg pool, int k,
+                                                         int nseg, int32_t* __restrict__ out_idx,
+                                                         uint2* __restrict__ out_list)
 {
     constexpr int H = NHT * 16;
     constexpr int G = H / 4;
@@ -44,15 +47,20 @@ __global__ __launch_bounds__(1024) void k_score_topk_pool(RowsArg rows, CacheArg
     __shared__ int32_t s_bid[kFusedCap / 8];
     __shared__ __attribute__((aligned(16))) uint32_t s_key[kFusedCap];
 
-    int row, unused;
-    xcd_row_chunk(blockIdx.x, rows.n, 1, &row, &unused);
+    int row, seg;
+    xcd_row_chunk(blockIdx.x, rows.n, nseg, &row, &seg);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = rows.req[row];
     const int64_t R = reach(rows.pos[row], cache.ratio_m, cache.n_entries[r]);
     const int prow = pool.row_map ? pool.row_map[row] : row;
-    const int nb = R > 0 ? pool.nblocks[prow] : 0;  // <= max_blocks <= 2048 (host-checked)
-    const int ncol = __builtin_amdgcn_readfirstlane(nb * 8);
+    const int nb_row = R > 0 ? pool.nblocks[prow] : 0;  // <= max_blocks <= 2048 (host-checked)
+    const int ncol_row = nb_row * 8;
+    const int c_begin = seg * kFusedCap;            // the segment's first pool column
+    const int nb0 = c_begin / 8;                    // and block
+    int nbs = nb_row - nb0;                         // blocks of the segment
+    nbs = nbs < 0 ? 0 : (nbs > kFusedCap / 8 ? kFusedCap / 8 : nbs);
+    const int ncol = __builtin_amdgcn_readfirstlane(nbs * 8);  // columns of the segment
     const int R32 = __builtin_amdgcn_readfirstlane((int)R);  // positions < n_entries fit 32 bits
 
     // ---- the row's index q quantized into A operands (one 32-element block per thread),
@@ -77,8 +85,8 @@ __global__ __launch_bounds__(1024) void k_score_topk_pool(RowsArg rows, CacheArg
         s_qs[t][l] = sb;
     }
     {
-        const int32_t* bid_row = pool.blocks + (int64_t)prow * pool.max_blocks;
-        for (int i = tid; i < kFusedCap / 8; i += kFusedNT) s_bid[i] = i < nb ? bid_row[i] : 0;
+        const int32_t* bid_row = pool.blocks + (int64_t)prow * pool.max_blocks + nb0;
+        for (int i = tid; i < kFusedCap / 8; i += kFusedNT) s_bid[i] = i < nbs ? bid_row[i] : 0;
     }
     const int g = lane >> 4;
     float wr[NHT * 4];
@@ -99,7 +107,7 @@ __global__ __launch_bounds__(1024) void k_score_topk_pool(RowsArg rows, CacheArg
         sa[t] = (int)s_qs[t][lane];
     }
 
-    // ---- scores of 64 columns per wave and group; wave w takes groups w, w + 16, ...,
+    // ---- scores of 64 columns per wave and group; wave w takes groups w, w + NW, ...,
     // loading the next group's key tiles while it scores the current one
     const int64_t krow0 = cache.row_start[r];
     const uint8_t* kd_base = kdata + krow0 * 64 + 16 * (lane >> 4);
@@ -188,29 +196,38 @@ __global__ __launch_bounds__(1024) void k_score_topk_pool(RowsArg rows, CacheArg
     sel.src.rows = rows;
     sel.src.cache = cache;
     sel.src.pool = pool;
-    sel.src.stride = kFusedCap;
+    sel.src.stride = (int64_t)pool.block * pool.max_blocks;
     sel.block = 8;
     sel.block_shift = 3;
     sel.k = k;
-    sel.nseg = 1;
+    sel.nseg = nseg;
     sel.seg_len = kFusedCap;
     sel.out_idx = out_idx;
+    sel.out_list = out_list;
     sel.out_stride = k;
-    sel.out_mode = OUT_IDX;
-    select_core<kFusedKPT, SRC_POOL, kFusedNT>(sel, row, 0, R, ncol, prow, 0, (int64_t)kFusedKPT * tid, key, bid,
-                                               true);
+    sel.out_mode = nseg > 1 ? OUT_LIST : OUT_IDX;
+    select_core<kFusedKPT, SRC_POOL, kFusedNT>(sel, row, seg, R, (int64_t)ncol_row, prow, c_begin,
+                                               (int64_t)kFusedKPT * tid, key, bid, true);
+}
+
+size_t score_topk_pool_workspace(int n, int64_t cols, int k)
+{
+    const int64_t nseg = (cols + kFusedCap - 1) / kFusedCap;
+    return nseg > 1 ? (size_t)n * nseg * k * sizeof(uint2) : 0;
 }
 
 hipError_t launch_score_topk_pool(const RowsArg& rows, const CacheArg& cache, const uint16_t* q, int heads,
                                   const float* w, int64_t w_stride, const uint8_t* kdata, const uint8_t* kscale,
-                                  const PoolArg& pool, int k, int32_t* out_idx, hipStream_t stream)
+                                  const PoolArg& pool, int k, int32_t* out_idx, void* ws, hipStream_t stream)
 {
     if (rows.n == 0) return hipSuccess;
-    const dim3 grid((unsigned)rows.n);
+    const int nseg = (int)(((int64_t)pool.block * pool.max_blocks + kFusedCap - 1) / kFusedCap);
+    uint2* lists = nseg > 1 ? static_cast<uint2*>(ws) : nullptr;
+    const dim3 grid((unsigned)((int64_t)rows.n * nseg));
 #define CSA2_FUSED_CASE(T)                                                                                     \
     case T:                                                                                                    \
         hipLaunchKernelGGL((k_score_topk_pool<T>), grid, dim3(kFusedNT), 0, stream, rows, cache, q, w, w_stride, \
-                           kdata, kscale, pool, k, out_idx);                                                   \
+                           kdata, kscale, pool, k, nseg, out_idx, lists);                                       \
         break;
     switch (heads / 16) {
         CSA2_FUSED_CASE(1)
@@ -220,7 +237,10 @@ hipError_t launch_score_topk_pool(const RowsArg& rows, const CacheArg& cache, co
             return hipErrorInvalidValue;
     }
 #undef CSA2_FUSED_CASE
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || nseg == 1) return e;
+    SelSource src{nullptr, (int64_t)pool.block * pool.max_blocks, rows, cache, pool};
+    return launch_list_merge(src, k, nseg, lists, out_idx, stream);
 }
 
 }  // namespace csa2

@@ -413,6 +413,23 @@ size_t topk_workspace(int n, int64_t stride, int k, bool pool)
     return plan_workspace(make_plan(stride, k, pool ? SRC_POOL : SRC_FULL), n, k);
 }
 
+hipError_t launch_list_merge(const SelSource& src, int k, int nlists, const uint2* lists, int32_t* out,
+                             hipStream_t stream)
+{
+    SelArgs a{};
+    a.src = src;
+    a.k = k;
+    a.nseg = 1;
+    a.seg_len = nlists;
+    a.nlists_prev = nlists;
+    a.in = lists;
+    a.out_idx = out;
+    a.out_stride = k;
+    a.out_mode = OUT_IDX;
+    hipError_t e = launch_level<SRC_LIST>(dim3((unsigned)src.rows.n), (int64_t)nlists * k, src.rows.n, a, stream);
+    return e == hipSuccess ? hipGetLastError() : e;
+}
+
 hipError_t launch_topk(const SelSource& src, int k, int32_t* out, void* ws, size_t ws_bytes, hipStream_t stream)
 {
     (void)ws_bytes;

@@ -188,10 +188,14 @@ int csa2_topk(const csa2_rows* rows, const csa2_cache* cache, const float* score
  * the k best pool positions below the row's reach, ascending, -1 padded (ties to the lower
  * position).  Supported: MXFP4 keys of dim 128, BF16 index q, heads 16 / 32 / 64, pool
  * block 8 with max_blocks <= 2048 (the pages' 16,384-position pool), k 1..2048.
+ * A pool is scored in segments of 4096 columns; pools of more than one segment need
+ * workspace (csa2_workspace_size(CSA2_OP_TOPK_POOL_FUSED, n, block * max_blocks, k, 0):
+ * each segment's top-k as (key, position) lists, merged exactly by a second launch).
  * ------------------------------------------------------------------------------- */
 int csa2_index_topk_pool(const csa2_rows* rows, const csa2_cache* cache, const void* q_idx, csa2_dtype q_dtype,
                          int32_t heads, const float* w, int64_t w_row_stride, const csa2_index_keys* keys,
-                         const csa2_pool* pool, int32_t k, int32_t* out_idx, void* stream);
+                         const csa2_pool* pool, int32_t k, int32_t* out_idx, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------
  * csa2_topk_hier -- the source pass of the hierarchical indexer ([MOD] "Hierarchical
@@ -338,10 +342,11 @@ int csa2_kv_produce(const csa2_rows* rows, const csa2_cache* cache, const float*
 /* ---------------------------------------------------------------------------------
  * Helpers.
  * ------------------------------------------------------------------------------- */
-enum { CSA2_OP_TOPK = 1, CSA2_OP_TOPK_HIER = 2, CSA2_OP_ATTN = 3 };
+enum { CSA2_OP_TOPK = 1, CSA2_OP_TOPK_HIER = 2, CSA2_OP_ATTN = 3, CSA2_OP_TOPK_POOL_FUSED = 4 };
 
-/* Workspace bytes for an op: n rows, `cols` = score_stride (TOPK / TOPK_HIER) or
- * the number of selected entries k (ATTN), k, max_blocks (TOPK_HIER). */
+/* Workspace bytes for an op: n rows, `cols` = score_stride (TOPK / TOPK_HIER), the pool's
+ * block * max_blocks (TOPK_POOL_FUSED) or the number of selected entries k (ATTN), k,
+ * max_blocks (TOPK_HIER). */
 size_t csa2_workspace_size(int op, int32_t n, int64_t cols, int32_t k, int32_t max_blocks);
 
 /* Message of the calling thread's last error ("" after success). */

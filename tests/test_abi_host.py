@@ -247,3 +247,26 @@ def test_kv_produce_arg_errors():
     assert call(comp=M) == B.CSA2_E_ARG and "16-byte" in _err()
     assert call(kv=M) == B.CSA2_E_ARG and "16-byte" in _err()
     assert call(m=3) == B.CSA2_E_UNSUPPORTED
+
+
+def test_index_topk_pool_arg_errors():
+    L = B.lib()
+    keys = B._IndexKeys(B.MXFP4, 128, P, P)
+
+    def call(heads=64, block=8, maxb=2048, k=512, ws=P, nbytes=1 << 30, qdt=B.BF16, kk=None):
+        pool = B._Pool(block, maxb, P, P, None)
+        return L.csa2_index_topk_pool(ctypes.byref(_rows()), ctypes.byref(_cache()), P, qdt, ctypes.c_int32(heads), P,
+                                      ctypes.c_int64(64), ctypes.byref(kk or keys), ctypes.byref(pool),
+                                      ctypes.c_int32(k), P, ws, ctypes.c_size_t(nbytes), None)
+
+    assert call(heads=48) == B.CSA2_E_UNSUPPORTED
+    assert call(block=16) == B.CSA2_E_UNSUPPORTED
+    assert call(maxb=4096) == B.CSA2_E_UNSUPPORTED
+    assert call(k=0) == B.CSA2_E_ARG and call(k=2049) == B.CSA2_E_ARG
+    assert call(qdt=B.F32) == B.CSA2_E_UNSUPPORTED
+    assert call(kk=B._IndexKeys(B.F32, 128, P, None)) == B.CSA2_E_UNSUPPORTED
+    need = B.workspace_size(B.OP_TOPK_POOL_FUSED, 4, 8 * 2048, 512)
+    assert need == 4 * 4 * 512 * 8
+    assert B.workspace_size(B.OP_TOPK_POOL_FUSED, 4, 8 * 512, 512) == 0   # one segment: no lists
+    assert call(ws=None) == B.CSA2_E_WORKSPACE
+    assert call(nbytes=need - 1) == B.CSA2_E_WORKSPACE
