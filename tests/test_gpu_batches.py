@@ -270,3 +270,60 @@ def test_encoder_replay_flow(orc):
                         + [int(rs[0]) + 127, int(rs[0]) + 128, int(rs[1]) + 49, int(rs[1]) + 50]))
     L = _Layer(orc, "enc", 503, n, win)
     _full_layer(orc, own, rows, L, sample)
+
+
+def test_multi_token_decode_rows(orc):
+    """Decode steps with several query rows per request (verify rows at consecutive
+    positions sharing one cache): 6 requests x 4 rows at S - 4 .. S - 1 (m = 2), through
+    full-range scores, the hierarchical selection, attention with FP4 main KV, and a
+    Reindex layer through the fused pool top-k; every row checked against the oracle."""
+    say("case: multi-token decode rows (6 requests x 4 verify rows)")
+    seq = [9000, 20001, 33333, 4097, 16384, 65536]
+    T = 4
+    geom = synth.Geometry(seq, 2)
+    cache = dict(ratio_m=2, n_entries=np.array(geom.n_entries), row_start=np.array(geom.row_start))
+    cd = dev_cache(cache)
+    req = np.repeat(np.arange(len(seq)), T).astype(np.int32)
+    pos = np.concatenate([np.arange(s - T, s) for s in seq]).astype(np.int32)
+    rows = dict(req_of_row=req, pos_of_row=pos)
+    n = len(req)
+    rd = B.Rows(i32(req).to(DEV), i32(pos).to(DEV))
+    raw = synth.normal((geom.total_entries, DI), 504, "index_keys", device=DEV)
+    kd, ksd = B.quant_mx(B.MXFP4, raw)
+    ko, kso = orc.mx_quant(orc.E2M1, raw.cpu().numpy())
+    keys = B.IndexKeys(kd, ksd, DI)
+    kv = synth.normal_bf16((geom.total_entries, D), 504, "kv", device=DEV)
+    kv4, kv4s = B.quant_mx(B.FP4_S16, kv)
+    kv4o, kv4so = orc.fp4s16_quant(kv.float().cpu().numpy())
+    assert np.array_equal(kv4o, kv4.cpu().numpy()) and np.array_equal(kv4so, kv4s.cpu().numpy())
+    win = synth.window_cache_geometry(geom, 128, rows_held=[128 + T] * len(seq))
+    C = max(geom.n_entries)
+    kk, nbk = 512, 2048
+    sm = synth.sm_scale(D)
+    lay = [_Layer(orc, "mt%d" % l, 504, n, win) for l in range(2)]
+    # source layer
+    sc = B.index_score(rd, cd, lay[0].qi, lay[0].w, keys, score_stride=C)
+    idx, pb, pn = B.topk_hier(rd, cd, sc, kk, BLK, nbk)
+    out0 = B.sparse_swa_attn(rd, cd, lay[0].q, kv4, idx, lay[0].win_d, sm, kv_scale=kv4s)
+    # Reindex layer through the fused pool top-k
+    pool = B.Pool(pb, pn, BLK)
+    idx1 = B.index_topk_pool(rd, cd, lay[1].qi, lay[1].w, keys, pool, kk)
+    out1 = B.sparse_swa_attn(rd, cd, lay[1].q, kv4, idx1, lay[1].win_d, sm, kv_scale=kv4s)
+    torch.cuda.synchronize()
+    s_o, bad = orc.index_score(rows, cache, lay[0].qi.float().cpu().numpy(), lay[0].w.cpu().numpy(), ko,
+                               key_scales=kso, heads=HI, dim=DI, score_stride=C)
+    assert bad == 0
+    check_scores(sc.cpu().numpy(), s_o, [min((p + 1) // 2, geom.n_entries[r]) for r, p in zip(req, pos)])
+    i_o, b_o, n_o = orc.topk_hier(rows, cache, s_o, kk, BLK, nbk)
+    assert np.array_equal(idx.cpu().numpy(), i_o)
+    assert np.array_equal(pb.cpu().numpy(), b_o) and np.array_equal(pn.cpu().numpy(), n_o)
+    pool_o = dict(blocks=b_o, nblocks=n_o, block=BLK, max_blocks=nbk)
+    s1, bad = orc.index_score(rows, cache, lay[1].qi.float().cpu().numpy(), lay[1].w.cpu().numpy(), ko,
+                              key_scales=kso, heads=HI, dim=DI, score_stride=BLK * nbk, pool=pool_o)
+    assert bad == 0
+    i1 = orc.topk(rows, cache, s1, kk, pool=pool_o)
+    assert np.array_equal(idx1.cpu().numpy(), i1)
+    for L, sel_o, out in ((lay[0], i_o, out0), (lay[1], i1, out1)):
+        a_o, _ = orc.sparse_swa_attn(rows, cache, bits(L.q), 1, kv4o, orc.DT_FP4S16, sel_o, L.win_o, heads=H, dim=D,
+                                     sm_scale=sm, kv_scale=kv4so)
+        check_attn(out.float().cpu().numpy(), a_o)
