@@ -1,21 +1,37 @@
 """Static check of gfx9 device assembly: no instruction touches a register whose vector
-memory load is still in flight.
+memory load is still in flight, and no LDS access happens while an earlier group of
+LDS-DMA copies may still be landing.
 
-The kernels issue some global loads from inline assembly and wait for them with explicit
-``s_waitcnt vmcnt(N)``.  The compiler does not know such a load writes its destination
-later than the instruction issues, so it could move arithmetic on the value above the
-wait, copy the register early, or hand the register to another value while the data is
-still on its way (the late write then corrupts that value, possibly an address).  This
-module replays the vector-memory counter over the control-flow graph of each kernel in
-the assembly that hipcc emits and reports every such access.
+Loads issued from inline assembly and waited for with explicit ``s_waitcnt vmcnt(N)`` are
+invisible to the compiler: it could move arithmetic on the value above the wait, copy the
+register early, or hand the register to another value while the data is still on its way
+(the late write then corrupts that value, possibly an address).  The attention kernel's
+direct global-to-LDS copies (``global_load_lds_dwordx4`` from inline assembly) are waited
+for by hand the same way; there the hazard is an LDS read of a tile that is still being
+copied.  This module replays the vector-memory counter over the control-flow graph of each
+kernel in the assembly that hipcc emits and reports every such access.
+
+LDS copies are checked by groups: a run of LDS-DMA instructions with no LDS access and no
+``s_waitcnt`` on vmcnt between them is one group (one tile's rows; waits on lgkmcnt alone,
+for the scalar loads of row addresses, may sit inside it), and a new group makes the ones
+before it "earlier".  A kernel that double-buffers tiles waits, after issuing a group, for
+everything before it and then reads the tile that has landed; so after every ``s_waitcnt``
+that follows a copy group, each LDS access (``ds_*`` other than the lane permutes) up to the
+next copy must find no copy of an earlier group in flight: at most the newest group is
+landing, into the other half of the buffer (the half is the kernel's construction; the check
+sees counts, not addresses).  This is the wait a miscount would break.
 
 Model (the one the compiler's own wait insertion uses on gfx9): every vector memory
 instruction (load, store, atomic, LDS-DMA load) takes one slot of the counter; they
 complete in issue order; ``s_waitcnt vmcnt(N)`` leaves at most the N newest in flight;
 at most 63 are in flight (issue stalls beyond that).  A load's destination registers are
-pending while its slot is in flight.  At a block with several predecessors the pending
-state is the slot-wise union, aligned on the newest slot, so a register pending on any
-path counts as pending.
+pending while its slot is in flight.  The replay is path-sensitive: each distinct state
+reaching a block is carried on by itself, never joined with another (joining the slot
+lists of two paths lines up loads of different tiles and invents hazards), so the check
+sees every path through the kernel's branches and loops that the counter model can tell
+apart.  Only where a block is reached in more than a few hundred distinct states (long
+loops of stores, say) are the rest joined: slot-wise union aligned on the newest slot, so
+a register pending on any of those paths counts as pending there (coarser, never blind).
 
 Lanes: the check is per register, not per lane, with one refinement.  The compiler puts
 ``s_cbranch_execz`` skips after code that leaves the exec mask alone; that edge is taken
@@ -138,24 +154,38 @@ def _load_dst(insn: Insn) -> set[tuple[str, int]]:
     return regs_of(first)
 
 
-# A state is a tuple of slots, oldest first; a slot is (registers it will write, whether
-# it was issued after the last write of exec on every path reaching here).
+# A state is (slots, open, waited): slots oldest first, each (registers it will write,
+# whether it was issued after the last write of exec on every path reaching here, copy
+# group: 0 not an LDS copy, 1 the newest group, 2 an earlier group); open is whether the
+# newest copy group may still grow (no LDS access or wait since its last copy); waited is
+# whether an s_waitcnt has come since the last copy (LDS accesses are checked then).
 State = tuple
-_EMPTY = (frozenset(), False)
+_EMPTY = (frozenset(), False, 0)
+_NO_LDS = ("ds_bpermute", "ds_permute", "ds_swizzle")
 
 
 def _merge(a: State, b: State) -> State:
-    if len(a) < len(b):
-        a, b = b, a
-    pad = (_EMPTY,) * (len(a) - len(b)) + tuple(b)
-    return tuple((x[0] | y[0], x[1] and y[1]) for x, y in zip(a, pad))
+    """Join of two states (sound, coarser): slots aligned on the newest, registers united."""
+    (sa, oa, wa), (sb, ob, wb) = a, b
+    if len(sa) < len(sb):
+        sa, sb = sb, sa
+    pad = (_EMPTY,) * (len(sa) - len(sb)) + tuple(sb)
+    return (tuple((x[0] | y[0], x[1] and y[1], max(x[2], y[2])) for x, y in zip(sa, pad)), oa and ob, wa or wb)
 
 
-def _pending(state: State) -> set[tuple[str, int]]:
+def _pending(slots) -> set[tuple[str, int]]:
     out: set[tuple[str, int]] = set()
-    for regs, _ in state:
+    for regs, _, _ in slots:
         out |= regs
     return out
+
+
+def _is_lds_copy(insn: Insn) -> bool:
+    return _is_vmem(insn.op) and ("_lds" in insn.op or "lds" in set(insn.operands.replace(",", " ").split()))
+
+
+def _is_lds_access(insn: Insn) -> bool:
+    return insn.op.startswith("ds_") and not insn.op.startswith(_NO_LDS)
 
 
 def _writes_exec(insn: Insn) -> bool:
@@ -166,19 +196,25 @@ def _writes_exec(insn: Insn) -> bool:
 
 
 def _exec_zero(state: State) -> State:
-    """The state along an edge taken only when exec is all zero."""
-    return tuple((frozenset(), True) if fresh else (regs, fresh) for regs, fresh in state)
+    """The state along an edge taken only when exec is all zero (such instructions had no
+    lane active: they write no register and copy nothing)."""
+    slots, op, wt = state
+    return (tuple((frozenset(), True, 0) if fresh else (regs, fresh, g) for regs, fresh, g in slots), op, wt)
 
 
 def _step(state: State, insn: Insn, report) -> State:
+    slots, open_, waited = state
     if insn.op == "s_waitcnt":
         m = _VMCNT.search(insn.operands)
         if m:
             n = int(m.group(1))
-            state = state[len(state) - n:] if n < len(state) else state
+            slots = slots[len(slots) - n:] if n < len(slots) else slots
             if n == 0:
-                state = ()
-        return state
+                slots = ()
+            return (slots, False, True)
+        # a wait on lgkmcnt alone (scalar loads, LDS reads) neither lands a copy nor
+        # touches LDS: the copies around it still form one group
+        return (slots, open_, waited)
     used = regs_of(insn.operands)
     dst = _load_dst(insn) if _is_vmem(insn.op) else set()
     if dst:
@@ -186,50 +222,70 @@ def _step(state: State, insn: Insn, report) -> State:
         # complete in order, so the later value lands last (its address and data
         # operands still count)
         used = regs_of(insn.operands.split(",", 1)[1] if "," in insn.operands else "")
-    hit = used & _pending(state)
+    hit = used & _pending(slots)
     if hit and report is not None:
         report(insn, hit)
+    if _is_lds_access(insn):
+        if report is not None and waited and any(g == 2 for _, _, g in slots):
+            report(insn, None)
+        open_ = False
     if _is_vmem(insn.op):
-        state = state + ((frozenset(dst), True),)
-        if len(state) > _MAX_INFLIGHT:
-            state = state[len(state) - _MAX_INFLIGHT:]
+        group = 0
+        if _is_lds_copy(insn):
+            if not open_:  # a new group: the ones before it become earlier groups
+                slots = tuple((r, f, 2 if g else 0) for r, f, g in slots)
+            group, open_, waited = 1, True, False
+        slots = slots + ((frozenset(dst), True, group),)
+        if len(slots) > _MAX_INFLIGHT:
+            slots = slots[len(slots) - _MAX_INFLIGHT:]
     if _writes_exec(insn):
-        state = tuple((regs, False) for regs, _ in state)
-    return state
+        slots = tuple((regs, False, g) for regs, _, g in slots)
+    return (slots, open_, waited)
 
 
-def check_function(body: list[tuple[int, str]]) -> list[str]:
-    """Accesses to in-flight load destinations in one kernel, as readable strings."""
+def check_function(body: list[tuple[int, str]], exact_per_block: int = 256) -> list[str]:
+    """Accesses to in-flight load destinations in one kernel, as readable strings.
+
+    Path-sensitive: up to exact_per_block distinct states reaching a block are carried on
+    one by one (joining the slot lists of two paths lines up loads that belong to different
+    tiles and invents hazards).  Beyond that budget a block's further states are joined into
+    one widened state, which covers them all, so the replay ends on any kernel."""
     blocks = build_cfg(body)
-    entry: list[State | None] = [None] * len(blocks)
-    entry[0] = ()
-    work = [0]
-    while work:
-        i = work.pop()
-        st = entry[i]
-        for insn in blocks[i].insns:
-            st = _step(st, insn, None)
-        for j, zero in blocks[i].succ:
-            out = _exec_zero(st) if zero else st
-            new = out if entry[j] is None else _merge(entry[j], out)
-            if new != entry[j]:
-                entry[j] = new
-                work.append(j)
-    found: list[str] = []
+    seen: list[set] = [set() for _ in blocks]
+    wide: list[State | None] = [None] * len(blocks)
+    init: State = ((), False, False)
+    seen[0].add(init)
+    work = [(0, init)]
+    found: dict[int, str] = {}
 
     def report(insn: Insn, hit):
+        if hit is None:
+            found.setdefault(insn.line, "line %d: %s %s  <- an earlier LDS copy group may still be landing"
+                             % (insn.line, insn.op, insn.operands))
+            return
         regs = ", ".join("%s%d" % r for r in sorted(hit))
-        found.append("line %d: %s %s  <- in flight: %s" % (insn.line, insn.op, insn.operands, regs))
+        found.setdefault(insn.line, "line %d: %s %s  <- in flight: %s" % (insn.line, insn.op, insn.operands, regs))
 
-    for i, b in enumerate(blocks):
-        if entry[i] is None:
-            continue
-        st = entry[i]
-        for insn in b.insns:
+    while work:
+        i, st = work.pop()
+        for insn in blocks[i].insns:
             st = _step(st, insn, report)
-    return found
+        for j, zero in blocks[i].succ:
+            out = _exec_zero(st) if zero else st
+            if out in seen[j] or out == wide[j]:
+                continue
+            if len(seen[j]) < exact_per_block:
+                seen[j].add(out)
+                work.append((j, out))
+                continue
+            joined = out if wide[j] is None else _merge(wide[j], out)
+            if joined != wide[j]:
+                wide[j] = joined
+                work.append((j, joined))
+    return [found[k] for k in sorted(found)]
 
 
 def check_asm(asm: str) -> dict[str, list[str]]:
-    """Kernel symbol -> its accesses to in-flight load destinations (empty if none)."""
+    """Kernel symbol -> its accesses to in-flight load destinations and LDS accesses under
+    an earlier copy group (empty if none)."""
     return {name: check_function(body) for name, body in split_functions(asm).items()}

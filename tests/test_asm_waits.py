@@ -1,11 +1,14 @@
-"""The built device code never touches a register whose vector memory load is in flight.
+"""The built device code never touches a register whose vector memory load is in flight,
+and never accesses LDS while an earlier group of LDS-DMA copies may still be landing.
 
-The index-score kernel loads its key tiles, q, weights and pool block ids with inline
-assembly and waits for them explicitly; this compiles every HIP source of the library to
-gfx950 assembly with the library's own flags and replays the vector-memory counter over
-each kernel's control flow (tests/asm_waitcheck.py).  The checker itself is pinned on
-small hand-written listings first: a use before the wait, a use after it, a wait that
-leaves the needed load in flight, and a loop whose back edge carries a load.
+The attention kernel copies its KV tiles into LDS with inline-assembly
+global_load_lds_dwordx4 and waits for them with hand-placed s_waitcnt vmcnt(N); this
+compiles every HIP source of the library to gfx950 assembly with the library's own flags
+and replays the vector-memory counter over each kernel's control flow
+(tests/asm_waitcheck.py).  The checker itself is pinned on small hand-written listings
+first: a use before the wait, a use after it, a wait that leaves the needed load in
+flight, a loop whose back edge carries a load, and double-buffered copy groups whose wait
+is right or one group short.
 """
 import concurrent.futures as cf
 import os
@@ -119,6 +122,85 @@ def test_checker_atomics_and_lds_modifier():
 \ts_endpgm""")
     (hits,) = W.check_asm(asm).values()
     assert len(hits) == 1 and "v1, v5" in hits[0]
+
+
+def _copies(n, base=0):
+    return "\n".join("\tglobal_load_lds_dwordx4 v%d, s[4:5] offset:%d" % (10 + i % 4, base + 1072 * i)
+                     for i in range(n))
+
+
+def test_checker_lds_copy_groups():
+    # double buffer: group A (4 copies), read of the index list, group B, wait that keeps
+    # only B in flight, operand reads: clean.  With vmcnt(6) two copies of A may still land
+    # when the operands are read: flagged.  Reads while only the newest group lands: clean.
+    body = """
+%s
+\tds_read_b128 v[20:23], v1
+%s
+\ts_waitcnt vmcnt(%%d)
+\tds_read_b128 v[24:27], v2
+\ts_endpgm""" % (_copies(4), _copies(4, 8192))
+    (ok,) = W.check_asm(_kernel(body % 4)).values()
+    assert ok == []
+    (hits,) = W.check_asm(_kernel(body % 6)).values()
+    assert len(hits) == 1 and "ds_read_b128 v[24:27]" in hits[0] and "earlier LDS copy" in hits[0]
+    # a loop: each iteration starts the next group, then waits for all but it; with the
+    # wait the previous iteration's group has landed when the loop body reads LDS again
+    loop = """
+%s
+.LBB0_1:
+\tds_read_b64_tr_b16 v[30:31], v3
+%s
+\ts_waitcnt vmcnt(%%d)
+\tds_read_b128 v[24:27], v2
+\ts_cbranch_scc0 .LBB0_1
+\ts_endpgm""" % (_copies(4), _copies(4, 8192))
+    (ok,) = W.check_asm(_kernel(loop % 4)).values()
+    assert ok == []
+    (hits,) = W.check_asm(_kernel(loop % 8)).values()
+    assert hits and all("earlier LDS copy" in h for h in hits)
+
+
+def test_checker_groups_span_lgkmcnt_waits():
+    # the row addresses of a tile come from scalar loads, so the copies of one group are
+    # separated by lgkmcnt waits; they still form one group (a wait for all but that group
+    # is clean), and leaving two copies of the previous group in flight is still flagged
+    def tile(base):
+        return "%s\n\ts_waitcnt lgkmcnt(0)\n%s" % (_copies(2, base), _copies(2, base + 4096))
+    body = """
+%s
+\tds_read_b128 v[20:23], v1
+%s
+\ts_waitcnt vmcnt(%%d)
+\tds_read_b128 v[24:27], v2
+\ts_endpgm""" % (tile(0), tile(8192))
+    (ok,) = W.check_asm(_kernel(body % 4)).values()
+    assert ok == []
+    (hits,) = W.check_asm(_kernel(body % 6)).values()
+    assert len(hits) == 1 and "ds_read_b128 v[24:27]" in hits[0]
+
+
+def test_checker_keeps_paths_apart():
+    # one path drains the copies, the other starts the next group without a wait; an LDS
+    # read after the join is clean on both paths.  Joining them (a wait seen on one path,
+    # an earlier group in flight on the other) would report it: the exact replay does not,
+    # the replay forced to join every state at once (a budget of 0 exact states) does
+    body = """
+%s
+\ts_cbranch_scc0 .LBB0_2
+\ts_waitcnt vmcnt(0)
+\ts_branch .LBB0_3
+.LBB0_2:
+\tds_read_b128 v[20:23], v1
+%s
+.LBB0_3:
+\tds_read_b128 v[24:27], v2
+\ts_waitcnt vmcnt(0)
+\ts_endpgm""" % (_copies(4), _copies(4, 8192))
+    ((name, fbody),) = W.split_functions(_kernel(body)).items()
+    assert W.check_function(fbody) == []
+    joined = W.check_function(fbody, exact_per_block=0)
+    assert len(joined) == 1 and "ds_read_b128 v[24:27]" in joined[0]
 
 
 def _device_asm(src: str, out_dir: str) -> str:
