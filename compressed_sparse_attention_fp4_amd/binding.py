@@ -14,7 +14,8 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libcsa2.so")
+# CSA2_LIBRARY names another build of the same library (a sanitized host build, say)
+LIB_PATH = os.environ.get("CSA2_LIBRARY") or os.path.join(_HERE, "libcsa2.so")
 
 CSA2_OK, CSA2_E_ARG, CSA2_E_UNSUPPORTED, CSA2_E_WORKSPACE, CSA2_E_LAUNCH = 0, 1, 2, 3, 4
 F32, BF16, MXFP4, MXFP8_E4M3, FP4_S16 = 0, 1, 2, 3, 4

@@ -1,9 +1,10 @@
 """numpy front end of the C oracle (test infrastructure only).
 
 Each wrapper names the section of the pages that its C function follows; the
-citations are repeated in ``csa2_oracle.c``.  Parity unpinned: the attention
-sink (the pages only mention that a sink exists, [P4] section 6); everything
-else is pinned by tests in ``tests/test_oracle_*.py``.
+citations are repeated in ``csa2_oracle.c``.  Every function is pinned by tests in
+``tests/test_oracle_*.py``.  The attention sink is a reading (the pages only mention
+that a sink exists, [P4] section 6): an extra key of value zero, pinned against torch
+SDPA with an appended zero row.  Parity unpinned: V = K including the RoPE dimensions.
 """
 from __future__ import annotations
 
@@ -41,8 +42,9 @@ def _load():
     global _lib
     with _lock:
         if _lib is None:
-            build()
-            _lib = ctypes.CDLL(_LIB)
+            # CSA2_ORACLE_LIBRARY names another build of csa2_oracle.c (a sanitized one, say)
+            path = os.environ.get("CSA2_ORACLE_LIBRARY") or build()
+            _lib = ctypes.CDLL(path)
             _lib.orc_e2m1_value.restype = ctypes.c_double
             _lib.orc_e4m3_value.restype = ctypes.c_double
             _lib.orc_e8m0_value.restype = ctypes.c_double
