@@ -195,6 +195,23 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
         for (int u = 0; u < 4; u++) sk[u] = gload_u8<0>(sp[u]);
     };
     auto load = [&](int off0, u32x4_t (&kd)[4], int (&sk)[4]) {
+        if (!POOL && off0 + 64 <= ncc) {
+            // a whole group inside a full-range chunk: positions c_begin + off0 + 16 u + c,
+            // all reachable, one address per lane and the tiles at immediate offsets (the
+            // same eight loads in the same order as below)
+            const uint32_t j = (uint32_t)c_begin + (uint32_t)off0 + (uint32_t)(lane & 15);
+            const uint8_t* kp = kd_base + ((uint64_t)j << 6);
+            const uint8_t* sp = ks_base + ((uint64_t)j << 2);
+            kd[0] = gload_x4<0>(kp);
+            kd[1] = gload_x4<1024>(kp);
+            kd[2] = gload_x4<2048>(kp);
+            kd[3] = gload_x4<3072>(kp);
+            sk[0] = gload_u8<0>(sp);
+            sk[1] = gload_u8<64>(sp);
+            sk[2] = gload_u8<128>(sp);
+            sk[3] = gload_u8<192>(sp);
+            return;
+        }
         const uint8_t* kp[4];
         const uint8_t* sp[4];
         gather_b(off0, kp, sp);

@@ -58,6 +58,43 @@ def test_quant_mx_all_bf16_patterns(orc):
     assert np.array_equal(cd.cpu().numpy(), co) and np.array_equal(sd.cpu().numpy(), so)
 
 
+def _every_value_under_every_scale():
+    """Blocks of 32 bf16 values: the first pins the block's shared exponent e (its maximum
+    magnitude lies in [2^(e+2), 2^(e+3)), or below 2^-125 for the clamped e = -127), the
+    other 31 run through every finite bf16 value whose magnitude does not exceed it, so
+    every (value, e) pair a block can produce is quantized once."""
+    b = np.arange(65536, dtype=np.uint32)
+    expo = (b >> 7) & 0xFF
+    finite = expo < 255
+    blocks = []
+    for e in range(-127, 126):
+        if e == -127:
+            amax_bits, lim = 0x00FF, 0x00FF                      # just below 2^-125
+        else:
+            amax_bits = ((e + 2 + 127) << 7) | 0x7F              # 1.9921875 * 2^(e + 2)
+            lim = amax_bits
+        mag = b & 0x7FFF
+        xs = b[finite & (mag <= lim)].astype(np.uint16)
+        pad = (-len(xs)) % 31
+        xs = np.concatenate([xs, np.zeros(pad, np.uint16)]).reshape(-1, 31)
+        head = np.full((xs.shape[0], 1), amax_bits, np.uint16)
+        blocks.append(np.concatenate([head, xs], axis=1))
+    allb = np.concatenate(blocks).astype(np.uint16)
+    return torch.from_numpy(allb.view(np.int16)).view(torch.bfloat16)
+
+
+def test_quant_mxfp4_every_value_under_every_scale(orc):
+    """The E2M1 rounding of csa2_quant_mx (and of every kernel that quantizes index q or
+    keys in-kernel, which share its block routine) equals the oracle's for every finite
+    bf16 value under every shared exponent a block can give it."""
+    say("case: quant_mx MXFP4, every finite bf16 value under every shared exponent")
+    x = _every_value_under_every_scale()
+    cd, sd = B.quant_mx(B.MXFP4, x.to(DEV))
+    co, so = orc.mx_quant(orc.E2M1, x.float().numpy())
+    assert np.array_equal(sd.cpu().numpy(), so), "scales"
+    assert np.array_equal(cd.cpu().numpy(), co), "codes"
+
+
 def test_quant_mx_ties_and_ranges(orc):
     say("case: quant_mx ties, saturation, zero blocks, tiny and huge magnitudes")
     rng = np.random.default_rng(3)
