@@ -181,6 +181,26 @@ __device__ __forceinline__ uint32_t order_key(float s)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Pin values: an empty asm consumes them unconditionally, so the compiler cannot sink
+// their computation into the branch of a later mask (for a load, that would serialize
+// every load of a thread behind a full memory round trip).
+__device__ __forceinline__ void pin(uint32_t x)
+{
+    asm volatile("" ::"v"(x));
+}
+__device__ __forceinline__ void pin(int32_t x)
+{
+    asm volatile("" ::"v"(x));
+}
+__device__ __forceinline__ void pin(float x)
+{
+    asm volatile("" ::"v"(x));
+}
+__device__ __forceinline__ void pin(const float4& v)
+{
+    asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w));
+}
+
 // Workgroups are dealt to the GPU's 8 XCDs (each with its own L2) round-robin by block
 // index.  A grid of nrows x nchunks workgroups keeps the chunks of row r on XCD r % 8, the
 // XCD every kernel of the path gives row r, so that a row's scores, selections and rows of

@@ -59,26 +59,6 @@ __device__ __forceinline__ int64_t pool_position(const SelSource& s, int shift, 
 
 constexpr int bid_slots(int kpt) { return kpt / 8 > 0 ? kpt / 8 : 1; }
 
-// Pin loaded values: an empty asm consumes them unconditionally, so the compiler cannot
-// sink a load into the branch of a later mask (which would serialize every load of a
-// thread behind a full memory round trip).
-__device__ __forceinline__ void pin(uint32_t x)
-{
-    asm volatile("" ::"v"(x));
-}
-__device__ __forceinline__ void pin(int32_t x)
-{
-    asm volatile("" ::"v"(x));
-}
-__device__ __forceinline__ void pin(float x)
-{
-    asm volatile("" ::"v"(x));
-}
-__device__ __forceinline__ void pin(const float4& v)
-{
-    asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w));
-}
-
 // Keys of candidates [e0, e0 + KPT) of this workgroup's slice (blocked layout), loaded
 // without per-element branches: addresses are clamped and invalid slots masked after.
 // Pool sources with whole blocks per thread (KPT % 8 == 0, slice start % 8 == 0) also

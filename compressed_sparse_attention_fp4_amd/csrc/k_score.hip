@@ -103,54 +103,64 @@ __global__ __launch_bounds__(256) void k_score_f32(RowsArg rows, CacheArg cache,
 }
 
 // ---------------------------------------------------------------------------- MXFP4
-// Workgroup = 4 waves on one query row and a chunk of columns.  The row's bf16 index q
+// Workgroup = 4 waves on NR query rows and a chunk of columns.  Each row's bf16 index q
 // is quantized once per workgroup into LDS (one 32-element block per lane, which is
 // exactly the lane's slice of the MFMA A operand).  Each wave then takes 64 columns
 // at a time: 4 key tiles of 16 positions, each scored against NHT head tiles with
 // v_mfma_scale_f32_16x16x128_f8f6f4 (E2M1 x E2M1, E8M0 block scales): key tile lane
 // (g, c) loads position c's 16-byte code block g (one 32-element block) and its scale.
-template <int NHT, bool POOL>
-__global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cache, const uint16_t* __restrict__ q,
-                                                     const float* __restrict__ w, int64_t w_stride,
-                                                     const uint8_t* __restrict__ kdata,
-                                                     const uint8_t* __restrict__ kscale, PoolArg pool,
-                                                     float* __restrict__ scores, int64_t stride, int chunk,
-                                                     int nchunks)
+// With NR = 2 the two rows belong to one request and share every key tile (prefill rows
+// reach nearly the same positions): each row still has its own products, its own head
+// sum in the canonical order and its own stores, so its scores are those of NR = 1.
+template <int NHT, bool POOL, int NR>
+__device__ __forceinline__ void score_rows(const RowsArg& rows, const CacheArg& cache, const uint16_t* __restrict__ q,
+                                           const float* __restrict__ w, int64_t w_stride,
+                                           const uint8_t* __restrict__ kdata, const uint8_t* __restrict__ kscale,
+                                           const PoolArg& pool, float* __restrict__ scores, int64_t stride,
+                                           int chunk, int chk, const int (&rowv)[NR])
 {
+    static_assert(NR == 1 || !POOL, "rows share key tiles only over the full range");
     constexpr int H = NHT * 16;
     constexpr int G = H / 4;
-    __shared__ uint4 s_qa[NHT][64];
-    __shared__ uint32_t s_qs[NHT][64];
+    __shared__ uint4 s_qa[NR][NHT][64];
+    __shared__ uint32_t s_qs[NR][NHT][64];
     __shared__ int32_t s_bid[POOL ? kScoreMaxBlocks : 1];
 
-    int row, chk;
-    xcd_row_chunk(blockIdx.x, rows.n, nchunks, &row, &chk);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar loop control
-    int64_t R;
-    int prow;
-    const int64_t ncol = row_columns(rows, cache, pool, row, stride, &R, &prow);
     const int64_t c_begin = (int64_t)chk * chunk;
-    // the chunk's columns past the row's reach (or its pool) hold -inf
+    // the chunk's columns past a row's reach (or its pool) hold -inf
     const int64_t cover = output_columns(pool, stride) < c_begin + chunk ? output_columns(pool, stride)
                                                                            : c_begin + chunk;
-    if (c_begin >= ncol) {
-        fill_neg_inf(scores + (int64_t)row * stride, c_begin, cover);
+    // (the rows' sizes are read through vector loads; readfirstlane makes the branches on
+    // them scalar, so that no wave runs both sides of one)
+    int nccr[NR];  // columns of this chunk each row covers (<= 8192)
+    int ncc = 0;   // columns whose keys are loaded: the most any row covers
+    int R32 = 0;   // positions are below n_entries, so 32 bits hold them
+    int prow = rowv[0];
+#pragma unroll
+    for (int r = 0; r < NR; r++) {
+        int64_t R;
+        const int64_t ncol = row_columns(rows, cache, pool, rowv[r], stride, &R, &prow);
+        const int64_t c_end = (c_begin + chunk < ncol) ? c_begin + chunk : ncol;
+        nccr[r] = __builtin_amdgcn_readfirstlane((int)(c_end > c_begin ? c_end - c_begin : 0));
+        ncc = nccr[r] > ncc ? nccr[r] : ncc;
+        const int r32 = __builtin_amdgcn_readfirstlane((int)R);
+        R32 = r32 > R32 ? r32 : R32;
+    }
+    if (ncc == 0) {
+#pragma unroll
+        for (int r = 0; r < NR; r++) fill_neg_inf(scores + (int64_t)rowv[r] * stride, c_begin, cover);
         return;
     }
-    const int64_t c_end = (c_begin + chunk < ncol) ? c_begin + chunk : ncol;
 
-    const int64_t krow0 = cache.row_start[rows.req[row]];
+    const int64_t krow0 = cache.row_start[rows.req[rowv[0]]];
     // Pool rows: the chunk's block ids go to LDS (a chunk starts on a block boundary and
     // spans at most kScoreMaxBlocks blocks; the block size is a power of two).
     const int bshift = POOL ? __builtin_ctz((unsigned)pool.block) : 0;
-    // (the row's sizes are read through vector loads; readfirstlane makes the branches on
-    // them scalar, so that no wave runs both sides of one)
-    const int ncc = __builtin_amdgcn_readfirstlane((int)(c_end - c_begin));  // columns of this chunk (<= 8192)
 
     // Position of chunk column `off` (0 <= off < ncc); R or beyond when the column lies
-    // past the row's reach.  Positions are below n_entries, so 32 bits hold them.
-    const int R32 = __builtin_amdgcn_readfirstlane((int)R);
+    // past the row's reach.
     auto pos_of = [&](int off) -> int {
         if (!POOL) return (int)c_begin + off;
         return (s_bid[off >> bshift] << bshift) | (off & (pool.block - 1));
@@ -164,9 +174,7 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
     // eight loads (four 16-byte code blocks, four scale bytes), after looking the row
     // addresses up (gather_b).  It has no branch (a column past the chunk looks up column
     // 0), so the compiler sees one sequence of loads on every path and waits for each key
-    // tile just before its products.  (A second loader for full-row groups, one base
-    // address and immediate tile offsets, made the full-range launch slower: the two loops
-    // it needs raise the register count from 120 to 164.)
+    // tile just before its products.
     auto lookup_b = [&](int off0, int (&jj)[4]) {
 #pragma unroll
         for (int u = 0; u < 4; u++) {
@@ -217,35 +225,39 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
         gather_b(off0, kp, sp);
         issue_b(kp, sp, kd, sk);
     };
-    // ---- loads, all issued before their first use: the row's index q (one 32-element
+    // ---- loads, all issued before their first use: the rows' index q (one 32-element
     // block per thread and pass), the head weights and the pool block ids, then (full
     // rows) the wave's first two groups of key tiles, so that HBM is busy from the start.
     constexpr int QP = (NHT * 64 + 255) / 256;
-    u32x4_t qraw[QP][4];
+    u32x4_t qraw[NR][QP][4];
 #pragma unroll
-    for (int pp = 0; pp < QP; pp++) {
-        const int idx = threadIdx.x + 256 * pp;
-        if (idx < NHT * 64) {
-            const int t = idx >> 6, l = idx & 63;
-            const int m = l & 15, blk = l >> 4;
-            const int head = G * (m >> 2) + 4 * t + (m & 3);
-            const uint16_t* src = q + ((int64_t)row * H + head) * 128 + blk * 32;
-            qraw[pp][0] = gload_x4<0>(src);
-            qraw[pp][1] = gload_x4<16>(src);
-            qraw[pp][2] = gload_x4<32>(src);
-            qraw[pp][3] = gload_x4<48>(src);
+    for (int r = 0; r < NR; r++) {
+#pragma unroll
+        for (int pp = 0; pp < QP; pp++) {
+            const int idx = threadIdx.x + 256 * pp;
+            if (idx < NHT * 64) {
+                const int t = idx >> 6, l = idx & 63;
+                const int m = l & 15, blk = l >> 4;
+                const int head = G * (m >> 2) + 4 * t + (m & 3);
+                const uint16_t* src = q + ((int64_t)rowv[r] * H + head) * 128 + blk * 32;
+                qraw[r][pp][0] = gload_x4<0>(src);
+                qraw[r][pp][1] = gload_x4<16>(src);
+                qraw[r][pp][2] = gload_x4<32>(src);
+                qraw[r][pp][3] = gload_x4<48>(src);
+            }
         }
     }
     const int g = lane >> 4;
-    float wr[NHT * 4];
-    {
-        const float* wrow = w + (int64_t)row * w_stride + G * g;
+    float wr[NR][NHT * 4];
+#pragma unroll
+    for (int r = 0; r < NR; r++) {
+        const float* wrow = w + (int64_t)rowv[r] * w_stride + G * g;
 #pragma unroll
         for (int t = 0; t < NHT; t++) {
-            wr[4 * t + 0] = gload_f32<0>(wrow + 4 * t);
-            wr[4 * t + 1] = gload_f32<4>(wrow + 4 * t);
-            wr[4 * t + 2] = gload_f32<8>(wrow + 4 * t);
-            wr[4 * t + 3] = gload_f32<12>(wrow + 4 * t);
+            wr[r][4 * t + 0] = gload_f32<0>(wrow + 4 * t);
+            wr[r][4 * t + 1] = gload_f32<4>(wrow + 4 * t);
+            wr[r][4 * t + 2] = gload_f32<8>(wrow + 4 * t);
+            wr[r][4 * t + 3] = gload_f32<12>(wrow + 4 * t);
         }
     }
     constexpr int BPT = POOL ? kScoreMaxBlocks / 256 : 1;  // pool block ids staged per thread
@@ -273,7 +285,7 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
         load(off0 + 256, kb, sb4);
     }
 
-    // ---- pool block ids to LDS; the row's index q quantized into A operands
+    // ---- pool block ids to LDS; the rows' index q quantized into A operands
     if (POOL) {
 #pragma unroll
         for (int i = 0; i < BPT; i++) {
@@ -282,34 +294,40 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
         }
     }
 #pragma unroll
-    for (int pp = 0; pp < QP; pp++) {
-        const int idx = threadIdx.x + 256 * pp;
-        if (idx < NHT * 64) {
-            const int t = idx >> 6, l = idx & 63;
-            float v[32];
+    for (int r = 0; r < NR; r++) {
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
+        for (int pp = 0; pp < QP; pp++) {
+            const int idx = threadIdx.x + 256 * pp;
+            if (idx < NHT * 64) {
+                const int t = idx >> 6, l = idx & 63;
+                float v[32];
 #pragma unroll
-                for (int jj = 0; jj < 4; jj++) {
-                    v[i * 8 + 2 * jj] = __uint_as_float(qraw[pp][i][jj] << 16);
-                    v[i * 8 + 2 * jj + 1] = __uint_as_float(qraw[pp][i][jj] & 0xFFFF0000u);
+                for (int i = 0; i < 4; i++) {
+#pragma unroll
+                    for (int jj = 0; jj < 4; jj++) {
+                        v[i * 8 + 2 * jj] = __uint_as_float(qraw[r][pp][i][jj] << 16);
+                        v[i * 8 + 2 * jj + 1] = __uint_as_float(qraw[r][pp][i][jj] & 0xFFFF0000u);
+                    }
                 }
+                uint32_t o[4], sb;
+                quant_block_e2m1(v, o, &sb);
+                s_qa[r][t][l] = make_uint4(o[0], o[1], o[2], o[3]);
+                s_qs[r][t][l] = sb;
             }
-            uint32_t o[4], sb;
-            quant_block_e2m1(v, o, &sb);
-            s_qa[t][l] = make_uint4(o[0], o[1], o[2], o[3]);
-            s_qs[t][l] = sb;
         }
     }
     __syncthreads();
 
-    i32x8 a[NHT];
-    int sa[NHT];
+    i32x8 a[NR][NHT];
+    int sa[NR][NHT];
 #pragma unroll
-    for (int t = 0; t < NHT; t++) {
-        const uint4 u = s_qa[t][lane];
-        a[t] = i32x8{(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
-        sa[t] = (int)s_qs[t][lane];
+    for (int r = 0; r < NR; r++) {
+#pragma unroll
+        for (int t = 0; t < NHT; t++) {
+            const uint4 u = s_qa[r][t][lane];
+            a[r][t] = i32x8{(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
+            sa[r][t] = (int)s_qs[r][t][lane];
+        }
     }
     if (POOL) {
         load(off0, ka, sa4);
@@ -318,37 +336,55 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
 
     // score the 64 columns off0 .. off0 + 63 from their key tiles
     auto score_group = [&](int off0, const u32x4_t (&kd)[4], const int (&sk)[4]) {
-        // tiles one at a time: NHT products into separate registers, then the head sum
-        float P[4];
+        // tiles one at a time: NHT products per row into separate registers, then the
+        // rows' head sums
+        float P[NR][4];
 #pragma unroll
         for (int u = 0; u < 4; u++) {
-            f32x4 d[NHT];
             const i32x8 b = i32x8{(int)kd[u][0], (int)kd[u][1], (int)kd[u][2], (int)kd[u][3], 0, 0, 0, 0};
 #pragma unroll
-            for (int t = 0; t < NHT; t++) {
-                const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-                d[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[t], b, zero, 4, 4, 0, sa[t], 0, sk[u]);
+            for (int r = 0; r < NR; r++) {
+                f32x4 d[NHT];
+#pragma unroll
+                for (int t = 0; t < NHT; t++) {
+                    const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+                    d[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[r][t], b, zero, 4, 4, 0, sa[r][t], 0,
+                                                                           sk[u]);
+                }
+                float pp = 0.0f;
+#pragma unroll
+                for (int t = 0; t < NHT; t++)
+#pragma unroll
+                    for (int i = 0; i < 4; i++) pp = __builtin_fmaf(wr[r][4 * t + i], relu_bits(d[t][i]), pp);
+                P[r][u] = pp;
             }
-            float pp = 0.0f;
-#pragma unroll
-            for (int t = 0; t < NHT; t++)
-#pragma unroll
-                for (int i = 0; i < 4; i++) pp = __builtin_fmaf(wr[4 * t + i], relu_bits(d[t][i]), pp);
-            P[u] = pp;
         }
-        // Lane group g holds P_g for tiles 0..3.  Pair groups (0,1) and (2,3) per tile,
-        // then (01, 23): lane (g, c) ends with the score of tile g, position c.
-        auto s01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(P[0]), __float_as_uint(P[1]), false, false);
-        auto s23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(P[2]), __float_as_uint(P[3]), false, false);
-        const float h01 = __uint_as_float(s01[0]) + __uint_as_float(s01[1]);
-        const float h23 = __uint_as_float(s23[0]) + __uint_as_float(s23[1]);
-        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(h01), __float_as_uint(h23), false, false);
-        float score = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-
         const int off = off0 + lane;
-        if (off < ncc) {
-            if (POOL && pos_of(off) >= R32) score = -INFINITY;
-            scores[(int64_t)row * stride + c_begin + off] = score;
+        float score[NR];
+#pragma unroll
+        for (int r = 0; r < NR; r++) {
+            // Lane group g holds P_g for tiles 0..3.  Pair groups (0,1) and (2,3) per
+            // tile, then (01, 23): lane (g, c) ends with the score of tile g, position c.
+            auto s01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(P[r][0]), __float_as_uint(P[r][1]), false,
+                                                        false);
+            auto s23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(P[r][2]), __float_as_uint(P[r][3]), false,
+                                                        false);
+            const float h01 = __uint_as_float(s01[0]) + __uint_as_float(s01[1]);
+            const float h23 = __uint_as_float(s23[0]) + __uint_as_float(s23[1]);
+            auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(h01), __float_as_uint(h23), false, false);
+            score[r] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        }
+        // Every row's scores are computed before the first (lane-masked) store: otherwise
+        // the compiler sinks a row's products past the previous row's store branch, and
+        // the block boundary keeps them from overlapping that row's head sums.
+#pragma unroll
+        for (int r = 0; r < NR; r++) pin(score[r]);
+#pragma unroll
+        for (int r = 0; r < NR; r++) {
+            if (off < nccr[r]) {
+                if (POOL && pos_of(off) >= R32) score[r] = -INFINITY;
+                scores[(int64_t)rowv[r] * stride + c_begin + off] = score[r];
+            }
         }
     };
 
@@ -376,7 +412,54 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
             if (rest == 1) score_group(off0 + 256 * i, ka, sa4);
         }
     }
-    if (c_end < cover) fill_neg_inf(scores + (int64_t)row * stride, c_end, cover);
+#pragma unroll
+    for (int r = 0; r < NR; r++)
+        if (c_begin + nccr[r] < cover) fill_neg_inf(scores + (int64_t)rowv[r] * stride, c_begin + nccr[r], cover);
+}
+
+// One query row per workgroup.
+template <int NHT, bool POOL>
+__global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cache, const uint16_t* __restrict__ q,
+                                                     const float* __restrict__ w, int64_t w_stride,
+                                                     const uint8_t* __restrict__ kdata,
+                                                     const uint8_t* __restrict__ kscale, PoolArg pool,
+                                                     float* __restrict__ scores, int64_t stride, int chunk,
+                                                     int nchunks)
+{
+    int row, chk;
+    xcd_row_chunk(blockIdx.x, rows.n, nchunks, &row, &chk);
+    const int rv[1] = {row};
+    score_rows<NHT, POOL, 1>(rows, cache, q, w, w_stride, kdata, kscale, pool, scores, stride, chunk, chk, rv);
+}
+
+// Rows 2 i and 2 i + 1 per workgroup (full range, launches over many rows): one pass
+// over shared key tiles when both belong to one request, else one row after the other.
+template <int NHT>
+__global__ __launch_bounds__(256, 3) void k_score_mxfp4_pair(RowsArg rows, CacheArg cache,
+                                                          const uint16_t* __restrict__ q,
+                                                          const float* __restrict__ w, int64_t w_stride,
+                                                          const uint8_t* __restrict__ kdata,
+                                                          const uint8_t* __restrict__ kscale, PoolArg pool,
+                                                          float* __restrict__ scores, int64_t stride, int chunk,
+                                                          int nchunks)
+{
+    int pair, chk;
+    xcd_row_chunk(blockIdx.x, (rows.n + 1) >> 1, nchunks, &pair, &chk);
+    const int r0 = 2 * pair, r1 = r0 + 1;
+    const bool shared =
+        __builtin_amdgcn_readfirstlane((int)(r1 < rows.n && rows.req[r0] == rows.req[r1])) != 0;
+    if (shared) {
+        const int rv[2] = {r0, r1};
+        score_rows<NHT, false, 2>(rows, cache, q, w, w_stride, kdata, kscale, pool, scores, stride, chunk, chk, rv);
+        return;
+    }
+    const int a0[1] = {r0};
+    score_rows<NHT, false, 1>(rows, cache, q, w, w_stride, kdata, kscale, pool, scores, stride, chunk, chk, a0);
+    if (r1 < rows.n) {
+        __syncthreads();  // the second row reuses the first one's LDS
+        const int a1[1] = {r1};
+        score_rows<NHT, false, 1>(rows, cache, q, w, w_stride, kdata, kscale, pool, scores, stride, chunk, chk, a1);
+    }
 }
 
 static int pick_chunk(int n, int64_t cols, int block)
@@ -391,19 +474,27 @@ static int pick_chunk(int n, int64_t cols, int block)
     return (int)chunk;
 }
 
+// Full-range launches over at least this many rows (prefill) score rows in pairs.
+constexpr int kPairRows = 1024;
+
 hipError_t launch_index_score_mxfp4(const RowsArg& rows, const CacheArg& cache, const uint16_t* q, int heads,
                                     const float* w, int64_t w_stride, const uint8_t* kdata, const uint8_t* kscale,
                                     const PoolArg& pool, float* scores, int64_t stride, hipStream_t stream)
 {
     if (rows.n == 0) return hipSuccess;
     const int64_t cols = pool.blocks ? (int64_t)pool.block * pool.max_blocks : stride;
-    const int chunk = pick_chunk(rows.n, cols, pool.blocks ? pool.block : 0);
+    const bool pairs = !pool.blocks && rows.n >= kPairRows;
+    const int units = pairs ? (rows.n + 1) / 2 : rows.n;  // workgroup rows
+    const int chunk = pick_chunk(units, cols, pool.blocks ? pool.block : 0);
     const int nchunks = (int)((cols + chunk - 1) / chunk);
-    dim3 grid((unsigned)((int64_t)nchunks * rows.n));
+    dim3 grid((unsigned)((int64_t)nchunks * units));
 #define CSA2_SCORE_CASE(T)                                                                                      \
     case T:                                                                                                     \
         if (pool.blocks)                                                                                        \
             hipLaunchKernelGGL((k_score_mxfp4<T, true>), grid, dim3(256), 0, stream, rows, cache, q, w, w_stride, \
+                               kdata, kscale, pool, scores, stride, chunk, nchunks);                            \
+        else if (pairs)                                                                                         \
+            hipLaunchKernelGGL((k_score_mxfp4_pair<T>), grid, dim3(256), 0, stream, rows, cache, q, w, w_stride, \
                                kdata, kscale, pool, scores, stride, chunk, nchunks);                            \
         else                                                                                                    \
             hipLaunchKernelGGL((k_score_mxfp4<T, false>), grid, dim3(256), 0, stream, rows, cache, q, w,         \

@@ -177,6 +177,53 @@ def test_index_score_mxfp4_full_range(orc, H):
                 i, p, R, len(bad_cols), bad_cols[:8], got[i, bad_cols[:4]], s_o[i, bad_cols[:4]]))
 
 
+@pytest.mark.parametrize("H", [64, 16])
+def test_index_score_mxfp4_row_pairs(orc, H):
+    """Full-range calls over 1024 rows or more score rows in pairs that share key tiles
+    when both rows belong to one request.  Requests of odd lengths put pairs across
+    request boundaries (scored one row after the other) and the row count is odd: every
+    row must equal the same row scored in calls of fewer rows (one row per workgroup),
+    bit for bit, and sampled rows the oracle."""
+    say("case: index_score MXFP4 in row pairs, heads=%d" % H)
+    rng = np.random.default_rng(40 + H)
+    lens = [301, 4, 1, 516, 233, 77, 1]           # prefill rows per request (sum 1133, odd)
+    S = [600, 5, 2, 1100, 240, 77, 3000]
+    m = 2
+    geom = synth.Geometry(S, m)
+    req = np.concatenate([np.full(L, r) for r, L in enumerate(lens)]).astype(np.int32)
+    pos = np.concatenate([np.sort(rng.choice(s, size=L, replace=False)) for s, L in zip(S, lens)]).astype(np.int32)
+    rows = dict(req_of_row=req, pos_of_row=pos)
+    cache = dict(ratio_m=m, n_entries=np.array(geom.n_entries), row_start=np.array(geom.row_start))
+    n = len(req)
+    assert n >= 1024 and n % 2 == 1
+    keys = synth.normal((geom.total_entries, 128), 40 + H, "index_keys")
+    q = synth.normal_bf16((n, H, 128), 40 + H, "index_q")
+    w = synth.uniform((n, H), 40 + H, "index_w")
+    stride = 1600
+    (kd, ksd), (ko, kso) = quant_both(orc, B.MXFP4, orc.E2M1, keys)
+    K = B.IndexKeys(kd, ksd, 128)
+    qd, wd = q.to(DEV), w.to(DEV)
+    whole = B.index_score(dev_rows(rows), dev_cache(cache), qd, wd, K, scores=poison((n, stride), torch.float32))
+    parts = poison((n, stride), torch.float32)
+    for a in range(0, n, 400):
+        b = min(n, a + 400)
+        sub = {k: v[a:b] for k, v in rows.items()}
+        B.index_score(dev_rows(sub), dev_cache(cache), qd[a:b], wd[a:b], K, scores=parts[a:b])
+    torch.cuda.synchronize()
+    assert torch.equal(whole.view(torch.int32), parts.view(torch.int32))
+    sample = sorted(set([0, 1, 2, 300, 301, 302, 304, 305, 306, 821, 822, n - 2, n - 1]) |
+                    set(rng.choice(n, 12, replace=False).tolist()))
+    rs = {k: v[sample] for k, v in rows.items()}
+    s_o, bad = orc.index_score(rs, cache, q[sample].float().numpy(), w[sample].numpy(), ko, key_scales=kso, heads=H,
+                               dim=128, score_stride=stride)
+    assert bad == 0
+    got = whole.cpu().numpy()[sample]
+    for i in range(len(sample)):
+        R = min((int(rs["pos_of_row"][i]) + 1) // m, int(cache["n_entries"][rs["req_of_row"][i]]))
+        assert np.array_equal(got[i, :R], s_o[i, :R]), "row %d" % sample[i]
+        assert np.all(got[i, R:] == -np.inf)
+
+
 def test_index_score_mxfp4_pool(orc):
     say("case: index_score MXFP4 over a candidate pool (ragged newest block, row map)")
     rows, cache, keys, q, w = _score_case(21, (4000, 999), 1, 64, 128, 10)
