@@ -40,8 +40,10 @@ def oracle_window(orc, raw_rows, nreq_rows, pos_start, window=128):
 # ------------------------------------------------------------------------- C3
 def test_c3_decode_step_sampled(orc):
     """The benchmark's decode step (64 requests x 1 query, S=131072, m=2, source layer
-    with hierarchical selection, then 7 Reindex layers), launched exactly as bench.py
-    times it; the source layer and the last Reindex layer checked on sampled rows."""
+    with hierarchical selection, then 7 Reindex layers through the fused pool scoring +
+    top-k), launched exactly as bench.py times it; the source layer and the last Reindex
+    layer checked on sampled rows (that layer's pool scores from the two-launch path's
+    scoring call on the same inputs)."""
     import bench
     say("case: C3 full decode step (bench input set 0), oracle on sampled rows")
     x = bench.InputSet(0, DEV)
@@ -102,7 +104,9 @@ def test_c3_decode_step_sampled(orc):
                               pool=pool_o)
     assert bad == 0
     say("  Reindex scores")
-    check_scores(x.scores_pool[sample].cpu().numpy(), s7, (rn * bench.BLK).tolist())
+    s7_d = B.index_score(x.rows, x.cache, L7["qi"], L7["w"], x.keys, pool=x.pool,
+                         scores=torch.full_like(x.scores_pool, float("nan")))
+    check_scores(s7_d[sample].cpu().numpy(), s7, (rn * bench.BLK).tolist())
     i7 = orc.topk(rows_o, cache_o, s7, bench.K, pool=pool_o)
     say("  Reindex selection")
     assert np.array_equal(x.idx[bench.LAYERS - 1][sample].cpu().numpy(), i7)
