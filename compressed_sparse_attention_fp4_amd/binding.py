@@ -177,18 +177,30 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 # ---------------------------------------------------------------- entry points
+def _index_q(q_idx: torch.Tensor, q_scale: Optional[torch.Tensor]):
+    """(dtype code, q_scale pointer): MXFP4 when the E8M0 scale plane comes with the codes."""
+    if q_scale is None:
+        return _dtype_code(q_idx), None
+    if q_idx.dtype != torch.uint8 or q_scale.dtype != torch.uint8:
+        raise TypeError("MXFP4 index q: uint8 codes [n, heads, dim / 2] and uint8 scales [n, heads, dim / 32]")
+    return MXFP4, _ptr(q_scale)
+
+
 def index_score(rows: Rows, cache: Cache, q_idx: torch.Tensor, w: torch.Tensor, keys: IndexKeys,
                 pool: Optional[Pool] = None, score_stride: Optional[int] = None, scores: Optional[torch.Tensor] = None,
-                stream=None) -> torch.Tensor:
-    """csa2_index_score.  q_idx [n, heads, dim]; w [n, heads] or [heads] (shared)."""
+                q_scale: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """csa2_index_score.  q_idx [n, heads, dim] (bf16 / fp32), or with q_scale the MXFP4 q as
+    quant_mx writes it (codes [n, heads, dim / 2], scales [n, heads, dim / 32]); w [n, heads]
+    or [heads] (shared)."""
     n, heads = q_idx.shape[0], q_idx.shape[1]
+    qdt, qsp = _index_q(q_idx, q_scale)
     if scores is None:
         if score_stride is None:
             raise ValueError("score_stride or scores is required")
         scores = torch.empty((n, score_stride), dtype=torch.float32, device=q_idx.device)
     w_stride = 0 if w.dim() == 1 else w.stride(0)
-    rc = lib().csa2_index_score(ctypes.byref(rows.c()), ctypes.byref(cache.c()), _ptr(q_idx),
-                                ctypes.c_int(_dtype_code(q_idx)), ctypes.c_int32(heads), _ptr(w),
+    rc = lib().csa2_index_score(ctypes.byref(rows.c()), ctypes.byref(cache.c()), _ptr(q_idx), ctypes.c_int(qdt), qsp,
+                                ctypes.c_int32(heads), _ptr(w),
                                 ctypes.c_int64(w_stride), ctypes.byref(keys.c()),
                                 ctypes.byref(pool.c()) if pool is not None else None, _ptr(scores),
                                 ctypes.c_int64(scores.stride(0)), _stream(stream))
@@ -198,17 +210,18 @@ def index_score(rows: Rows, cache: Cache, q_idx: torch.Tensor, w: torch.Tensor, 
 
 def index_topk_pool(rows: Rows, cache: Cache, q_idx: torch.Tensor, w: torch.Tensor, keys: IndexKeys, pool: Pool,
                     k: int, out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                    stream=None) -> torch.Tensor:
+                    q_scale: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """csa2_index_topk_pool: the pool top-k of csa2_index_score + csa2_topk without the score
-    rows; int32 [n, k] ascending positions, -1 padded."""
+    rows; int32 [n, k] ascending positions, -1 padded.  q_idx / q_scale as for index_score."""
     n, heads = q_idx.shape[0], q_idx.shape[1]
+    qdt, qsp = _index_q(q_idx, q_scale)
     if out is None:
         out = torch.empty((n, k), dtype=torch.int32, device=q_idx.device)
     if workspace is None:
         workspace = _workspace(workspace_size(OP_TOPK_POOL_FUSED, n, pool.block * pool.max_blocks, k), q_idx.device)
     w_stride = 0 if w.dim() == 1 else w.stride(0)
-    rc = lib().csa2_index_topk_pool(ctypes.byref(rows.c()), ctypes.byref(cache.c()), _ptr(q_idx),
-                                    ctypes.c_int(_dtype_code(q_idx)), ctypes.c_int32(heads), _ptr(w),
+    rc = lib().csa2_index_topk_pool(ctypes.byref(rows.c()), ctypes.byref(cache.c()), _ptr(q_idx), ctypes.c_int(qdt),
+                                    qsp, ctypes.c_int32(heads), _ptr(w),
                                     ctypes.c_int64(w_stride), ctypes.byref(keys.c()), ctypes.byref(pool.c()),
                                     ctypes.c_int32(k), _ptr(out), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
                                     _stream(stream))

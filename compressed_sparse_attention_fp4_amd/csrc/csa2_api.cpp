@@ -166,9 +166,22 @@ size_t csa2_workspace_size(int op, int32_t n, int64_t cols, int32_t k, int32_t m
     }
 }
 
+// Index q of the MXFP4 kernels: BF16, or MXFP4 codes with their E8M0 scale plane.
+static int check_index_q(const void* q_idx, csa2_dtype q_dtype, const uint8_t* q_scale, const char* who)
+{
+    if (q_dtype != CSA2_BF16 && q_dtype != CSA2_MXFP4)
+        return fail(CSA2_E_UNSUPPORTED, "%s: index q dtype %d (BF16 or MXFP4)", who, (int)q_dtype);
+    if ((q_dtype == CSA2_MXFP4) != (q_scale != nullptr))
+        return fail(CSA2_E_ARG, q_dtype == CSA2_MXFP4 ? "%s: MXFP4 index q without q_scale"
+                                                      : "%s: q_scale given for a BF16 index q", who);
+    if (misaligned(q_idx, 16)) return fail(CSA2_E_ARG, "%s: q_idx must start on a 16-byte boundary", who);
+    return CSA2_OK;
+}
+
 int csa2_index_score(const csa2_rows* rows, const csa2_cache* cache, const void* q_idx, csa2_dtype q_dtype,
-                     int32_t heads, const float* w, int64_t w_row_stride, const csa2_index_keys* keys,
-                     const csa2_pool* pool, float* scores, int64_t score_stride, void* stream)
+                     const uint8_t* q_scale, int32_t heads, const float* w, int64_t w_row_stride,
+                     const csa2_index_keys* keys, const csa2_pool* pool, float* scores, int64_t score_stride,
+                     void* stream)
 {
     int rc;
     if ((rc = check_rows(rows)) || (rc = check_cache(cache))) return rc;
@@ -178,16 +191,16 @@ int csa2_index_score(const csa2_rows* rows, const csa2_cache* cache, const void*
     if (w_row_stride < 0) return fail(CSA2_E_ARG, "w_row_stride < 0");
     if ((rc = check_pool(pool, score_stride))) return rc;
     if (keys->dtype == CSA2_MXFP4) {
-        if (q_dtype != CSA2_BF16) return fail(CSA2_E_UNSUPPORTED, "MXFP4 keys need a BF16 index q");
+        if ((rc = check_index_q(q_idx, q_dtype, q_scale, "MXFP4 keys"))) return rc;
         if (keys->dim != 128) return fail(CSA2_E_UNSUPPORTED, "MXFP4 keys: dim %d (128 supported)", keys->dim);
         if (!keys->scale) return fail(CSA2_E_ARG, "MXFP4 keys without a scale plane");
-        if (misaligned(q_idx, 16) || misaligned(keys->data, 16))
-            return fail(CSA2_E_ARG, "q_idx / keys->data must start on a 16-byte boundary");
+        if (misaligned(keys->data, 16)) return fail(CSA2_E_ARG, "keys->data must start on a 16-byte boundary");
         if (heads < 16 || heads > 128 || heads % 16)
             return fail(CSA2_E_UNSUPPORTED, "MXFP4 scoring: heads %d (multiple of 16, at most 128)", heads);
         if (w_row_stride != 0 && w_row_stride < heads) return fail(CSA2_E_ARG, "w_row_stride < heads");
     } else if (keys->dtype == CSA2_F32) {
         if (q_dtype != CSA2_F32) return fail(CSA2_E_UNSUPPORTED, "F32 keys need an F32 index q");
+        if (q_scale) return fail(CSA2_E_ARG, "q_scale given for an F32 index q");
         if (keys->dim < 1 || keys->dim > 1024) return fail(CSA2_E_UNSUPPORTED, "F32 keys: dim %d", keys->dim);
         if (heads < 4 || heads > 128 || heads % 4)
             return fail(CSA2_E_UNSUPPORTED, "F32 scoring: heads %d (multiple of 4, at most 128)", heads);
@@ -200,7 +213,7 @@ int csa2_index_score(const csa2_rows* rows, const csa2_cache* cache, const void*
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (keys->dtype == CSA2_MXFP4)
         return launch_result(csa2::launch_index_score_mxfp4(rows_arg(rows), cache_arg(cache),
-                                                            static_cast<const uint16_t*>(q_idx), heads, w,
+                                                            csa2::IndexQ{q_idx, q_scale}, heads, w,
                                                             w_row_stride, static_cast<const uint8_t*>(keys->data),
                                                             keys->scale, pool_arg(pool), scores, score_stride, s),
                              "csa2_index_score");
@@ -212,9 +225,9 @@ int csa2_index_score(const csa2_rows* rows, const csa2_cache* cache, const void*
 }
 
 int csa2_index_topk_pool(const csa2_rows* rows, const csa2_cache* cache, const void* q_idx, csa2_dtype q_dtype,
-                         int32_t heads, const float* w, int64_t w_row_stride, const csa2_index_keys* keys,
-                         const csa2_pool* pool, int32_t k, int32_t* out_idx, void* workspace,
-                         size_t workspace_bytes, void* stream)
+                         const uint8_t* q_scale, int32_t heads, const float* w, int64_t w_row_stride,
+                         const csa2_index_keys* keys, const csa2_pool* pool, int32_t k, int32_t* out_idx,
+                         void* workspace, size_t workspace_bytes, void* stream)
 {
     int rc;
     if ((rc = check_rows(rows)) || (rc = check_cache(cache))) return rc;
@@ -228,19 +241,18 @@ int csa2_index_topk_pool(const csa2_rows* rows, const csa2_cache* cache, const v
     if ((rc = check_pool(pool, (int64_t)pool->block * pool->max_blocks))) return rc;
     if (keys->dtype != CSA2_MXFP4 || keys->dim != 128 || !keys->scale)
         return fail(CSA2_E_UNSUPPORTED, "fused pool top-k: MXFP4 keys of dim 128 with a scale plane");
-    if (q_dtype != CSA2_BF16) return fail(CSA2_E_UNSUPPORTED, "fused pool top-k: BF16 index q");
+    if ((rc = check_index_q(q_idx, q_dtype, q_scale, "fused pool top-k"))) return rc;
     if (heads != 16 && heads != 32 && heads != 64)
         return fail(CSA2_E_UNSUPPORTED, "fused pool top-k: heads %d (16, 32 or 64)", heads);
     if (w_row_stride != 0 && w_row_stride < heads) return fail(CSA2_E_ARG, "w_row_stride < heads");
-    if (misaligned(q_idx, 16) || misaligned(keys->data, 16))
-        return fail(CSA2_E_ARG, "q_idx / keys->data must start on a 16-byte boundary");
+    if (misaligned(keys->data, 16)) return fail(CSA2_E_ARG, "keys->data must start on a 16-byte boundary");
     if (rows->n == 0) return ok();
     const size_t need = csa2::score_topk_pool_workspace(rows->n, (int64_t)pool->block * pool->max_blocks, k);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(CSA2_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
     if ((rc = check_device())) return rc;
     return launch_result(csa2::launch_score_topk_pool(rows_arg(rows), cache_arg(cache),
-                                                      static_cast<const uint16_t*>(q_idx), heads, w, w_row_stride,
+                                                      csa2::IndexQ{q_idx, q_scale}, heads, w, w_row_stride,
                                                       static_cast<const uint8_t*>(keys->data), keys->scale,
                                                       pool_arg(pool), k, out_idx, workspace,
                                                       static_cast<hipStream_t>(stream)),

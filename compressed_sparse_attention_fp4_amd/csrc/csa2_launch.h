@@ -43,8 +43,15 @@ hipError_t launch_quant_mx(bool fp4, bool bf16_in, const void* x, int64_t nblock
 hipError_t launch_quant_fp4s16(bool bf16_in, const void* x, int64_t nblocks, uint8_t* codes, uint8_t* scales,
                                hipStream_t stream);
 
-// Index scores.  MXFP4 path: q bf16 [n][heads][128]; F32 path: q, keys fp32.
-hipError_t launch_index_score_mxfp4(const RowsArg& rows, const CacheArg& cache, const uint16_t* q, int heads,
+// Index q of the MXFP4 scoring kernels: bf16 [n][heads][128] (quantized in-kernel), or with
+// q_scale non-null its MXFP4 codes [n][heads][64 B] and E8M0 scales [n][heads][4].
+struct IndexQ {
+    const void* q;
+    const uint8_t* q_scale;
+};
+
+// Index scores.  MXFP4 path: q as above; F32 path: q, keys fp32.
+hipError_t launch_index_score_mxfp4(const RowsArg& rows, const CacheArg& cache, const IndexQ& q, int heads,
                                     const float* w, int64_t w_stride, const uint8_t* kdata, const uint8_t* kscale,
                                     const PoolArg& pool, float* scores, int64_t stride, hipStream_t stream);
 hipError_t launch_index_score_f32(const RowsArg& rows, const CacheArg& cache, const float* q, int heads, int dim,
@@ -69,7 +76,7 @@ hipError_t launch_list_merge(const SelSource& src, int k, int nlists, const uint
 // Fused pool scoring + top-k (block 8, at most 2048 blocks; heads 16, 32 or 64); pools
 // of more than 4096 columns need the segment lists' workspace.
 size_t score_topk_pool_workspace(int n, int64_t cols, int k);
-hipError_t launch_score_topk_pool(const RowsArg& rows, const CacheArg& cache, const uint16_t* q, int heads,
+hipError_t launch_score_topk_pool(const RowsArg& rows, const CacheArg& cache, const IndexQ& q, int heads,
                                   const float* w, int64_t w_stride, const uint8_t* kdata, const uint8_t* kscale,
                                   const PoolArg& pool, int k, int32_t* out_idx, void* ws, hipStream_t stream);
 hipError_t launch_topk(const SelSource& src, int k, int32_t* out, void* ws, size_t ws_bytes, hipStream_t stream);

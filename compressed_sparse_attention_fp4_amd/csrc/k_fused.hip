@@ -32,7 +32,8 @@ constexpr int kFusedKPT = 8;
 constexpr int kFusedCap = kFusedNT * kFusedKPT;  // 4096 pool columns per segment
 
 template <int NHT>
-__global__ __launch_bounds__(512) void k_score_topk_pool(RowsArg rows, CacheArg cache, const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(512) void k_score_topk_pool(RowsArg rows, CacheArg cache, const void* __restrict__ q,
+                                                         const uint8_t* __restrict__ q_scale,
                                                          const float* __restrict__ w, int64_t w_stride,
                                                          const uint8_t* __restrict__ kdata,
                                                          const uint8_t* __restrict__ kscale, PoolArg pool, int k,
@@ -63,13 +64,21 @@ __global__ __launch_bounds__(512) void k_score_topk_pool(RowsArg rows, CacheArg 
     const int ncol = __builtin_amdgcn_readfirstlane(nbs * 8);  // columns of the segment
     const int R32 = __builtin_amdgcn_readfirstlane((int)R);  // positions < n_entries fit 32 bits
 
-    // ---- the row's index q quantized into A operands (one 32-element block per thread),
-    // the pool's block ids and the lane group's head weights
-    if (tid < NHT * 64) {
+    // ---- the row's index q quantized into A operands (one 32-element block per thread;
+    // with q_scale, its MXFP4 codes and scale as given), the pool's block ids and the lane
+    // group's head weights
+    if (tid < NHT * 64 && q_scale) {
+        const int t = tid >> 6, l = tid & 63;
+        const int m = l & 15, blk = l >> 4;
+        const int64_t rh = (int64_t)row * H + G * (m >> 2) + 4 * t + (m & 3);
+        const u32x4_t c = gload_x4<0>(static_cast<const uint8_t*>(q) + rh * 64 + blk * 16);
+        s_qa[t][l] = make_uint4(c[0], c[1], c[2], c[3]);
+        s_qs[t][l] = (uint32_t)gload_u8<0>(q_scale + rh * 4 + blk);
+    } else if (tid < NHT * 64) {
         const int t = tid >> 6, l = tid & 63;
         const int m = l & 15, blk = l >> 4;
         const int head = G * (m >> 2) + 4 * t + (m & 3);
-        const uint16_t* src = q + ((int64_t)row * H + head) * 128 + blk * 32;
+        const uint16_t* src = static_cast<const uint16_t*>(q) + ((int64_t)row * H + head) * 128 + blk * 32;
         u32x4_t x[4] = {gload_x4<0>(src), gload_x4<16>(src), gload_x4<32>(src), gload_x4<48>(src)};
         float v[32];
 #pragma unroll
@@ -216,7 +225,7 @@ size_t score_topk_pool_workspace(int n, int64_t cols, int k)
     return nseg > 1 ? (size_t)n * nseg * k * sizeof(uint2) : 0;
 }
 
-hipError_t launch_score_topk_pool(const RowsArg& rows, const CacheArg& cache, const uint16_t* q, int heads,
+hipError_t launch_score_topk_pool(const RowsArg& rows, const CacheArg& cache, const IndexQ& qin, int heads,
                                   const float* w, int64_t w_stride, const uint8_t* kdata, const uint8_t* kscale,
                                   const PoolArg& pool, int k, int32_t* out_idx, void* ws, hipStream_t stream)
 {
@@ -226,8 +235,8 @@ hipError_t launch_score_topk_pool(const RowsArg& rows, const CacheArg& cache, co
     const dim3 grid((unsigned)((int64_t)rows.n * nseg));
 #define CSA2_FUSED_CASE(T)                                                                                     \
     case T:                                                                                                    \
-        hipLaunchKernelGGL((k_score_topk_pool<T>), grid, dim3(kFusedNT), 0, stream, rows, cache, q, w, w_stride, \
-                           kdata, kscale, pool, k, nseg, out_idx, lists);                                       \
+        hipLaunchKernelGGL((k_score_topk_pool<T>), grid, dim3(kFusedNT), 0, stream, rows, cache, qin.q,        \
+                           qin.q_scale, w, w_stride, kdata, kscale, pool, k, nseg, out_idx, lists);             \
         break;
     switch (heads / 16) {
         CSA2_FUSED_CASE(1)

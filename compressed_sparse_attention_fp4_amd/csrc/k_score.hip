@@ -113,8 +113,9 @@ __global__ __launch_bounds__(256) void k_score_f32(RowsArg rows, CacheArg cache,
 // reach nearly the same positions): each row still has its own products, its own head
 // sum in the canonical order and its own stores, so its scores are those of NR = 1.
 template <int NHT, bool POOL, int NR>
-__device__ __forceinline__ void score_rows(const RowsArg& rows, const CacheArg& cache, const uint16_t* __restrict__ q,
-                                           const float* __restrict__ w, int64_t w_stride,
+__device__ __forceinline__ void score_rows(const RowsArg& rows, const CacheArg& cache, const void* __restrict__ q,
+                                           const uint8_t* __restrict__ q_scale, const float* __restrict__ w,
+                                           int64_t w_stride,
                                            const uint8_t* __restrict__ kdata, const uint8_t* __restrict__ kscale,
                                            const PoolArg& pool, float* __restrict__ scores, int64_t stride,
                                            int chunk, int chk, const int (&rowv)[NR])
@@ -226,10 +227,14 @@ __device__ __forceinline__ void score_rows(const RowsArg& rows, const CacheArg& 
         issue_b(kp, sp, kd, sk);
     };
     // ---- loads, all issued before their first use: the rows' index q (one 32-element
-    // block per thread and pass), the head weights and the pool block ids, then (full
-    // rows) the wave's first two groups of key tiles, so that HBM is busy from the start.
+    // block per thread and pass: bf16 values, or with q_scale its MXFP4 codes and scale),
+    // the head weights and the pool block ids, then (full rows) the wave's first two groups
+    // of key tiles, so that HBM is busy from the start.
     constexpr int QP = (NHT * 64 + 255) / 256;
+    const bool q4 = q_scale != nullptr;  // the same for every thread
     u32x4_t qraw[NR][QP][4];
+    u32x4_t qcode[NR][QP];
+    int qsc[NR][QP];
 #pragma unroll
     for (int r = 0; r < NR; r++) {
 #pragma unroll
@@ -239,11 +244,17 @@ __device__ __forceinline__ void score_rows(const RowsArg& rows, const CacheArg& 
                 const int t = idx >> 6, l = idx & 63;
                 const int m = l & 15, blk = l >> 4;
                 const int head = G * (m >> 2) + 4 * t + (m & 3);
-                const uint16_t* src = q + ((int64_t)rowv[r] * H + head) * 128 + blk * 32;
-                qraw[r][pp][0] = gload_x4<0>(src);
-                qraw[r][pp][1] = gload_x4<16>(src);
-                qraw[r][pp][2] = gload_x4<32>(src);
-                qraw[r][pp][3] = gload_x4<48>(src);
+                const int64_t rh = (int64_t)rowv[r] * H + head;
+                if (q4) {
+                    qcode[r][pp] = gload_x4<0>(static_cast<const uint8_t*>(q) + rh * 64 + blk * 16);
+                    qsc[r][pp] = gload_u8<0>(q_scale + rh * 4 + blk);
+                } else {
+                    const uint16_t* src = static_cast<const uint16_t*>(q) + rh * 128 + blk * 32;
+                    qraw[r][pp][0] = gload_x4<0>(src);
+                    qraw[r][pp][1] = gload_x4<16>(src);
+                    qraw[r][pp][2] = gload_x4<32>(src);
+                    qraw[r][pp][3] = gload_x4<48>(src);
+                }
             }
         }
     }
@@ -298,7 +309,11 @@ __device__ __forceinline__ void score_rows(const RowsArg& rows, const CacheArg& 
 #pragma unroll
         for (int pp = 0; pp < QP; pp++) {
             const int idx = threadIdx.x + 256 * pp;
-            if (idx < NHT * 64) {
+            if (idx < NHT * 64 && q4) {
+                const int t = idx >> 6, l = idx & 63;
+                s_qa[r][t][l] = make_uint4(qcode[r][pp][0], qcode[r][pp][1], qcode[r][pp][2], qcode[r][pp][3]);
+                s_qs[r][t][l] = (uint32_t)qsc[r][pp];
+            } else if (idx < NHT * 64) {
                 const int t = idx >> 6, l = idx & 63;
                 float v[32];
 #pragma unroll
@@ -419,7 +434,8 @@ __device__ __forceinline__ void score_rows(const RowsArg& rows, const CacheArg& 
 
 // One query row per workgroup.
 template <int NHT, bool POOL>
-__global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cache, const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cache, const void* __restrict__ q,
+                                                     const uint8_t* __restrict__ q_scale,
                                                      const float* __restrict__ w, int64_t w_stride,
                                                      const uint8_t* __restrict__ kdata,
                                                      const uint8_t* __restrict__ kscale, PoolArg pool,
@@ -429,14 +445,16 @@ __global__ __launch_bounds__(256) void k_score_mxfp4(RowsArg rows, CacheArg cach
     int row, chk;
     xcd_row_chunk(blockIdx.x, rows.n, nchunks, &row, &chk);
     const int rv[1] = {row};
-    score_rows<NHT, POOL, 1>(rows, cache, q, w, w_stride, kdata, kscale, pool, scores, stride, chunk, chk, rv);
+    score_rows<NHT, POOL, 1>(rows, cache, q, q_scale, w, w_stride, kdata, kscale, pool, scores, stride, chunk, chk,
+                             rv);
 }
 
 // Rows 2 i and 2 i + 1 per workgroup (full range, launches over many rows): one pass
 // over shared key tiles when both belong to one request, else one row after the other.
 template <int NHT>
 __global__ __launch_bounds__(256, 3) void k_score_mxfp4_pair(RowsArg rows, CacheArg cache,
-                                                          const uint16_t* __restrict__ q,
+                                                          const void* __restrict__ q,
+                                                          const uint8_t* __restrict__ q_scale,
                                                           const float* __restrict__ w, int64_t w_stride,
                                                           const uint8_t* __restrict__ kdata,
                                                           const uint8_t* __restrict__ kscale, PoolArg pool,
@@ -450,15 +468,18 @@ __global__ __launch_bounds__(256, 3) void k_score_mxfp4_pair(RowsArg rows, Cache
         __builtin_amdgcn_readfirstlane((int)(r1 < rows.n && rows.req[r0] == rows.req[r1])) != 0;
     if (shared) {
         const int rv[2] = {r0, r1};
-        score_rows<NHT, false, 2>(rows, cache, q, w, w_stride, kdata, kscale, pool, scores, stride, chunk, chk, rv);
+        score_rows<NHT, false, 2>(rows, cache, q, q_scale, w, w_stride, kdata, kscale, pool, scores, stride, chunk,
+                                  chk, rv);
         return;
     }
     const int a0[1] = {r0};
-    score_rows<NHT, false, 1>(rows, cache, q, w, w_stride, kdata, kscale, pool, scores, stride, chunk, chk, a0);
+    score_rows<NHT, false, 1>(rows, cache, q, q_scale, w, w_stride, kdata, kscale, pool, scores, stride, chunk, chk,
+                              a0);
     if (r1 < rows.n) {
         __syncthreads();  // the second row reuses the first one's LDS
         const int a1[1] = {r1};
-        score_rows<NHT, false, 1>(rows, cache, q, w, w_stride, kdata, kscale, pool, scores, stride, chunk, chk, a1);
+        score_rows<NHT, false, 1>(rows, cache, q, q_scale, w, w_stride, kdata, kscale, pool, scores, stride, chunk,
+                                  chk, a1);
     }
 }
 
@@ -477,7 +498,7 @@ static int pick_chunk(int n, int64_t cols, int block)
 // Full-range launches over at least this many rows (prefill) score rows in pairs.
 constexpr int kPairRows = 1024;
 
-hipError_t launch_index_score_mxfp4(const RowsArg& rows, const CacheArg& cache, const uint16_t* q, int heads,
+hipError_t launch_index_score_mxfp4(const RowsArg& rows, const CacheArg& cache, const IndexQ& qin, int heads,
                                     const float* w, int64_t w_stride, const uint8_t* kdata, const uint8_t* kscale,
                                     const PoolArg& pool, float* scores, int64_t stride, hipStream_t stream)
 {
@@ -488,17 +509,20 @@ hipError_t launch_index_score_mxfp4(const RowsArg& rows, const CacheArg& cache, 
     const int chunk = pick_chunk(units, cols, pool.blocks ? pool.block : 0);
     const int nchunks = (int)((cols + chunk - 1) / chunk);
     dim3 grid((unsigned)((int64_t)nchunks * units));
-#define CSA2_SCORE_CASE(T)                                                                                      \
-    case T:                                                                                                     \
-        if (pool.blocks)                                                                                        \
-            hipLaunchKernelGGL((k_score_mxfp4<T, true>), grid, dim3(256), 0, stream, rows, cache, q, w, w_stride, \
-                               kdata, kscale, pool, scores, stride, chunk, nchunks);                            \
-        else if (pairs)                                                                                         \
-            hipLaunchKernelGGL((k_score_mxfp4_pair<T>), grid, dim3(256), 0, stream, rows, cache, q, w, w_stride, \
-                               kdata, kscale, pool, scores, stride, chunk, nchunks);                            \
-        else                                                                                                    \
-            hipLaunchKernelGGL((k_score_mxfp4<T, false>), grid, dim3(256), 0, stream, rows, cache, q, w,         \
-                               w_stride, kdata, kscale, pool, scores, stride, chunk, nchunks);                  \
+#define CSA2_SCORE_CASE(T)                                                                               \
+    case T:                                                                                              \
+        if (pool.blocks)                                                                                 \
+            hipLaunchKernelGGL((k_score_mxfp4<T, true>), grid, dim3(256), 0, stream, rows, cache, qin.q,   \
+                               qin.q_scale, w, w_stride, kdata, kscale, pool, scores, stride, chunk,       \
+                               nchunks);                                                                 \
+        else if (pairs)                                                                                  \
+            hipLaunchKernelGGL((k_score_mxfp4_pair<T>), grid, dim3(256), 0, stream, rows, cache, qin.q,    \
+                               qin.q_scale, w, w_stride, kdata, kscale, pool, scores, stride, chunk,       \
+                               nchunks);                                                                 \
+        else                                                                                             \
+            hipLaunchKernelGGL((k_score_mxfp4<T, false>), grid, dim3(256), 0, stream, rows, cache, qin.q,  \
+                               qin.q_scale, w, w_stride, kdata, kscale, pool, scores, stride, chunk,       \
+                               nchunks);                                                                 \
         break;
     switch (heads / 16) {
         CSA2_SCORE_CASE(1)

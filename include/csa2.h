@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define CSA2_VERSION 2
+#define CSA2_VERSION 3
 
 enum {
     CSA2_OK = 0,
@@ -148,7 +148,12 @@ typedef struct csa2_swa {
  * head groups, P_g = fma(w_h, max(d_h,0), P_g) over the group in ascending h from +0,
  * s = (P_0 + P_1) + (P_2 + P_3).
  *
- * q_idx   [n][heads][keys->dim]: BF16 for MXFP4 keys, F32 for F32 keys (q_dtype says which).
+ * q_idx   [n][heads][keys->dim]: BF16 or MXFP4 for MXFP4 keys, F32 for F32 keys (q_dtype
+ *         says which).  MXFP4 q is the quantized BF16 q as csa2_quant_mx (MXFP4) writes it
+ *         for the [n * heads * dim / 32] blocks: q_idx the E2M1 codes [n][heads][dim / 2]
+ *         (element 2i in the low nibble), q_scale the E8M0 bytes [n][heads][dim / 32]; the
+ *         scores are then exactly those of the BF16 q it came from (the same quantization
+ *         happens in-kernel for BF16 q).  q_scale is NULL for the other dtypes.
  * heads   MXFP4: a multiple of 16, at most 128; F32: a multiple of 4, at most 128.
  * w       float [n][heads] with row stride w_row_stride (0: one row shared by all).
  * pool    NULL: column j of row q is compressed position j; every column j < score_stride
@@ -161,8 +166,9 @@ typedef struct csa2_swa {
  * Errors: E_ARG (null pointers, n < 0, bad strides), E_UNSUPPORTED (dtype/dim/heads).
  * ------------------------------------------------------------------------------- */
 int csa2_index_score(const csa2_rows* rows, const csa2_cache* cache, const void* q_idx, csa2_dtype q_dtype,
-                     int32_t heads, const float* w, int64_t w_row_stride, const csa2_index_keys* keys,
-                     const csa2_pool* pool, float* scores, int64_t score_stride, void* stream);
+                     const uint8_t* q_scale, int32_t heads, const float* w, int64_t w_row_stride,
+                     const csa2_index_keys* keys, const csa2_pool* pool, float* scores, int64_t score_stride,
+                     void* stream);
 
 /* ---------------------------------------------------------------------------------
  * csa2_topk -- the k best candidates of every row ([MOD] "Hierarchical Sparse Indexer":
@@ -186,16 +192,17 @@ int csa2_topk(const csa2_rows* rows, const csa2_cache* cache, const float* score
  * section's measurement notes name the fused module of restricted scoring and selection).
  * out_idx [n][k] is exactly what csa2_index_score (pool) followed by csa2_topk (pool) give:
  * the k best pool positions below the row's reach, ascending, -1 padded (ties to the lower
- * position).  Supported: MXFP4 keys of dim 128, BF16 index q, heads 16 / 32 / 64, pool
+ * position).  Supported: MXFP4 keys of dim 128, BF16 or MXFP4 index q (q_idx / q_scale as
+ * for csa2_index_score), heads 16 / 32 / 64, pool
  * block 8 with max_blocks <= 2048 (the pages' 16,384-position pool), k 1..2048.
  * A pool is scored in segments of 4096 columns; pools of more than one segment need
  * workspace (csa2_workspace_size(CSA2_OP_TOPK_POOL_FUSED, n, block * max_blocks, k, 0):
  * each segment's top-k as (key, position) lists, merged exactly by a second launch).
  * ------------------------------------------------------------------------------- */
 int csa2_index_topk_pool(const csa2_rows* rows, const csa2_cache* cache, const void* q_idx, csa2_dtype q_dtype,
-                         int32_t heads, const float* w, int64_t w_row_stride, const csa2_index_keys* keys,
-                         const csa2_pool* pool, int32_t k, int32_t* out_idx, void* workspace,
-                         size_t workspace_bytes, void* stream);
+                         const uint8_t* q_scale, int32_t heads, const float* w, int64_t w_row_stride,
+                         const csa2_index_keys* keys, const csa2_pool* pool, int32_t k, int32_t* out_idx,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------
  * csa2_topk_hier -- the source pass of the hierarchical indexer ([MOD] "Hierarchical

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     L = B.lib()
     for name in _declared():
         assert hasattr(L, name), name
-    assert L.csa2_version() == 2
+    assert L.csa2_version() == 3
 
 
 def _rows(n=4):
@@ -49,18 +49,24 @@ M = ctypes.c_void_p(4104)  # the same, not on a 16-byte boundary
 def test_index_score_arg_errors():
     L = B.lib()
     keys = B._IndexKeys(B.MXFP4, 128, P, P)
-    args = lambda **kw: dict(dict(rows=ctypes.byref(_rows()), cache=ctypes.byref(_cache()), q=P, qdt=B.BF16, heads=64,
-                                  w=P, ws=64, keys=ctypes.byref(keys), pool=None, scores=P, stride=512), **kw)
+    args = lambda **kw: dict(dict(rows=ctypes.byref(_rows()), cache=ctypes.byref(_cache()), q=P, qdt=B.BF16, qs=None,
+                                  heads=64, w=P, ws=64, keys=ctypes.byref(keys), pool=None, scores=P, stride=512), **kw)
 
     def call(a):
-        return L.csa2_index_score(a["rows"], a["cache"], a["q"], a["qdt"], a["heads"], a["w"], ctypes.c_int64(a["ws"]),
-                                  a["keys"], a["pool"], a["scores"], ctypes.c_int64(a["stride"]), None)
+        return L.csa2_index_score(a["rows"], a["cache"], a["q"], a["qdt"], a["qs"], a["heads"], a["w"],
+                                  ctypes.c_int64(a["ws"]), a["keys"], a["pool"], a["scores"], ctypes.c_int64(a["stride"]),
+                                  None)
 
     assert call(args(rows=None)) == B.CSA2_E_ARG
     assert call(args(q=None)) == B.CSA2_E_ARG
     assert call(args(stride=0)) == B.CSA2_E_ARG
     assert call(args(heads=8)) == B.CSA2_E_UNSUPPORTED and "heads" in _err()
     assert call(args(qdt=B.F32)) == B.CSA2_E_UNSUPPORTED
+    # MXFP4 index q: codes plus the E8M0 plane; a scale plane only with MXFP4 q
+    assert call(args(qdt=B.MXFP4)) == B.CSA2_E_ARG and "q_scale" in _err()
+    assert call(args(qs=P)) == B.CSA2_E_ARG and "q_scale" in _err()
+    assert call(args(qdt=B.MXFP4, qs=P, q=M)) == B.CSA2_E_ARG and "16-byte" in _err()
+    assert call(args(qdt=B.MXFP4, qs=P, rows=ctypes.byref(B._Rows(0, None, None, None)))) == B.CSA2_OK
     assert call(args(cache=ctypes.byref(_cache(m=3)))) == B.CSA2_E_UNSUPPORTED
     bad_dim = B._IndexKeys(B.MXFP4, 64, P, P)
     assert call(args(keys=ctypes.byref(bad_dim))) == B.CSA2_E_UNSUPPORTED
@@ -73,6 +79,7 @@ def test_index_score_arg_errors():
     assert call(args(keys=ctypes.byref(odd_keys))) == B.CSA2_E_ARG and "16-byte" in _err()
     f32 = B._IndexKeys(B.F32, 64, P, None)
     assert call(args(keys=ctypes.byref(f32), qdt=B.F32, heads=6)) == B.CSA2_E_UNSUPPORTED
+    assert call(args(keys=ctypes.byref(f32), qdt=B.F32, heads=8, qs=P)) == B.CSA2_E_ARG and "q_scale" in _err()
     # zero rows: valid and a no-op
     zero = B._Rows(0, None, None, None)
     assert call(args(rows=ctypes.byref(zero))) == B.CSA2_OK
@@ -197,8 +204,8 @@ def test_f32_index_dim_range():
 
     def call(dim):
         keys = B._IndexKeys(B.F32, dim, P, None)
-        return L.csa2_index_score(ctypes.byref(_rows()), ctypes.byref(_cache()), P, B.F32, 8, P, ctypes.c_int64(8),
-                                  ctypes.byref(keys), None, P, ctypes.c_int64(512), None)
+        return L.csa2_index_score(ctypes.byref(_rows()), ctypes.byref(_cache()), P, B.F32, None, 8, P,
+                                  ctypes.c_int64(8), ctypes.byref(keys), None, P, ctypes.c_int64(512), None)
 
     for dim in (0, 1025):
         assert call(dim) == B.CSA2_E_UNSUPPORTED and "dim" in _err()
@@ -253,10 +260,10 @@ def test_index_topk_pool_arg_errors():
     L = B.lib()
     keys = B._IndexKeys(B.MXFP4, 128, P, P)
 
-    def call(heads=64, block=8, maxb=2048, k=512, ws=P, nbytes=1 << 30, qdt=B.BF16, kk=None):
+    def call(heads=64, block=8, maxb=2048, k=512, ws=P, nbytes=1 << 30, qdt=B.BF16, kk=None, qs=None):
         pool = B._Pool(block, maxb, P, P, None)
-        return L.csa2_index_topk_pool(ctypes.byref(_rows()), ctypes.byref(_cache()), P, qdt, ctypes.c_int32(heads), P,
-                                      ctypes.c_int64(64), ctypes.byref(kk or keys), ctypes.byref(pool),
+        return L.csa2_index_topk_pool(ctypes.byref(_rows()), ctypes.byref(_cache()), P, qdt, qs, ctypes.c_int32(heads),
+                                      P, ctypes.c_int64(64), ctypes.byref(kk or keys), ctypes.byref(pool),
                                       ctypes.c_int32(k), P, ws, ctypes.c_size_t(nbytes), None)
 
     assert call(heads=48) == B.CSA2_E_UNSUPPORTED
@@ -264,6 +271,8 @@ def test_index_topk_pool_arg_errors():
     assert call(maxb=4096) == B.CSA2_E_UNSUPPORTED
     assert call(k=0) == B.CSA2_E_ARG and call(k=2049) == B.CSA2_E_ARG
     assert call(qdt=B.F32) == B.CSA2_E_UNSUPPORTED
+    assert call(qdt=B.MXFP4) == B.CSA2_E_ARG and "q_scale" in _err()
+    assert call(qs=P) == B.CSA2_E_ARG and "q_scale" in _err()
     assert call(kk=B._IndexKeys(B.F32, 128, P, None)) == B.CSA2_E_UNSUPPORTED
     need = B.workspace_size(B.OP_TOPK_POOL_FUSED, 4, 8 * 2048, 512)
     assert need == 4 * 4 * 512 * 8

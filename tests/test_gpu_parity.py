@@ -224,6 +224,65 @@ def test_index_score_mxfp4_row_pairs(orc, H):
         assert np.all(got[i, R:] == -np.inf)
 
 
+def test_index_score_mxfp4_q_input(orc):
+    """MXFP4 index q (codes and E8M0 scales from csa2_quant_mx of the bf16 q) gives the
+    scores of that bf16 q bit for bit: one row per workgroup, row pairs (1024 rows or
+    more) and pool columns, and through the fused pool top-k."""
+    say("case: index_score with MXFP4 index q")
+    rng = np.random.default_rng(50)
+    lens, S, m = [700, 450, 1], [1400, 900, 5000], 2
+    geom = synth.Geometry(S, m)
+    req = np.concatenate([np.full(L, r) for r, L in enumerate(lens)]).astype(np.int32)
+    pos = np.concatenate([np.sort(rng.choice(s_, size=L, replace=False)) for s_, L in zip(S, lens)]).astype(np.int32)
+    rows = dict(req_of_row=req, pos_of_row=pos)
+    cache = dict(ratio_m=m, n_entries=np.array(geom.n_entries), row_start=np.array(geom.row_start))
+    n = len(req)
+    keys = synth.normal((geom.total_entries, 128), 50, "index_keys")
+    q = synth.normal_bf16((n, 64, 128), 50, "index_q").to(DEV)
+    w = synth.uniform((n, 64), 50, "index_w").to(DEV)
+    kd, ksd = B.quant_mx(B.MXFP4, keys.to(DEV))
+    K = B.IndexKeys(kd, ksd, 128)
+    qc, qs = B.quant_mx(B.MXFP4, q)
+    assert qc.shape == (n, 64, 64) and qs.shape == (n, 64, 4)
+    rd, cd = dev_rows(rows), dev_cache(cache)
+    stride = 2600
+    for part in (slice(0, n), slice(0, 300)):          # pairs (n >= 1024), then one row per workgroup
+        sub = {k_: v[part] for k_, v in rows.items()}
+        a = B.index_score(dev_rows(sub), cd, q[part], w[part], K, scores=poison((len(sub["req_of_row"]), stride),
+                                                                              torch.float32))
+        b = B.index_score(dev_rows(sub), cd, qc[part], w[part], K, q_scale=qs[part],
+                          scores=poison((len(sub["req_of_row"]), stride), torch.float32))
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    # pool columns and the fused pool top-k
+    NB = 96
+    blocks = np.full((n, NB), -1, np.int32)
+    nblocks = np.zeros(n, np.int32)
+    for i in range(n):
+        R = min((int(pos[i]) + 1) // m, geom.n_entries[req[i]])
+        nb = (R + 7) // 8
+        pick = list(range(nb)) if nb <= NB else sorted(set(rng.choice(nb - 1, NB - 1, replace=False).tolist()) | {nb - 1})
+        blocks[i, :len(pick)] = pick
+        nblocks[i] = len(pick)
+    pd = B.Pool(i32(blocks).to(DEV), i32(nblocks).to(DEV), 8)
+    a = B.index_score(rd, cd, q, w, K, pool=pd, scores=poison((n, NB * 8), torch.float32))
+    b = B.index_score(rd, cd, qc, w, K, pool=pd, scores=poison((n, NB * 8), torch.float32), q_scale=qs)
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    fa = B.index_topk_pool(rd, cd, q, w, K, pd, 128, out=poison((n, 128), torch.int32))
+    fb = B.index_topk_pool(rd, cd, qc, w, K, pd, 128, out=poison((n, 128), torch.int32), q_scale=qs)
+    assert torch.equal(fa, fb)
+    # and the bf16 scores are the oracle's (sampled rows)
+    sample = [0, 1, 699, 700, 1149, 1150]
+    rs = {k_: v[sample] for k_, v in rows.items()}
+    ko, kso = orc.mx_quant(orc.E2M1, keys.numpy())
+    s_o, bad = orc.index_score(rs, cache, q[sample].float().cpu().numpy(), w[sample].cpu().numpy(), ko, key_scales=kso,
+                               heads=64, dim=128, score_stride=stride)
+    assert bad == 0
+    full = B.index_score(rd, cd, qc, w, K, q_scale=qs, scores=poison((n, stride), torch.float32)).cpu().numpy()
+    for i, r in enumerate(sample):
+        R = min((int(pos[r]) + 1) // m, geom.n_entries[req[r]])
+        assert np.array_equal(full[r, :R], s_o[i, :R])
+
+
 def test_index_score_mxfp4_pool(orc):
     say("case: index_score MXFP4 over a candidate pool (ragged newest block, row map)")
     rows, cache, keys, q, w = _score_case(21, (4000, 999), 1, 64, 128, 10)
