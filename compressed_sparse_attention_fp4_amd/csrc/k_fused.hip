@@ -7,14 +7,16 @@
 // selection and its data movement); "SGLang and Miles Day-0 support for DeepSeek-V4.1",
 // section 5 (the indexer scores the FP4 cache directly, MQA form).
 //
-// One workgroup of 512 threads per query row and segment of 4096 pool columns (512
-// blocks of 8; a pool of 2048 blocks has 4 segments).  Its 8 waves score the segment
-// exactly as csa2_index_score does for a pool (the same MXFP4 MFMA tiles, head
-// permutation and fixed head-sum order, so every score is bit for bit the same), turn
-// each score into its order key in LDS (a column past the pool, or a pool position past
-// the row's reach, is no candidate), and run the radix selection of csa2_topk over those
-// keys: thread t takes keys [8 t, 8 t + 8), one whole pool block, so positions follow
-// from the block ids in LDS.  A one-segment pool writes the index set directly; longer
+// One workgroup per query row and segment of pool columns: launches over many rows take
+// a whole pool of up to 16,384 columns (2,048 blocks of 8) per 1024-thread workgroup;
+// few rows (a decode batch) split the pool into segments of 4,096 columns on 512
+// threads, so that the scoring spreads over every CU.  Its waves score the segment exactly as
+// csa2_index_score does for a pool (the same MXFP4 MFMA tiles, head permutation and fixed
+// head-sum order, so every score is bit for bit the same), turn each score into its order
+// key in LDS (a column past the pool, or a pool position past the row's reach, is no
+// candidate), and run the radix selection of csa2_topk over those keys: thread t takes
+// keys [KPT t, KPT t + KPT), whole pool blocks, so positions follow from the block ids in
+// LDS.  A one-segment pool writes the index set directly, with no second launch; longer
 // pools write each segment's top-k as (key, position) lists, which csa2_topk's exact list
 // merge reduces to the index set.  The result is what csa2_index_score + csa2_topk give,
 // without the 64 KiB score row per query going to memory and back.
@@ -27,12 +29,13 @@
 
 namespace csa2 {
 
-constexpr int kFusedNT = 512;
-constexpr int kFusedKPT = 8;
-constexpr int kFusedCap = kFusedNT * kFusedKPT;  // 4096 pool columns per segment
+// Segment shapes: a whole pool of up to 16,384 columns in one workgroup (no merge), or
+// segments of 4,096 columns merged afterwards.
+constexpr int kWholeNT = 1024, kWholeKPT = 16, kWholeCap = kWholeNT * kWholeKPT;
+constexpr int kSegNT = 512, kSegKPT = 8, kSegCap = kSegNT * kSegKPT;
 
-template <int NHT>
-__global__ __launch_bounds__(512) void k_score_topk_pool(RowsArg rows, CacheArg cache, const void* __restrict__ q,
+template <int NHT, int kFusedNT, int kFusedKPT>
+__global__ __launch_bounds__(kFusedNT) void k_score_topk_pool(RowsArg rows, CacheArg cache, const void* __restrict__ q,
                                                          const uint8_t* __restrict__ q_scale,
                                                          const float* __restrict__ w, int64_t w_stride,
                                                          const uint8_t* __restrict__ kdata,
@@ -43,6 +46,7 @@ __global__ __launch_bounds__(512) void k_score_topk_pool(RowsArg rows, CacheArg 
     constexpr int H = NHT * 16;
     constexpr int G = H / 4;
     constexpr int NW = kFusedNT / 64;
+    constexpr int kFusedCap = kFusedNT * kFusedKPT;
     __shared__ uint4 s_qa[NHT][64];
     __shared__ uint32_t s_qs[NHT][64];
     __shared__ int32_t s_bid[kFusedCap / 8];
@@ -219,9 +223,24 @@ __global__ __launch_bounds__(512) void k_score_topk_pool(RowsArg rows, CacheArg 
                                                (int64_t)kFusedKPT * tid, key, bid, true);
 }
 
+// Rows from which a launch takes whole pools.  One workgroup then scores a row's whole
+// pool on one CU, so with fewer rows most CUs would idle; from half the CU count on, the
+// saved list merge (a second launch) outweighs that (measured: 128 rows of 8,192 pool
+// columns 27.6 against 31.7 us, 256 rows 28.3 against 51.1 us; 64 rows of 16,384 columns
+// 44.0 against 28.8 us).
+constexpr int kWholeRows = 128;
+
+// Columns per segment: the whole pool when it fits one workgroup and the launch has rows
+// enough.
+static int64_t fused_cap(int n, int64_t cols)
+{
+    return (n >= kWholeRows && cols <= kWholeCap) ? kWholeCap : kSegCap;
+}
+
 size_t score_topk_pool_workspace(int n, int64_t cols, int k)
 {
-    const int64_t nseg = (cols + kFusedCap - 1) / kFusedCap;
+    const int64_t cap = fused_cap(n, cols);
+    const int64_t nseg = (cols + cap - 1) / cap;
     return nseg > 1 ? (size_t)n * nseg * k * sizeof(uint2) : 0;
 }
 
@@ -230,13 +249,20 @@ hipError_t launch_score_topk_pool(const RowsArg& rows, const CacheArg& cache, co
                                   const PoolArg& pool, int k, int32_t* out_idx, void* ws, hipStream_t stream)
 {
     if (rows.n == 0) return hipSuccess;
-    const int nseg = (int)(((int64_t)pool.block * pool.max_blocks + kFusedCap - 1) / kFusedCap);
+    const int64_t cols = (int64_t)pool.block * pool.max_blocks;
+    const bool whole = fused_cap(rows.n, cols) == kWholeCap;
+    const int nseg = whole ? 1 : (int)((cols + kSegCap - 1) / kSegCap);
     uint2* lists = nseg > 1 ? static_cast<uint2*>(ws) : nullptr;
     const dim3 grid((unsigned)((int64_t)rows.n * nseg));
-#define CSA2_FUSED_CASE(T)                                                                                     \
-    case T:                                                                                                    \
-        hipLaunchKernelGGL((k_score_topk_pool<T>), grid, dim3(kFusedNT), 0, stream, rows, cache, qin.q,        \
-                           qin.q_scale, w, w_stride, kdata, kscale, pool, k, nseg, out_idx, lists);             \
+#define CSA2_FUSED_LAUNCH(T, NT, KPT)                                                                        \
+    hipLaunchKernelGGL((k_score_topk_pool<T, NT, KPT>), grid, dim3(NT), 0, stream, rows, cache, qin.q,        \
+                       qin.q_scale, w, w_stride, kdata, kscale, pool, k, nseg, out_idx, lists)
+#define CSA2_FUSED_CASE(T)                              \
+    case T:                                             \
+        if (whole)                                      \
+            CSA2_FUSED_LAUNCH(T, kWholeNT, kWholeKPT);  \
+        else                                            \
+            CSA2_FUSED_LAUNCH(T, kSegNT, kSegKPT);      \
         break;
     switch (heads / 16) {
         CSA2_FUSED_CASE(1)
@@ -246,9 +272,10 @@ hipError_t launch_score_topk_pool(const RowsArg& rows, const CacheArg& cache, co
             return hipErrorInvalidValue;
     }
 #undef CSA2_FUSED_CASE
+#undef CSA2_FUSED_LAUNCH
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || nseg == 1) return e;
-    SelSource src{nullptr, (int64_t)pool.block * pool.max_blocks, rows, cache, pool};
+    SelSource src{nullptr, cols, rows, cache, pool};
     return launch_list_merge(src, k, nseg, lists, out_idx, stream);
 }
 

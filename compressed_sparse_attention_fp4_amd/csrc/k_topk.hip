@@ -426,6 +426,11 @@ hipError_t launch_list_merge(const SelSource& src, int k, int nlists, const uint
     a.out_idx = out;
     a.out_stride = k;
     a.out_mode = OUT_IDX;
+    if ((int64_t)nlists * k <= 2048 && src.rows.n < kManyRows) {
+        // a decode batch's few short lists: 512 threads pass the barriers sooner than 1024
+        hipLaunchKernelGGL((k_select<4, SRC_LIST, 512>), dim3((unsigned)src.rows.n), dim3(512), 0, stream, a);
+        return hipGetLastError();
+    }
     hipError_t e = launch_level<SRC_LIST>(dim3((unsigned)src.rows.n), (int64_t)nlists * k, src.rows.n, a, stream);
     return e == hipSuccess ? hipGetLastError() : e;
 }

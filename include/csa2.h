@@ -195,9 +195,11 @@ int csa2_topk(const csa2_rows* rows, const csa2_cache* cache, const float* score
  * position).  Supported: MXFP4 keys of dim 128, BF16 or MXFP4 index q (q_idx / q_scale as
  * for csa2_index_score), heads 16 / 32 / 64, pool
  * block 8 with max_blocks <= 2048 (the pages' 16,384-position pool), k 1..2048.
- * A pool is scored in segments of 4096 columns; pools of more than one segment need
- * workspace (csa2_workspace_size(CSA2_OP_TOPK_POOL_FUSED, n, block * max_blocks, k, 0):
- * each segment's top-k as (key, position) lists, merged exactly by a second launch).
+ * Calls over 128 rows or more score and select each row's whole pool in one workgroup
+ * and need no workspace.  Fewer rows (a decode batch) split each pool into segments of
+ * 4096 columns, spread over the CUs; pools of more than one segment then need workspace
+ * (csa2_workspace_size(CSA2_OP_TOPK_POOL_FUSED, n, block * max_blocks, k, 0): each
+ * segment's top-k as (key, position) lists, merged exactly by a second launch).
  * ------------------------------------------------------------------------------- */
 int csa2_index_topk_pool(const csa2_rows* rows, const csa2_cache* cache, const void* q_idx, csa2_dtype q_dtype,
                          const uint8_t* q_scale, int32_t heads, const float* w, int64_t w_row_stride,

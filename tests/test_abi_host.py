@@ -277,5 +277,7 @@ def test_index_topk_pool_arg_errors():
     need = B.workspace_size(B.OP_TOPK_POOL_FUSED, 4, 8 * 2048, 512)
     assert need == 4 * 4 * 512 * 8
     assert B.workspace_size(B.OP_TOPK_POOL_FUSED, 4, 8 * 512, 512) == 0   # one segment: no lists
+    assert B.workspace_size(B.OP_TOPK_POOL_FUSED, 128, 8 * 2048, 512) == 0  # whole pools: no lists
+    assert B.workspace_size(B.OP_TOPK_POOL_FUSED, 127, 8 * 2048, 512) == 127 * 4 * 512 * 8
     assert call(ws=None) == B.CSA2_E_WORKSPACE
     assert call(nbytes=need - 1) == B.CSA2_E_WORKSPACE

@@ -219,6 +219,12 @@ def test_c2_replay_flow_sampled(orc):
     idx_t = B.topk(rt_d, cd, sc_t, cfg.topk, pool=pool_d, workspace=torch.empty(
         max(1, B.workspace_size(B.OP_TOPK, nt, cfg.max_blocks * cfg.block, cfg.topk)), dtype=torch.uint8,
         device=DEV))
+    # the fused Reindex call (960 rows: one workgroup per whole pool) gives the same sets
+    ws_f = torch.empty(max(1, B.workspace_size(B.OP_TOPK_POOL_FUSED, nt, cfg.max_blocks * cfg.block, cfg.topk)),
+                       dtype=torch.uint8, device=DEV)
+    idx_f = B.index_topk_pool(rt_d, cd, qi_t, w_t, keys, pool_d, cfg.topk, workspace=ws_f,
+                              out=torch.full((nt, cfg.topk), -7, dtype=torch.int32, device=DEV))
+    assert torch.equal(idx_f, idx_t)
     kv = synth.normal_bf16((g.total_entries, cfg.dim), cfg.seed, "kv", device=DEV)
     win = synth.window_cache_geometry(g, 128)
     outs = {}

@@ -4,7 +4,8 @@ Its result is defined as csa2_index_score over the pool followed by csa2_topk ov
 scores, so the index sets must equal that two-launch path and the oracle's index sets bit
 for bit: pools of every size up to 2048 blocks (partial pools, the newest block cut by the
 reach, empty rows), a row map, heads 16 / 32 / 64, k from 1 to 2048, and rows whose scores
-tie."""
+tie; decode-sized calls (pool segments and a list merge) and calls over 128 rows or more
+(whole pools per workgroup)."""
 import numpy as np
 import pytest
 import torch
@@ -78,6 +79,28 @@ def test_fused_equals_two_launches_and_oracle(orc, H, k):
     sample = [0, 2, 4, 6, 7, 8, 9]
     rs = {key: v[sample] for key, v in rows.items()}
     pool_o = dict(pool, blocks=pool["blocks"][sample], nblocks=pool["nblocks"][sample])
+    s_o, bad = orc.index_score(rs, cache, qi[sample].float().numpy(), w[sample].numpy(), ko, key_scales=kso, heads=H,
+                               dim=128, score_stride=8 * pool["max_blocks"], pool=pool_o)
+    assert bad == 0
+    i_o = orc.topk(rs, cache, s_o, k, pool=pool_o)
+    assert np.array_equal(fused[sample], i_o)
+
+
+@pytest.mark.parametrize("H,k,map_rows", [(64, 512, False), (16, 2048, True), (32, 1, False)])
+def test_fused_whole_pools(orc, H, k, map_rows):
+    """Launches over 128 rows or more score and select each row's whole pool in one
+    workgroup (no list merge): the same index sets as the two launches and the oracle."""
+    say("case: fused pool top-k over 160 rows (whole pools) H=%d k=%d map=%s" % (H, k, map_rows))
+    R_list = [16390, 3000, 2049, 100, 8, 1, 0, 5000] * 20
+    rows, cache, keys, qi, w, pool, C = _case(330 + H + k, R_list, H, map_rows=map_rows)
+    fused, two, sc = _both(rows, cache, keys, qi, w, pool, k)
+    assert not np.any(fused == POISON_I32)
+    assert np.array_equal(fused, two)
+    ko, kso = orc.mx_quant(orc.E2M1, keys.numpy())
+    sample = [0, 1, 2, 6, 7, 159]
+    rs = {key: v[sample] for key, v in rows.items()}
+    pr = pool["row_map"][sample] if map_rows else np.array(sample)
+    pool_o = dict(pool, blocks=pool["blocks"][pr], nblocks=pool["nblocks"][pr], row_map=None)
     s_o, bad = orc.index_score(rs, cache, qi[sample].float().numpy(), w[sample].numpy(), ko, key_scales=kso, heads=H,
                                dim=128, score_stride=8 * pool["max_blocks"], pool=pool_o)
     assert bad == 0
