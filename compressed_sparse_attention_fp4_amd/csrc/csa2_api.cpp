@@ -246,6 +246,7 @@ int csa2_index_topk_pool(const csa2_rows* rows, const csa2_cache* cache, const v
         return fail(CSA2_E_UNSUPPORTED, "fused pool top-k: heads %d (16, 32 or 64)", heads);
     if (w_row_stride != 0 && w_row_stride < heads) return fail(CSA2_E_ARG, "w_row_stride < heads");
     if (misaligned(keys->data, 16)) return fail(CSA2_E_ARG, "keys->data must start on a 16-byte boundary");
+    if (misaligned(keys->scale, 4)) return fail(CSA2_E_ARG, "keys->scale must start on a 4-byte boundary");
     if (rows->n == 0) return ok();
     const size_t need = csa2::score_topk_pool_workspace(rows->n, (int64_t)pool->block * pool->max_blocks, k);
     if (need > 0 && (!workspace || workspace_bytes < need))

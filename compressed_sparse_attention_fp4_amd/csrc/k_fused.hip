@@ -33,8 +33,11 @@ namespace csa2 {
 // segments of 4,096 columns merged afterwards.
 constexpr int kWholeNT = 1024, kWholeKPT = 16, kWholeCap = kWholeNT * kWholeKPT;
 constexpr int kSegNT = 512, kSegKPT = 8, kSegCap = kSegNT * kSegKPT;
+// Key groups in flight per wave: 1024-thread workgroups have 128 VGPRs per lane, 512-thread
+// ones 256 (a group takes 20).
+constexpr int kWholeDepth = 2, kSegDepth = 2;
 
-template <int NHT, int kFusedNT, int kFusedKPT>
+template <int NHT, int kFusedNT, int kFusedKPT, int DEPTH>
 __global__ __launch_bounds__(kFusedNT) void k_score_topk_pool(RowsArg rows, CacheArg cache, const void* __restrict__ q,
                                                          const uint8_t* __restrict__ q_scale,
                                                          const float* __restrict__ w, int64_t w_stride,
@@ -124,28 +127,47 @@ __global__ __launch_bounds__(kFusedNT) void k_score_topk_pool(RowsArg rows, Cach
     // loading the next group's key tiles while it scores the current one
     const int64_t krow0 = cache.row_start[r];
     const uint8_t* kd_base = kdata + krow0 * 64 + 16 * (lane >> 4);
-    const uint8_t* ks_base = kscale + krow0 * 4 + (lane >> 4);
-    auto load = [&](int off0, u32x4_t (&kd)[4], int (&sk)[4]) {
+    // Each lane loads all four block scales of its key (one dword) and takes its own byte
+    // where the MFMA reads it: a byte load would leave 8-bit loop-carried registers that
+    // the compiler widens at the loop's back edge, waiting there for the tiles just issued.
+    const uint8_t* ks_base = kscale + krow0 * 4;
+    const int sshift = 8 * (lane >> 4);
+    // Lane (g, c) of tile u takes column off0 + 16 u + c.  The four block-id lookups are
+    // issued together (no lane skips one: a column past the segment looks column 0 up),
+    // and the lane keeps the position of column off0 + lane (tile g, its own column of the
+    // group's scores) for the candidate test after scoring: -1 when that column is no
+    // candidate.
+    auto load = [&](int off0, u32x4_t (&kd)[4], int (&sk)[4], int& mypos) {
+        int oc[4], bv[4];
 #pragma unroll
         for (int u = 0; u < 4; u++) {
             const int off = off0 + 16 * u + (lane & 15);
-            const int oc = off < ncol ? off : 0;
-            const int pos = (s_bid[oc >> 3] << 3) | (oc & 7);
-            const int j = (off < ncol && pos < R32) ? pos : 0;
+            oc[u] = off < ncol ? off : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; u++) bv[u] = s_bid[oc[u] >> 3];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const int off = off0 + 16 * u + (lane & 15);
+            const int pos = (bv[u] << 3) | (oc[u] & 7);
+            const bool cand = (off < ncol) & (pos < R32);
+            const int j = cand ? pos : 0;
+            mypos = (u == g) ? (cand ? pos : -1) : mypos;
             kd[u] = gload_x4<0>(kd_base + ((uint64_t)(uint32_t)j << 6));
-            sk[u] = gload_u8<0>(ks_base + ((uint64_t)(uint32_t)j << 2));
+            sk[u] = gload_i32<0>(ks_base + ((uint64_t)(uint32_t)j << 2));
         }
     };
-    auto score_group = [&](int off0, const u32x4_t (&kd)[4], const int (&sk)[4]) {
+    auto score_group = [&](int off0, const u32x4_t (&kd)[4], const int (&sk)[4], int mypos) {
         float P[4];
 #pragma unroll
         for (int u = 0; u < 4; u++) {
             f32x4 d[NHT];
             const i32x8 b = i32x8{(int)kd[u][0], (int)kd[u][1], (int)kd[u][2], (int)kd[u][3], 0, 0, 0, 0};
+            const int sb = (int)(((uint32_t)sk[u] >> sshift) & 0xffu);
 #pragma unroll
             for (int t = 0; t < NHT; t++) {
                 const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-                d[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[t], b, zero, 4, 4, 0, sa[t], 0, sk[u]);
+                d[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[t], b, zero, 4, 4, 0, sa[t], 0, sb);
             }
             float pp = 0.0f;
 #pragma unroll
@@ -162,28 +184,26 @@ __global__ __launch_bounds__(kFusedNT) void k_score_topk_pool(RowsArg rows, Cach
         const float h23 = __uint_as_float(s23[0]) + __uint_as_float(s23[1]);
         auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(h01), __float_as_uint(h23), false, false);
         const float score = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-        const int off = off0 + lane;
-        uint32_t key = 0u;
-        if (off < ncol) {
-            const int pos = (s_bid[off >> 3] << 3) | (off & 7);
-            key = pos < R32 ? order_key(score) : 0u;
-        }
-        s_key[off] = key;
+        s_key[off0 + lane] = mypos >= 0 ? order_key(score) : 0u;
     };
     const int ngrp = (ncol + 63) >> 6;
     const int mine = wave < ngrp ? (ngrp - wave + NW - 1) / NW : 0;  // groups of this wave
-    {
-        u32x4_t ka[4], kb[4];
-        int sa4[4], sb4[4];
-        if (mine > 0) load(64 * wave, ka, sa4);
-        int i = 0;
-        for (; i + 1 < mine; i += 2) {
-            load(64 * (wave + NW * (i + 1)), kb, sb4);
-            score_group(64 * (wave + NW * i), ka, sa4);
-            if (i + 2 < mine) load(64 * (wave + NW * (i + 2)), ka, sa4);
-            score_group(64 * (wave + NW * (i + 1)), kb, sb4);
+    if (mine > 0) {
+        // A ring of DEPTH key groups: group i is scored while groups i + 1 .. i + DEPTH - 1
+        // are in flight.  Every pass issues the same loads (a group past the wave's last
+        // reads column 0 again, never scored), so the compiler's wait before each group's
+        // products is the same on every path and leaves the later groups in flight.
+        u32x4_t kr[DEPTH][4];
+        int sr[DEPTH][4], pr[DEPTH];
+#pragma unroll
+        for (int d = 0; d < DEPTH; d++) load(64 * (wave + NW * d), kr[d], sr[d], pr[d]);
+        for (int i = 0; i < mine; i += DEPTH) {
+#pragma unroll
+            for (int d = 0; d < DEPTH; d++) {
+                if (i + d < mine) score_group(64 * (wave + NW * (i + d)), kr[d], sr[d], pr[d]);
+                load(64 * (wave + NW * (i + d + DEPTH)), kr[d], sr[d], pr[d]);
+            }
         }
-        if (i < mine) score_group(64 * (wave + NW * i), ka, sa4);
     }
     // groups past the pool hold no candidate
     for (int c = 64 * ngrp + tid; c < kFusedCap; c += kFusedNT) s_key[c] = 0u;
@@ -254,15 +274,15 @@ hipError_t launch_score_topk_pool(const RowsArg& rows, const CacheArg& cache, co
     const int nseg = whole ? 1 : (int)((cols + kSegCap - 1) / kSegCap);
     uint2* lists = nseg > 1 ? static_cast<uint2*>(ws) : nullptr;
     const dim3 grid((unsigned)((int64_t)rows.n * nseg));
-#define CSA2_FUSED_LAUNCH(T, NT, KPT)                                                                        \
-    hipLaunchKernelGGL((k_score_topk_pool<T, NT, KPT>), grid, dim3(NT), 0, stream, rows, cache, qin.q,        \
+#define CSA2_FUSED_LAUNCH(T, NT, KPT, DEPTH)                                                                 \
+    hipLaunchKernelGGL((k_score_topk_pool<T, NT, KPT, DEPTH>), grid, dim3(NT), 0, stream, rows, cache, qin.q, \
                        qin.q_scale, w, w_stride, kdata, kscale, pool, k, nseg, out_idx, lists)
-#define CSA2_FUSED_CASE(T)                              \
-    case T:                                             \
-        if (whole)                                      \
-            CSA2_FUSED_LAUNCH(T, kWholeNT, kWholeKPT);  \
-        else                                            \
-            CSA2_FUSED_LAUNCH(T, kSegNT, kSegKPT);      \
+#define CSA2_FUSED_CASE(T)                                           \
+    case T:                                                          \
+        if (whole)                                                   \
+            CSA2_FUSED_LAUNCH(T, kWholeNT, kWholeKPT, kWholeDepth);  \
+        else                                                         \
+            CSA2_FUSED_LAUNCH(T, kSegNT, kSegKPT, kSegDepth);        \
         break;
     switch (heads / 16) {
         CSA2_FUSED_CASE(1)

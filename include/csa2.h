@@ -35,7 +35,8 @@
  *   - Element arrays move in 16-byte vectors and must start on a 16-byte boundary (every
  *     hipMalloc / torch allocation does): q_idx and keys->data of csa2_index_score (MXFP4);
  *     q, kv, kv_scale, out, swa->data and swa->scale of csa2_sparse_swa_attn (BF16); x and
- *     codes of csa2_quant_mx.  A misaligned pointer is CSA2_E_ARG.  Row pitches follow from
+ *     codes of csa2_quant_mx; keys->scale of csa2_index_topk_pool moves in 4-byte words and
+ *     must start on a 4-byte boundary.  A misaligned pointer is CSA2_E_ARG.  Row pitches follow from
  *     the shapes (64 + 4 bytes per MXFP4 key, 1 KiB per bf16 KV row, 256 + 32 bytes per
  *     FP4_S16 KV row), so aligned bases keep every row aligned.
  *   - Results are deterministic: the same inputs give bitwise-identical outputs, and a

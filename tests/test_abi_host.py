@@ -274,6 +274,7 @@ def test_index_topk_pool_arg_errors():
     assert call(qdt=B.MXFP4) == B.CSA2_E_ARG and "q_scale" in _err()
     assert call(qs=P) == B.CSA2_E_ARG and "q_scale" in _err()
     assert call(kk=B._IndexKeys(B.F32, 128, P, None)) == B.CSA2_E_UNSUPPORTED
+    assert call(kk=B._IndexKeys(B.MXFP4, 128, P, ctypes.c_void_p(4098))) == B.CSA2_E_ARG and "keys->scale" in _err()
     need = B.workspace_size(B.OP_TOPK_POOL_FUSED, 4, 8 * 2048, 512)
     assert need == 4 * 4 * 512 * 8
     assert B.workspace_size(B.OP_TOPK_POOL_FUSED, 4, 8 * 512, 512) == 0   # one segment: no lists
