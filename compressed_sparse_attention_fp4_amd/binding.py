@@ -24,7 +24,8 @@ OP_TOPK, OP_TOPK_HIER, OP_ATTN, OP_TOPK_POOL_FUSED = 1, 2, 3, 4
 # Every symbol include/csa2.h declares.
 EXPORTS = ["csa2_index_score", "csa2_topk", "csa2_topk_hier", "csa2_topk_hier_noalloc", "csa2_sparse_swa_attn",
            "csa2_replay_tail_layout", "csa2_encoder_replay_layout", "csa2_workspace_size", "csa2_last_error",
-           "csa2_version", "csa2_quant_mx", "csa2_kv_produce", "csa2_index_topk_pool"]
+           "csa2_version", "csa2_quant_mx", "csa2_kv_produce", "csa2_index_topk_pool", "csa2_check_inputs"]
+BAD_REQ, BAD_POS, BAD_WIN_LO, BAD_CACHE, BAD_POOL_MAP, BAD_POOL, BAD_SEL_MAP, BAD_SEL = 1, 2, 4, 8, 16, 32, 64, 128
 TAIL_BORROW_PREFIX_WINDOW = 1
 
 
@@ -227,6 +228,24 @@ def index_topk_pool(rows: Rows, cache: Cache, q_idx: torch.Tensor, w: torch.Tens
                                     _stream(stream))
     _check(rc)
     return out
+
+
+def check_inputs(rows: Rows, cache: Cache, pool: Optional[Pool] = None, sel: Optional[torch.Tensor] = None,
+                 sel_row_map: Optional[torch.Tensor] = None, word: Optional[torch.Tensor] = None,
+                 stream=None) -> torch.Tensor:
+    """csa2_check_inputs: a device uint32 word (as int32 [1]) of CSA2_BAD_* bits; 0 when
+    every checked precondition holds.  sel: int32 [sel_rows, k] index sets."""
+    if word is None:
+        word = torch.empty(1, dtype=torch.int32, device=rows.req_of_row.device)
+    k = sel.shape[1] if sel is not None else 0
+    rc = lib().csa2_check_inputs(ctypes.byref(rows.c()), ctypes.byref(cache.c()),
+                                 ctypes.byref(pool.c()) if pool is not None else None,
+                                 ctypes.c_int32(pool.blocks.shape[0] if pool is not None else 0), _ptr(sel),
+                                 ctypes.c_int32(k), ctypes.c_int64(sel.stride(0) if sel is not None else 0),
+                                 _ptr(sel_row_map), ctypes.c_int32(sel.shape[0] if sel is not None else 0),
+                                 _ptr(word), _stream(stream))
+    _check(rc)
+    return word
 
 
 def workspace_size(op: int, n: int, cols: int, k: int, max_blocks: int = 0) -> int:

@@ -18,7 +18,8 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libcsa2.so")
 BUILD = os.path.join(ROOT, "_build", "csa2")
 
-SOURCES = ["csa2_api.cpp", "k_tail_quant.hip", "k_score.hip", "k_topk.hip", "k_attn.hip", "k_produce.hip", "k_fused.hip"]
+SOURCES = ["csa2_api.cpp", "k_tail_quant.hip", "k_score.hip", "k_topk.hip", "k_attn.hip", "k_produce.hip", "k_fused.hip",
+           "k_check.hip"]
 
 
 def hipcc() -> str:

@@ -477,4 +477,32 @@ int csa2_quant_mx(csa2_dtype fmt, const void* x, csa2_dtype x_dtype, int64_t nbl
                          "csa2_quant_mx");
 }
 
+
+int csa2_check_inputs(const csa2_rows* rows, const csa2_cache* cache, const csa2_pool* pool, int32_t pool_rows,
+                      const int32_t* sel, int32_t k, int64_t sel_stride, const int32_t* sel_row_map,
+                      int32_t sel_rows, uint32_t* error_word, void* stream)
+{
+    int rc;
+    if ((rc = check_rows(rows)) || (rc = check_cache(cache))) return rc;
+    if (!error_word) return fail(CSA2_E_ARG, "error_word is NULL");
+    if (misaligned(error_word, 4)) return fail(CSA2_E_ARG, "error_word must start on a 4-byte boundary");
+    if (pool) {
+        if ((rc = check_pool(pool, (int64_t)pool->block * pool->max_blocks))) return rc;
+        if (pool_rows < 1) return fail(CSA2_E_ARG, "pool_rows = %d < 1", pool_rows);
+    }
+    if (sel) {
+        if (k < 0) return fail(CSA2_E_ARG, "k = %d < 0", k);
+        if (sel_stride < k) return fail(CSA2_E_ARG, "sel_stride %lld < k %d", (long long)sel_stride, k);
+        if (sel_row_map && sel_rows < 1) return fail(CSA2_E_ARG, "sel_rows = %d < 1", sel_rows);
+    } else if (sel_row_map) {
+        return fail(CSA2_E_ARG, "sel_row_map without sel");
+    }
+    if ((rc = check_device())) return rc;
+    return launch_result(csa2::launch_check_inputs(rows_arg(rows), cache->nreq, cache_arg(cache), pool_arg(pool),
+                                                   pool ? pool_rows : 0, sel, sel ? k : 0, sel_stride, sel_row_map,
+                                                   sel_row_map ? sel_rows : rows->n, error_word,
+                                                   static_cast<hipStream_t>(stream)),
+                         "csa2_check_inputs");
+}
+
 }  // extern "C"

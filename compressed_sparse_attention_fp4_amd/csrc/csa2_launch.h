@@ -112,4 +112,9 @@ hipError_t launch_kv_produce(int n, const int32_t* req_of_row, const int32_t* po
                              const float* rope, int64_t max_pos, bool fp4_kv, void* kv, uint8_t* kv_scale,
                              uint8_t* idx_codes, uint8_t* idx_scales, hipStream_t stream);
 
+// Debug check of device-array preconditions into an error word (cleared first).
+hipError_t launch_check_inputs(const RowsArg& rows, int nreq, const CacheArg& cache, const PoolArg& pool,
+                               int pool_rows, const int32_t* sel, int k, int64_t sel_stride,
+                               const int32_t* sel_row_map, int sel_rows, uint32_t* word, hipStream_t stream);
+
 }  // namespace csa2

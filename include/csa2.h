@@ -31,7 +31,8 @@
  *     detected before launch (every CSA2_E_ARG / CSA2_E_UNSUPPORTED / CSA2_E_WORKSPACE).
  *     csa2_last_error() gives a message for the calling thread.
  *   - Device-array contents (positions, lengths, indices) are preconditions stated per
- *     call; they are not checked.
+ *     call; the calls do not check them.  csa2_check_inputs checks the row, cache, pool
+ *     and index-set ones on the device into an error word, for debugging callers.
  *   - Element arrays move in 16-byte vectors and must start on a 16-byte boundary (every
  *     hipMalloc / torch allocation does): q_idx and keys->data of csa2_index_score (MXFP4);
  *     q, kv, kv_scale, out, swa->data and swa->scale of csa2_sparse_swa_attn (BF16); x and
@@ -55,7 +56,7 @@
 extern "C" {
 #endif
 
-#define CSA2_VERSION 3
+#define CSA2_VERSION 4
 
 enum {
     CSA2_OK = 0,
@@ -358,6 +359,34 @@ enum { CSA2_OP_TOPK = 1, CSA2_OP_TOPK_HIER = 2, CSA2_OP_ATTN = 3, CSA2_OP_TOPK_P
  * block * max_blocks (TOPK_POOL_FUSED) or the number of selected entries k (ATTN), k,
  * max_blocks (TOPK_HIER). */
 size_t csa2_workspace_size(int op, int32_t n, int64_t cols, int32_t k, int32_t max_blocks);
+
+/* ---------------------------------------------------------------------------------
+ * csa2_check_inputs -- debug check of the device-array preconditions the calls above
+ * state, for callers that want them verified (the calls themselves assume them): on
+ * `stream`, *error_word (a device uint32, 4-byte aligned) is cleared, then every
+ * violation found ORs its bit in.  Nothing else is written.  The caller reads the word
+ * after the stream reaches the check; 0 means every checked precondition holds.
+ *   rows, cache: required.  CSA2_BAD_REQ: req_of_row outside [0, nreq);
+ *     CSA2_BAD_POS: pos_of_row < 0; CSA2_BAD_WIN_LO: win_lo < 0 or > pos_of_row;
+ *     CSA2_BAD_CACHE: n_entries < 0 or row_start < 0 (every request).
+ *   pool (or NULL) with pool_rows rows of blocks / nblocks: CSA2_BAD_POOL_MAP: a row's
+ *     pool row (row_map, else the row itself) outside [0, pool_rows); CSA2_BAD_POOL:
+ *     nblocks outside [0, max_blocks], or a pool row's block ids not strictly ascending,
+ *     negative, or so large that a position of the block overflows int32.
+ *   sel (or NULL) [sel_rows][sel_stride], k per row, read through sel_row_map (or NULL:
+ *     row q reads sel row q): CSA2_BAD_SEL_MAP: a mapped row outside [0, sel_rows);
+ *     CSA2_BAD_SEL: an index neither -1 nor in [0, R(q)).
+ * Only the pool and index rows that some query row reads are checked; a row whose
+ * request or position is invalid has no reach, so its pool and index rows are skipped.
+ * Two launches (clear, check); the check reads each checked array once.
+ * ------------------------------------------------------------------------------- */
+enum {
+    CSA2_BAD_REQ = 1, CSA2_BAD_POS = 2, CSA2_BAD_WIN_LO = 4, CSA2_BAD_CACHE = 8,
+    CSA2_BAD_POOL_MAP = 16, CSA2_BAD_POOL = 32, CSA2_BAD_SEL_MAP = 64, CSA2_BAD_SEL = 128
+};
+int csa2_check_inputs(const csa2_rows* rows, const csa2_cache* cache, const csa2_pool* pool, int32_t pool_rows,
+                      const int32_t* sel, int32_t k, int64_t sel_stride, const int32_t* sel_row_map,
+                      int32_t sel_rows, uint32_t* error_word, void* stream);
 
 /* Message of the calling thread's last error ("" after success). */
 const char* csa2_last_error(void);

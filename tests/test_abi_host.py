@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     L = B.lib()
     for name in _declared():
         assert hasattr(L, name), name
-    assert L.csa2_version() == 3
+    assert L.csa2_version() == 4
 
 
 def _rows(n=4):
@@ -282,3 +282,23 @@ def test_index_topk_pool_arg_errors():
     assert B.workspace_size(B.OP_TOPK_POOL_FUSED, 127, 8 * 2048, 512) == 127 * 4 * 512 * 8
     assert call(ws=None) == B.CSA2_E_WORKSPACE
     assert call(nbytes=need - 1) == B.CSA2_E_WORKSPACE
+
+
+def test_check_inputs_arg_errors():
+    L = B.lib()
+    W = ctypes.c_void_p(4096)
+
+    def call(rows=None, pool=None, prows=4, sel=None, k=8, stride=8, smap=None, srows=4, word=W):
+        return L.csa2_check_inputs(ctypes.byref(rows or _rows()), ctypes.byref(_cache()),
+                                   ctypes.byref(pool) if pool is not None else None, ctypes.c_int32(prows), sel,
+                                   ctypes.c_int32(k), ctypes.c_int64(stride), smap, ctypes.c_int32(srows), word, None)
+
+    assert call(word=None) == B.CSA2_E_ARG and "error_word" in _err()
+    assert call(word=ctypes.c_void_p(4098)) == B.CSA2_E_ARG and "4-byte" in _err()
+    assert call(rows=B._Rows(-1, P, P, None)) == B.CSA2_E_ARG
+    assert call(pool=B._Pool(8, 64, P, P, None), prows=0) == B.CSA2_E_ARG and "pool_rows" in _err()
+    assert call(pool=B._Pool(3, 64, P, P, None)) == B.CSA2_E_ARG and "block" in _err()
+    assert call(sel=P, k=-1) == B.CSA2_E_ARG
+    assert call(sel=P, k=8, stride=4) == B.CSA2_E_ARG and "sel_stride" in _err()
+    assert call(sel=P, smap=P, srows=0) == B.CSA2_E_ARG and "sel_rows" in _err()
+    assert call(smap=P) == B.CSA2_E_ARG and "sel_row_map without sel" in _err()
