@@ -98,7 +98,10 @@ int check_pool(const csa2_pool* pool, int64_t score_stride)
 }
 
 csa2::RowsArg rows_arg(const csa2_rows* r) { return csa2::RowsArg{r->n, r->req_of_row, r->pos_of_row, r->win_lo}; }
-csa2::CacheArg cache_arg(const csa2_cache* c) { return csa2::CacheArg{c->ratio_m, c->n_entries, c->row_start}; }
+csa2::CacheArg cache_arg(const csa2_cache* c)
+{
+    return csa2::CacheArg{c->ratio_m, c->n_entries, c->row_start, c->nreq};
+}
 csa2::PoolArg pool_arg(const csa2_pool* p)
 {
     if (!p) return csa2::PoolArg{nullptr, nullptr, nullptr, 0, 0};

@@ -19,6 +19,7 @@ struct CacheArg {
     int ratio_m;
     const int32_t* n_entries;
     const int64_t* row_start;
+    int nreq;  // entries of n_entries / row_start
 };
 
 struct PoolArg {

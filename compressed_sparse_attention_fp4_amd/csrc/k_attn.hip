@@ -21,6 +21,7 @@ struct RowKeys {
     int64_t t0;    // first window position
     int nwin;      // window rows
     const int32_t* sel;
+    int64_t wbase;  // window row of position 0 (row_keys_spec only)
 };
 
 __device__ __forceinline__ RowKeys row_keys(const RowsArg& rows, const CacheArg& cache, const SwaArg& swa,
@@ -34,6 +35,36 @@ __device__ __forceinline__ RowKeys row_keys(const RowsArg& rows, const CacheArg&
     int64_t t0 = (int64_t)rk.p - swa.window + 1;
     const int64_t lo = rows.win_lo ? rows.win_lo[row] : 0;
     const int64_t ps = swa.pos_start[rk.r];
+    t0 = t0 > lo ? t0 : lo;
+    t0 = t0 > ps ? t0 : ps;
+    rk.t0 = t0;
+    rk.nwin = (int)((int64_t)rk.p - t0 + 1 > 0 ? (int64_t)rk.p - t0 + 1 : 0);
+    rk.sel = sel ? sel + (int64_t)(sel_row_map ? sel_row_map[row] : row) * sel_stride : nullptr;
+    return rk;
+}
+
+// row_keys for the bf16 kernel, with the request's metadata loaded speculatively: in a
+// decode batch row q usually serves request q, so the per-request values of request
+// `row` (when such a request exists) are loaded together with the row's own request
+// number and used when it matches; only a row of another request waits for a second
+// round of loads.  The result is row_keys' in every case.
+__device__ __forceinline__ RowKeys row_keys_spec(const RowsArg& rows, const CacheArg& cache, const SwaArg& swa,
+                                                 const int32_t* sel, int64_t sel_stride,
+                                                 const int32_t* sel_row_map, int row)
+{
+    const int g = row < cache.nreq ? row : 0;
+    const int64_t kv0_g = cache.row_start[g];
+    const int64_t ps_g = swa.pos_start[g];
+    const int64_t ws_g = swa.row_start[g];
+    RowKeys rk;
+    rk.r = rows.req[row];
+    rk.p = rows.pos[row];
+    const bool hit = rk.r == g;
+    rk.kv0 = hit ? kv0_g : cache.row_start[rk.r];
+    const int64_t ps = hit ? ps_g : swa.pos_start[rk.r];
+    rk.wbase = (hit ? ws_g : swa.row_start[rk.r]) - ps;
+    int64_t t0 = (int64_t)rk.p - swa.window + 1;
+    const int64_t lo = rows.win_lo ? rows.win_lo[row] : 0;
     t0 = t0 > lo ? t0 : lo;
     t0 = t0 > ps ? t0 : ps;
     rk.t0 = t0;
@@ -274,9 +305,9 @@ __global__ __launch_bounds__(256) void k_attn_bf16(RowsArg rows, CacheArg cache,
 #pragma unroll
         for (int s = 0; s < 16; s++) qb[s] = load_bf16x8(qrow + 32 * s);
     }
-    const RowKeys rk = row_keys(rows, cache, swa, sel, sel_stride, sel_row_map, row);
+    const RowKeys rk = row_keys_spec(rows, cache, swa, sel, sel_stride, sel_row_map, row);
     const int ntiles = sel_tiles + ((rk.nwin + 15) >> 4);
-    const int64_t swa_base = swa.row_start[rk.r] - swa.pos_start[rk.r] + rk.t0;
+    const int64_t swa_base = rk.wbase + rk.t0;
     const int win_first = wave + 4 * ntw;  // the wave's first window tile
 
     // FP8 window tiles go through registers: the raw rows of the wave's next window tile
