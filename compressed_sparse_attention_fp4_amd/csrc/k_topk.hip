@@ -472,6 +472,21 @@ __global__ __launch_bounds__(256) void k_block_max(SelSource s, uint32_t* __rest
     bmax[(int64_t)row * bstride + c] = m;
 }
 
+// Pools of rows whose every block fits: blocks 0 .. ceil(ncol / block) - 1 ascending, -1
+// padded (the hierarchy keeps every block of such a row, the newest included).
+__global__ __launch_bounds__(256) void k_pool_all(SelSource s, int block_shift, int32_t* __restrict__ out_blocks,
+                                                  int max_blocks, int32_t* __restrict__ out_nblocks)
+{
+    const int row = blockIdx.x;
+    int64_t R, ncol;
+    int prow;
+    row_info(s, row, &R, &ncol, &prow);
+    const int nblk = (int)((ncol + (1 << block_shift) - 1) >> block_shift);  // <= max_blocks (host-checked)
+    int32_t* o = out_blocks + (int64_t)row * max_blocks;
+    for (int i = threadIdx.x; i < max_blocks; i += blockDim.x) o[i] = i < nblk ? i : -1;
+    if (threadIdx.x == 0) out_nblocks[row] = nblk;
+}
+
 // The two-stage hierarchy (blocks of 8, k <= max_blocks - 1): block maxima, the pool's
 // blocks selected from them, then the flat top-k taken over the pool's positions only.
 // The last step is exact: an entry outside the pool lies in a non-newest block with at
@@ -486,6 +501,7 @@ static size_t bmax_bytes(int n, int64_t stride)
 
 size_t topk_hier_workspace(int n, int64_t stride, int k, int block, int max_blocks)
 {
+    if ((stride + block - 1) / block <= max_blocks) return plan_workspace(make_plan(stride, k, SRC_FULL), n, k);
     if (two_stage(k, block, max_blocks)) {
         const int64_t bstride = (stride + 7) / 8;
         const size_t blk = plan_workspace(make_plan(bstride, max_blocks - 1, SRC_BMAX), n, max_blocks - 1);
@@ -504,6 +520,18 @@ hipError_t launch_topk_hier(const SelSource& src, int k, int block, int max_bloc
     (void)ws_bytes;
     const int n = src.rows.n;
     if (n == 0) return hipSuccess;
+    if ((src.stride + block - 1) / block <= max_blocks) {
+        // Every row keeps all its blocks (a score row has at most ceil(stride / block)), so
+        // the pool needs no selection and the flat top-k runs over the score rows directly
+        // (e.g. a replay's source layer: 8192 positions, pools of 2048 blocks).
+        hipError_t e = run_plan(src, SRC_FULL, 0, k, src.stride, OUT_IDX, out_idx, k, nullptr, ws, stream);
+        if (e != hipSuccess) return e;
+        SelSource sb = src;
+        sb.pool = PoolArg{nullptr, nullptr, nullptr, block, max_blocks};
+        hipLaunchKernelGGL(k_pool_all, dim3((unsigned)n), dim3(256), 0, stream, sb, ilog2(block), out_blocks,
+                           max_blocks, out_nblocks);
+        return hipGetLastError();
+    }
     if (two_stage(k, block, max_blocks)) {
         const int64_t bstride = (src.stride + 7) / 8;
         uint32_t* bmax = static_cast<uint32_t*>(ws);

@@ -471,6 +471,23 @@ def test_topk_hier(orc, ties):
     assert np.array_equal(idx.cpu().numpy(), ri)
 
 
+@pytest.mark.parametrize("ties,max_blocks,k", [(None, 1025, 512), (2.0, 2048, 512), (None, 1100, 2048)])
+def test_topk_hier_all_blocks_fit(orc, ties, max_blocks, k):
+    """Score rows of at most max_blocks blocks (a replay's source layer: 8192 positions, pools
+    of 2048 blocks): every row keeps all its blocks and the flat top-k runs on the score
+    rows directly; ragged reaches, a stride that is not a multiple of the block, ties."""
+    say("case: topk_hier with every block in the pool ties=%s max_blocks=%d k=%d" % (ties, max_blocks, k))
+    R_list = [0, 1, 7, 9, 100, 513, 4096, 8191, 8199, 8200, 8200, 3000]
+    stride = 8200
+    rows, cache, scores = _topk_inputs(57, R_list, stride, ties)
+    idx, blocks, nblocks = _hier(dev_rows(rows), dev_cache(cache), torch.from_numpy(scores).to(DEV), k, 8,
+                                 max_blocks)
+    ri, rb, rn = orc.topk_hier(rows, cache, scores, k, 8, max_blocks)
+    assert np.array_equal(nblocks.cpu().numpy(), rn)
+    assert np.array_equal(blocks.cpu().numpy(), rb)
+    assert np.array_equal(idx.cpu().numpy(), ri)
+
+
 # ------------------------------------------------------------------ attention
 def test_attn_f32_c0(orc):
     say("case: sparse+window attention fp32 (C0), k=64 and k=512 (dense equivalence)")
