@@ -305,9 +305,11 @@ static size_t plan_workspace(const Plan& p, int n, int k)
 }
 
 // Launches over many rows (a prefill, a replay over thousands of extend rows) select
-// with 256-thread workgroups: a workgroup's passes are a chain of barriers whose cost
-// grows with its wave count, and four times as many of them fit on a CU, so rows per
-// second rise; few rows (a decode batch) keep 1024 threads, which finish one row
+// with small workgroups: a workgroup's passes are a chain of barriers whose cost grows
+// with its wave count, and more of them fit on a CU, so rows per second rise.  Slices
+// of up to 4096 candidates take 256 threads; 8192 take 512 threads of 16 (32 per thread
+// on 256 threads needs 170 VGPRs, two workgroups per CU: 27,332 rows of 8192 took 686
+// against 518 us).  Few rows (a decode batch) keep 1024 threads, which finish one row
 // sooner.  The selection is exact either way.
 constexpr int kManyRows = 1024;
 
@@ -323,7 +325,7 @@ static hipError_t launch_level(dim3 grid, int64_t cap, int nrows, const SelArgs&
         else if (cap <= 4096)
             hipLaunchKernelGGL((k_select<16, SRC, 256>), grid, dim3(256), 0, stream, a);
         else
-            hipLaunchKernelGGL((k_select<32, SRC, 256>), grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((k_select<16, SRC, 512>), grid, dim3(512), 0, stream, a);
         return hipSuccess;
     }
     if (cap <= 4096)  // (pool gathers take whole blocks: at least 8 per thread)

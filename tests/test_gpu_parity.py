@@ -377,8 +377,8 @@ def test_topk_flat(orc, k, ties):
 @pytest.mark.parametrize("stride", [2048, 4096, 8192])
 @pytest.mark.parametrize("ties", [None, 4.0])
 def test_topk_many_rows(orc, stride, ties):
-    """At least 1024 rows select with 256-thread workgroups (8, 16 or 32 candidates per
-    thread by the row length): ragged reaches around k and the slice sizes, with and
+    """At least 1024 rows select with small workgroups (256 threads of 8 or 16 candidates,
+    512 threads of 16, by the row length): ragged reaches around k and the slice sizes, with and
     without ties, checked row by row against the oracle; the same rows in a batch of
     16 (1024-thread workgroups) give the same index sets."""
     say("case: topk many rows stride=%d ties=%s" % (stride, ties))
