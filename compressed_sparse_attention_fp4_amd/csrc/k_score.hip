@@ -486,13 +486,13 @@ __global__ __launch_bounds__(256, 3) void k_score_mxfp4_pair(RowsArg rows, Cache
 static int pick_chunk(int n, int64_t cols, int block)
 {
     // Each workgroup quantizes its row's index q once, so columns per workgroup should be
-    // many (1024..8192); shrink only while there are fewer than 512 workgroups (two per CU:
-    // a decode batch of 64 rows over 65,536 positions took 49.7 us in 512 workgroups of
-    // 8192 columns against 51.6 us in 2048 of 2048; 32 rows over 262,144 positions do not
-    // depend on it).  A pool chunk spans at most kScoreMaxBlocks blocks (1024 columns
-    // suffice for block 1).
+    // many (1024..8192); shrink only while there are fewer than 2048 workgroups (about two
+    // rounds of the 256 CUs at 4 workgroups each, which evens out the finish; 512
+    // workgroups of 8192 columns were no faster for a decode batch of 64 rows over 65,536
+    // positions, and 32 rows over 262,144 do not depend on it).  A pool chunk spans at most
+    // kScoreMaxBlocks blocks (1024 columns suffice for block 1).
     int64_t chunk = 8192;
-    while (chunk > 1024 && (int64_t)n * ((cols + chunk - 1) / chunk) < 512) chunk >>= 1;
+    while (chunk > 1024 && (int64_t)n * ((cols + chunk - 1) / chunk) < 2048) chunk >>= 1;
     while (block > 0 && chunk / block > kScoreMaxBlocks) chunk >>= 1;
     return (int)chunk;
 }
