@@ -270,6 +270,12 @@ def test_index_score_mxfp4_q_input(orc):
     fa = B.index_topk_pool(rd, cd, q, w, K, pd, 128, out=poison((n, 128), torch.int32))
     fb = B.index_topk_pool(rd, cd, qc, w, K, pd, 128, out=poison((n, 128), torch.int32), q_scale=qs)
     assert torch.equal(fa, fb)
+    # the decode-sized shape (fewer than 128 rows: pool segments) gives the same sets
+    few = {k_: v[:100] for k_, v in rows.items()}
+    pf = B.Pool(pd.blocks[:100].contiguous(), pd.nblocks[:100].contiguous(), 8)
+    fc = B.index_topk_pool(dev_rows(few), cd, qc[:100], w[:100], K, pf, 128, out=poison((100, 128), torch.int32),
+                           q_scale=qs[:100])
+    assert torch.equal(fc, fa[:100])
     # and the bf16 scores are the oracle's (sampled rows)
     sample = [0, 1, 699, 700, 1149, 1150]
     rs = {k_: v[sample] for k_, v in rows.items()}
