@@ -1,4 +1,4 @@
-"""GPU parity at the workloads' full sizes, on sampled rows.
+"""GPU parity at the workloads' full sizes.
 
 Each test runs the HIP path on a whole workload (the decode step exactly as the
 benchmark launches it for C3; C1 prefill with its full 8192-token requests; the C2
@@ -7,7 +7,10 @@ oracle, row by row: index scores and index sets bit for bit, attention outputs w
 |g - r| <= 2e-2 + 1e-2 |r| and a per-row relative L2 error <= 1e-2.  Sampled rows
 include the boundary positions (0, 126..129, 510..512, S - 1).  Every oracle input is
 regenerated from the seeded generator and quantized by the oracle's own quantizer; its
-bytes are checked against the library's before use."""
+bytes are checked against the library's before use.  For the decode workloads (C3, C4)
+every row is checked as well: each row's selection against its definition evaluated on
+the host over the device's scores, and each row's attention against the oracle over a
+compact cache of the rows it selected."""
 import math
 
 import numpy as np
@@ -38,7 +41,66 @@ def oracle_window(orc, raw_rows, nreq_rows, pos_start, window=128):
 
 
 # ------------------------------------------------------------------------- C3
-def test_c3_decode_step_sampled(orc):
+@pytest.fixture(scope="module")
+def c3_step():
+    """The benchmark's input set 0 after one decode step, launched as bench.py times it."""
+    import bench
+    x = bench.InputSet(0, DEV)
+    bench.step(x)
+    torch.cuda.synchronize()
+    return x
+
+
+def order_keys(v):
+    """float32 -> the selection's order-preserving uint32 keys (larger key = larger value)."""
+    b = np.asarray(v, np.float32).view(np.uint32)
+    return np.where(b >> 31, ~b, b | np.uint32(0x80000000)).astype(np.uint32)
+
+
+def top_positions(keys, pos, k):
+    """The k best (key desc, position asc) positions, ascending."""
+    order = np.lexsort((pos, -keys.astype(np.int64)))
+    return np.sort(pos[order[:k]])
+
+
+def check_hier_by_definition(scores, reach, pb, pn, idx, k, nb, blk):
+    """Hierarchical selection of every row, by its definition over the given score rows: the
+    pool is the nb - 1 best non-newest blocks by maximum score (ties to the lower block id)
+    plus the newest block, or every block when they fit; the index set is the k best pool
+    positions below the reach (ties to the lower position), ascending."""
+    for r, R in enumerate(reach):
+        sk = order_keys(scores[r, :R])
+        nblk = (R + blk - 1) // blk
+        if nblk <= nb:
+            pool = np.arange(nblk)
+        else:
+            full = (R // blk) * blk
+            bmax = sk[:full].reshape(-1, blk).max(axis=1)[:nblk - 1]
+            pool = np.sort(np.concatenate([top_positions(bmax, np.arange(nblk - 1), nb - 1), [nblk - 1]]))
+        assert pn[r] == len(pool) and np.array_equal(pb[r, :pn[r]], pool), r
+        assert np.all(pb[r, pn[r]:] == -1), r
+        cand = (pool[:, None] * blk + np.arange(blk)[None, :]).ravel()
+        cand = cand[cand < R]
+        want = top_positions(sk[cand], cand, k)
+        assert np.array_equal(idx[r, :len(want)], want) and np.all(idx[r, len(want):] == -1), r
+
+
+def check_attn_compact(orc, kv, row_start, sel, q, wo, pos, ratio_m, heads, dim):
+    """Attention of every row against the oracle over a compact cache: row r's selected
+    main-KV rows (kv[row_start[r] + sel[r, i]]) gathered to rows r * k + i.  sel must hold
+    no -1 slots (every row reaches more than k entries)."""
+    n, k = sel.shape
+    assert bool((sel >= 0).all())
+    kv_c = bits(kv[(row_start.to(torch.int64)[:, None] + sel.to(torch.int64)).reshape(-1)])
+    rows_o = dict(req_of_row=np.arange(n), pos_of_row=np.asarray(pos))
+    cache_o = dict(ratio_m=ratio_m, n_entries=np.full(n, k), row_start=np.arange(n, dtype=np.int64) * k)
+    sel_o = np.tile(np.arange(k, dtype=np.int32), (n, 1))
+    out_o, _ = orc.sparse_swa_attn(rows_o, cache_o, bits(q), 1, kv_c, 1, sel_o, wo, heads=heads, dim=dim,
+                                   sm_scale=synth.sm_scale(dim))
+    return out_o
+
+
+def test_c3_decode_step_sampled(orc, c3_step):
     """The benchmark's decode step (64 requests x 1 query, S=131072, m=2, source layer
     with hierarchical selection, then 7 Reindex layers through the fused pool scoring +
     top-k), launched exactly as bench.py times it; the source layer and the last Reindex
@@ -46,9 +108,7 @@ def test_c3_decode_step_sampled(orc):
     scoring call on the same inputs)."""
     import bench
     say("case: C3 full decode step (bench input set 0), oracle on sampled rows")
-    x = bench.InputSet(0, DEV)
-    bench.step(x)
-    torch.cuda.synchronize()
+    x = c3_step
     seed, C, S, W = 3000, bench.C, bench.SEQ, bench.W
     sample = [0, 45]
     ns = len(sample)
@@ -114,6 +174,47 @@ def test_c3_decode_step_sampled(orc):
                                   window_for(bench.LAYERS - 1), heads=bench.H, dim=bench.D, sm_scale=sm)
     say("  Reindex attention")
     check_attn(x.out[bench.LAYERS - 1][sample].float().cpu().numpy(), out7)
+
+
+def test_c3_decode_step_every_row(orc, c3_step):
+    """Every row of every layer of the decode step.  Selections: the source layer's pools and
+    index sets, and each Reindex layer's index set, equal their definitions evaluated on the
+    host over the device's own scores (full-range scores from the step; pool scores from the
+    scoring call, bit-exact to the oracle on the sampled rows above).  Attention: all 64 rows
+    of all 8 layers against the oracle, each row's selected main-KV rows gathered into a
+    compact cache (attention depends on the selected rows only), the FP8 window regenerated
+    and quantized by the oracle."""
+    import bench
+    say("case: C3 full decode step, every row of every layer")
+    x = c3_step
+    seed, C, S, W, K, NB, BLK, n = 3000, bench.C, bench.SEQ, bench.W, bench.K, bench.NB, bench.BLK, bench.NREQ
+    R = min(S // bench.M, C)
+    # source layer: block maxima, the pool (NB - 1 best non-newest blocks plus the newest), top-K
+    pb, pn = x.pool_blocks.cpu().numpy(), x.pool_n.cpu().numpy()
+    check_hier_by_definition(x.scores_full.cpu().numpy(), [R] * n, pb, pn, x.idx[0].cpu().numpy(), K, NB, BLK)
+    say("  source pools and index sets: %d rows" % n)
+    # Reindex layers: top-K over the pool positions by the pool scores
+    for l in range(1, bench.LAYERS):
+        L = x.layers[l]
+        sp = B.index_score(x.rows, x.cache, L["qi"], L["w"], x.keys, pool=x.pool,
+                           scores=torch.full_like(x.scores_pool, float("nan"))).cpu().numpy()
+        got = x.idx[l].cpu().numpy()
+        for r in range(n):
+            cols = np.arange(pn[r] * BLK)
+            posn = pb[r, cols // BLK] * BLK + cols % BLK
+            ok = posn < R
+            assert np.array_equal(got[r], top_positions(order_keys(sp[r, cols[ok]]), posn[ok], K)), (l, r)
+    say("  Reindex index sets: %d layers x %d rows" % (bench.LAYERS - 1, n))
+    # attention of every row and layer, over a compact cache of the selected rows
+    for l in range(bench.LAYERS):
+        raw = synth.normal((n * W, bench.D), seed, "swa/%d" % l, device=DEV).cpu().numpy()
+        codes, scales, wo = oracle_window(orc, raw, n, [S - W] * n, W)
+        wd = x.layers[l]["window"]
+        assert np.array_equal(codes, wd.data.cpu().numpy()) and np.array_equal(scales, wd.scale.cpu().numpy())
+        out_o = check_attn_compact(orc, x.kv, x.cache.row_start, x.idx[l], x.layers[l]["q"], wo, [S - 1] * n, bench.M,
+                                   bench.H, bench.D)
+        check_attn(x.out[l].float().cpu().numpy(), out_o)
+    say("  attention: %d layers x %d rows" % (bench.LAYERS, n))
 
 
 # ------------------------------------------------------------------------- C1
@@ -287,7 +388,9 @@ def test_c2_replay_flow_sampled(orc):
 @pytest.mark.parametrize("nreq", [1, 32])
 def test_c4_long_decode_sampled(orc, nreq):
     """C4 long-context decode (S=524288, m=2: 262144 reachable entries per row): full
-    scan, hierarchical selection and attention for every row; one row checked."""
+    scan, hierarchical selection and attention for every row; one row checked against the
+    oracle end to end, every row's selection by its definition over the device scores and
+    every row's attention against the oracle."""
     cfg = synth.config(4, nreq=nreq)
     g = cfg.geom
     say("case: %s" % cfg.name)
@@ -345,3 +448,13 @@ def test_c4_long_decode_sampled(orc, nreq):
                                    heads=cfg.heads, dim=cfg.dim, sm_scale=synth.sm_scale(cfg.dim))
     say("  attention")
     check_attn(out[i:i + 1].float().cpu().numpy(), out_o)
+    # every row: selection by its definition over the device scores, attention over a
+    # compact cache of its selected rows
+    check_hier_by_definition(scores.cpu().numpy(), [C] * nreq, pb.cpu().numpy(), pn.cpu().numpy(),
+                             idx.cpu().numpy(), cfg.topk, cfg.max_blocks, cfg.block)
+    say("  every row's selection")
+    codes, scales, wo = oracle_window(orc, swa_raw.cpu().numpy(), nreq, [S - W] * nreq, W)
+    assert np.array_equal(codes, scd.cpu().numpy()) and np.array_equal(scales, ssd.cpu().numpy())
+    out_all = check_attn_compact(orc, kv, cd.row_start, idx, q, wo, [S - 1] * nreq, 2, cfg.heads, cfg.dim)
+    check_attn(out.float().cpu().numpy(), out_all)
+    say("  every row's attention")
