@@ -219,12 +219,13 @@ def test_c3_decode_step_every_row(orc, c3_step):
 
 # ------------------------------------------------------------------------- C1
 def test_c1_prefill_sampled(orc):
-    """C1 Full-layer prefill (m=1, 8192-token requests, top-512, fp8 window) on its
-    first two requests: scores, flat top-512 and attention for every row on the GPU,
-    sampled rows checked."""
-    cfg = synth.config(1, nreq=2)
+    """C1 Full-layer prefill (m=1, 8 requests of 8192 tokens, top-512, fp8 window): scores,
+    flat top-512 and attention for every row on the GPU; sampled rows of every request
+    checked against the oracle, and every row's top-512 against its definition over the
+    device's scores."""
+    cfg = synth.config(1)
     g = cfg.geom
-    say("case: %s (2 of 8 requests, every row on the GPU)" % cfg.name)
+    say("case: %s (every row on the GPU)" % cfg.name)
     rows = synth.prefill_rows(g)
     n = rows["req_of_row"].numel()
     cache = dict(ratio_m=1, n_entries=np.array(g.n_entries), row_start=np.array(g.row_start))
@@ -245,11 +246,28 @@ def test_c1_prefill_sampled(orc):
     out = B.sparse_swa_attn(rd, cd, q, kv, idx, wd, synth.sm_scale(cfg.dim))
     torch.cuda.synchronize()
 
-    rng = np.random.default_rng(11)
+    # every row: the top-512 by (score desc, position asc) among the reachable positions,
+    # evaluated with a composite key (order key, then the complement of the position)
     S = g.seq_len[0]
+    with torch.no_grad():
+        for r0 in range(0, n, 8192):
+            sc = scores[r0:r0 + 8192]
+            b = sc.view(torch.int32).to(torch.int64) & 0xFFFFFFFF
+            key = torch.where(b >= 0x80000000, 0xFFFFFFFF - b, b | 0x80000000)
+            col = torch.arange(S, device=DEV, dtype=torch.int64)
+            comp = key * 8192 + (8191 - col)
+            reach = (rd.pos_of_row[r0:r0 + 8192].to(torch.int64) + 1)[:, None]
+            comp = torch.where(col[None, :] < reach, comp, torch.full_like(comp, -1))
+            top = torch.topk(comp, cfg.topk, dim=1).values
+            want = torch.where(top >= 0, 8191 - (top % 8192), torch.full_like(top, 1 << 40))
+            want = torch.sort(want, dim=1).values
+            want = torch.where(want == (1 << 40), torch.full_like(want, -1), want)
+            assert torch.equal(want.to(torch.int32), idx[r0:r0 + 8192]), r0
+    say("  every row's top-512")
+    rng = np.random.default_rng(11)
     sample = []
     for r in range(g.nreq):
-        pos = {0, 1, 126, 127, 128, 129, 510, 511, 512, S - 1} | set(rng.choice(S, size=4, replace=False).tolist())
+        pos = {0, 1, 127, 128, 511, 512, S - 1} | set(rng.choice(S, size=2, replace=False).tolist())
         sample += [r * S + p for p in sorted(pos)]
     req = rows["req_of_row"].numpy()[sample]
     pos = rows["pos_of_row"].numpy()[sample]
