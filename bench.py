@@ -508,7 +508,7 @@ def _time_graph(fn, steps: int, warmup: int, per: int) -> float:
 def c2_replay(steps: int, warmup: int, dev) -> dict:
     """C2 decoder bounded replay: 8 requests of S = 8192 (m = 1) with extends
     8192, 8192, 4096, 4096, 2048, 512, 128, 64.  A Full layer scores every extend row
-    (27,332 rows) and selects top-512 plus pools; the tail layout keeps each request's last
+    (27,328 rows) and selects top-512 plus pools; the tail layout keeps each request's last
     min(128, E) rows (960); a Reindex layer rescored over the source pools (through the
     tail -> extend row map) with its own top-512 and attention; a Reuse layer attending to
     the source layer's top-512 through the same map.  Each stage timed by graph replay."""
@@ -609,7 +609,7 @@ def c2_replay(steps: int, warmup: int, dev) -> dict:
             two_launch[name]["alg_GBs"] = round(nbytes[name] / (us * 1e-6) / 1e9, 1)
     two_launch["us_total"] = round(sum(v["us_per_launch"] for v in two_launch.values()), 2)
     att = stages["attn_reindex"]
-    return {"measurement": "C2 decoder bounded replay: Full layer over 27,332 extend rows, 960 tail rows through "
+    return {"measurement": "C2 decoder bounded replay: Full layer over 27,328 extend rows, 960 tail rows through "
                            "Reindex and Reuse (8 requests, S=8192, m=1, top-512, pools of 2048 blocks of 8)",
             "us_per_flow": round(total, 2), "stages": stages, "reindex_two_launch": two_launch,
             "attn_roofline": {"bound": "hbm", "achieved": att["alg_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -308,7 +308,7 @@ static size_t plan_workspace(const Plan& p, int n, int k)
 // with small workgroups: a workgroup's passes are a chain of barriers whose cost grows
 // with its wave count, and more of them fit on a CU, so rows per second rise.  Slices
 // of up to 4096 candidates take 256 threads; 8192 take 512 threads of 16 (32 per thread
-// on 256 threads needs 170 VGPRs, two workgroups per CU: 27,332 rows of 8192 took 686
+// on 256 threads needs 170 VGPRs, two workgroups per CU: 27,328 rows of 8192 took 686
 // against 518 us).  Few rows (a decode batch) keep 1024 threads, which finish one row
 // sooner.  The selection is exact either way.
 constexpr int kManyRows = 1024;

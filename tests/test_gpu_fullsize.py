@@ -7,10 +7,10 @@ oracle, row by row: index scores and index sets bit for bit, attention outputs w
 |g - r| <= 2e-2 + 1e-2 |r| and a per-row relative L2 error <= 1e-2.  Sampled rows
 include the boundary positions (0, 126..129, 510..512, S - 1).  Every oracle input is
 regenerated from the seeded generator and quantized by the oracle's own quantizer; its
-bytes are checked against the library's before use.  For the decode workloads (C3, C4)
-every row is checked as well: each row's selection against its definition evaluated on
-the host over the device's scores, and each row's attention against the oracle over a
-compact cache of the rows it selected."""
+bytes are checked against the library's before use.  Every row is checked as well: each
+row's selection against its definition evaluated over the device's scores (C1, C2, C3,
+C4), and each row's attention against the oracle over a compact cache of the rows it
+selected (C2's tail rows, C3, C4)."""
 import math
 
 import numpy as np
@@ -85,19 +85,43 @@ def check_hier_by_definition(scores, reach, pb, pn, idx, k, nb, blk):
         assert np.array_equal(idx[r, :len(want)], want) and np.all(idx[r, len(want):] == -1), r
 
 
-def check_attn_compact(orc, kv, row_start, sel, q, wo, pos, ratio_m, heads, dim):
+def check_attn_compact(orc, kv, kv_base, sel, q, wo, pos, ratio_m, heads, dim, win_lo=None):
     """Attention of every row against the oracle over a compact cache: row r's selected
-    main-KV rows (kv[row_start[r] + sel[r, i]]) gathered to rows r * k + i.  sel must hold
-    no -1 slots (every row reaches more than k entries)."""
+    main-KV rows (kv[kv_base[r] + sel[r, i]]) gathered to rows r * k + i (-1 slots stay
+    -1), row r being request r of the compact cache (so `wo` gives each row's window by
+    row: row_start / pos_start indexed by the row's own request)."""
     n, k = sel.shape
-    assert bool((sel >= 0).all())
-    kv_c = bits(kv[(row_start.to(torch.int64)[:, None] + sel.to(torch.int64)).reshape(-1)])
+    valid = sel >= 0
+    src = kv_base.to(torch.int64)[:, None] + torch.where(valid, sel, torch.zeros_like(sel)).to(torch.int64)
+    kv_c = bits(kv[src.reshape(-1)])
     rows_o = dict(req_of_row=np.arange(n), pos_of_row=np.asarray(pos))
+    if win_lo is not None:
+        rows_o["win_lo"] = np.asarray(win_lo)
     cache_o = dict(ratio_m=ratio_m, n_entries=np.full(n, k), row_start=np.arange(n, dtype=np.int64) * k)
-    sel_o = np.tile(np.arange(k, dtype=np.int32), (n, 1))
+    sel_o = np.where(valid.cpu().numpy(), np.arange(k, dtype=np.int32)[None, :], -1).astype(np.int32)
     out_o, _ = orc.sparse_swa_attn(rows_o, cache_o, bits(q), 1, kv_c, 1, sel_o, wo, heads=heads, dim=dim,
                                    sm_scale=synth.sm_scale(dim))
     return out_o
+
+
+def check_flat_topk_torch(scores, reach, idx, k):
+    """Every row's flat top-k (score desc, position asc, among positions below its reach),
+    ascending and -1 padded, evaluated on the device with a composite key (the selection's
+    order key, then the complement of the position) in chunks of rows."""
+    n, cols = scores.shape
+    col = torch.arange(cols, device=scores.device, dtype=torch.int64)
+    with torch.no_grad():
+        for r0 in range(0, n, 4096):
+            b = scores[r0:r0 + 4096].contiguous().view(torch.int32).to(torch.int64) & 0xFFFFFFFF
+            key = torch.where(b >= 0x80000000, 0xFFFFFFFF - b, b | 0x80000000)
+            comp = key * cols + (cols - 1 - col)
+            comp = torch.where(col[None, :] < reach[r0:r0 + 4096, None], comp, torch.full_like(comp, -1))
+            top = torch.topk(comp, k, dim=1).values
+            big = 1 << 40
+            want = torch.where(top >= 0, cols - 1 - (top % cols), torch.full_like(top, big))
+            want = torch.sort(want, dim=1).values
+            want = torch.where(want == big, torch.full_like(want, -1), want)
+            assert torch.equal(want.to(torch.int32), idx[r0:r0 + 4096]), r0
 
 
 def test_c3_decode_step_sampled(orc, c3_step):
@@ -246,23 +270,9 @@ def test_c1_prefill_sampled(orc):
     out = B.sparse_swa_attn(rd, cd, q, kv, idx, wd, synth.sm_scale(cfg.dim))
     torch.cuda.synchronize()
 
-    # every row: the top-512 by (score desc, position asc) among the reachable positions,
-    # evaluated with a composite key (order key, then the complement of the position)
+    # every row: the top-512 by its definition over the device's scores
     S = g.seq_len[0]
-    with torch.no_grad():
-        for r0 in range(0, n, 8192):
-            sc = scores[r0:r0 + 8192]
-            b = sc.view(torch.int32).to(torch.int64) & 0xFFFFFFFF
-            key = torch.where(b >= 0x80000000, 0xFFFFFFFF - b, b | 0x80000000)
-            col = torch.arange(S, device=DEV, dtype=torch.int64)
-            comp = key * 8192 + (8191 - col)
-            reach = (rd.pos_of_row[r0:r0 + 8192].to(torch.int64) + 1)[:, None]
-            comp = torch.where(col[None, :] < reach, comp, torch.full_like(comp, -1))
-            top = torch.topk(comp, cfg.topk, dim=1).values
-            want = torch.where(top >= 0, 8191 - (top % 8192), torch.full_like(top, 1 << 40))
-            want = torch.sort(want, dim=1).values
-            want = torch.where(want == (1 << 40), torch.full_like(want, -1), want)
-            assert torch.equal(want.to(torch.int32), idx[r0:r0 + 8192]), r0
+    check_flat_topk_torch(scores, rd.pos_of_row.to(torch.int64) + 1, idx, cfg.topk)
     say("  every row's top-512")
     rng = np.random.default_rng(11)
     sample = []
@@ -400,6 +410,40 @@ def test_c2_replay_flow_sampled(orc):
                                        dim=cfg.dim, sm_scale=synth.sm_scale(cfg.dim))
         say("  %s attention" % layer)
         check_attn(out[sample].float().cpu().numpy(), out_o)
+
+    # every row.  Source layer: 8192 positions are 1024 blocks of 8, within the 2048 a pool
+    # holds, so every pool is all blocks of its row and the index set is the flat top-512.
+    reach_s = torch.minimum(re_d.pos_of_row.to(torch.int64) + 1, torch.tensor(C, device=DEV))
+    check_flat_topk_torch(sc_s, reach_s, idx_s, cfg.topk)
+    nblk = (reach_s + cfg.block - 1) // cfg.block
+    assert torch.equal(pn.to(torch.int64), nblk)
+    ar = torch.arange(cfg.max_blocks, device=DEV, dtype=torch.int64)[None, :]
+    assert torch.equal(pb.to(torch.int64), torch.where(ar < nblk[:, None], ar, torch.full_like(ar, -1)))
+    say("  every source row's pool and top-512 (%d rows)" % n_ext)
+    # Reindex: every tail row's top-512 over its pool by the pool scores
+    sct, pbn, pnn, it = sc_t.cpu().numpy(), pb.cpu().numpy(), pn.cpu().numpy(), idx_t.cpu().numpy()
+    srcs = t_o["src_row"]
+    for i in range(nt):
+        p_r, R = srcs[i], min(int(t_o["abs_pos"][i]) + 1, C)
+        cols = np.arange(pnn[p_r] * cfg.block)
+        posn = pbn[p_r, cols // cfg.block] * cfg.block + cols % cfg.block
+        ok = posn < R
+        want = top_positions(order_keys(sct[i, cols[ok]]), posn[ok], cfg.topk)
+        assert np.array_equal(it[i, :len(want)], want) and np.all(it[i, len(want):] == -1), i
+    say("  every tail row's Reindex top-512 (%d rows)" % nt)
+    # attention of every tail row in both layers, over compact caches
+    kv_base = cd.row_start.to(torch.int64)[t["req_of_row"][:nt].to(torch.int64)]
+    req_t = t_o["req_of_row"]
+    for layer, sel in (("reindex", idx_t), ("reuse", idx_s[src_map.to(torch.int64)])):
+        raw, scd_l, ssd_l = windows[layer]
+        codes, scales = orc.mx_quant(orc.E4M3, raw)
+        wo_rows = dict(data=codes, dtype=3, scale=scales, row_start=win["row_start"].numpy()[req_t],
+                       pos_start=win["pos_start"].numpy()[req_t], window=128)
+        q, out = outs[layer]
+        out_o = check_attn_compact(orc, kv, kv_base, sel, q, wo_rows, t_o["abs_pos"], 1, cfg.heads, cfg.dim,
+                                   win_lo=t_o["win_lo"])
+        check_attn(out.float().cpu().numpy(), out_o)
+        say("  every tail row's %s attention (%d rows)" % (layer, nt))
 
 
 # ------------------------------------------------------------------------- C4
