@@ -86,13 +86,15 @@ def test_fused_equals_two_launches_and_oracle(orc, H, k):
     assert np.array_equal(fused[sample], i_o)
 
 
-@pytest.mark.parametrize("H,k,map_rows", [(64, 512, False), (16, 2048, True), (32, 1, False)])
-def test_fused_whole_pools(orc, H, k, map_rows):
+@pytest.mark.parametrize("H,k,map_rows,nb_max", [(64, 512, False, 2048), (16, 2048, True, 2048), (32, 1, False, 2048),
+                                                  (64, 128, True, 64), (64, 512, False, 1000)])
+def test_fused_whole_pools(orc, H, k, map_rows, nb_max):
     """Launches over 128 rows or more score and select each row's whole pool in one
-    workgroup (no list merge): the same index sets as the two launches and the oracle."""
-    say("case: fused pool top-k over 160 rows (whole pools) H=%d k=%d map=%s" % (H, k, map_rows))
+    workgroup (no list merge): the same index sets as the two launches and the oracle,
+    for full and small pools."""
+    say("case: fused pool top-k over 160 rows (whole pools) H=%d k=%d map=%s max_blocks=%d" % (H, k, map_rows, nb_max))
     R_list = [16390, 3000, 2049, 100, 8, 1, 0, 5000] * 20
-    rows, cache, keys, qi, w, pool, C = _case(330 + H + k, R_list, H, map_rows=map_rows)
+    rows, cache, keys, qi, w, pool, C = _case(330 + H + k + nb_max, R_list, H, nb_max=nb_max, map_rows=map_rows)
     fused, two, sc = _both(rows, cache, keys, qi, w, pool, k)
     assert not np.any(fused == POISON_I32)
     assert np.array_equal(fused, two)
