@@ -231,10 +231,11 @@ def measured_traffic(stage: str):
     return None
 
 
-# The 7 Reindex launches of a step rescore the same 71 MB of pool keys, which the 256 MiB
-# last-level cache holds: their rate is cache-served, not HBM bandwidth.
-STAGE_NOTES = {"reindex": {"served_from": "last-level cache (pool keys reread by 7 launches)"},
-               "score_pool": {"served_from": "last-level cache (pool keys reread by 7 launches)"},
+# The 7 Reindex launches of a step rescore the same 71 MB of pool keys, which fit the 256
+# MiB last-level cache; the counters (FETCH_SIZE) show what leaves L2, not whether the
+# last-level cache or HBM answers, so these rates are not quoted as HBM bandwidth.
+STAGE_NOTES = {"reindex": {"served_from": "HBM or last-level cache (pool keys reread by 7 launches)"},
+               "score_pool": {"served_from": "HBM or last-level cache (pool keys reread by 7 launches)"},
                "topk_pool": {"served_from": "L2 / last-level cache (scores written by the previous launch)"}}
 
 STAGE_KERNEL = {"score_full": "k_score_mxfp4", "topk_hier": "k_block_max + k_select (2 launches)",
