@@ -243,6 +243,33 @@ __global__ __launch_bounds__(kFusedNT) void k_score_topk_pool(RowsArg rows, Cach
                                                (int64_t)kFusedKPT * tid, key, bid, true);
 }
 
+// The exact merge of a decode batch's segment lists (each segment's top-k as (key, position)
+// pairs, at most 2,048 candidates per row): the selection of csa2_topk's list merge, built in
+// this file so that it shares its scheduling.  One 512-thread workgroup per row, 4 candidates
+// per thread, the row's workgroup on the XCD of its segments.
+constexpr int kMergeNT = 512, kMergeKPT = 4;
+
+__global__ __launch_bounds__(kMergeNT) void k_merge_segment_lists(SelArgs a)
+{
+    int row, seg;
+    xcd_row_chunk(blockIdx.x, a.src.rows.n, 1, &row, &seg);
+    int64_t R, ncol;
+    int prow;
+    row_info(a.src, row, &R, &ncol, &prow);
+    const int64_t e0 = (int64_t)threadIdx.x * kMergeKPT;
+    const int64_t lim = (int64_t)a.nlists_prev * a.k;
+    const uint2* in = a.in + (int64_t)row * lim;
+    uint32_t v[kMergeKPT], key[kMergeKPT];
+#pragma unroll
+    for (int i = 0; i < kMergeKPT; i++) v[i] = in[e0 + i < lim ? e0 + i : 0].x;
+#pragma unroll
+    for (int i = 0; i < kMergeKPT; i++) pin(v[i]);
+#pragma unroll
+    for (int i = 0; i < kMergeKPT; i++) key[i] = e0 + i < lim ? v[i] : 0u;
+    int32_t bid[bid_slots(kMergeKPT)] = {0};
+    select_core<kMergeKPT, SRC_LIST, kMergeNT>(a, row, 0, R, ncol, prow, 0, e0, key, bid, false);
+}
+
 // Rows from which a launch takes whole pools.  One workgroup then scores a row's whole
 // pool on one CU, so with fewer rows most CUs would idle; from half the CU count on, the
 // saved list merge (a second launch) outweighs that (measured: 128 rows of 8,192 pool
@@ -296,7 +323,19 @@ hipError_t launch_score_topk_pool(const RowsArg& rows, const CacheArg& cache, co
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || nseg == 1) return e;
     SelSource src{nullptr, cols, rows, cache, pool};
-    return launch_list_merge(src, k, nseg, lists, out_idx, stream);
+    if ((int64_t)nseg * k > (int64_t)kMergeNT * kMergeKPT) return launch_list_merge(src, k, nseg, lists, out_idx, stream);
+    SelArgs a{};
+    a.src = src;
+    a.k = k;
+    a.nseg = 1;
+    a.seg_len = nseg;
+    a.nlists_prev = nseg;
+    a.in = lists;
+    a.out_idx = out_idx;
+    a.out_stride = k;
+    a.out_mode = OUT_IDX;
+    hipLaunchKernelGGL(k_merge_segment_lists, dim3((unsigned)rows.n), dim3(kMergeNT), 0, stream, a);
+    return hipGetLastError();
 }
 
 }  // namespace csa2
