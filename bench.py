@@ -239,7 +239,7 @@ STAGE_NOTES = {"reindex": {"served_from": "HBM or last-level cache (pool keys re
                "topk_pool": {"served_from": "L2 / last-level cache (scores written by the previous launch)"}}
 
 STAGE_KERNEL = {"score_full": "k_score_mxfp4", "topk_hier": "k_block_max + k_select (2 launches)",
-                "attn": "k_attn_bf16", "reindex": "k_score_topk_pool + k_select (list merge)",
+                "attn": "k_attn_bf16", "reindex": "k_score_topk_pool + k_merge_segment_lists",
                 "score_pool": "k_score_mxfp4 (pool)", "topk_pool": "k_select"}
 
 
