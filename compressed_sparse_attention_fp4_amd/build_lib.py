@@ -37,12 +37,12 @@ COMMON = [
 ]
 
 
-# Per-source flags.  The index-score kernel consumes every MFMA result with VALU
-# arithmetic at once, so its MFMAs write VGPRs (no AGPR round trip).  The fused pool
-# scoring + top-k schedules for instruction-level parallelism (its launches 1.5-2% faster;
-# the attention and full-range scoring kernels were slower or unchanged under it).
+# Per-source flags.  The index-score kernels consume every MFMA result with VALU
+# arithmetic at once, so their MFMAs write VGPRs (no AGPR round trip).  The fused pool
+# scoring + top-k also schedules for instruction-level parallelism (its launches 1.5-2%
+# faster; the attention and full-range scoring kernels were slower or unchanged under it).
 EXTRA = {"k_score.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-         "k_fused.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+         "k_fused.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:
