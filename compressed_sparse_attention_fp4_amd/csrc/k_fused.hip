@@ -50,6 +50,8 @@ __global__ __launch_bounds__(kFusedNT) void k_score_topk_pool(RowsArg rows, Cach
     constexpr int G = H / 4;
     constexpr int NW = kFusedNT / 64;
     constexpr int kFusedCap = kFusedNT * kFusedKPT;
+    // the selection takes each thread's pool block ids from its own slots of s_bid
+    static_assert(kFusedKPT % 8 == 0, "each thread holds whole pool blocks of 8 candidates");
     __shared__ uint4 s_qa[NHT][64];
     __shared__ uint32_t s_qs[NHT][64];
     __shared__ int32_t s_bid[kFusedCap / 8];
