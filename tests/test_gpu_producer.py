@@ -129,6 +129,39 @@ def test_kv_produce_decode_steps_equal_one_call(orc):
             assert torch.equal(a.view(torch.uint8) if a.dtype != torch.uint8 else a, b.view(torch.uint8) if b.dtype != torch.uint8 else b)
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_kv_produce_random_call_splits(orc, seed):
+    """Each request's tokens cut at random points into several calls (chunked prefill
+    followed by shorter extends, pairs left open across calls): the caches and the
+    pending state after the last call equal the oracle's single call, byte for byte."""
+    rng = np.random.default_rng(4800 + seed)
+    nreq = int(rng.integers(1, 6))
+    lens = [int(rng.integers(1, 400)) for _ in range(nreq)]
+    prefix = [int(rng.integers(0, 3000)) for _ in range(nreq)]
+    m = int(rng.choice([1, 2]))
+    fp4 = bool(rng.random() < 0.5)
+    ncalls = int(rng.integers(2, 6))
+    say("case: kv producer, random call splits seed=%d m=%d fp4=%s calls=%d lens=%s prefix=%s" %
+        (seed, m, fp4, ncalls, lens, prefix))
+    st = _Stream(4900 + seed, lens, prefix, m)
+    o = orc.kv_produce(st.rows(), m, st.row_start, st.rows_cache, st.comp.numpy(), st.pending.numpy(), bits(st.wb),
+                       st.rope, kv_dt=orc.DT_FP4S16 if fp4 else orc.DT_BF16, fill=FILL)
+    caches = _dev_caches(st.rows_cache, fp4)
+    pend = st.pending.clone().to(DEV)
+    starts = np.cumsum([0] + lens[:-1])
+    cuts = [[0] + sorted(rng.integers(0, L + 1, size=ncalls - 1).tolist()) + [L] for L in lens]
+    for c in range(ncalls):
+        sel = [i for r in range(nreq) for i in range(starts[r] + cuts[r][c], starts[r] + cuts[r][c + 1])]
+        if sel:
+            _run_dev(st, np.array(sel, dtype=np.int64), pend if m == 2 else None, caches)
+    _compare(caches, o, fp4)
+    if m == 2:
+        # a request whose stream ends at an even position leaves that token pending; one
+        # that ends on a closed pair keeps whatever its last open pair left (not compared)
+        open_pair = [r for r in range(nreq) if (prefix[r] + lens[r] - 1) % 2 == 0]
+        assert np.array_equal(pend.cpu().numpy()[open_pair], o["pending"][open_pair]), "pending state"
+
+
 def test_produced_caches_feed_a_full_layer(orc):
     """The producer fills an owner's caches (m = 2, FP4 main KV) over a 2000-token prefill
     of two requests; a Full layer (scores, hierarchical top-k, attention over FP4 entries)
