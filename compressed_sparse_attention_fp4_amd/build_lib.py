@@ -38,10 +38,11 @@ COMMON = [
 
 
 # Per-source flags.  The index-score kernels consume every MFMA result with VALU
-# arithmetic at once, so their MFMAs write VGPRs (no AGPR round trip).  The fused pool
-# scoring + top-k also schedules for instruction-level parallelism (its launches 1.5-2%
-# faster; the attention and full-range scoring kernels were slower or unchanged under it).
-EXTRA = {"k_score.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+# arithmetic at once, so their MFMAs write VGPRs (no AGPR round trip).  They also schedule
+# for instruction-level parallelism: the fused pool scoring + top-k 1.5-2% faster, prefill
+# scoring (row pairs) 1.5-2% faster, decode scoring unchanged; the attention kernel was
+# slower under it.
+EXTRA = {"k_score.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-mllvm", "-amdgpu-sched-strategy=max-ilp"],
          "k_fused.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
