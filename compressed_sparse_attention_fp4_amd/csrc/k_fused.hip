@@ -255,9 +255,10 @@ __global__ __launch_bounds__(kMergeNT) void k_merge_segment_lists(SelArgs a)
 {
     int row, seg;
     xcd_row_chunk(blockIdx.x, a.src.rows.n, 1, &row, &seg);
-    int64_t R, ncol;
-    int prow;
-    row_info(a.src, row, &R, &ncol, &prow);
+    // list entries carry their positions and index outputs need neither the reach nor the
+    // pool row, so no row metadata is loaded before the lists
+    const int64_t R = 0, ncol = 0;
+    const int prow = row;
     const int64_t e0 = (int64_t)threadIdx.x * kMergeKPT;
     const int64_t lim = (int64_t)a.nlists_prev * a.k;
     const uint2* in = a.in + (int64_t)row * lim;

@@ -226,9 +226,12 @@ __global__ __launch_bounds__(NT) void k_select(SelArgs a)
     const int tid = threadIdx.x;
     const SelSource& s = a.src;
 
-    int64_t R, ncol;
-    int prow;
-    row_info(s, row, &R, &ncol, &prow);
+    int64_t R = 0, ncol = 0;
+    int prow = row;
+    // a merge level's entries carry their positions: only a level that writes a pool
+    // (whose newest block follows from the row's columns) needs the row metadata, and no
+    // other waits for it before its loads
+    if (SRC != SRC_LIST || a.out_mode == OUT_BLOCKS) row_info(s, row, &R, &ncol, &prow);
     const int64_t base = (int64_t)seg * (SRC == SRC_LIST ? a.seg_len * a.k : a.seg_len);
     const int64_t e0 = (int64_t)tid * KPT;  // blocked: thread t owns [t*KPT, (t+1)*KPT)
 
