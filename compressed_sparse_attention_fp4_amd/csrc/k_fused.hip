@@ -61,10 +61,13 @@ __global__ __launch_bounds__(kFusedNT) void k_score_topk_pool(RowsArg rows, Cach
     xcd_row_chunk(blockIdx.x, rows.n, nseg, &row, &seg);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // The pool row's block count and block ids are read beside the row's request lookups,
+    // not after them (a row without reach ignores them; its pool row is valid all the same).
+    const int prow = pool.row_map ? pool.row_map[row] : row;
+    const int nb_pool = pool.nblocks[prow];
     const int r = rows.req[row];
     const int64_t R = reach(rows.pos[row], cache.ratio_m, cache.n_entries[r]);
-    const int prow = pool.row_map ? pool.row_map[row] : row;
-    const int nb_row = R > 0 ? pool.nblocks[prow] : 0;  // <= max_blocks <= 2048 (host-checked)
+    const int nb_row = R > 0 ? nb_pool : 0;  // <= max_blocks <= 2048 (host-checked)
     const int ncol_row = nb_row * 8;
     const int c_begin = seg * kFusedCap;            // the segment's first pool column
     const int nb0 = c_begin / 8;                    // and block
@@ -104,7 +107,11 @@ __global__ __launch_bounds__(kFusedNT) void k_score_topk_pool(RowsArg rows, Cach
     }
     {
         const int32_t* bid_row = pool.blocks + (int64_t)prow * pool.max_blocks + nb0;
-        for (int i = tid; i < kFusedCap / 8; i += kFusedNT) s_bid[i] = i < nbs ? bid_row[i] : 0;
+        const int nslot = pool.max_blocks - nb0;  // slots of the pool row from the segment on (> 0)
+        for (int i = tid; i < kFusedCap / 8; i += kFusedNT) {
+            const int32_t b = bid_row[i < nslot ? i : 0];
+            s_bid[i] = i < nbs ? b : 0;
+        }
     }
     const int g = lane >> 4;
     float wr[NHT * 4];
