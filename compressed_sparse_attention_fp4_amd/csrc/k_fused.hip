@@ -254,9 +254,10 @@ __global__ __launch_bounds__(kFusedNT) void k_score_topk_pool(RowsArg rows, Cach
 
 // The exact merge of a decode batch's segment lists (each segment's top-k as (key, position)
 // pairs, at most 2,048 candidates per row): the selection of csa2_topk's list merge, built in
-// this file so that it shares its scheduling.  One 512-thread workgroup per row, 4 candidates
-// per thread, the row's workgroup on the XCD of its segments.
-constexpr int kMergeNT = 512, kMergeKPT = 4;
+// this file so that it shares its scheduling.  One 1024-thread workgroup per row, 2
+// candidates per thread (slightly ahead of 512 threads of 4; 256 of 8 was behind), the
+// row's workgroup on the XCD of its segments.
+constexpr int kMergeNT = 1024, kMergeKPT = 2;
 
 __global__ __launch_bounds__(kMergeNT) void k_merge_segment_lists(SelArgs a)
 {
